@@ -1,0 +1,167 @@
+"""CPU oracle for windowed grouped-query attention (ctypes binding of ``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package; the product path (the HIP library and its binding) never does, and shares
+no code with it. Arrays are numpy, host memory; results are f32 computed in f64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_f32p = ctypes.POINTER(ctypes.c_float)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def compile_source(src: str, so: str) -> str:
+    """gcc -O2 -fopenmp (strict IEEE: no fast-math) of one C file into a shared library."""
+    tmp = so + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall",
+                           "-Wno-unknown-pragmas", "-Wno-maybe-uninitialized", src, "-o", tmp,
+                           "-lm"])
+    os.replace(tmp, so)
+    return so
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so next to its source."""
+    if force or not os.path.exists(_SO):
+        compile_source(_SRC, _SO)
+    return _SO
+
+
+def source_path() -> str:
+    return _SRC
+
+
+def load_library(path: str):
+    """A ctypes handle on a compiled oracle library with its signatures declared."""
+    lib = ctypes.CDLL(path)
+    i, f = ctypes.c_int, ctypes.c_float
+    lib.oracle_window_chunk.argtypes = [_f32p, _f32p, _u32p, _f32p, _f32p, _f32p, _f32p, _f32p,
+                                        _f32p, i, i, i, i, i, i, f]
+    lib.oracle_window_chunk_select.argtypes = [_f32p, _f32p, _u32p, _f32p, _f32p, _f32p,
+                                               _f32p, _f32p, i, i, i, i, i, i, f, _i32p,
+                                               _i32p, i, _f32p]
+    lib.oracle_window_chunk_weights.argtypes = [_f32p, _f32p, _u32p, _f32p, _f32p, _f32p,
+                                                _f32p, _f32p, i, i, i, i, i, i, f, i, i, _f64p]
+    lib.oracle_window_gated.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
+                                        _f32p, _f32p, _f32p, i, i, i, i, i, i, i, f, f]
+    lib.oracle_meta_ok.argtypes = [_u32p, i, i]
+    for name in ("oracle_window_chunk", "oracle_window_chunk_select",
+                 "oracle_window_chunk_weights", "oracle_window_gated", "oracle_meta_ok"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        _lib = load_library(_SO)
+    return _lib
+
+
+def use_library(lib) -> None:
+    """Route this module's calls through another compiled oracle (the mutation tests use it)."""
+    global _lib
+    _lib = lib
+
+
+def _f32(a):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a, a.ctypes.data_as(_f32p)
+
+
+def _opt_f32(a):
+    if a is None or a.size == 0:
+        return None, None
+    return _f32(a)
+
+
+def _chunk_ptrs(inp):
+    arrs = {}
+    arrs["rk"], prk = _f32(inp.ring_k)
+    arrs["rv"], prv = _f32(inp.ring_v)
+    arrs["meta"] = np.ascontiguousarray(inp.meta, dtype=np.uint32)
+    pm = arrs["meta"].ctypes.data_as(_u32p)
+    arrs["sk"], psk = _opt_f32(inp.sink_k)
+    arrs["sv"], psv = _opt_f32(inp.sink_v)
+    arrs["q"], pq = _f32(inp.q)
+    arrs["ck"], pck = _f32(inp.chunk_k)
+    arrs["cv"], pcv = _f32(inp.chunk_v)
+    return arrs, (prk, prv, pm, psk, psv, pq, pck, pcv)
+
+
+def window_chunk(inp) -> np.ndarray:
+    """out [rows][nh][d] for a ChunkInputs-like object."""
+    lib = _load()
+    keep, ptrs = _chunk_ptrs(inp)
+    out = np.zeros((inp.rows, inp.ng * inp.hpg, inp.d), dtype=np.float32)
+    rc = lib.oracle_window_chunk(*ptrs, out.ctypes.data_as(_f32p), inp.rows, inp.ng, inp.hpg,
+                                 inp.d, inp.w, inp.ns, inp.scale)
+    if rc != 0:
+        raise ValueError(f"oracle_window_chunk rejected its arguments (rc={rc})")
+    return out
+
+
+def window_chunk_select(inp, rows_sel, heads_sel) -> np.ndarray:
+    """out[k] = output vector of (rows_sel[k], heads_sel[k]); shape [len][d]."""
+    lib = _load()
+    keep, ptrs = _chunk_ptrs(inp)
+    rs = np.ascontiguousarray(rows_sel, dtype=np.int32)
+    hs = np.ascontiguousarray(heads_sel, dtype=np.int32)
+    out = np.zeros((rs.size, inp.d), dtype=np.float32)
+    rc = lib.oracle_window_chunk_select(*ptrs, inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns,
+                                        inp.scale, rs.ctypes.data_as(_i32p),
+                                        hs.ctypes.data_as(_i32p), rs.size,
+                                        out.ctypes.data_as(_f32p))
+    if rc != 0:
+        raise ValueError(f"oracle_window_chunk_select rejected its arguments (rc={rc})")
+    return out
+
+
+def window_chunk_weights(inp, row: int, gh: int) -> np.ndarray:
+    """Normalised weights of (row, gh) in key-list order: sinks, then window oldest->newest."""
+    lib = _load()
+    keep, ptrs = _chunk_ptrs(inp)
+    wts = np.zeros(inp.ns + inp.w, dtype=np.float64)
+    n = lib.oracle_window_chunk_weights(*ptrs, inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns,
+                                        inp.scale, row, gh, wts.ctypes.data_as(_f64p))
+    if n < 0:
+        raise ValueError("oracle_window_chunk_weights rejected its arguments")
+    return wts[:n].copy()
+
+
+def window_gated(inp):
+    """(z [rows][nh][hd], ring_k after, ring_v after) for a GatedInputs-like object."""
+    lib = _load()
+    rk = np.array(inp.ring_k, dtype=np.float32, copy=True, order="C")
+    rv = np.array(inp.ring_v, dtype=np.float32, copy=True, order="C")
+    keep = [_f32(a) for a in (inp.yq, inp.yk, inp.yv, inp.rope, inp.q_scale, inp.gate,
+                              inp.gate_scale)]
+    out = np.zeros((inp.rows, inp.nh, inp.hd), dtype=np.float32)
+    rc = lib.oracle_window_gated(*[p for _, p in keep], rk.ctypes.data_as(_f32p),
+                                 rv.ctypes.data_as(_f32p), out.ctypes.data_as(_f32p), inp.rows,
+                                 inp.pos0, inp.cap, inp.window, inp.nh, inp.nk, inp.hd, inp.scale,
+                                 inp.eps)
+    if rc != 0:
+        raise ValueError(f"oracle_window_gated rejected its arguments (rc={rc})")
+    return out, rk, rv
+
+
+def meta_ok(meta, ng: int, w: int) -> bool:
+    lib = _load()
+    m = np.ascontiguousarray(meta, dtype=np.uint32)
+    return bool(lib.oracle_meta_ok(m.ctypes.data_as(_u32p), ng, w))

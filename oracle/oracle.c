@@ -1,0 +1,290 @@
+/*
+ * CPU oracle for windowed grouped-query attention over a ring buffer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or load this file:
+ * only the tests, the smoke check and the benchmark's CPU-baseline leg use it. It shares no
+ * code, header or table with the HIP library.
+ *
+ * It is the plain definition, written out in double precision with a two-pass softmax and an
+ * explicit walk over each row's key list, rounding to f32 only where a value is stored
+ * (the output, the ring slots). Sources:
+ *
+ *  - o1c page ("A sealed layer's attention for a chunk of rows, on Metal", crate cortiq-engine
+ *    0.8.79): the layout header comment; `wgf` (per-group window override); `o1c_score` (a row's
+ *    window over the ring then the chunk's rows up to its own); `o1c_max`, `o1c_soft`, `o1c_sum`,
+ *    `o1c_add` (max, exp, 1/sum, value sum). The far-field landmark terms are taken with zero
+ *    landmarks, so the far mass and far numerators vanish and the near softmax is the result.
+ *  - dory page ("Dory's token path", crate cortiq-engine 0.8.57): `dory_prep` (rotation, unit
+ *    heads, query scale, ring write), `low_key`, `dory_score`, `dory_soft`, `dory_sum`, `dory_gate`.
+ *
+ * Readings where the pages leave a step open are listed in the design notes; the ones that
+ * matter here: a window of wg keys ends at and includes the row itself; the RoPE table is an
+ * input; eps is added to the sum of squares inside the square root; every row's prep and ring
+ * write happens before any row attends.
+ *
+ * Return codes: 0 on success, -1 on invalid arguments or meta.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Per-group window: a non-zero override in meta field 3 replaces the default w (`wgf`). */
+static uint32_t group_window(const uint32_t *meta, int g, int w) {
+    uint32_t ov = meta[4 * g + 3];
+    return ov != 0u ? ov : (uint32_t)w;
+}
+
+static int meta_ok(const uint32_t *meta, int ng, int w) {
+    for (int g = 0; g < ng; ++g) {
+        uint32_t wg = group_window(meta, g, w);
+        uint32_t len0 = meta[4 * g], head0 = meta[4 * g + 1];
+        if (wg > (uint32_t)w || len0 > wg) return 0;
+        if (len0 > 0 && head0 >= wg) return 0;
+    }
+    return 1;
+}
+
+/*
+ * Key list of chunk row i in group g, as pointers to K and V rows, in order: the ns sinks,
+ * then the window's logical entries oldest to newest. Logical entry x < len0 is ring entry x,
+ * stored at slot (head0 + x) mod wg of the group's ring (stride w); x >= len0 is chunk row
+ * x - len0. The window is the last min(wg, len0 + i + 1) entries up to and including row i
+ * (`o1c_score`). Returns the number of keys.
+ */
+static int key_list(const float *ring_k, const float *ring_v, const uint32_t *meta,
+                    const float *sink_k, const float *sink_v, const float *chunk_k,
+                    const float *chunk_v, int ng, int d, int w, int ns, int g, int i,
+                    const float **kp, const float **vp) {
+    uint32_t wg = group_window(meta, g, w);
+    uint32_t len0 = meta[4 * g], head0 = meta[4 * g + 1];
+    uint32_t end = len0 + (uint32_t)i + 1u;            /* one past the row's own entry */
+    uint32_t win = wg < end ? wg : end;
+    int n = 0;
+    for (int s = 0; s < ns; ++s) {
+        kp[n] = sink_k + ((size_t)g * ns + s) * d;
+        vp[n] = sink_v + ((size_t)g * ns + s) * d;
+        ++n;
+    }
+    for (uint32_t x = end - win; x < end; ++x) {
+        if (x < len0) {
+            size_t slot = (size_t)((head0 + x) % wg);
+            kp[n] = ring_k + ((size_t)g * w + slot) * d;
+            vp[n] = ring_v + ((size_t)g * w + slot) * d;
+        } else {
+            size_t row = (size_t)(x - len0);
+            kp[n] = chunk_k + (row * ng + g) * d;
+            vp[n] = chunk_v + (row * ng + g) * d;
+        }
+        ++n;
+    }
+    return n;
+}
+
+/*
+ * Exact softmax attention of one query over n keys, in double:
+ * s_j = scale * <q, K_j>; m = max s_j; p_j = exp(s_j - m); out = sum_j p_j V_j / sum_j p_j.
+ * `qd` is the query in double. `wts` (n doubles) receives the normalised weights if non-NULL.
+ */
+static void attend(const double *qd, const float *const *kp, const float *const *vp, int n,
+                   int d, double scale, double *sc, double *acc, double *wts) {
+    double m = -INFINITY;
+    for (int j = 0; j < n; ++j) {
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e) dot += qd[e] * (double)kp[j][e];
+        sc[j] = scale * dot;
+        if (sc[j] > m) m = sc[j];
+    }
+    double l = 0.0;
+    for (int j = 0; j < n; ++j) {
+        sc[j] = exp(sc[j] - m);
+        l += sc[j];
+    }
+    for (int e = 0; e < d; ++e) acc[e] = 0.0;
+    for (int j = 0; j < n; ++j)
+        for (int e = 0; e < d; ++e) acc[e] += sc[j] * (double)vp[j][e];
+    for (int e = 0; e < d; ++e) acc[e] /= l;
+    if (wts)
+        for (int j = 0; j < n; ++j) wts[j] = sc[j] / l;
+}
+
+static int chunk_args_ok(const float *ring_k, const float *ring_v, const uint32_t *meta,
+                         const float *sink_k, const float *sink_v, const float *q,
+                         const float *chunk_k, const float *chunk_v, int rows, int ng, int hpg,
+                         int d, int w, int ns) {
+    if (rows < 1 || ng < 1 || hpg < 1 || d < 1 || w < 1 || ns < 0) return 0;
+    if (!ring_k || !ring_v || !meta || !q || !chunk_k || !chunk_v) return 0;
+    if (ns > 0 && (!sink_k || !sink_v)) return 0;
+    return meta_ok(meta, ng, w);
+}
+
+/* One output vector: chunk row i, query head gh = g*hpg + h (heads of a group are contiguous). */
+static void chunk_one(const float *ring_k, const float *ring_v, const uint32_t *meta,
+                      const float *sink_k, const float *sink_v, const float *q,
+                      const float *chunk_k, const float *chunk_v, int ng, int hpg, int d, int w,
+                      int ns, double scale, int i, int gh, float *out_vec, double *wts,
+                      int *nkeys) {
+    int nh = ng * hpg, g = gh / hpg;
+    int cap = ns + w;
+    const float **kp = (const float **)malloc(sizeof(float *) * (size_t)cap);
+    const float **vp = (const float **)malloc(sizeof(float *) * (size_t)cap);
+    double *sc = (double *)malloc(sizeof(double) * (size_t)cap);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+    double *qd = (double *)calloc((size_t)d, sizeof(double));
+    int n = key_list(ring_k, ring_v, meta, sink_k, sink_v, chunk_k, chunk_v, ng, d, w, ns, g, i,
+                     kp, vp);
+    const float *qv = q + ((size_t)i * nh + gh) * d;
+    for (int e = 0; e < d; ++e) qd[e] = (double)qv[e];
+    attend(qd, kp, vp, n, d, scale, sc, acc, wts);
+    if (out_vec)
+        for (int e = 0; e < d; ++e) out_vec[e] = (float)acc[e];
+    if (nkeys) *nkeys = n;
+    free(kp); free(vp); free(sc); free(acc); free(qd);
+}
+
+/* The full chunk call: out[rows][nh][d]. Parallel over (row, query head). */
+int oracle_window_chunk(const float *ring_k, const float *ring_v, const uint32_t *meta,
+                        const float *sink_k, const float *sink_v, const float *q,
+                        const float *chunk_k, const float *chunk_v, float *out, int rows, int ng,
+                        int hpg, int d, int w, int ns, float scale) {
+    if (!chunk_args_ok(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v, rows, ng, hpg,
+                       d, w, ns) || !out)
+        return -1;
+    int nh = ng * hpg;
+    long total = (long)rows * nh;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long t = 0; t < total; ++t) {
+        int i = (int)(t / nh), gh = (int)(t % nh);
+        chunk_one(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v, ng, hpg, d, w, ns,
+                  (double)scale, i, gh, out + (size_t)t * d, NULL, NULL);
+    }
+    return 0;
+}
+
+/* Selected outputs only: out_sel[k][d] for (sel_rows[k], sel_heads[k]), k < nsel. */
+int oracle_window_chunk_select(const float *ring_k, const float *ring_v, const uint32_t *meta,
+                               const float *sink_k, const float *sink_v, const float *q,
+                               const float *chunk_k, const float *chunk_v, int rows, int ng,
+                               int hpg, int d, int w, int ns, float scale, const int32_t *sel_rows,
+                               const int32_t *sel_heads, int nsel, float *out_sel) {
+    if (!chunk_args_ok(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v, rows, ng, hpg,
+                       d, w, ns) || !out_sel || nsel < 0 || (nsel > 0 && (!sel_rows || !sel_heads)))
+        return -1;
+    for (int k = 0; k < nsel; ++k)
+        if (sel_rows[k] < 0 || sel_rows[k] >= rows || sel_heads[k] < 0 || sel_heads[k] >= ng * hpg)
+            return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int k = 0; k < nsel; ++k)
+        chunk_one(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v, ng, hpg, d, w, ns,
+                  (double)scale, sel_rows[k], sel_heads[k], out_sel + (size_t)k * d, NULL, NULL);
+    return 0;
+}
+
+/*
+ * The normalised softmax weights of one (row, query head), in key-list order (sinks, then the
+ * window oldest to newest). `wts` must hold ns + w doubles. Returns the key count, or -1.
+ */
+int oracle_window_chunk_weights(const float *ring_k, const float *ring_v, const uint32_t *meta,
+                                const float *sink_k, const float *sink_v, const float *q,
+                                const float *chunk_k, const float *chunk_v, int rows, int ng,
+                                int hpg, int d, int w, int ns, float scale, int row, int gh,
+                                double *wts) {
+    if (!chunk_args_ok(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v, rows, ng, hpg,
+                       d, w, ns) || !wts || row < 0 || row >= rows || gh < 0 || gh >= ng * hpg)
+        return -1;
+    int n = 0;
+    chunk_one(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v, ng, hpg, d, w, ns,
+              (double)scale, row, gh, NULL, wts, &n);
+    return n;
+}
+
+/*
+ * Rotate-half RoPE and L2 normalisation of one head vector (`dory_prep`): with x, y the two
+ * halves of the raw head and c, s the halves of the table row, u = x c - y s, v = y c + x s,
+ * inv = 1 / sqrt(sum u^2 + sum v^2 + eps); result (u, v) * inv, in double.
+ */
+static void rotate_unit(const float *raw, const float *rope_row, int hd, double eps, double *res) {
+    int half = hd / 2;
+    double ss = 0.0;
+    for (int e = 0; e < half; ++e) {
+        double x = raw[e], y = raw[half + e];
+        double c = rope_row[e], s = rope_row[half + e];
+        double u = x * c - y * s, v = y * c + x * s;
+        res[e] = u;
+        res[half + e] = v;
+        ss += u * u + v * v;
+    }
+    double inv = 1.0 / sqrt(ss + eps);
+    for (int e = 0; e < hd; ++e) res[e] *= inv;
+}
+
+/*
+ * The gated call. First, for every row (position pos0 + row): each KV head's unit key and raw
+ * value go to ring slot (pos0 + row) mod cap (rounded to f32 there). Then each query head a of
+ * each row attends, with its unit query times the learned scale, over positions
+ * [lo, pos] (`low_key`: lo = pos + 1 - window when pos + 1 > window, else 0), reading slot
+ * j mod cap of KV head a / (nh / nk). Finally z = o / (1 + exp(-gate * gate_scale)) (`dory_gate`).
+ * ring_k / ring_v are updated in place; out is z [rows][nh][hd].
+ */
+int oracle_window_gated(const float *yq, const float *yk, const float *yv, const float *rope,
+                        const float *q_scale, const float *gate, const float *gate_scale,
+                        float *ring_k, float *ring_v, float *out, int rows, int pos0, int cap,
+                        int window, int nh, int nk, int hd, float scale, float eps) {
+    if (rows < 1 || pos0 < 0 || cap < 1 || window < 1 || nh < 1 || nk < 1 || hd < 2 || hd % 2)
+        return -1;
+    if (nh % nk != 0 || cap < window + rows - 1) return -1;
+    if (!yq || !yk || !yv || !rope || !q_scale || !gate || !gate_scale || !ring_k || !ring_v || !out)
+        return -1;
+    int hpg = nh / nk;
+    double *tmp = (double *)malloc(sizeof(double) * (size_t)hd);
+    for (int r = 0; r < rows; ++r) {
+        size_t slot = (size_t)(((long)pos0 + r) % cap);
+        for (int kh = 0; kh < nk; ++kh) {
+            rotate_unit(yk + ((size_t)r * nk + kh) * hd, rope + (size_t)r * hd, hd, (double)eps, tmp);
+            float *kd = ring_k + (slot * nk + kh) * hd;
+            float *vd = ring_v + (slot * nk + kh) * hd;
+            const float *vs = yv + ((size_t)r * nk + kh) * hd;
+            for (int e = 0; e < hd; ++e) {
+                kd[e] = (float)tmp[e];
+                vd[e] = vs[e];
+            }
+        }
+    }
+    free(tmp);
+    long total = (long)rows * nh;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long t = 0; t < total; ++t) {
+        int r = (int)(t / nh), a = (int)(t % nh);
+        int kh = a / hpg;
+        long pos = (long)pos0 + r;
+        long lo = pos + 1 > window ? pos + 1 - window : 0;
+        int n = (int)(pos - lo + 1);
+        const float **kp = (const float **)malloc(sizeof(float *) * (size_t)n);
+        const float **vp = (const float **)malloc(sizeof(float *) * (size_t)n);
+        double *sc = (double *)malloc(sizeof(double) * (size_t)n);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)hd);
+        double *qd = (double *)malloc(sizeof(double) * (size_t)hd);
+        for (int j = 0; j < n; ++j) {
+            size_t slot = (size_t)((lo + j) % cap);
+            kp[j] = ring_k + (slot * nk + kh) * hd;
+            vp[j] = ring_v + (slot * nk + kh) * hd;
+        }
+        rotate_unit(yq + ((size_t)r * nh + a) * hd, rope + (size_t)r * hd, hd, (double)eps, qd);
+        for (int e = 0; e < hd; ++e) qd[e] *= (double)q_scale[(size_t)a * hd + e];
+        attend(qd, kp, vp, n, hd, (double)scale, sc, acc, NULL);
+        float *z = out + ((size_t)r * nh + a) * hd;
+        for (int e = 0; e < hd; ++e) {
+            size_t ge = (size_t)a * hd + e;
+            double gs = (double)gate[(size_t)r * nh * hd + ge] * (double)gate_scale[ge];
+            z[e] = (float)(acc[e] / (1.0 + exp(-gs)));
+        }
+        free(kp); free(vp); free(sc); free(acc); free(qd);
+    }
+    return 0;
+}
+
+/* Host-side meta validation with the same rules the oracle enforces (1 = valid). */
+int oracle_meta_ok(const uint32_t *meta, int ng, int w) {
+    if (!meta || ng < 1 || w < 1) return 0;
+    return meta_ok(meta, ng, w);
+}

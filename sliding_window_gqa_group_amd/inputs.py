@@ -1,0 +1,185 @@
+"""Seeded synthetic inputs for windowed grouped-query attention over a ring buffer.
+
+This module only draws numbers and lays them out; it holds none of the attention arithmetic.
+Both the HIP path (through the binding) and the CPU oracle are fed from the arrays built here.
+
+Layouts follow the header comment of the o1c page ("A sealed layer's attention for a chunk of
+rows, on Metal"): ring k/v ``[g][w][d]``, sink k/v ``[g][ns][d]``, q ``[row][nh][d]``, chunk k/v
+``[row][g][d]``, out ``[row][nh][d]``, and ``meta[g*4] = len | head | far_len | window``.
+The gated layouts follow the dory page ("Dory's token path", ``dory_prep``): raw yq
+``[row][nh][hd]``, yk/yv ``[row][nk][hd]``, a RoPE table row per position whose first half is
+cos and second half sin, a learned query scale ``[nh][hd]``, a gate ``[row][nh*hd]`` with its scale
+``[nh*hd]``, and a position-indexed ring ``[cap][nk][hd]``.
+
+Draw order per config (numpy PCG64, seed = config index): meta draws, ring K, ring V, sink K,
+sink V, q, chunk K, chunk V; gated: ring K, ring V, yq, yk, yv, q_scale, gate, gate_scale.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass
+class ChunkInputs:
+    """Inputs of one windowed-attention call over a chunk of rows."""
+    name: str
+    rows: int
+    ng: int
+    hpg: int
+    d: int
+    w: int
+    ns: int
+    scale: float
+    meta: np.ndarray          # uint32 [ng][4]
+    ring_k: np.ndarray        # f32 [ng][w][d]
+    ring_v: np.ndarray        # f32 [ng][w][d]
+    sink_k: np.ndarray        # f32 [ng][ns][d]
+    sink_v: np.ndarray        # f32 [ng][ns][d]
+    q: np.ndarray             # f32 [rows][nh][d]
+    chunk_k: np.ndarray       # f32 [rows][ng][d]
+    chunk_v: np.ndarray       # f32 [rows][ng][d]
+    seed: int = 0
+
+    @property
+    def nh(self) -> int:
+        return self.ng * self.hpg
+
+
+@dataclass
+class GatedInputs:
+    """Inputs of one gated unit-head windowed-attention call."""
+    name: str
+    rows: int
+    pos0: int
+    cap: int
+    window: int
+    nh: int
+    nk: int
+    hd: int
+    scale: float
+    eps: float
+    yq: np.ndarray            # f32 [rows][nh][hd]
+    yk: np.ndarray            # f32 [rows][nk][hd]
+    yv: np.ndarray            # f32 [rows][nk][hd]
+    rope: np.ndarray          # f32 [rows][hd]: cos | sin at position pos0+row
+    q_scale: np.ndarray       # f32 [nh][hd]
+    gate: np.ndarray          # f32 [rows][nh*hd]
+    gate_scale: np.ndarray    # f32 [nh*hd]
+    ring_k: np.ndarray        # f32 [cap][nk][hd] (state before the call)
+    ring_v: np.ndarray        # f32 [cap][nk][hd]
+    seed: int = 0
+
+
+def _normal(rng: np.random.Generator, shape) -> np.ndarray:
+    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+def make_chunk(rows: int, ng: int, hpg: int, d: int, w: int, ns: int, meta, seed: int,
+               name: str = "custom", scale: float | None = None) -> ChunkInputs:
+    """Draw ring/sink/q/chunk tensors for given meta rows ``(len, head, far_len, window)``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    meta = np.ascontiguousarray(np.asarray(meta, dtype=np.uint32).reshape(ng, 4))
+    return _fill_chunk(rng, name, rows, ng, hpg, d, w, ns, meta, seed, scale)
+
+
+def _fill_chunk(rng, name, rows, ng, hpg, d, w, ns, meta, seed, scale) -> ChunkInputs:
+    nh = ng * hpg
+    ring_k = _normal(rng, (ng, w, d))
+    ring_v = _normal(rng, (ng, w, d))
+    sink_k = _normal(rng, (ng, ns, d))
+    sink_v = _normal(rng, (ng, ns, d))
+    q = _normal(rng, (rows, nh, d))
+    chunk_k = _normal(rng, (rows, ng, d))
+    chunk_v = _normal(rng, (rows, ng, d))
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(d)))
+    return ChunkInputs(name, rows, ng, hpg, d, w, ns, float(scale), meta, ring_k, ring_v,
+                       sink_k, sink_v, q, chunk_k, chunk_v, seed)
+
+
+def rope_table(rows: int, pos0: int, hd: int, base: float = 10000.0) -> np.ndarray:
+    """cos | sin table for positions pos0..pos0+rows-1, computed in f64 and rounded to f32.
+
+    Frequencies theta_i = p * base^(-2i/hd) for i < hd/2, pairing element i with i + hd/2
+    (rotate-half). The table is an input of the gated call; the pages take it as a buffer.
+    """
+    half = hd // 2
+    pos = np.arange(pos0, pos0 + rows, dtype=np.float64)[:, None]
+    inv_freq = base ** (-2.0 * np.arange(half, dtype=np.float64) / hd)
+    ang = pos * inv_freq[None, :]
+    return np.ascontiguousarray(np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32))
+
+
+def make_gated(rows: int, pos0: int, cap: int, window: int, nh: int, nk: int, hd: int, seed: int,
+               name: str = "custom", scale: float | None = None, eps: float = 1e-6,
+               rope_base: float = 10000.0) -> GatedInputs:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    # State of the ring before the call: unit-norm keys (a Gaussian direction, normalised
+    # without epsilon) and N(0,1) values in every slot.
+    rk = rng.standard_normal(size=(cap, nk, hd), dtype=np.float32).astype(np.float64)
+    rk /= np.linalg.norm(rk, axis=-1, keepdims=True)
+    ring_k = np.ascontiguousarray(rk.astype(np.float32))
+    ring_v = _normal(rng, (cap, nk, hd))
+    yq = _normal(rng, (rows, nh, hd))
+    yk = _normal(rng, (rows, nk, hd))
+    yv = _normal(rng, (rows, nk, hd))
+    q_scale = rng.uniform(0.5, 1.5, size=(nh, hd)).astype(np.float32)
+    gate = _normal(rng, (rows, nh * hd))
+    gate_scale = _normal(rng, (nh * hd,))
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(hd)))
+    return GatedInputs(name, rows, pos0, cap, window, nh, nk, hd, float(scale), float(eps), yq, yk,
+                       yv, rope_table(rows, pos0, hd, rope_base), q_scale, gate, gate_scale,
+                       ring_k, ring_v, seed)
+
+
+# ── The five named workloads ────────────────────────────────────────────────────────────────
+
+def tiny() -> ChunkInputs:
+    """1 row, 1 KV group of 4 query heads, d=64, w=16 full ring with head 5, 2 sinks."""
+    return make_chunk(1, 1, 4, 64, 16, 2, [(16, 5, 0, 0)], seed=0, name="tiny")
+
+
+def decode(seed: int = 1) -> ChunkInputs:
+    """1 row, 8 KV groups x 4 heads, d=128, w=4096 full ring, seeded head offsets, 4 sinks."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ng, w = 8, 4096
+    heads = rng.integers(0, w, size=ng)
+    meta = np.array([(w, int(h), 0, 0) for h in heads], dtype=np.uint32)
+    return _fill_chunk(rng, "decode", 1, ng, 4, 128, w, 4, meta, seed, None)
+
+
+def prefill() -> ChunkInputs:
+    """512 rows, 8 KV groups x 4 heads, d=128, w=4096, ring len 3000 head 0, 4 sinks."""
+    return make_chunk(512, 8, 4, 128, 4096, 4, [(3000, 0, 0, 0)] * 8, seed=2, name="prefill")
+
+
+def gated() -> GatedInputs:
+    """64 rows at pos0=20000, cap 8192, window 1024, 16 q heads over 4 KV heads, hd=256."""
+    return make_gated(64, 20000, 8192, 1024, 16, 4, 256, seed=3, name="gated")
+
+
+def large_meta(seed: int = 4, ng: int = 8, w: int = 32768):
+    """Per-group (len, head, 0, window override) for the Large workload, plus its generator."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows_meta = []
+    for _ in range(ng):
+        ov = int(rng.choice([0, 4096, 8192]))
+        wg = ov if ov else w
+        ln = int(rng.integers(0, wg + 1))
+        hd = int(rng.integers(0, wg))
+        rows_meta.append((ln, hd, 0, ov))
+    return rng, np.array(rows_meta, dtype=np.uint32)
+
+
+def large(seed: int = 4) -> ChunkInputs:
+    """2048 rows, 8 KV groups x 8 heads, d=128, w=32768 with per-group overrides, 4 sinks."""
+    rng, meta = large_meta(seed)
+    return _fill_chunk(rng, "large", 2048, 8, 8, 128, 32768, 4, meta, seed, None)
+
+
+CHUNK_CONFIGS = {"tiny": tiny, "decode": decode, "prefill": prefill, "large": large}
+GATED_CONFIGS = {"gated": gated}

@@ -1,0 +1,70 @@
+"""The oracle's pins have teeth: plausible mistakes planted in a copy of the oracle fail them.
+
+Each mutant is a one-line edit of ``oracle/oracle.c`` (a dropped term, a wrong sign, index or
+operand), compiled on the CPU into a temporary library; the pin suite of test_oracle_pins.py is
+then run against it and at least one pin must fail. The real oracle is restored afterwards.
+"""
+import os
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+# (name, text in oracle.c, replacement)
+MUTANTS = [
+    ("window one short", "uint32_t win = wg < end ? wg : end;",
+     "uint32_t win = wg - 1 < end ? wg - 1 : end;"),
+    ("row excludes itself", "uint32_t end = len0 + (uint32_t)i + 1u;",
+     "uint32_t end = len0 + (uint32_t)i + (i > 0 ? 0u : 1u);"),
+    ("head offset ignored", "size_t slot = (size_t)((head0 + x) % wg);",
+     "size_t slot = (size_t)(x % wg);"),
+    ("modulus is w, not the group window", "size_t slot = (size_t)((head0 + x) % wg);",
+     "size_t slot = (size_t)((head0 + x) % (uint32_t)w);"),
+    ("override ignored", "return ov != 0u ? ov : (uint32_t)w;", "return (uint32_t)w;"),
+    ("sinks dropped", "for (int s = 0; s < ns; ++s) {", "for (int s = 0; s < 0; ++s) {"),
+    ("values read from keys", "vp[n] = ring_v + ((size_t)g * w + slot) * d;",
+     "vp[n] = ring_k + ((size_t)g * w + slot) * d;"),
+    ("chunk row of the wrong group", "kp[n] = chunk_k + (row * ng + g) * d;",
+     "kp[n] = chunk_k + (row * ng + (ng - 1 - g)) * d;"),
+    ("scale dropped", "sc[j] = scale * dot;", "sc[j] = dot;"),
+    ("not normalised", "for (int e = 0; e < d; ++e) acc[e] /= l;",
+     "for (int e = 0; e < d; ++e) acc[e] /= (l > 1.0 ? 1.0 : 1.0);"),
+    ("query head of the wrong row", "const float *qv = q + ((size_t)i * nh + gh) * d;",
+     "const float *qv = q + ((size_t)0 * nh + gh) * d;"),
+    ("rotation sign", "double u = x * c - y * s, v = y * c + x * s;",
+     "double u = x * c + y * s, v = y * c - x * s;"),
+    ("eps outside the square root", "double inv = 1.0 / sqrt(ss + eps);",
+     "double inv = 1.0 / (sqrt(ss) + eps);"),
+    ("gate sign", "z[e] = (float)(acc[e] / (1.0 + exp(-gs)));",
+     "z[e] = (float)(acc[e] / (1.0 + exp(gs)));"),
+    ("kv head interleaved", "int kh = a / hpg;", "int kh = a % nk;"),
+    ("window start off by one", "long lo = pos + 1 > window ? pos + 1 - window : 0;",
+     "long lo = pos + 1 > window ? pos - window : 0;"),
+    ("query scale dropped", "for (int e = 0; e < hd; ++e) qd[e] *= (double)q_scale[(size_t)a * hd + e];",
+     "for (int e = 0; e < hd; ++e) qd[e] *= 1.0;"),
+    ("ring value not written", "vd[e] = vs[e];", "vd[e] = vd[e];"),
+]
+
+PIN_TESTS = [getattr(pins, n) for n in dir(pins) if n.startswith("test_")]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(oracle.source_path()).read()
+    assert src.count(old) == 1, f"mutation anchor not found once: {old!r}"
+    mpath = os.path.join(tmp_path, "mutant.c")
+    with open(mpath, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.load_library(oracle.compile_source(mpath, os.path.join(tmp_path, "libmutant.so")))
+    caught = []
+    try:
+        oracle.use_library(lib)
+        for t in PIN_TESTS:
+            try:
+                t()
+            except (AssertionError, ValueError, FloatingPointError):
+                caught.append(t.__name__)
+    finally:
+        oracle.use_library(None)
+    assert caught, f"no pin caught the mutant '{name}'"

@@ -1,0 +1,457 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test checks the oracle against a fact fixed by the pages' definition or by mathematics:
+a brute force that simulates the ring pushes with a bounded deque, torch's f64 scaled-dot-product
+attention, closed forms (uniform weights give the arithmetic-series mean of visible positions),
+special cases (a one-key window returns its value), invariants (ring rotation, chunk == a
+sequence of decodes, a group's override == that group alone with w = override), and hand-derived
+worked examples under tests/golden/.
+
+Definition followed (o1c page, "A sealed layer's attention for a chunk of rows, on Metal"):
+row i of a group sees its ns sinks and the last min(wg, len0 + i + 1) entries of the stream
+[ring entries oldest->newest, chunk rows 0..i]; wg is the per-group override or w (`wgf`).
+"""
+import collections
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sliding_window_gqa_group_amd import inputs as gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ── Independent brute force: simulate the ring as a bounded deque ─────────────────────────────
+
+def _ring_entries(inp, g):
+    """(k, v) of the group's ring entries, oldest first, read by walking slots from the head."""
+    ln, head, _, ov = (int(x) for x in inp.meta[g])
+    wg = ov if ov else inp.w
+    out, slot = [], head
+    for _ in range(ln):
+        out.append((inp.ring_k[g, slot].astype(np.float64), inp.ring_v[g, slot].astype(np.float64)))
+        slot += 1
+        if slot == wg:
+            slot = 0
+    return out, wg
+
+
+def brute_chunk(inp):
+    rows, ng, hpg, d = inp.rows, inp.ng, inp.hpg, inp.d
+    out = np.zeros((rows, ng * hpg, d))
+    for g in range(ng):
+        entries, wg = _ring_entries(inp, g)
+        window = collections.deque(entries, maxlen=wg)   # push evicts the oldest when full
+        sinks = [(inp.sink_k[g, s].astype(np.float64), inp.sink_v[g, s].astype(np.float64))
+                 for s in range(inp.ns)]
+        for i in range(rows):
+            window.append((inp.chunk_k[i, g].astype(np.float64), inp.chunk_v[i, g].astype(np.float64)))
+            keys = sinks + list(window)
+            for h in range(hpg):
+                qv = inp.q[i, g * hpg + h].astype(np.float64)
+                sc = [inp.scale * float(np.dot(qv, k)) for k, _ in keys]
+                m = max(sc)
+                p = [math.exp(s - m) for s in sc]
+                tot = math.fsum(p)
+                acc = np.zeros(d)
+                for pj, (_, v) in zip(p, keys):
+                    acc += pj * v
+                out[i, g * hpg + h] = acc / tot
+    return out
+
+
+def _random_case(rng, d=None, ns=None, rows=None):
+    ng = int(rng.integers(1, 4))
+    hpg = int(rng.choice([1, 2, 3, 4]))
+    d = int(d if d is not None else rng.choice([4, 8, 12, 16]))
+    w = int(rng.integers(1, 10))
+    ns = int(ns if ns is not None else rng.choice([0, 1, 3]))
+    rows = int(rows if rows is not None else rng.integers(1, 7))
+    meta = []
+    for _ in range(ng):
+        ov = int(rng.integers(0, w + 1)) if rng.random() < 0.4 else 0
+        wg = ov if ov else w
+        ln = int(rng.integers(0, wg + 1))
+        head = int(rng.integers(0, wg)) if ln > 0 else int(rng.integers(0, wg))
+        meta.append((ln, head, int(rng.integers(0, 5)), ov))
+    return gen.make_chunk(rows, ng, hpg, d, w, ns, meta, seed=int(rng.integers(1 << 30)),
+                          scale=float(rng.choice([0.25, 0.5, 1.0])))
+
+
+def test_oracle_matches_deque_bruteforce():
+    rng = np.random.default_rng(1234)
+    for _ in range(300):
+        inp = _random_case(rng)
+        ref = brute_chunk(inp)
+        got = oracle.window_chunk(inp)
+        np.testing.assert_allclose(got, ref, rtol=3e-7, atol=1e-8)
+
+
+# ── Library routine: torch f64 scaled-dot-product attention ──────────────────────────────────
+
+def test_oracle_matches_torch_causal_gqa():
+    """len0 = 0, ns = 0 and a window no shorter than the chunk: plain causal GQA attention."""
+    rng = np.random.default_rng(7)
+    for rows, ng, hpg, d in [(5, 2, 3, 8), (17, 1, 4, 16), (9, 3, 1, 12)]:
+        w = rows + int(rng.integers(0, 4))
+        inp = gen.make_chunk(rows, ng, hpg, d, w, 0, [(0, int(rng.integers(0, w)), 0, 0)] * ng,
+                             seed=int(rng.integers(1 << 30)))
+        q = torch.from_numpy(inp.q.astype(np.float64)).permute(1, 0, 2)[None]       # [1,nh,L,d]
+        k = torch.from_numpy(inp.chunk_k.astype(np.float64)).permute(1, 0, 2)[None]  # [1,ng,L,d]
+        v = torch.from_numpy(inp.chunk_v.astype(np.float64)).permute(1, 0, 2)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q, k, v, is_causal=True, scale=inp.scale, enable_gqa=True)[0].permute(1, 0, 2).numpy()
+        np.testing.assert_allclose(oracle.window_chunk(inp), ref, rtol=3e-7, atol=1e-8)
+
+
+def test_oracle_matches_torch_with_window_mask():
+    """Sinks + wrapped ring + chunk as one key panel and a boolean mask, through torch f64 SDPA."""
+    rng = np.random.default_rng(8)
+    for _ in range(20):
+        inp = _random_case(rng, d=8)
+        for g in range(inp.ng):
+            entries, wg = _ring_entries(inp, g)
+            ln = len(entries)
+            keys = ([inp.sink_k[g, s] for s in range(inp.ns)] + [e[0] for e in entries] +
+                    [inp.chunk_k[i, g] for i in range(inp.rows)])
+            vals = ([inp.sink_v[g, s] for s in range(inp.ns)] + [e[1] for e in entries] +
+                    [inp.chunk_v[i, g] for i in range(inp.rows)])
+            K = torch.tensor(np.array(keys, dtype=np.float64))[None, None]
+            V = torch.tensor(np.array(vals, dtype=np.float64))[None, None]
+            n = K.shape[2]
+            mask = torch.zeros(inp.rows, n, dtype=torch.bool)
+            for i in range(inp.rows):
+                mask[i, :inp.ns] = True
+                end = ln + i + 1
+                start = end - min(wg, end)
+                mask[i, inp.ns + start: inp.ns + end] = True
+            heads = slice(g * inp.hpg, (g + 1) * inp.hpg)
+            Q = torch.tensor(inp.q[:, heads].astype(np.float64)).permute(1, 0, 2)[None]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                Q, K.expand(1, inp.hpg, n, inp.d), V.expand(1, inp.hpg, n, inp.d),
+                attn_mask=mask, scale=inp.scale)[0].permute(1, 0, 2).numpy()
+            np.testing.assert_allclose(oracle.window_chunk(inp)[:, heads], ref, rtol=3e-7, atol=1e-8)
+
+
+# ── Closed forms and special cases ───────────────────────────────────────────────────────────
+
+def _coded_case(rows, ng, hpg, w, ns, meta, d=4):
+    """q = 0 (uniform weights); V carries (position code, 1, code^2, 0)."""
+    inp = gen.make_chunk(rows, ng, hpg, d, w, ns, meta, seed=5)
+    inp.q[:] = 0.0
+    for g in range(ng):
+        ln, head, _, ov = (int(x) for x in inp.meta[g])
+        wg = ov if ov else w
+        for x in range(ln):
+            slot = (head + x) % wg
+            inp.ring_v[g, slot, :3] = (x, 1.0, x * x)
+        for i in range(rows):
+            inp.chunk_v[i, g, :3] = (ln + i, 1.0, (ln + i) ** 2)
+        for s in range(ns):
+            inp.sink_v[g, s, :3] = (-1 - s, 1.0, (1 + s) ** 2)
+    return inp
+
+
+def test_uniform_weights_give_arithmetic_series_mean():
+    cases = [
+        (6, 2, 2, 8, 2, [(8, 3, 0, 0), (5, 2, 0, 6)]),
+        (3, 1, 1, 16, 0, [(16, 5, 0, 0)]),
+        (9, 3, 1, 5, 1, [(0, 0, 0, 0), (2, 4, 0, 0), (3, 1, 0, 3)]),
+    ]
+    for rows, ng, hpg, w, ns, meta in cases:
+        inp = _coded_case(rows, ng, hpg, w, ns, meta)
+        out = oracle.window_chunk(inp)
+        for g in range(ng):
+            ln, _, _, ov = meta[g]
+            wg = ov if ov else w
+            for i in range(rows):
+                hi = ln + i + 1
+                win = min(wg, hi)
+                lo = hi - win
+                n = ns + win
+                pos_sum = (lo + hi - 1) * win / 2.0 - ns * (ns + 1) / 2.0
+                sq_sum = (sum(x * x for x in range(lo, hi)) + sum((1 + s) ** 2 for s in range(ns)))
+                for h in range(hpg):
+                    o = out[i, g * hpg + h]
+                    assert o[0] == pytest.approx(pos_sum / n, rel=1e-6, abs=1e-6)
+                    assert o[1] == pytest.approx(1.0, rel=1e-7)
+                    assert o[2] == pytest.approx(sq_sum / n, rel=1e-6)
+
+
+def test_window_of_one_returns_own_value():
+    inp = gen.make_chunk(7, 3, 2, 8, 5, 0, [(1, 0, 0, 1), (0, 0, 0, 1), (1, 0, 0, 1)], seed=11)
+    out = oracle.window_chunk(inp)
+    for i in range(inp.rows):
+        for g in range(inp.ng):
+            for h in range(inp.hpg):
+                np.testing.assert_array_equal(out[i, g * inp.hpg + h], inp.chunk_v[i, g])
+
+
+def test_one_hot_query_with_large_scale_selects_argmax_key():
+    inp = gen.make_chunk(1, 1, 1, 8, 6, 0, [(6, 4, 0, 0)], seed=12, scale=200.0)
+    inp.ring_k[:] = 0.0
+    inp.chunk_k[:] = 0.0
+    inp.q[:] = 0.0
+    inp.q[0, 0, 3] = 1.0
+    # logical entry x sits at slot (4 + x) % 6; row 0 sees x = 1..5 and itself
+    target_slot = (4 + 2) % 6
+    inp.ring_k[0, target_slot, 3] = 1.0
+    inp.ring_k[0, (4 + 0) % 6, 3] = 2.0          # oldest entry: evicted for row 0, must not win
+    out = oracle.window_chunk(inp)
+    np.testing.assert_allclose(out[0, 0], inp.ring_v[0, target_slot], rtol=1e-6, atol=1e-6)
+
+
+def test_weights_sum_to_one_and_count_matches_window():
+    rng = np.random.default_rng(21)
+    for _ in range(40):
+        inp = _random_case(rng)
+        i = int(rng.integers(0, inp.rows))
+        gh = int(rng.integers(0, inp.ng * inp.hpg))
+        g = gh // inp.hpg
+        ln, _, _, ov = (int(x) for x in inp.meta[g])
+        wg = ov if ov else inp.w
+        wts = oracle.window_chunk_weights(inp, i, gh)
+        assert wts.size == inp.ns + min(wg, ln + i + 1)
+        assert math.fsum(wts) == pytest.approx(1.0, abs=1e-12)
+        assert np.all(wts > 0)
+
+
+# ── Invariants ───────────────────────────────────────────────────────────────────────────────
+
+def test_ring_rotation_invariance_is_bitwise():
+    rng = np.random.default_rng(31)
+    for _ in range(30):
+        inp = _random_case(rng)
+        base = oracle.window_chunk(inp)
+        rot = gen.make_chunk(inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns, inp.meta.copy(), 0,
+                             scale=inp.scale)
+        for name in ("sink_k", "sink_v", "q", "chunk_k", "chunk_v"):
+            setattr(rot, name, getattr(inp, name).copy())
+        for g in range(inp.ng):
+            ln, head, far, ov = (int(x) for x in inp.meta[g])
+            wg = ov if ov else inp.w
+            r = int(rng.integers(0, wg))
+            # slot s moves to (s + r) mod wg; the head moves with it
+            idx = (np.arange(wg) + r) % wg
+            rot.ring_k[g, idx] = inp.ring_k[g, :wg]
+            rot.ring_v[g, idx] = inp.ring_v[g, :wg]
+            rot.ring_k[g, wg:] = inp.ring_k[g, wg:]
+            rot.ring_v[g, wg:] = inp.ring_v[g, wg:]
+            rot.meta[g] = (ln, (head + r) % wg, far, ov)
+        np.testing.assert_array_equal(oracle.window_chunk(rot), base)
+
+
+def _push(inp, g, k, v):
+    """One ring push with the commit rules of the o1c page (`o1c_ring_commit`, `o1c_meta`):
+    the row lands in slot (head + len) mod wg; a full ring advances its head instead."""
+    ln, head, far, ov = (int(x) for x in inp.meta[g])
+    wg = ov if ov else inp.w
+    slot = (head + ln) % wg
+    inp.ring_k[g, slot] = k
+    inp.ring_v[g, slot] = v
+    if ln + 1 <= wg:
+        inp.meta[g] = (ln + 1, head, far, ov)
+    else:
+        inp.meta[g] = (wg, (head + 1) % wg, far + 1, ov)
+
+
+def test_chunk_equals_sequence_of_decodes():
+    rng = np.random.default_rng(41)
+    for _ in range(25):
+        inp = _random_case(rng)
+        full = oracle.window_chunk(inp)
+        state = gen.make_chunk(1, inp.ng, inp.hpg, inp.d, inp.w, inp.ns, inp.meta.copy(), 0,
+                               scale=inp.scale)
+        state.ring_k = inp.ring_k.copy()
+        state.ring_v = inp.ring_v.copy()
+        state.sink_k, state.sink_v = inp.sink_k, inp.sink_v
+        for i in range(inp.rows):
+            state.q = inp.q[i:i + 1].copy()
+            state.chunk_k = inp.chunk_k[i:i + 1].copy()
+            state.chunk_v = inp.chunk_v[i:i + 1].copy()
+            one = oracle.window_chunk(state)
+            np.testing.assert_allclose(one[0], full[i], rtol=1e-7, atol=1e-9)
+            for g in range(inp.ng):
+                _push(state, g, inp.chunk_k[i, g], inp.chunk_v[i, g])
+
+
+def test_group_override_equals_group_alone_restrided():
+    rng = np.random.default_rng(51)
+    inp = gen.make_chunk(6, 3, 2, 8, 12, 2, [(12, 7, 0, 0), (4, 3, 0, 5), (7, 2, 0, 9)], seed=52)
+    full = oracle.window_chunk(inp)
+    for g in range(inp.ng):
+        ln, head, far, ov = (int(x) for x in inp.meta[g])
+        wg = ov if ov else inp.w
+        alone = gen.make_chunk(inp.rows, 1, inp.hpg, inp.d, wg, inp.ns, [(ln, head, far, 0)], 0,
+                               scale=inp.scale)
+        alone.ring_k = inp.ring_k[g:g + 1, :wg].copy()
+        alone.ring_v = inp.ring_v[g:g + 1, :wg].copy()
+        alone.sink_k = inp.sink_k[g:g + 1].copy()
+        alone.sink_v = inp.sink_v[g:g + 1].copy()
+        alone.q = inp.q[:, g * inp.hpg:(g + 1) * inp.hpg].copy()
+        alone.chunk_k = inp.chunk_k[:, g:g + 1].copy()
+        alone.chunk_v = inp.chunk_v[:, g:g + 1].copy()
+        np.testing.assert_array_equal(oracle.window_chunk(alone),
+                                      full[:, g * inp.hpg:(g + 1) * inp.hpg])
+
+
+def test_select_matches_full():
+    inp = gen.make_chunk(9, 2, 3, 16, 10, 2, [(10, 4, 0, 0), (6, 1, 0, 7)], seed=61)
+    full = oracle.window_chunk(inp)
+    rows = np.array([0, 8, 3, 5])
+    heads = np.array([5, 0, 2, 4])
+    np.testing.assert_array_equal(oracle.window_chunk_select(inp, rows, heads), full[rows, heads])
+
+
+def test_invalid_meta_is_rejected():
+    bad = [
+        [(17, 0, 0, 0)],      # len beyond w
+        [(4, 4, 0, 4)],       # head not below the window
+        [(3, 0, 0, 20)],      # override beyond the storage stride w
+    ]
+    for meta in bad:
+        inp = gen.make_chunk(2, 1, 2, 4, 16, 0, meta, seed=1)
+        assert not oracle.meta_ok(inp.meta, 1, 16)
+        with pytest.raises(ValueError):
+            oracle.window_chunk(inp)
+
+
+def test_golden_chunk_pow2():
+    with open(os.path.join(GOLDEN, "chunk_pow2.json")) as f:
+        gd = json.load(f)
+    q = np.array([[[math.log(2) if x == "ln2" else x for x in hv] for hv in row] for row in gd["q"]],
+                 dtype=np.float32)
+    inp = gen.make_chunk(gd["rows"], gd["ng"], gd["hpg"], gd["d"], gd["w"], gd["ns"], gd["meta"], 0,
+                         scale=gd["scale"])
+    inp.ring_k = np.array(gd["ring_k"], dtype=np.float32)
+    inp.ring_v = np.array(gd["ring_v"], dtype=np.float32)
+    inp.sink_k = np.array(gd["sink_k"], dtype=np.float32)
+    inp.sink_v = np.array(gd["sink_v"], dtype=np.float32)
+    inp.chunk_k = np.array(gd["chunk_k"], dtype=np.float32)
+    inp.chunk_v = np.array(gd["chunk_v"], dtype=np.float32)
+    inp.q = q
+    np.testing.assert_allclose(oracle.window_chunk(inp), np.array(gd["expected"]), rtol=gd["rtol"],
+                               atol=1e-7)
+
+
+# ── Gated variant ────────────────────────────────────────────────────────────────────────────
+
+def _rotate_unit_complex(raw, rope_row, eps):
+    """Rotate-half as complex multiplication: (x + iy)(c + is), then unit-normalise with eps."""
+    half = raw.shape[-1] // 2
+    z = raw[:half].astype(np.float64) + 1j * raw[half:].astype(np.float64)
+    r = rope_row[:half].astype(np.float64) + 1j * rope_row[half:].astype(np.float64)
+    rot = z * r
+    vec = np.concatenate([rot.real, rot.imag])
+    return vec / np.sqrt(np.sum(np.abs(rot) ** 2) + eps)
+
+
+def brute_gated(inp):
+    from scipy.special import expit
+    rk = inp.ring_k.copy()
+    rv = inp.ring_v.copy()
+    for r in range(inp.rows):
+        slot = (inp.pos0 + r) % inp.cap
+        for kh in range(inp.nk):
+            rk[slot, kh] = _rotate_unit_complex(inp.yk[r, kh], inp.rope[r], inp.eps).astype(np.float32)
+            rv[slot, kh] = inp.yv[r, kh]
+    hpg = inp.nh // inp.nk
+    z = np.zeros((inp.rows, inp.nh, inp.hd))
+    for r in range(inp.rows):
+        pos = inp.pos0 + r
+        positions = [p for p in range(0, pos + 1) if pos - p < inp.window]
+        for a in range(inp.nh):
+            kh = a // hpg
+            qv = _rotate_unit_complex(inp.yq[r, a], inp.rope[r], inp.eps) * inp.q_scale[a]
+            K = np.array([rk[p % inp.cap, kh] for p in positions], dtype=np.float64)
+            V = np.array([rv[p % inp.cap, kh] for p in positions], dtype=np.float64)
+            s = inp.scale * (K @ qv)
+            p = np.exp(s - s.max())
+            o = (p[:, None] * V).sum(0) / p.sum()
+            gsl = slice(a * inp.hd, (a + 1) * inp.hd)
+            z[r, a] = o * expit(inp.gate[r, gsl].astype(np.float64) * inp.gate_scale[gsl])
+    return z, rk, rv
+
+
+def test_gated_matches_complex_bruteforce():
+    cases = [(3, 5, 8, 4, 4, 2, 8), (4, 0, 7, 4, 2, 2, 16), (2, 30, 9, 6, 6, 3, 4), (5, 2, 11, 7, 4, 1, 8)]
+    for rows, pos0, cap, window, nh, nk, hd in cases:
+        inp = gen.make_gated(rows, pos0, cap, window, nh, nk, hd, seed=rows * 100 + pos0, scale=0.7)
+        z, rk, rv = oracle.window_gated(inp)
+        bz, brk, brv = brute_gated(inp)
+        np.testing.assert_allclose(rk, brk, rtol=2e-7, atol=1e-8)
+        np.testing.assert_array_equal(rv, brv)
+        np.testing.assert_allclose(z, bz, rtol=1e-6, atol=1e-8)
+
+
+def test_gated_identity_table_is_pure_normalisation():
+    inp = gen.make_gated(3, 0, 4, 2, 2, 1, 8, seed=71)
+    inp.rope[:, :4] = 1.0
+    inp.rope[:, 4:] = 0.0
+    inp.yk[2] *= 3e-4          # a key whose sum of squares is comparable to eps
+    _, rk, _ = oracle.window_gated(inp)
+    for r in range(inp.rows):
+        raw = inp.yk[r, 0].astype(np.float64)
+        ss = float(np.sum(raw * raw))
+        slot = (inp.pos0 + r) % inp.cap
+        np.testing.assert_allclose(rk[slot, 0], raw / math.sqrt(ss + inp.eps), rtol=2e-7)
+        assert float(np.sum(rk[slot, 0].astype(np.float64) ** 2)) == pytest.approx(ss / (ss + inp.eps), rel=1e-6)
+
+
+def test_gated_rotation_preserves_norm():
+    inp = gen.make_gated(4, 1000, 8, 4, 2, 2, 16, seed=72, eps=0.0)
+    _, rk, _ = oracle.window_gated(inp)
+    for r in range(inp.rows):
+        for kh in range(inp.nk):
+            k = rk[(inp.pos0 + r) % inp.cap, kh].astype(np.float64)
+            assert float(np.dot(k, k)) == pytest.approx(1.0, abs=1e-6)
+
+
+def test_gated_zero_gate_is_half_of_chunk_attention():
+    """gate = 0 gives z = attn / 2; the attention equals the chunk path on the prepped ring with
+    ns = 0, window override = window, the ring tail as the ring and the new rows as the chunk."""
+    inp = gen.make_gated(5, 9, 12, 6, 4, 2, 8, seed=73, scale=0.9)
+    inp.gate[:] = 0.0
+    z, rk, rv = oracle.window_gated(inp)
+    hpg = inp.nh // inp.nk
+    ln = min(inp.window - 1, inp.pos0)
+    first = inp.pos0 - ln
+    ch = gen.make_chunk(inp.rows, inp.nk, hpg, inp.hd, inp.window, 0,
+                        [(ln, 0, 0, 0)] * inp.nk, seed=0, scale=inp.scale)
+    for x in range(ln):
+        ch.ring_k[:, x] = rk[(first + x) % inp.cap]
+        ch.ring_v[:, x] = rv[(first + x) % inp.cap]
+    for r in range(inp.rows):
+        ch.chunk_k[r] = rk[(inp.pos0 + r) % inp.cap]
+        ch.chunk_v[r] = rv[(inp.pos0 + r) % inp.cap]
+        for a in range(inp.nh):
+            ch.q[r, a] = (_rotate_unit_complex(inp.yq[r, a], inp.rope[r], inp.eps) * inp.q_scale[a])
+    attn = oracle.window_chunk(ch)
+    # q goes through f32 on the chunk side; allow for that rounding
+    np.testing.assert_allclose(z, 0.5 * attn, rtol=2e-6, atol=1e-7)
+
+
+def test_gated_rejects_small_cap():
+    inp = gen.make_gated(4, 10, 6, 4, 2, 1, 8, seed=74)
+    with pytest.raises(ValueError):
+        oracle.window_gated(inp)      # cap 6 < window + rows - 1 = 7
+
+
+def test_golden_gated_unit():
+    with open(os.path.join(GOLDEN, "gated_unit.json")) as f:
+        gd = json.load(f)
+    inp = gen.make_gated(gd["rows"], gd["pos0"], gd["cap"], gd["window"], gd["nh"], gd["nk"],
+                         gd["hd"], seed=0, scale=gd["scale"], eps=gd["eps"])
+    for name in ("yq", "yk", "yv", "rope", "q_scale", "gate", "gate_scale"):
+        setattr(inp, name, np.array(gd[name], dtype=np.float32))
+    inp.ring_k = np.array(gd["ring_k_before"], dtype=np.float32)
+    inp.ring_v = np.array(gd["ring_v_before"], dtype=np.float32)
+    z, rk, rv = oracle.window_gated(inp)
+    np.testing.assert_allclose(z, np.array(gd["expected_z"]), rtol=gd["rtol"], atol=gd["atol"])
+    np.testing.assert_allclose(rk, np.array(gd["expected_ring_k"]), rtol=1e-7, atol=1e-8)
+    np.testing.assert_array_equal(rv, np.array(gd["expected_ring_v"], dtype=np.float32))

@@ -1,0 +1,245 @@
+"""Throughput of windowed grouped-query attention on one MI355X.
+
+Default workload: the decode call (1 row, 8 KV groups x 4 query heads, d=128, full 4096-slot
+rings with seeded head offsets, 4 sinks). A step is one attn_window_chunk call on one of
+`--sets` copies of the inputs at distinct addresses (>= 0.5 GB in total, so the 256 MB
+Infinity Cache cannot hold them and the K/V stream comes from HBM). Prints ONE JSON line.
+
+value = distinct K/V bytes per call / time per call (GB/s); rows/s and the fraction of the
+8 TB/s HBM peak are reported beside it. `roofline` times the attention kernel with HIP events
+on the stream it runs on; `cpu_baseline` times the CPU oracle on a bounded sample. `also` holds
+the other workloads (timed on resident inputs, labelled hot-cache).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+F32_PEAK_TFLOPS = 157.3
+METRIC = "KV GB/s and rows/s for windowed GQA attention; % of HBM peak"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_valu_counters.json")
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sliding_window_gqa_group_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources; else None."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def chunk_tensors(inp, torch, dev):
+    from sliding_window_gqa_group_amd import inputs as gen
+    t = gen.to_device(inp, dev)
+    if inp.ns == 0:
+        t["sink_k"] = t["sink_v"] = None
+    return t
+
+
+def run_chunk(B, t, scale, out, ws):
+    return B.attn_window_chunk(t["ring_k"], t["ring_v"], t["meta"], t["sink_k"], t["sink_v"],
+                               t["q"], t["chunk_k"], t["chunk_v"], scale, out=out, workspace=ws)
+
+
+def time_calls(torch, fn, n_sets, steps, warmup):
+    """(ms per step over the bracketed region, mean per-launch event ms)."""
+    stream = torch.cuda.current_stream()
+    for s in range(warmup):
+        fn(s % n_sets)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for s in range(steps):
+        starts[s].record(stream)
+        fn(s % n_sets)
+        ends[s].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1)
+    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    return total / steps, float(np.mean(per)), float(np.median(per))
+
+
+def bench_decode(args, torch, B, gen, acct):
+    dev = "cuda:0"
+    inp = gen.decode()
+    base = chunk_tensors(inp, torch, dev)
+    sets = [base] + [{k: (v.clone() if v is not None else None) for k, v in base.items()}
+                     for _ in range(args.sets - 1)]
+    outs = [torch.empty((inp.rows, inp.nh, inp.d), dtype=torch.float32, device=dev)
+            for _ in range(args.sets)]
+    ws = B.Workspace(dev)
+    ws.get(B.chunk_workspace_bytes(inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns))
+
+    # correctness gate on the timed configuration
+    import oracle
+    run_chunk(B, sets[0], inp.scale, outs[0], ws)
+    torch.cuda.synchronize()
+    ref = oracle.window_chunk(inp)
+    got = outs[0].cpu().numpy()
+    ok = bool(np.all(np.abs(got - ref) <= np.maximum(1e-4 * np.abs(ref), 1e-5)))
+    if not ok:
+        raise SystemExit("bench: decode output does not match the oracle")
+
+    ms, ev_mean, ev_med = time_calls(torch, lambda i: run_chunk(B, sets[i], inp.scale, outs[i], ws),
+                                     args.sets, args.steps, args.warmup)
+    kv = acct.unique_kv_bytes(inp)
+    tot = acct.total_bytes(inp)
+    set_bytes = sum(v.numel() * v.element_size() for v in base.values() if v is not None)
+    return inp, ms, ev_mean, ev_med, kv, tot, set_bytes
+
+
+def cpu_baseline(inp, seconds: float):
+    import oracle
+    from sliding_window_gqa_group_amd import accounting as acct
+    oracle.window_chunk(inp)   # load / warm
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.window_chunk(inp)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 10000:
+            break
+    per = el / n
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(acct.unique_kv_bytes(inp) / per / 1e9, 4), "unit": "GB/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{n} full decode calls (f64 accumulation), {el:.1f} s wall, "
+                      f"{per * 1e3:.3f} ms per call"}
+
+
+def bench_others(args, torch, B, gen, acct):
+    dev = "cuda:0"
+    res = {}
+    for name, make in (("tiny", gen.tiny), ("prefill", gen.prefill), ("large", gen.large)):
+        inp = make()
+        t = chunk_tensors(inp, torch, dev)
+        out = torch.empty((inp.rows, inp.nh, inp.d), dtype=torch.float32, device=dev)
+        ws = B.Workspace(dev)
+        ws.get(B.chunk_workspace_bytes(inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns))
+        steps = 5 if name == "large" else 20
+        ms, ev_mean, _ = time_calls(torch, lambda i: run_chunk(B, t, inp.scale, out, ws), 1, steps, 3)
+        flops = acct.chunk_flops(inp)
+        kern = B.chunk_plan(inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns)
+        res[name] = {"ms": round(ms, 5), "kv_gbs": round(acct.unique_kv_bytes(inp) / ms / 1e6, 2),
+                     "rows_per_s": round(inp.rows / ms * 1e3, 1),
+                     "tflops": round(flops / ms / 1e9, 3),
+                     "tflops_frac_f32_peak": round(flops / ms / 1e9 / F32_PEAK_TFLOPS, 4),
+                     "kernel": "mfma" if kern[0] == 2 else "valu", "splits": kern[2],
+                     "cache": "hot (inputs resident, reused)"}
+        del t, out, ws
+        torch.cuda.empty_cache()
+    g = gen.gated()
+    t = gen.to_device(g, dev)
+    out = torch.empty((g.rows, g.nh, g.hd), dtype=torch.float32, device=dev)
+
+    def gated_call(i):
+        B.attn_window_gated(t["yq"], t["yk"], t["yv"], t["rope"], t["q_scale"], t["gate"],
+                            t["gate_scale"], t["ring_k"], t["ring_v"], g.pos0, g.window, g.scale,
+                            g.eps, out=out)
+    ms, _, _ = time_calls(torch, gated_call, 1, 20, 3)
+    kv, tot, flops = acct.gated_counts(g)
+    res["gated"] = {"ms": round(ms, 5), "kv_gbs": round(kv / ms / 1e6, 2),
+                    "rows_per_s": round(g.rows / ms * 1e3, 1),
+                    "tflops": round(flops / ms / 1e9, 3),
+                    "tflops_frac_f32_peak": round(flops / ms / 1e9 / F32_PEAK_TFLOPS, 4),
+                    "cache": "hot (inputs resident, reused)"}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=20, help="rotating input copies (>= 16)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-others", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only; run with --gpus 1 (the per-GPU "
+              "sharding by KV group is described in the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sliding_window_gqa_group_amd import accounting as acct
+    from sliding_window_gqa_group_amd import binding as B
+    from sliding_window_gqa_group_amd import inputs as gen
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    B.load()
+    inp, ms, ev_mean, ev_med, kv, tot, set_bytes = bench_decode(args, torch, B, gen, acct)
+    value = kv / (ms * 1e-3) / 1e9
+    plan = B.chunk_plan(inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns)
+    traffic = measured_traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1), numpy PCG64 seed 1)",
+        "config": {"workload": "decode", "rows": inp.rows, "ng": inp.ng, "hpg": inp.hpg,
+                   "nh": inp.nh, "d": inp.d, "w": inp.w, "ns": inp.ns, "ring": "full, seeded heads",
+                   "input_sets": args.sets, "rotating_bytes": args.sets * set_bytes,
+                   "kernel": "valu split-K" if plan[0] == 1 else "mfma", "splits": plan[2]},
+        "rows_per_s": round(inp.rows / (ms * 1e-3), 1),
+        "hbm_frac": round(tot / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(tot / (ev_mean * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(tot / (ev_mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "attn_valu_kernel<128,4,false>",
+            "algorithmic_bytes_per_launch": tot,
+            "launch_ms_mean": round(ev_mean, 6),
+            "launch_ms_median": round(ev_med, 6),
+        },
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    if not args.no_others:
+        line["also"] = bench_others(args, torch, B, gen, acct)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+/*
+ * winattn.h — C-ABI of the MI355X (gfx950) windowed grouped-query attention library.
+ *
+ * Two operations, both defined on the pages of crate cortiq-engine:
+ *
+ *  attn_window_chunk — exact softmax attention of a chunk of rows over a per-KV-group ring
+ *    buffer window with optional sink keys and causal visibility inside the chunk. Defined by
+ *    the o1c page ("A sealed layer's attention for a chunk of rows, on Metal"): the layout
+ *    header comment, `wgf`, `o1c_score`, `o1c_max`, `o1c_soft`, `o1c_sum`, `o1c_add`, and the
+ *    token path `o1c_tok_near` / `o1c_tok_merge`, all taken with zero far-field landmarks.
+ *
+ *  attn_window_gated — the unit-head variant of the dory page ("Dory's token path"):
+ *    `dory_prep` (rotate-half RoPE, L2 unit heads, learned query scale, K/V into a
+ *    position-indexed ring), `low_key`, `dory_score`, `dory_soft`, `dory_sum`, `dory_gate`.
+ *
+ * Conventions for every entry point:
+ *  - Tensors are contiguous f32 (meta: u32) in DEVICE memory owned by the caller, each base
+ *    pointer 16-byte aligned. The library never allocates on these paths.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls are asynchronous
+ *    on that stream and never synchronise; results are ready when the stream reaches them.
+ *  - Return 0 on success or a negative WINATTN_E* code; nothing is launched on error except
+ *    for WINATTN_ELAUNCH, which reports a failed launch.
+ *  - `workspace` is caller-owned device memory of at least the size the matching *_workspace
+ *    query returns (0 means the call needs none and NULL may be passed). Its first 64 KiB hold
+ *    split counters at a fixed place for every call shape: they must be zero before the first
+ *    call that uses the workspace (a fresh zeroed allocation, or attn_workspace_init), and
+ *    every call leaves them at zero again, so one workspace serves calls of any shapes in
+ *    sequence. Two calls that may run at the same time must not share a workspace.
+ */
+#ifndef WINATTN_H
+#define WINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WINATTN_ABI_VERSION 1
+
+#define WINATTN_OK 0
+#define WINATTN_EINVAL (-1)      /* a size, pointer, alignment or constraint is invalid */
+#define WINATTN_EWORKSPACE (-2)  /* workspace missing or smaller than the query returned */
+#define WINATTN_ELAUNCH (-3)     /* the HIP runtime reported an error at launch */
+#define WINATTN_EUNSUPPORTED (-4)
+
+/* Ring metadata of one KV group, four u32 per group, laid out as the o1c page's header comment
+ * gives it: entries held, slot of the oldest entry, far-field count (ignored here), and a
+ * per-group window override (0 = the call's default w; `wgf`). */
+typedef struct {
+    uint32_t len;
+    uint32_t head;
+    uint32_t far_len;
+    uint32_t window;
+} attn_ring_meta;
+
+/*
+ * attn_window_chunk — out[i][g*hpg+h] = softmax attention of q[i][g*hpg+h] over the keys
+ * visible to chunk row i of KV group g (o1c page: `o1c_score` defines the key set).
+ *
+ * Key set of row i, group g, with wg = meta[g].window ? meta[g].window : w,
+ * len0 = meta[g].len, head0 = meta[g].head:
+ *   the ns sinks sink_k[g][0..ns), then the last min(wg, len0 + i + 1) entries of the stream
+ *   [ring entries 0..len0-1, chunk rows 0..i], where ring entry x (0 = oldest) is slot
+ *   (head0 + x) mod wg of ring_k[g] and stream entry len0 + j is chunk row j. The window ends
+ *   at and includes the row's own key, so a full ring's oldest entry is not seen by row 0.
+ * Scores are scale * <q, k>; the result is sum_j softmax_j * v_j.
+ *
+ * Arguments (all device pointers):
+ *   ring_k, ring_v   [ng][w][d]   ring storage; the slot stride is w even when wg < w
+ *   meta             [ng][4] u32  attn_ring_meta per group; read only. Requirements (not
+ *                                 checked on the device: see attn_window_check_meta):
+ *                                 window <= w, len <= wg, head < wg when len > 0. The kernels
+ *                                 clamp out-of-range fields so they never read out of bounds;
+ *                                 the result is then unspecified.
+ *   sink_k, sink_v   [ng][ns][d]  may be NULL iff ns == 0
+ *   q                [rows][nh][d], nh = ng*hpg; heads g*hpg .. g*hpg+hpg-1 read group g
+ *   chunk_k, chunk_v [rows][ng][d] the chunk's own keys and values
+ *   out              [rows][nh][d] fully overwritten
+ *   rows, ng, hpg, w >= 1; ns >= 0; d a multiple of 4, 4 <= d <= 256; scale finite
+ * Only `out` and the workspace are written.
+ */
+int attn_window_chunk(const float* ring_k, const float* ring_v, const uint32_t* meta,
+                      const float* sink_k, const float* sink_v, const float* q,
+                      const float* chunk_k, const float* chunk_v, float* out, int rows, int ng,
+                      int hpg, int d, int w, int ns, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_window_chunk needs for these sizes (0 if the sizes are invalid). */
+size_t attn_window_chunk_workspace(int rows, int ng, int hpg, int d, int w, int ns);
+
+/*
+ * attn_window_gated — the gated unit-head call for rows at positions pos0 .. pos0+rows-1
+ * (dory page). Steps, in this order:
+ *  1. For each row and KV head kh: x, y = the halves of yk[row][kh]; c, s = the halves of
+ *     rope[row]; u = x*c - y*s, v = y*c + x*s; k' = (u, v) / sqrt(sum u^2 + sum v^2 + eps).
+ *     k' goes to ring_k[(pos0+row) % cap][kh] and yv[row][kh] to ring_v[(pos0+row) % cap][kh].
+ *     Query head a is rotated and normalised the same way and multiplied by q_scale[a].
+ *  2. Row `row` (pos = pos0+row) attends with query head a over positions lo..pos,
+ *     lo = pos+1 > window ? pos+1-window : 0, reading slot p % cap of KV head a / (nh/nk),
+ *     with scores scale * <q', k'> (`dory_score`, `dory_soft`, `dory_sum`).
+ *  3. out[row][a][e] = o[e] / (1 + exp(-gate[row][a*hd+e] * gate_scale[a*hd+e])) (`dory_gate`).
+ *
+ * Arguments (all device pointers):
+ *   yq [rows][nh][hd], yk and yv [rows][nk][hd]   raw heads
+ *   rope [rows][hd]        cos of the row's angles in [0, hd/2), sin in [hd/2, hd)
+ *   q_scale [nh][hd], gate [rows][nh*hd], gate_scale [nh*hd]
+ *   ring_k, ring_v [cap][nk][hd]   read, and written at the rows' slots (step 1)
+ *   out [rows][nh][hd]             fully overwritten
+ *   rows, cap, window, nk >= 1; pos0 >= 0; nh a multiple of nk; hd a multiple of 8,
+ *   8 <= hd <= 256; cap >= window + rows - 1 (so no row's write clobbers a key an earlier
+ *   row still needs); eps >= 0.
+ * Ring slots that no row reads and no row writes are left untouched.
+ */
+int attn_window_gated(const float* yq, const float* yk, const float* yv, const float* rope,
+                      const float* q_scale, const float* gate, const float* gate_scale,
+                      float* ring_k, float* ring_v, float* out, int rows, int pos0, int cap,
+                      int window, int nh, int nk, int hd, float scale, float eps,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_window_gated needs for these sizes (0 if the sizes are invalid). */
+size_t attn_window_gated_workspace(int rows, int nh, int nk, int hd, int window);
+
+/* Zero `bytes` bytes of device memory at `workspace` on `stream` with a fill kernel. */
+int attn_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* Host-side check of ring metadata in HOST memory against the rules above: 0 if every group is
+ * valid, WINATTN_EINVAL otherwise (also for a NULL pointer or ng, w < 1). */
+int attn_window_check_meta(const uint32_t* host_meta, int ng, int w);
+
+/* Diagnostics: how attn_window_chunk would run these sizes. kernel = 1 (vector-ALU split-K
+ * kernel) or 2 (f32 matrix-core kernel); query_block = query vectors per workgroup; splits =
+ * key splits reserved per query block; keys_per_split = keys each split covers at most.
+ * Output pointers may be NULL. Returns 0 or WINATTN_EINVAL. */
+int attn_window_chunk_plan(int rows, int ng, int hpg, int d, int w, int ns, int* kernel,
+                           int* query_block, int* splits, int* keys_per_split);
+
+/* Self-test of the matrix-core operand layout the wide-chunk kernel relies on (after the
+ * fragment-layout probe of the egemma2 page, `eg_fragprobe`): one 32x32x2 f32 product with
+ * A[i][0] = i, A[i][1] = 1, B[0][j] = 1, B[1][j] = 64 j, so element (i, j) holds i + 64 j.
+ * out: device [64][16] floats; out[lane*16 + r] = accumulator r of lane `lane`. */
+int attn_mfma_layout_probe(float* out, void* stream);
+
+/* Tuning knobs for tests and benchmarks (process-wide, not thread-safe; 0 = automatic).
+ * They change the launch plan and therefore the workspace size: query the size after setting
+ * them. */
+#define WINATTN_TUNE_FORCE_KERNEL 1    /* 1 = vector-ALU kernel, 2 = matrix-core kernel */
+#define WINATTN_TUNE_TILES_PER_SPLIT 2 /* key tiles per split */
+#define WINATTN_TUNE_TARGET_BLOCKS 3   /* workgroups the split count aims for */
+int attn_tuning_set(int knob, int value);
+
+/* A static, human-readable description of a return code. */
+const char* attn_strerror(int code);
+
+/* WINATTN_ABI_VERSION of the built library. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WINATTN_H */

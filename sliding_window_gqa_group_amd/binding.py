@@ -1,0 +1,225 @@
+"""ctypes binding of libwinattn.so (include/winattn.h) over torch device tensors.
+
+Argument marshalling only: every step of the attention runs in the library's HIP kernels on the
+caller's (or torch's current) stream. Missing library => ImportError at first use; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwinattn.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "winattn.h")
+
+OK, EINVAL, EWORKSPACE, ELAUNCH, EUNSUPPORTED = 0, -1, -2, -3, -4
+TUNE_FORCE_KERNEL, TUNE_TILES_PER_SPLIT, TUNE_TARGET_BLOCKS = 1, 2, 3
+
+_lib = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+_ip = ctypes.POINTER(ctypes.c_int)
+
+
+class WinattnError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed with code {code}: {strerror(code)}")
+        self.code = code
+
+
+def load(path: str = LIB_PATH):
+    """Load (once) and return the ctypes handle; raises ImportError if the library is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m sliding_window_gqa_group_amd.build` "
+                          "or __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.attn_window_chunk.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _vp, _sz, _vp]
+    lib.attn_window_chunk.restype = _i
+    lib.attn_window_chunk_workspace.argtypes = [_i] * 6
+    lib.attn_window_chunk_workspace.restype = _sz
+    lib.attn_window_gated.argtypes = [_vp] * 10 + [_i] * 7 + [_f, _f, _vp, _sz, _vp]
+    lib.attn_window_gated.restype = _i
+    lib.attn_window_gated_workspace.argtypes = [_i] * 5
+    lib.attn_window_gated_workspace.restype = _sz
+    lib.attn_workspace_init.argtypes = [_vp, _sz, _vp]
+    lib.attn_workspace_init.restype = _i
+    lib.attn_window_check_meta.argtypes = [_vp, _i, _i]
+    lib.attn_window_check_meta.restype = _i
+    lib.attn_window_chunk_plan.argtypes = [_i] * 6 + [_ip] * 4
+    lib.attn_window_chunk_plan.restype = _i
+    lib.attn_mfma_layout_probe.argtypes = [_vp, _vp]
+    lib.attn_mfma_layout_probe.restype = _i
+    lib.attn_tuning_set.argtypes = [_i, _i]
+    lib.attn_tuning_set.restype = _i
+    lib.attn_strerror.argtypes = [_i]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_abi_version.argtypes = []
+    lib.attn_abi_version.restype = _i
+    _lib = lib
+    return lib
+
+
+def declared_functions(header: str = HEADER):
+    """Names of the functions include/winattn.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def strerror(code: int) -> str:
+    return load().attn_strerror(int(code)).decode()
+
+
+def abi_version() -> int:
+    return load().attn_abi_version()
+
+
+def tuning_set(knob: int, value: int) -> None:
+    rc = load().attn_tuning_set(knob, value)
+    if rc != OK:
+        raise WinattnError("attn_tuning_set", rc)
+
+
+def chunk_workspace_bytes(rows, ng, hpg, d, w, ns) -> int:
+    return int(load().attn_window_chunk_workspace(rows, ng, hpg, d, w, ns))
+
+
+def gated_workspace_bytes(rows, nh, nk, hd, window) -> int:
+    return int(load().attn_window_gated_workspace(rows, nh, nk, hd, window))
+
+
+def chunk_plan(rows, ng, hpg, d, w, ns):
+    """(kernel 1=VALU 2=MFMA, query block, splits, keys per split) for these sizes."""
+    vals = [ctypes.c_int(0) for _ in range(4)]
+    rc = load().attn_window_chunk_plan(rows, ng, hpg, d, w, ns, *[ctypes.byref(v) for v in vals])
+    if rc != OK:
+        raise WinattnError("attn_window_chunk_plan", rc)
+    return tuple(v.value for v in vals)
+
+
+def check_meta(meta_host, ng: int, w: int) -> int:
+    import numpy as np
+    m = np.ascontiguousarray(meta_host, dtype=np.uint32)
+    return load().attn_window_check_meta(m.ctypes.data, ng, w)
+
+
+# ── workspaces ──────────────────────────────────────────────────────────────────────────────
+
+class Workspace:
+    """Zero-initialised device scratch for one stream; grows on demand (a growth is a fresh
+    zeroed allocation, so the counters the library keeps there start at zero)."""
+
+    def __init__(self, device):
+        self.device = torch.device(device)
+        self.buf = None
+
+    def get(self, nbytes: int):
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self.buf.data_ptr(), self.buf.numel()
+
+
+_workspaces = {}
+
+
+def _default_workspace(device, stream_ptr):
+    key = (torch.device(device).index, stream_ptr)
+    ws = _workspaces.get(key)
+    if ws is None:
+        ws = _workspaces[key] = Workspace(device)
+    return ws
+
+
+def _ptr(t, name, dtypes=(torch.float32,)):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream_ptr(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def attn_window_chunk(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v, scale,
+                      out=None, workspace=None, stream=None):
+    """out[rows][nh][d] = windowed GQA attention of a chunk (see include/winattn.h).
+
+    ring_k/ring_v [ng][w][d], meta [ng][4] int32/uint32, sink_k/sink_v [ng][ns][d] (or None),
+    q [rows][nh][d], chunk_k/chunk_v [rows][ng][d].
+    """
+    ng, w, d = ring_k.shape
+    rows, nh, dq = q.shape
+    if dq != d or nh % ng:
+        raise ValueError("q must be [rows][ng*hpg][d] matching ring_k [ng][w][d]")
+    ns = 0 if sink_k is None else sink_k.shape[1]
+    if out is None:
+        out = torch.empty((rows, nh, d), dtype=torch.float32, device=q.device)
+    st = _stream_ptr(stream, q.device)
+    need = chunk_workspace_bytes(rows, ng, nh // ng, d, w, ns)
+    ws = workspace if workspace is not None else _default_workspace(q.device, st)
+    wp, wb = ws.get(need)
+    rc = load().attn_window_chunk(
+        _ptr(ring_k, "ring_k"), _ptr(ring_v, "ring_v"),
+        _ptr(meta, "meta", (torch.int32, torch.uint32)), _ptr(sink_k, "sink_k"),
+        _ptr(sink_v, "sink_v"), _ptr(q, "q"), _ptr(chunk_k, "chunk_k"), _ptr(chunk_v, "chunk_v"),
+        _ptr(out, "out"), rows, ng, nh // ng, d, w, ns, float(scale), wp, wb, st)
+    if rc != OK:
+        raise WinattnError("attn_window_chunk", rc)
+    return out
+
+
+def attn_window_gated(yq, yk, yv, rope, q_scale, gate, gate_scale, ring_k, ring_v, pos0, window,
+                      scale, eps, out=None, workspace=None, stream=None):
+    """z[rows][nh][hd] of the gated unit-head call; writes the rows' ring slots."""
+    rows, nh, hd = yq.shape
+    nk = yk.shape[1]
+    cap = ring_k.shape[0]
+    if out is None:
+        out = torch.empty((rows, nh, hd), dtype=torch.float32, device=yq.device)
+    st = _stream_ptr(stream, yq.device)
+    need = gated_workspace_bytes(rows, nh, nk, hd, window)
+    ws = workspace if workspace is not None else _default_workspace(yq.device, st)
+    wp, wb = ws.get(need)
+    rc = load().attn_window_gated(
+        _ptr(yq, "yq"), _ptr(yk, "yk"), _ptr(yv, "yv"), _ptr(rope, "rope"),
+        _ptr(q_scale, "q_scale"), _ptr(gate, "gate"), _ptr(gate_scale, "gate_scale"),
+        _ptr(ring_k, "ring_k"), _ptr(ring_v, "ring_v"), _ptr(out, "out"), rows, int(pos0), cap,
+        int(window), nh, nk, hd, float(scale), float(eps), wp, wb, st)
+    if rc != OK:
+        raise WinattnError("attn_window_gated", rc)
+    return out
+
+
+def mfma_layout_probe(device="cuda", stream=None):
+    """[64][16] accumulator map of one 32x32x2 f32 matrix-core product (see the header)."""
+    out = torch.full((64, 16), -1.0, dtype=torch.float32, device=device)
+    rc = load().attn_mfma_layout_probe(out.data_ptr(), _stream_ptr(stream, out.device))
+    if rc != OK:
+        raise WinattnError("attn_mfma_layout_probe", rc)
+    return out
+
+
+def workspace_init(buf: torch.Tensor, stream=None) -> None:
+    st = _stream_ptr(stream, buf.device)
+    rc = load().attn_workspace_init(buf.data_ptr(), buf.numel() * buf.element_size(), st)
+    if rc != OK:
+        raise WinattnError("attn_workspace_init", rc)

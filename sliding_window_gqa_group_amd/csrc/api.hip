@@ -1,0 +1,340 @@
+// The C-ABI of winattn.h: argument validation, the launch plan (kernel, query block, key
+// splits, workspace layout) and dispatch on the caller's stream. Nothing here allocates or
+// synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "launch.h"
+#include "winattn.h"
+
+namespace winattn {
+namespace {
+
+// Tuning knobs (attn_tuning_set); 0 = automatic.
+int g_force_kernel = 0;     // 1 VALU, 2 MFMA
+int g_tiles_per_split = 0;
+int g_target_blocks = 0;
+
+constexpr int kValuMaxQ = 16;
+// Split counters sit at the start of every workspace, at the same place for every plan, so
+// that a workspace reused by calls of other shapes never finds partial sums where it expects
+// counters. Plans with more query blocks than counters run unsplit (they fill the GPU anyway).
+constexpr size_t kTicketBytes = 64 * 1024;
+constexpr long long kMaxTickets = kTicketBytes / sizeof(unsigned int);
+
+struct Plan {
+    bool mfma;
+    int dpad;
+    int qb;             // query vectors per block
+    int nqblocks;
+    int tk;             // keys per tile
+    int tps;            // tiles per split
+    int nsplit;         // splits reserved per block
+    size_t off_q, off_pacc, off_pm, off_pl, off_tickets, bytes;
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+int pad_d(int d) { return d <= 64 ? 64 : (d <= 128 ? 128 : 256); }
+
+// rows/hpg/d: the call's shape; wcap: the largest window any row can have; qbuf_floats: extra
+// workspace for the gated call's prepared queries.
+Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_floats) {
+    Plan pl{};
+    const long long nq_tot = (long long)rows * hpg;
+    pl.dpad = pad_d(d);
+    pl.mfma = nq_tot > kValuMaxQ;
+    if (g_force_kernel == 1) pl.mfma = false;
+    if (g_force_kernel == 2) pl.mfma = true;
+    if (pl.mfma) {
+        pl.qb = mfma_query_block();
+        pl.tk = mfma_tile_keys();
+    } else {
+        pl.qb = nq_tot <= 4 ? 4 : (nq_tot <= 8 ? 8 : 16);
+        pl.tk = valu_tile_keys(pl.dpad);
+    }
+    pl.nqblocks = cdiv(nq_tot, pl.qb);
+    // A block of qb consecutive (row, head) queries spans at most this many rows.
+    const long long span = std::min<long long>(rows, (pl.qb - 1) / hpg + 2);
+    // Longest stream range a block can cover (sinks are extra tiles of split 0).
+    const long long keys_max = (long long)wcap + span - 1;
+    const int max_tiles = cdiv(keys_max, pl.tk);
+    const long long blocks = (long long)pl.nqblocks * ng;
+    const int target = g_target_blocks > 0 ? g_target_blocks : (pl.mfma ? 1024 : 256);
+    int s_target = cdiv(target, blocks);
+    if (s_target < 1) s_target = 1;
+    if (s_target > max_tiles) s_target = max_tiles;
+    int tps = cdiv(max_tiles, s_target);
+    // A matrix-core split should amortise its partial (qb x d floats) over a few tiles.
+    const int tps_min = pl.mfma ? 4 : 1;
+    if (tps < tps_min) tps = tps_min;
+    // Long windows: bound a split's work so the blocks of unequal groups balance.
+    const int tps_cap = pl.mfma ? 128 : 64;
+    if (tps > tps_cap) tps = tps_cap;
+    // The merge is one CU reading every split's partial of a block: keep that under 2 MiB.
+    const long long nsplit_cap = std::max<long long>(1, (2LL << 20) / ((long long)pl.qb * pl.dpad * 4));
+    if (cdiv(max_tiles, tps) > nsplit_cap) tps = cdiv(max_tiles, nsplit_cap);
+    if (g_tiles_per_split > 0) tps = g_tiles_per_split;
+    if (blocks > kMaxTickets) tps = max_tiles;
+    pl.tps = tps;
+    pl.nsplit = cdiv(max_tiles, tps);
+
+    // Layout: [counters][prepared queries][partials], each region 256-byte aligned.
+    const bool split = pl.nsplit > 1;
+    if (!split && qbuf_floats == 0) {
+        pl.bytes = 0;
+        return pl;
+    }
+    size_t off = 0;
+    pl.off_tickets = off;
+    off += kTicketBytes;
+    pl.off_q = off;
+    off = align_up(off + qbuf_floats * sizeof(float), 256);
+    if (split) {
+        const size_t slots = (size_t)blocks * pl.nsplit * pl.qb;
+        pl.off_pacc = off;
+        off = align_up(off + slots * pl.dpad * sizeof(float), 256);
+        pl.off_pm = off;
+        off = align_up(off + slots * sizeof(float), 256);
+        pl.off_pl = off;
+        off = align_up(off + slots * sizeof(float), 256);
+    }
+    pl.bytes = off;
+    return pl;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool chunk_shape_ok(int rows, int ng, int hpg, int d, int w, int ns) {
+    if (rows < 1 || ng < 1 || hpg < 1 || w < 1 || ns < 0) return false;
+    if (d < 4 || d > 256 || d % 4 != 0) return false;
+    // Keep every index the kernels form inside 32 bits.
+    if (rows > (1 << 24) || w > (1 << 28) || ns > (1 << 20)) return false;
+    if ((long long)ng * hpg > (1 << 16)) return false;
+    if ((long long)rows * ng * hpg > (1LL << 30)) return false;
+    return true;
+}
+
+bool gated_shape_ok(int rows, int pos0, int cap, int window, int nh, int nk, int hd) {
+    if (rows < 1 || pos0 < 0 || cap < 1 || window < 1 || nh < 1 || nk < 1) return false;
+    if (nh % nk != 0 || hd < 8 || hd > 256 || hd % 8 != 0) return false;
+    if (rows > (1 << 24) || cap > (1 << 28) || window > (1 << 28) || nh > (1 << 16)) return false;
+    if ((long long)pos0 + rows > 0x7ffffff0LL) return false;
+    if ((long long)cap < (long long)window + rows - 1) return false;
+    return true;
+}
+
+int launch_attention(const Plan& pl, AttnParams& p, bool gated, char* ws, hipStream_t stream) {
+    p.tps = pl.tps;
+    p.nsplit_grid = pl.nsplit;
+    p.nqblocks = pl.nqblocks;
+    if (pl.nsplit > 1) {
+        p.pacc = reinterpret_cast<float*>(ws + pl.off_pacc);
+        p.pm = reinterpret_cast<float*>(ws + pl.off_pm);
+        p.pl = reinterpret_cast<float*>(ws + pl.off_pl);
+        p.tickets = reinterpret_cast<unsigned int*>(ws + pl.off_tickets);
+    }
+    hipError_t err;
+    if (pl.mfma)
+        err = launch_mfma(p, gated, pl.dpad, stream);
+    else
+        err = launch_valu(p, gated, pl.dpad, pl.qb, dim3(pl.nsplit, pl.nqblocks, p.ng), stream);
+    return err == hipSuccess ? WINATTN_OK : WINATTN_ELAUNCH;
+}
+
+}  // namespace
+}  // namespace winattn
+
+using namespace winattn;
+
+extern "C" {
+
+int attn_abi_version(void) { return WINATTN_ABI_VERSION; }
+
+const char* attn_strerror(int code) {
+    switch (code) {
+        case WINATTN_OK: return "success";
+        case WINATTN_EINVAL: return "invalid argument (size, pointer, alignment or constraint)";
+        case WINATTN_EWORKSPACE: return "workspace missing or too small";
+        case WINATTN_ELAUNCH: return "kernel launch failed";
+        case WINATTN_EUNSUPPORTED: return "unsupported configuration";
+        default: return "unknown error code";
+    }
+}
+
+int attn_window_check_meta(const uint32_t* host_meta, int ng, int w) {
+    if (!host_meta || ng < 1 || w < 1) return WINATTN_EINVAL;
+    for (int g = 0; g < ng; ++g) {
+        const uint32_t len = host_meta[4 * g], head = host_meta[4 * g + 1], ov = host_meta[4 * g + 3];
+        if (ov > (uint32_t)w) return WINATTN_EINVAL;
+        const uint32_t wg = ov != 0u ? ov : (uint32_t)w;
+        if (len > wg) return WINATTN_EINVAL;
+        if (len > 0 && head >= wg) return WINATTN_EINVAL;
+    }
+    return WINATTN_OK;
+}
+
+size_t attn_window_chunk_workspace(int rows, int ng, int hpg, int d, int w, int ns) {
+    if (!chunk_shape_ok(rows, ng, hpg, d, w, ns)) return 0;
+    return make_plan(rows, ng, hpg, d, w, ns, 0).bytes;
+}
+
+int attn_window_chunk(const float* ring_k, const float* ring_v, const uint32_t* meta,
+                      const float* sink_k, const float* sink_v, const float* q,
+                      const float* chunk_k, const float* chunk_v, float* out, int rows, int ng,
+                      int hpg, int d, int w, int ns, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    if (!chunk_shape_ok(rows, ng, hpg, d, w, ns) || !std::isfinite(scale)) return WINATTN_EINVAL;
+    if (!ring_k || !ring_v || !meta || !q || !chunk_k || !chunk_v || !out) return WINATTN_EINVAL;
+    if (ns > 0 && (!sink_k || !sink_v)) return WINATTN_EINVAL;
+    if (!aligned16(ring_k) || !aligned16(ring_v) || !aligned16(q) || !aligned16(chunk_k) ||
+        !aligned16(chunk_v) || !aligned16(out) || ((uintptr_t)meta & 3u) != 0)
+        return WINATTN_EINVAL;
+    if (ns > 0 && (!aligned16(sink_k) || !aligned16(sink_v))) return WINATTN_EINVAL;
+    const Plan pl = make_plan(rows, ng, hpg, d, w, ns, 0);
+    if (pl.bytes > 0 && (!workspace || workspace_bytes < pl.bytes)) return WINATTN_EWORKSPACE;
+    if (pl.bytes > 0 && !aligned16(workspace)) return WINATTN_EINVAL;
+
+    AttnParams p{};
+    p.ring_k = ring_k;
+    p.ring_v = ring_v;
+    p.meta = meta;
+    p.sink_k = ns > 0 ? sink_k : nullptr;
+    p.sink_v = ns > 0 ? sink_v : nullptr;
+    p.q = q;
+    p.chunk_k = chunk_k;
+    p.chunk_v = chunk_v;
+    p.out = out;
+    p.ring_gs = (long long)w * d;
+    p.ring_ss = d;
+    p.chunk_rs = (long long)ng * d;
+    p.chunk_gs = d;
+    p.rows = rows;
+    p.ng = ng;
+    p.hpg = hpg;
+    p.nh = ng * hpg;
+    p.d = d;
+    p.w = w;
+    p.ns = ns;
+    p.scale_log2 = scale * kLog2e;
+    return launch_attention(pl, p, false, static_cast<char*>(workspace),
+                            static_cast<hipStream_t>(stream));
+}
+
+size_t attn_window_gated_workspace(int rows, int nh, int nk, int hd, int window) {
+    if (rows < 1 || nh < 1 || nk < 1 || window < 1 || nh % nk != 0 || hd < 8 || hd > 256 ||
+        hd % 8 != 0)
+        return 0;
+    return make_plan(rows, nk, nh / nk, hd, window, 0, (size_t)rows * nh * hd).bytes;
+}
+
+int attn_window_gated(const float* yq, const float* yk, const float* yv, const float* rope,
+                      const float* q_scale, const float* gate, const float* gate_scale,
+                      float* ring_k, float* ring_v, float* out, int rows, int pos0, int cap,
+                      int window, int nh, int nk, int hd, float scale, float eps,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (!gated_shape_ok(rows, pos0, cap, window, nh, nk, hd)) return WINATTN_EINVAL;
+    if (!std::isfinite(scale) || !std::isfinite(eps) || eps < 0.0f) return WINATTN_EINVAL;
+    const void* ptrs[] = {yq, yk, yv, rope, q_scale, gate, gate_scale, ring_k, ring_v, out};
+    for (const void* ptr : ptrs)
+        if (!ptr || !aligned16(ptr)) return WINATTN_EINVAL;
+    const int hpg = nh / nk;
+    const Plan pl = make_plan(rows, nk, hpg, hd, window, 0, (size_t)rows * nh * hd);
+    if (!workspace || workspace_bytes < pl.bytes) return WINATTN_EWORKSPACE;
+    if (!aligned16(workspace)) return WINATTN_EINVAL;
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    PrepParams pp{};
+    pp.yq = yq;
+    pp.yk = yk;
+    pp.yv = yv;
+    pp.rope = rope;
+    pp.q_scale = q_scale;
+    pp.qout = reinterpret_cast<float*>(ws + pl.off_q);
+    pp.ring_k = ring_k;
+    pp.ring_v = ring_v;
+    pp.rows = rows;
+    pp.pos0 = pos0;
+    pp.cap = cap;
+    pp.nh = nh;
+    pp.nk = nk;
+    pp.hd = hd;
+    pp.eps = eps;
+    if (launch_gated_prep(pp, st) != hipSuccess) return WINATTN_ELAUNCH;
+
+    // Positions from p0 on, as a ring descriptor: entry x is position p0 + x at slot
+    // (p0 + x) mod cap; row r's window ends at position pos0 + r.
+    const long long p0 = std::max<long long>(0, (long long)pos0 + 1 - window);
+    AttnParams p{};
+    p.ring_k = ring_k;
+    p.ring_v = ring_v;
+    p.q = pp.qout;
+    p.out = out;
+    p.gate = gate;
+    p.gate_scale = gate_scale;
+    p.ring_gs = hd;
+    p.ring_ss = (long long)nk * hd;
+    p.rows = rows;
+    p.ng = nk;
+    p.hpg = hpg;
+    p.nh = nh;
+    p.d = hd;
+    p.w = window;
+    p.ns = 0;
+    p.scale_log2 = scale * kLog2e;
+    p.g_base = (int)(p0 % cap);
+    p.g_mod = cap;
+    p.g_hi0 = (int)((long long)pos0 + 1 - p0);
+    p.g_wcap = window;
+    return launch_attention(pl, p, true, ws, st);
+}
+
+int attn_workspace_init(void* workspace, size_t bytes, void* stream) {
+    if (bytes == 0) return WINATTN_OK;
+    if (!workspace || !aligned16(workspace)) return WINATTN_EINVAL;
+    return launch_fill_zero(workspace, bytes, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? WINATTN_OK
+               : WINATTN_ELAUNCH;
+}
+
+int attn_window_chunk_plan(int rows, int ng, int hpg, int d, int w, int ns, int* kernel,
+                           int* query_block, int* splits, int* keys_per_split) {
+    if (!chunk_shape_ok(rows, ng, hpg, d, w, ns)) return WINATTN_EINVAL;
+    const Plan pl = make_plan(rows, ng, hpg, d, w, ns, 0);
+    if (kernel) *kernel = pl.mfma ? 2 : 1;
+    if (query_block) *query_block = pl.qb;
+    if (splits) *splits = pl.nsplit;
+    if (keys_per_split) *keys_per_split = pl.tps * pl.tk;
+    return WINATTN_OK;
+}
+
+int attn_mfma_layout_probe(float* out, void* stream) {
+    if (!out) return WINATTN_EINVAL;
+    return launch_mfma_probe(out, static_cast<hipStream_t>(stream)) == hipSuccess ? WINATTN_OK
+                                                                                  : WINATTN_ELAUNCH;
+}
+
+int attn_tuning_set(int knob, int value) {
+    if (value < 0) return WINATTN_EINVAL;
+    switch (knob) {
+        case WINATTN_TUNE_FORCE_KERNEL:
+            if (value > 2) return WINATTN_EINVAL;
+            g_force_kernel = value;
+            return WINATTN_OK;
+        case WINATTN_TUNE_TILES_PER_SPLIT:
+            g_tiles_per_split = value;
+            return WINATTN_OK;
+        case WINATTN_TUNE_TARGET_BLOCKS:
+            g_target_blocks = value;
+            return WINATTN_OK;
+        default:
+            return WINATTN_EINVAL;
+    }
+}
+
+}  // extern "C"

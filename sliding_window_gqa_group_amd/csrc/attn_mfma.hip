@@ -1,0 +1,270 @@
+// Split-K windowed attention on the f32 matrix cores, for chunks with many query vectors per
+// KV group (prefill and wide verify chunks).
+//
+// Prior art: the o1c page's GEMM path (`o1c_gather`, `o1c_gmax`, `o1c_gsoft`, `o1c_gadd`:
+// a per-group panel of sinks, ring and chunk keys, score and value GEMMs, live-column masks)
+// and the staged flash kernels of the egemma2 page (K/V blocks in threadgroup memory shared by
+// several query tiles). Here nothing is materialised: scores stay in registers, and K/V tiles
+// are staged once per workgroup in LDS and shared by its four waves.
+//
+// Layout on v_mfma_f32_32x32x2f32 (A 32x2, B 2x32, 16 accumulators per lane; lane l supplies
+// A[l%32][l/32] and B[l/32][l%32]; accumulator r of lane l is element
+// (8*(r/4) + 4*(l/32) + r%4, l%32)):
+//   scores    S^T = K . Q^T   A = K tile (32 keys x d, from LDS), B = Q^T (registers)
+//             -> lane l holds query l%32 against keys 8*(r/4) + 4*(l/32) + r%4
+//   values    O^T = V^T . P^T A = V^T (from LDS), B = P^T = exactly the score registers
+//             after the softmax step, so P never leaves the lane
+// Each k-step of the score product takes d indices {8c + r, 8c + 4 + r} from the two lane
+// halves, which lets every lane read its K and Q operands as float4s.
+//
+// A workgroup owns 128 consecutive query vectors (row-major over (row, head) of one group),
+// 32 per wave, and one split of the key tiles that the block's rows can see. Work items are
+// mapped XCD-aware: consecutive query blocks of one (group, split) read nearly the same K/V
+// tiles, so they are placed on the same XCD to share its L2.
+#include "winattn_dev.h"
+#include "launch.h"
+
+namespace winattn {
+
+constexpr int kMfmaQB = 128;
+constexpr int kMfmaTK = 32;
+
+template <int D, bool GATED>
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(const AttnParams p) {
+    constexpr int TK = kMfmaTK, QB = kMfmaQB;
+    constexpr int D4 = D / 4, KST = D + 4, VST = D + 8;
+    constexpr int LPT = TK * D4 / kThreads;   // float4 loads per thread per tensor per tile
+    constexpr int NDB = D / 32;               // 32-wide d blocks of the output
+    static_assert(LPT >= 1 && TK * D4 == LPT * kThreads, "tile load must cover the tile");
+    static_assert(TK * KST >= kMergeScratch, "merge scratch reuses the K tile area");
+
+    __shared__ __align__(16) float s_k[TK * KST];
+    __shared__ __align__(16) float s_v[TK * VST];
+    __shared__ int s_flag;
+
+    // XCD-aware decode of the work item: hardware deals blocks to the 8 XCDs round-robin.
+    const int n_items = p.nsplit_grid * p.nqblocks * p.ng;
+    const int per_xcd = (n_items + 7) / 8;
+    const int item = (int)(blockIdx.x % 8u) * per_xcd + (int)(blockIdx.x / 8u);
+    if (item >= n_items) return;
+    const int qb = item % p.nqblocks;
+    const int split = (item / p.nqblocks) % p.nsplit_grid;
+    const int g = item / (p.nqblocks * p.nsplit_grid);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int qcol = lane & 31, hb = lane >> 5;
+    const int nq_tot = p.rows * p.hpg;
+    const int q0 = qb * QB;
+    const int nq = min(QB, nq_tot - q0);
+    const GroupWin gw = resolve_group<GATED>(p, g);
+
+    const int r_first = q0 / p.hpg, r_last = (q0 + nq - 1) / p.hpg;
+    const int hi_first = gw.hi0 + r_first;
+    const int xlo = window_lo(hi_first, gw.wcap);
+    const int xhi = gw.hi0 + r_last;
+    const Tiles tr = tile_range<TK>(p.ns, xlo, xhi, p.tps, split);
+    const int nsplit = tr.nsplit, nst = tr.nst;
+    if (split >= nsplit) return;
+    const int t_begin = tr.t_begin, t_end = tr.t_end;
+    const int d4 = p.d / 4;
+
+    // This lane's query (column qcol of its wave's 32) and its window in key-index space.
+    const int jq = wave * 32 + qcol;
+    const bool qvalid = jq < nq;
+    const int qi = q0 + (qvalid ? jq : nq - 1);
+    const int row = qi / p.hpg, gh = g * p.hpg + qi % p.hpg;
+    const int hi = gw.hi0 + row;
+    const int lo = window_lo(hi, gw.wcap);
+
+    float4 kreg[LPT], vreg[LPT];
+    auto load_tile = [&](int t) {
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) {
+            const int f = tid + kThreads * j;
+            const int key = f / D4, c = f % D4;
+            long long off = 0;
+            const int src = key_offset<TK>(p, gw, g, xlo, xhi, nst, t, key, off);
+            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+            if (src >= 0 && c < d4) {
+                const float *kp, *vp;
+                key_ptrs(p, src, off, kp, vp);
+                kv = *reinterpret_cast<const float4*>(kp + 4 * c);
+                vv = *reinterpret_cast<const float4*>(vp + 4 * c);
+            }
+            kreg[j] = kv;
+            vreg[j] = vv;
+        }
+    };
+
+    load_tile(t_begin);   // first tile in flight while the queries load
+
+    // Q^T operand: qreg[4c + r] = scale*log2e * q[8c + 4*hb + r].
+    float qreg[D / 2];
+    {
+        const float* qp = p.q + ((size_t)row * p.nh + gh) * p.d;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            const int e = 8 * c + 4 * hb;
+            if (e < p.d) v = *reinterpret_cast<const float4*>(qp + e);
+            qreg[4 * c + 0] = v.x * p.scale_log2;
+            qreg[4 * c + 1] = v.y * p.scale_log2;
+            qreg[4 * c + 2] = v.z * p.scale_log2;
+            qreg[4 * c + 3] = v.w * p.scale_log2;
+        }
+    }
+
+    floatx16 oacc[NDB];
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[b][r] = 0.0f;
+    float mrun = -INFINITY, lrun = 0.0f;
+
+    for (int t = t_begin; t < t_end; ++t) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) {
+            const int f = tid + kThreads * j;
+            const int key = f / D4, c = f % D4;
+            *reinterpret_cast<float4*>(s_k + key * KST + 4 * c) = kreg[j];
+            *reinterpret_cast<float4*>(s_v + key * VST + 4 * c) = vreg[j];
+        }
+        __syncthreads();
+        if (t + 1 < t_end) load_tile(t + 1);
+
+        const int tx = xlo + (t - nst) * TK;   // first stream entry of a stream tile
+        const bool sees = t < nst || (tx < hi && tx + TK > lo);
+        if (!__any(sees)) continue;   // the whole wave's queries miss this tile
+
+        floatx16 sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+        const float* kr = s_k + qcol * KST + 4 * hb;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+            const float4 k4 = *reinterpret_cast<const float4*>(kr + 8 * c);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.x, qreg[4 * c + 0], sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.y, qreg[4 * c + 1], sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.z, qreg[4 * c + 2], sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.w, qreg[4 * c + 3], sacc, 0, 0, 0);
+        }
+
+        // Mask by select (never multiply: masked slots may hold anything), online softmax.
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const bool vis = key_visible<TK>(p.ns, xlo, nst, t, 8 * (r >> 2) + 4 * hb + (r & 3),
+                                             lo, hi, true);
+            sacc[r] = vis ? sacc[r] : -INFINITY;
+            tmax = fmaxf(tmax, sacc[r]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(mrun, tmax);
+        const float mu = safe_max(m_new);
+        const float corr = __builtin_amdgcn_exp2f(mrun - mu);
+        float psum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            sacc[r] = __builtin_amdgcn_exp2f(sacc[r] - mu);
+            psum += sacc[r];
+        }
+        psum += __shfl_xor(psum, 32);
+        lrun = lrun * corr + psum;
+        mrun = m_new;
+#pragma unroll
+        for (int b = 0; b < NDB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[b][r] *= corr;
+
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float* vr = s_v + (8 * (r >> 2) + 4 * hb + (r & 3)) * VST + qcol;
+#pragma unroll
+            for (int b = 0; b < NDB; ++b)
+                oacc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[32 * b], sacc[r], oacc[b], 0, 0, 0);
+        }
+    }
+
+    // Lane holds, for its query, d = 32b + 8m + 4*hb + (0..3) in oacc[b][4m .. 4m+3].
+    const int blk = g * p.nqblocks + qb;
+    if (nsplit == 1) {
+        if (qvalid) {
+            const float inv = 1.0f / fmaxf(lrun, 1e-30f);
+#pragma unroll
+            for (int b = 0; b < NDB; ++b)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int e = 32 * b + 8 * m + 4 * hb;
+                    if (e < p.d) {
+                        float4 o = make_float4(oacc[b][4 * m] * inv, oacc[b][4 * m + 1] * inv,
+                                               oacc[b][4 * m + 2] * inv, oacc[b][4 * m + 3] * inv);
+                        store_out<GATED>(p, qi, g, e, o);
+                    }
+                }
+        }
+        return;
+    }
+    if (qvalid) {
+        const size_t at = ((size_t)blk * p.nsplit_grid + split) * QB + jq;
+#pragma unroll
+        for (int b = 0; b < NDB; ++b)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int e = 32 * b + 8 * m + 4 * hb;
+                store_dev4(p.pacc + at * D + e, make_float4(oacc[b][4 * m], oacc[b][4 * m + 1],
+                                                            oacc[b][4 * m + 2], oacc[b][4 * m + 3]));
+            }
+        if (hb == 0) {
+            store_dev(p.pm + at, mrun);
+            store_dev(p.pl + at, lrun);
+        }
+    }
+    merge_if_last<QB, D, GATED>(p, blk, nsplit, q0, nq, g, &s_flag, s_k);
+}
+
+template <int D, bool GATED>
+static hipError_t launch_mfma_t(const AttnParams& p, hipStream_t stream) {
+    const int n_items = p.nsplit_grid * p.nqblocks * p.ng;
+    const int blocks = 8 * ((n_items + 7) / 8);
+    hipLaunchKernelGGL((attn_mfma_kernel<D, GATED>), dim3(blocks), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma(const AttnParams& p, bool gated, int dpad, hipStream_t stream) {
+    if (gated) {
+        if (dpad == 64) return launch_mfma_t<64, true>(p, stream);
+        if (dpad == 128) return launch_mfma_t<128, true>(p, stream);
+        if (dpad == 256) return launch_mfma_t<256, true>(p, stream);
+    } else {
+        if (dpad == 64) return launch_mfma_t<64, false>(p, stream);
+        if (dpad == 128) return launch_mfma_t<128, false>(p, stream);
+        if (dpad == 256) return launch_mfma_t<256, false>(p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Layout probe of v_mfma_f32_32x32x2f32: A[i][0] = i, A[i][1] = 1, B[0][j] = 1,
+// B[1][j] = 64 j, so D[i][j] = i + 64 j names its own position. out[lane * 16 + r] receives
+// accumulator r of lane `lane`.
+__global__ __launch_bounds__(64) void mfma_layout_probe_kernel(float* out) {
+    const int lane = threadIdx.x;
+    const float a = lane < 32 ? (float)lane : 1.0f;
+    const float b = lane < 32 ? 1.0f : 64.0f * (float)(lane - 32);
+    floatx16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) out[lane * 16 + r] = acc[r];
+}
+
+hipError_t launch_mfma_probe(float* out, hipStream_t stream) {
+    hipLaunchKernelGGL(mfma_layout_probe_kernel, dim3(1), dim3(64), 0, stream, out);
+    return hipGetLastError();
+}
+
+int mfma_query_block() { return kMfmaQB; }
+int mfma_tile_keys() { return kMfmaTK; }
+
+}  // namespace winattn

@@ -1,0 +1,38 @@
+// Host-side launchers of the attention kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "winattn_dev.h"
+
+namespace winattn {
+
+// Split-K VALU kernel; grid = (splits, query blocks, groups); dpad in {64, 128, 256};
+// nq (query vectors per block) in {4, 8, 16}.
+hipError_t launch_valu(const AttnParams& p, bool gated, int dpad, int nq, dim3 grid,
+                       hipStream_t stream);
+int valu_tile_keys(int dpad);
+
+// Split-K MFMA kernel; 1-D grid over (group, split, query block) items, XCD-aware.
+hipError_t launch_mfma(const AttnParams& p, bool gated, int dpad, hipStream_t stream);
+int mfma_query_block();
+int mfma_tile_keys();
+hipError_t launch_mfma_probe(float* out, hipStream_t stream);
+
+struct PrepParams {
+    const float* yq;
+    const float* yk;
+    const float* yv;
+    const float* rope;
+    const float* q_scale;
+    float* qout;      // [rows][nh][hd] unit queries times the learned scale
+    float* ring_k;    // [cap][nk][hd]
+    float* ring_v;
+    int rows, pos0, cap, nh, nk, hd;
+    float eps;
+};
+hipError_t launch_gated_prep(const PrepParams& p, hipStream_t stream);
+
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
+
+}  // namespace winattn

@@ -1,0 +1,323 @@
+// Device-side pieces shared by the attention kernels: the launch parameters, the per-group
+// window, key addressing over sinks / ring / chunk, wave reductions and the split merge.
+//
+// Window semantics (o1c page, "A sealed layer's attention for a chunk of rows, on Metal":
+// `wgf`, `o1c_score`; dory page, "Dory's token path": `low_key`): every KV group has a logical
+// key stream; row i sees the stream's entries x in [lo_i, hi_i) with hi_i = hi0 + i and
+// lo_i = hi_i - min(wcap, hi_i), plus the group's ns sink keys. Entry x < xsplit lives in the
+// ring at slot (base + x) mod mod; entry x >= xsplit is chunk row x - xsplit.
+//   chunk call:  base = head0, mod = wg, xsplit = len0, hi0 = len0 + 1, wcap = wg
+//   gated call:  positions from P0 = max(0, pos0 + 1 - window) on; base = P0 mod cap,
+//                mod = cap, xsplit = never (the prep kernel wrote the chunk's rows into the
+//                ring), hi0 = pos0 + 1 - P0, wcap = window.
+// In both cases base < mod and every ring entry read has x < mod, so one conditional
+// subtraction gives the slot.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace winattn {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kThreads = 256;
+
+struct AttnParams {
+    const float* ring_k;
+    const float* ring_v;
+    const uint32_t* meta;        // chunk call only
+    const float* sink_k;
+    const float* sink_v;
+    const float* q;              // [rows][nh][d]
+    const float* chunk_k;
+    const float* chunk_v;
+    float* out;                  // [rows][nh][d]
+    const float* gate;           // gated call only: [rows][nh*d]
+    const float* gate_scale;     // gated call only: [nh*d]
+    float* pacc;                 // split partials: [blocks][nsplit_grid][QB][D]
+    float* pm;                   // [blocks][nsplit_grid][QB] running max (log2 domain)
+    float* pl;                   // [blocks][nsplit_grid][QB] running sum
+    unsigned int* tickets;       // [blocks]
+    long long ring_gs, ring_ss;  // ring strides in floats: per group, per slot
+    long long chunk_rs, chunk_gs;
+    int rows, ng, hpg, nh, d, w, ns;
+    int tps;                     // key tiles per split
+    int nsplit_grid;             // splits reserved per query block
+    int nqblocks;                // query blocks per group
+    float scale_log2;            // scale * log2(e): scores live in the log2 domain
+    int g_base, g_mod, g_hi0, g_wcap;   // gated call's ring descriptor
+};
+
+struct GroupWin {
+    int base, mod, xsplit, hi0, wcap;
+};
+
+template <bool GATED>
+__device__ inline GroupWin resolve_group(const AttnParams& p, int g) {
+    GroupWin r;
+    if constexpr (GATED) {
+        r.base = p.g_base;
+        r.mod = p.g_mod;
+        r.xsplit = 0x7fffffff;
+        r.hi0 = p.g_hi0;
+        r.wcap = p.g_wcap;
+    } else {
+        // Out-of-range meta is clamped so that no access leaves the group's ring.
+        const uint32_t* m = p.meta + 4 * g;
+        uint32_t ov = m[3];
+        uint32_t wg = (ov != 0u && ov < (uint32_t)p.w) ? ov : (uint32_t)p.w;
+        uint32_t len0 = m[0] < wg ? m[0] : wg;
+        uint32_t head0 = m[1];
+        if (head0 >= wg) head0 %= wg;
+        r.base = (int)head0;
+        r.mod = (int)wg;
+        r.xsplit = (int)len0;
+        r.hi0 = (int)len0 + 1;
+        r.wcap = (int)wg;
+    }
+    return r;
+}
+
+// First visible stream entry of a row whose window ends (exclusive) at hi.
+__device__ inline int window_lo(int hi, int wcap) { return hi - (wcap < hi ? wcap : hi); }
+
+// Key tiles of a query block: first ceil(ns / TK) sink tiles (sink index t*TK + k), then stream
+// tiles covering the block's stream range [xlo, xhi) (entry xlo + (t - nst)*TK + k). Sink tiles
+// belong to split 0; the stream tiles are cut into splits of `tps` tiles.
+struct Tiles {
+    int nst;       // sink tiles
+    int nstream;   // stream tiles
+    int nsplit;    // splits that have work
+    int t_begin, t_end;
+};
+
+template <int TK>
+__device__ inline Tiles tile_range(int ns, int xlo, int xhi, int tps, int split) {
+    Tiles r;
+    r.nst = (ns + TK - 1) / TK;
+    r.nstream = (xhi - xlo + TK - 1) / TK;
+    r.nsplit = (r.nstream + tps - 1) / tps;
+    r.t_begin = split == 0 ? 0 : r.nst + split * tps;
+    r.t_end = r.nst + min(r.nstream, (split + 1) * tps);
+    return r;
+}
+
+// Offset (floats) of the K/V row of key k of tile t. Returns the source tensor (0 sink, 1 ring,
+// 2 chunk) or -1 for a padding key (past the sinks or past the block's stream range).
+template <int TK>
+__device__ inline int key_offset(const AttnParams& p, const GroupWin& gw, int g, int xlo,
+                                 int xhi, int nst, int t, int k, long long& off) {
+    if (t < nst) {
+        const int si = t * TK + k;
+        if (si >= p.ns) return -1;
+        off = ((long long)g * p.ns + si) * p.d;
+        return 0;
+    }
+    const int x = xlo + (t - nst) * TK + k;
+    if (x >= xhi) return -1;
+    if (x < gw.xsplit) {
+        int slot = gw.base + x;
+        if (slot >= gw.mod) slot -= gw.mod;
+        off = (long long)g * p.ring_gs + (long long)slot * p.ring_ss;
+        return 1;
+    }
+    off = (long long)(x - gw.xsplit) * p.chunk_rs + (long long)g * p.chunk_gs;
+    return 2;
+}
+
+// Whether key k of tile t is visible to a query whose stream window is [lo, hi); `sinks` is
+// false for padding queries.
+template <int TK>
+__device__ inline bool key_visible(int ns, int xlo, int nst, int t, int k, int lo, int hi,
+                                   bool sinks) {
+    if (t < nst) return sinks && t * TK + k < ns;
+    const int x = xlo + (t - nst) * TK + k;
+    return x >= lo && x < hi;
+}
+
+__device__ inline void key_ptrs(const AttnParams& p, int src, long long off, const float*& kp,
+                                const float*& vp) {
+    if (src == 0) {
+        kp = p.sink_k + off;
+        vp = p.sink_v + off;
+    } else if (src == 1) {
+        kp = p.ring_k + off;
+        vp = p.ring_v + off;
+    } else {
+        kp = p.chunk_k + off;
+        vp = p.chunk_v + off;
+    }
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Numerically safe online-softmax step in the log2 domain. Given the running max m_old and the
+// new candidate max, returns the max to subtract (0 while nothing is visible, so that
+// exp2(-inf - m) = 0 instead of NaN).
+__device__ inline float safe_max(float m_new) { return m_new == -INFINITY ? 0.0f : m_new; }
+
+// Gate epilogue of the gated call (`dory_gate`): o / (1 + exp(-g * s)).
+__device__ inline float4 gate4(const AttnParams& p, int row, int gh, int e, float4 o) {
+    const size_t at = (size_t)gh * p.d + e;
+    float4 gv = *reinterpret_cast<const float4*>(p.gate + (size_t)row * p.nh * p.d + at);
+    float4 sv = *reinterpret_cast<const float4*>(p.gate_scale + at);
+    o.x = o.x / (1.0f + expf(-(gv.x * sv.x)));
+    o.y = o.y / (1.0f + expf(-(gv.y * sv.y)));
+    o.z = o.z / (1.0f + expf(-(gv.z * sv.z)));
+    o.w = o.w / (1.0f + expf(-(gv.w * sv.w)));
+    return o;
+}
+
+template <bool GATED>
+__device__ inline void store_out(const AttnParams& p, int qi, int g, int e, float4 o) {
+    const int row = qi / p.hpg, gh = g * p.hpg + qi % p.hpg;
+    if constexpr (GATED) o = gate4(p, row, gh, e, o);
+    *reinterpret_cast<float4*>(p.out + ((size_t)row * p.nh + gh) * p.d + e) = o;
+}
+
+// Split partials cross XCDs, whose L2 caches are not coherent with each other. Rather than
+// agent-scope fences (which write back and invalidate a whole L2 from every workgroup), the
+// partials are written and read with device-scope accesses: relaxed agent-scope atomics,
+// which the compiler emits as stores/loads carrying the device-scope cache bit.
+__device__ inline void store_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void store_dev4(float* p, float4 v) {
+    store_dev(p, v.x);
+    store_dev(p + 1, v.y);
+    store_dev(p + 2, v.z);
+    store_dev(p + 3, v.w);
+}
+__device__ inline float load_dev(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float4 load_dev4(const float* p) {
+    return make_float4(load_dev(p), load_dev(p + 1), load_dev(p + 2), load_dev(p + 3));
+}
+
+// After every split of a query block has written its partial (m, l, acc), the last one to
+// arrive combines them: c = max_s m_s, out = sum_s acc_s 2^(m_s - c) / sum_s l_s 2^(m_s - c)
+// (the token path's partial merge, `o1c_tok_merge`). All threads of the block call it after
+// writing their partials. `scratch` is free LDS of at least kMergeScratch floats.
+//
+// The merge is one CU reading every split's partial of the block, so it is laid out as one
+// round of loads: each thread owns an item (query j, float4 column c) and a subset of the
+// splits, issues all of that subset's loads together, folds them with the online rescaling,
+// and the subsets meet in LDS.
+constexpr int kMergeScratch = 6 * kThreads;
+constexpr int kMergeUnroll = 16;
+
+struct Part {
+    float m, l;
+    float4 a;
+};
+
+__device__ inline void part_fold(Part& x, float m, float l, float4 a) {
+    const float mn = fmaxf(x.m, m), mu = safe_max(mn);
+    const float cx = __builtin_amdgcn_exp2f(x.m - mu), cy = __builtin_amdgcn_exp2f(m - mu);
+    x.l = x.l * cx + l * cy;
+    x.a.x = x.a.x * cx + a.x * cy;
+    x.a.y = x.a.y * cx + a.y * cy;
+    x.a.z = x.a.z * cx + a.z * cy;
+    x.a.w = x.a.w * cx + a.w * cy;
+    x.m = mn;
+}
+
+// Fold splits s = s0, s0 + stride, ... < nsplit of item (j, c) into x, kMergeUnroll at a time.
+template <int QB, int D>
+__device__ inline void fold_splits(const AttnParams& p, size_t base, int j, int c, int s0,
+                                   int stride, int nsplit, Part& x) {
+    for (int s = s0; s < nsplit; s += kMergeUnroll * stride) {
+        float m[kMergeUnroll], l[kMergeUnroll];
+        float4 a[kMergeUnroll];
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) {
+            const int su = s + u * stride;
+            m[u] = -INFINITY;
+            l[u] = 0.0f;
+            a[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (su < nsplit) {
+                const size_t at = base + (size_t)su * QB + j;
+                m[u] = load_dev(p.pm + at);
+                l[u] = load_dev(p.pl + at);
+                a[u] = load_dev4(p.pacc + at * D + 4 * c);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) part_fold(x, m[u], l[u], a[u]);
+    }
+}
+
+template <int QB, int D, bool GATED>
+__device__ inline void merge_if_last(const AttnParams& p, int blk, int nsplit, int q0, int nq,
+                                     int g, int* s_flag, float* scratch) {
+    static_assert(QB <= kThreads && kThreads % QB == 0, "query block must divide the block");
+    // Every thread's device-scope partial stores are acknowledged before the counter moves.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned int prev =
+            __hip_atomic_fetch_add(p.tickets + blk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = (prev == (unsigned int)(nsplit - 1));
+        if (last) __hip_atomic_store(p.tickets + blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = last;
+    }
+    __syncthreads();
+    if (!*s_flag) return;
+
+    constexpr int D4 = D / 4;
+    const int d4 = p.d / 4;
+    const size_t base = (size_t)blk * p.nsplit_grid * QB;
+    constexpr int ITEMS = QB * D4;
+    if constexpr (ITEMS >= kThreads) {
+        constexpr int IPT = ITEMS / kThreads;
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) {
+            const int item = threadIdx.x + kThreads * k;
+            const int j = item / D4, c = item % D4;
+            Part x{-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
+            fold_splits<QB, D>(p, base, j, c, 0, 1, nsplit, x);
+            if (j < nq && c < d4) {
+                const float inv = 1.0f / fmaxf(x.l, 1e-30f);
+                store_out<GATED>(p, q0 + j, g, 4 * c,
+                                 make_float4(x.a.x * inv, x.a.y * inv, x.a.z * inv, x.a.w * inv));
+            }
+        }
+    } else {
+        constexpr int NSUB = kThreads / ITEMS;
+        const int item = threadIdx.x % ITEMS, sub = threadIdx.x / ITEMS;
+        const int j = item / D4, c = item % D4;
+        Part x{-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
+        fold_splits<QB, D>(p, base, j, c, sub, NSUB, nsplit, x);
+        float* s_m = scratch;
+        float* s_l = scratch + kThreads;
+        float4* s_a = reinterpret_cast<float4*>(scratch + 2 * kThreads);
+        s_m[threadIdx.x] = x.m;
+        s_l[threadIdx.x] = x.l;
+        s_a[threadIdx.x] = x.a;
+        __syncthreads();
+        if (threadIdx.x < ITEMS && j < nq && c < d4) {
+            for (int u = 1; u < NSUB; ++u) {
+                const int t = u * ITEMS + item;
+                part_fold(x, s_m[t], s_l[t], s_a[t]);
+            }
+            const float inv = 1.0f / fmaxf(x.l, 1e-30f);
+            store_out<GATED>(p, q0 + j, g, 4 * c,
+                             make_float4(x.a.x * inv, x.a.y * inv, x.a.z * inv, x.a.w * inv));
+        }
+    }
+}
+
+}  // namespace winattn

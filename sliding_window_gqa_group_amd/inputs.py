@@ -183,3 +183,16 @@ def large(seed: int = 4) -> ChunkInputs:
 
 CHUNK_CONFIGS = {"tiny": tiny, "decode": decode, "prefill": prefill, "large": large}
 GATED_CONFIGS = {"gated": gated}
+
+
+def to_device(inp, device="cuda"):
+    """The arrays of a ChunkInputs / GatedInputs as contiguous torch tensors on `device`."""
+    import torch
+    out = {}
+    for name, val in vars(inp).items():
+        if isinstance(val, np.ndarray):
+            if val.dtype == np.uint32:
+                out[name] = torch.from_numpy(val.view(np.int32).copy()).to(device)
+            else:
+                out[name] = torch.from_numpy(np.ascontiguousarray(val)).to(device)
+    return out

@@ -1,0 +1,134 @@
+"""The C-ABI library loads, exports every symbol include/winattn.h declares, and validates its
+arguments on the host (CPU only: no call here reaches a kernel launch)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from sliding_window_gqa_group_amd import binding as B
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = B.declared_functions()
+    assert "attn_window_chunk" in names and "attn_window_gated" in names
+    raw = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared in include/winattn.h but not exported"
+
+
+def test_version_and_strerror(lib):
+    assert B.abi_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert B.strerror(code)
+    assert "unknown" in B.strerror(-99)
+
+
+FAKE = 1 << 20   # a 16-byte aligned non-null address; never dereferenced (validation fails first)
+
+
+def _chunk(lib, **kw):
+    a = dict(ring_k=FAKE, ring_v=FAKE, meta=FAKE, sink_k=FAKE, sink_v=FAKE, q=FAKE, chunk_k=FAKE,
+             chunk_v=FAKE, out=FAKE, rows=1, ng=1, hpg=1, d=64, w=16, ns=0, scale=0.125,
+             ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.attn_window_chunk(a["ring_k"], a["ring_v"], a["meta"], a["sink_k"], a["sink_v"],
+                                 a["q"], a["chunk_k"], a["chunk_v"], a["out"], a["rows"], a["ng"],
+                                 a["hpg"], a["d"], a["w"], a["ns"], a["scale"], a["ws"], a["wsb"],
+                                 a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(rows=0), dict(ng=0), dict(hpg=0), dict(w=0), dict(ns=-1), dict(d=0), dict(d=6),
+    dict(d=260), dict(scale=float("inf")), dict(scale=float("nan")), dict(ring_k=None),
+    dict(meta=None), dict(out=None), dict(chunk_v=None), dict(ns=2, sink_k=None),
+    dict(q=FAKE + 4), dict(out=FAKE + 8), dict(meta=FAKE + 2),
+])
+def test_chunk_rejects_invalid_arguments(lib, kw):
+    assert _chunk(lib, **kw) == B.EINVAL
+
+
+def test_chunk_rejects_small_workspace(lib):
+    need = B.chunk_workspace_bytes(1, 8, 4, 128, 4096, 4)
+    assert need > 0
+    assert _chunk(lib, ng=8, hpg=4, d=128, w=4096, ns=4, ws=None, wsb=0) == B.EWORKSPACE
+    assert _chunk(lib, ng=8, hpg=4, d=128, w=4096, ns=4, ws=FAKE, wsb=need - 1) == B.EWORKSPACE
+
+
+def _gated(lib, **kw):
+    a = dict(yq=FAKE, yk=FAKE, yv=FAKE, rope=FAKE, q_scale=FAKE, gate=FAKE, gate_scale=FAKE,
+             ring_k=FAKE, ring_v=FAKE, out=FAKE, rows=4, pos0=10, cap=16, window=8, nh=4, nk=2,
+             hd=64, scale=0.125, eps=1e-6, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.attn_window_gated(a["yq"], a["yk"], a["yv"], a["rope"], a["q_scale"], a["gate"],
+                                 a["gate_scale"], a["ring_k"], a["ring_v"], a["out"], a["rows"],
+                                 a["pos0"], a["cap"], a["window"], a["nh"], a["nk"], a["hd"],
+                                 a["scale"], a["eps"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(rows=0), dict(pos0=-1), dict(cap=10), dict(window=0), dict(nh=5), dict(nk=0),
+    dict(hd=60), dict(hd=264), dict(hd=4), dict(eps=-1.0), dict(scale=float("nan")),
+    dict(yq=None), dict(ring_v=None), dict(gate=FAKE + 4),
+])
+def test_gated_rejects_invalid_arguments(lib, kw):
+    assert _gated(lib, **kw) == B.EINVAL
+
+
+def test_gated_rejects_small_workspace(lib):
+    need = B.gated_workspace_bytes(4, 4, 2, 64, 8)
+    assert need > 0
+    assert _gated(lib, ws=None, wsb=0) == B.EWORKSPACE
+    assert _gated(lib, wsb=need - 1) == B.EWORKSPACE
+
+
+def test_workspace_queries(lib):
+    assert B.chunk_workspace_bytes(0, 1, 1, 64, 16, 0) == 0
+    assert B.gated_workspace_bytes(1, 5, 2, 64, 8) == 0
+    # a single-split plan needs no workspace at all
+    kern, qb, splits, kps = B.chunk_plan(1, 1, 4, 64, 16, 2)
+    assert (kern, splits) == (1, 1)
+    assert B.chunk_workspace_bytes(1, 1, 4, 64, 16, 2) == 0
+    # gated always holds its prepared queries
+    assert B.gated_workspace_bytes(64, 16, 4, 256, 1024) >= 64 * 16 * 256 * 4
+
+
+def test_plans_of_the_named_workloads(lib):
+    assert B.chunk_plan(1, 8, 4, 128, 4096, 4)[0] == 1          # decode: vector-ALU split-K
+    assert B.chunk_plan(512, 8, 4, 128, 4096, 4)[0] == 2        # prefill: matrix cores
+    k, qb, splits, kps = B.chunk_plan(2048, 8, 8, 128, 32768, 4)
+    assert k == 2 and splits * kps >= 4 + 32768 + 16
+
+
+def test_tuning_knobs_change_the_plan(lib):
+    try:
+        B.tuning_set(B.TUNE_FORCE_KERNEL, 2)
+        assert B.chunk_plan(1, 8, 4, 128, 4096, 4)[0] == 2
+        B.tuning_set(B.TUNE_FORCE_KERNEL, 1)
+        B.tuning_set(B.TUNE_TILES_PER_SPLIT, 1)
+        k, qb, splits, kps = B.chunk_plan(512, 8, 4, 128, 4096, 4)
+        assert k == 1 and qb == 16 and kps == 64
+    finally:
+        B.tuning_set(B.TUNE_FORCE_KERNEL, 0)
+        B.tuning_set(B.TUNE_TILES_PER_SPLIT, 0)
+    with pytest.raises(B.WinattnError):
+        B.tuning_set(99, 1)
+
+
+def test_check_meta(lib):
+    assert B.check_meta(np.array([[16, 5, 0, 0]]), 1, 16) == 0
+    assert B.check_meta(np.array([[17, 0, 0, 0]]), 1, 16) == B.EINVAL     # len > w
+    assert B.check_meta(np.array([[4, 4, 0, 4]]), 1, 16) == B.EINVAL      # head >= window
+    assert B.check_meta(np.array([[3, 0, 0, 20]]), 1, 16) == B.EINVAL     # override > w
+    assert B.check_meta(np.array([[0, 99, 7, 0]]), 1, 16) == 0            # empty ring: head free
+    assert lib.attn_window_check_meta(None, 1, 16) == B.EINVAL
+
+
+def test_workspace_init_validation(lib):
+    assert lib.attn_workspace_init(None, 0, None) == 0
+    assert lib.attn_workspace_init(None, 64, None) == B.EINVAL
+    assert lib.attn_workspace_init(FAKE + 4, 64, None) == B.EINVAL

@@ -1,0 +1,358 @@
+"""Parity of the HIP path (through the C-ABI) with the CPU oracle, on seeded synthetic inputs.
+
+Bar (per element): |gpu - oracle| <= max(1e-4 * |oracle|, 1e-5). The named workloads run at
+their full sizes in the launch plan the benchmark uses; where the oracle would be slow (the
+512- and 2048-row chunks) it computes sampled (row, head) outputs one by one.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sliding_window_gqa_group_amd import binding as B
+from sliding_window_gqa_group_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+RTOL, ATOL = 1e-4, 1e-5
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load()   # fail loudly if the HIP library is missing
+    yield
+    for knob in (B.TUNE_FORCE_KERNEL, B.TUNE_TILES_PER_SPLIT, B.TUNE_TARGET_BLOCKS):
+        B.tuning_set(knob, 0)
+
+
+def assert_close(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    bound = np.maximum(RTOL * np.abs(ref), ATOL)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err / bound), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements out of tolerance; worst at "
+                             f"{i}: gpu {got[i]!r} oracle {ref[i]!r}")
+
+
+def gpu_chunk(inp, out=None, workspace=None):
+    t = gen.to_device(inp, DEV)
+    ns = inp.ns
+    res = B.attn_window_chunk(t["ring_k"], t["ring_v"], t["meta"],
+                              t["sink_k"] if ns else None, t["sink_v"] if ns else None,
+                              t["q"], t["chunk_k"], t["chunk_v"], inp.scale, out=out,
+                              workspace=workspace)
+    torch.cuda.synchronize()
+    return res
+
+
+def gpu_gated(inp):
+    t = gen.to_device(inp, DEV)
+    z = B.attn_window_gated(t["yq"], t["yk"], t["yv"], t["rope"], t["q_scale"], t["gate"],
+                            t["gate_scale"], t["ring_k"], t["ring_v"], inp.pos0, inp.window,
+                            inp.scale, inp.eps)
+    torch.cuda.synchronize()
+    return z.cpu().numpy(), t["ring_k"].cpu().numpy(), t["ring_v"].cpu().numpy()
+
+
+def _case(name):
+    print(f"[case] {name}", flush=True)
+
+
+# ── the matrix-core operand layout the wide-chunk kernel relies on ────────────────────────────
+
+def test_mfma_layout_probe():
+    _case("mfma layout probe")
+    out = B.mfma_layout_probe(DEV).cpu().numpy()
+    for lane in range(64):
+        for r in range(16):
+            i = 8 * (r // 4) + 4 * (lane // 32) + r % 4
+            j = lane % 32
+            assert out[lane, r] == i + 64 * j, (lane, r, out[lane, r])
+
+
+# ── the named workloads ──────────────────────────────────────────────────────────────────────
+
+def test_tiny():
+    _case("tiny")
+    inp = gen.tiny()
+    assert_close(gpu_chunk(inp).cpu().numpy(), oracle.window_chunk(inp), "tiny")
+
+
+def test_decode():
+    _case("decode")
+    inp = gen.decode()
+    assert_close(gpu_chunk(inp).cpu().numpy(), oracle.window_chunk(inp), "decode")
+
+
+def _sampled_rows(rows, k, seed):
+    rng = np.random.default_rng(seed)
+    fixed = {0, 1, 2, 15, 16, 31, 32, 33, 127, 128, rows // 2, rows - 2, rows - 1}
+    pick = set(int(x) for x in rng.choice(rows, size=min(k, rows), replace=False))
+    return sorted(r for r in fixed | pick if 0 <= r < rows)
+
+
+def test_prefill_sampled_rows():
+    _case("prefill")
+    inp = gen.prefill()
+    got = gpu_chunk(inp).cpu().numpy()
+    rows = _sampled_rows(inp.rows, 24, 2)
+    rr = np.repeat(rows, inp.nh)
+    hh = np.tile(np.arange(inp.nh), len(rows))
+    ref = oracle.window_chunk_select(inp, rr, hh)
+    assert_close(got[rr, hh], ref, "prefill")
+
+
+def test_large_sampled():
+    _case("large")
+    inp = gen.large()
+    got = gpu_chunk(inp).cpu().numpy()
+    rng = np.random.default_rng(44)
+    rows = np.concatenate([[0, 0, 1, 2047, 2047, 1024], rng.integers(0, inp.rows, 250)])
+    heads = np.concatenate([[0, 63, 8, 0, 63, 31], rng.integers(0, inp.nh, 250)])
+    ref = oracle.window_chunk_select(inp, rows, heads)
+    assert_close(got[rows, heads], ref, "large")
+
+
+def test_gated():
+    _case("gated")
+    inp = gen.gated()
+    z, rk, rv = gpu_gated(inp)
+    oz, ork, orv = oracle.window_gated(inp)
+    assert_close(z, oz, "gated z")
+    assert_close(rk, ork, "gated ring k")
+    np.testing.assert_array_equal(rv, orv)
+
+
+# ── shape sweep over both kernels and forced multi-split merges ──────────────────────────────
+
+def _rand_meta(rng, ng, w, kind):
+    meta = []
+    for g in range(ng):
+        k = kind if kind != "mix" else ["full", "partial", "empty", "override"][g % 4]
+        if k == "full":
+            meta.append((w, int(rng.integers(0, w)), 0, 0))
+        elif k == "partial":
+            meta.append((int(rng.integers(1, w)), int(rng.integers(0, w)), 0, 0))
+        elif k == "empty":
+            meta.append((0, int(rng.integers(0, w)), 0, 0))
+        else:
+            ov = int(rng.integers(1, w + 1))
+            meta.append((int(rng.integers(0, ov + 1)), int(rng.integers(0, ov)), 0, ov))
+    return meta
+
+
+SWEEP = [
+    # rows, ng, hpg, d, w, ns, meta kind
+    (1, 2, 1, 64, 40, 0, "full"),
+    (1, 3, 4, 128, 300, 4, "mix"),
+    (2, 1, 2, 128, 70, 4, "partial"),
+    (4, 2, 4, 256, 90, 4, "mix"),
+    (15, 2, 4, 64, 33, 3, "full"),
+    (16, 1, 8, 128, 100, 0, "override"),
+    (17, 3, 4, 256, 50, 4, "mix"),
+    (64, 2, 4, 128, 200, 4, "full"),
+    (513, 1, 4, 64, 90, 2, "mix"),
+    (33, 2, 1, 36, 60, 1, "partial"),
+    (5, 1, 3, 100, 20, 2, "mix"),
+    (40, 1, 32, 64, 64, 0, "full"),
+    (130, 4, 2, 128, 129, 5, "mix"),
+]
+
+VARIANTS = {
+    "auto": {},
+    "valu_many_splits": {B.TUNE_FORCE_KERNEL: 1, B.TUNE_TILES_PER_SPLIT: 1},
+    "mfma_many_splits": {B.TUNE_FORCE_KERNEL: 2, B.TUNE_TILES_PER_SPLIT: 1},
+}
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("shape", SWEEP, ids=[f"r{s[0]}g{s[1]}h{s[2]}d{s[3]}w{s[4]}s{s[5]}{s[6]}" for s in SWEEP])
+def test_sweep(shape, variant):
+    rows, ng, hpg, d, w, ns, kind = shape
+    _case(f"sweep {shape} {variant}")
+    rng = np.random.default_rng(zlib.crc32(repr((shape, variant)).encode()))
+    inp = gen.make_chunk(rows, ng, hpg, d, w, ns, _rand_meta(rng, ng, w, kind),
+                         seed=int(rng.integers(1 << 30)))
+    ref = oracle.window_chunk(inp)
+    try:
+        for knob, val in VARIANTS[variant].items():
+            B.tuning_set(knob, val)
+        got = gpu_chunk(inp).cpu().numpy()
+    finally:
+        for knob in VARIANTS[variant]:
+            B.tuning_set(knob, 0)
+    assert_close(got, ref, f"{shape} {variant}")
+
+
+GATED_SWEEP = [
+    # rows, pos0, cap, window, nh, nk, hd
+    (1, 5000, 4096, 1024, 8, 2, 128),
+    (3, 2, 16, 8, 4, 4, 64),
+    (20, 100, 300, 256, 8, 2, 64),
+    (64, 20000, 8192, 1024, 16, 4, 256),
+    (40, 10, 64, 25, 6, 3, 128),
+]
+
+
+@pytest.mark.parametrize("shape", GATED_SWEEP, ids=[f"r{s[0]}p{s[1]}c{s[2]}w{s[3]}h{s[4]}k{s[5]}d{s[6]}" for s in GATED_SWEEP])
+def test_gated_sweep(shape):
+    rows, pos0, cap, window, nh, nk, hd = shape
+    _case(f"gated sweep {shape}")
+    for scale in (None, float(np.sqrt(hd))):   # 1/sqrt(hd) and a sharp nGPT-like softmax
+        inp = gen.make_gated(rows, pos0, cap, window, nh, nk, hd, seed=rows + pos0, scale=scale)
+        z, rk, rv = gpu_gated(inp)
+        oz, ork, orv = oracle.window_gated(inp)
+        assert_close(z, oz, f"gated {shape} scale={scale}")
+        assert_close(rk, ork, "ring k")
+        np.testing.assert_array_equal(rv, orv)
+
+
+# ── strict: nothing outside the window is read, nothing outside out is written ───────────────
+
+def _visible_slots(inp, g):
+    ln, head, _, ov = (int(x) for x in inp.meta[g])
+    wg = ov if ov else inp.w
+    seen = set()
+    for i in range(inp.rows):
+        hi = ln + i + 1
+        lo = hi - min(wg, hi)
+        for x in range(lo, min(hi, ln)):
+            seen.add((head + x) % wg)
+    return seen
+
+
+@pytest.mark.parametrize("rows,hpg", [(1, 4), (3, 4), (70, 4)])
+def test_poisoned_slots_and_canaries(rows, hpg):
+    _case(f"poison rows={rows}")
+    ng, d, w, ns = 4, 128, 96, 2
+    meta = [(96, 17, 0, 0), (50, 80, 0, 0), (40, 39, 0, 64), (0, 3, 0, 0)]
+    inp = gen.make_chunk(rows, ng, hpg, d, w, ns, meta, seed=99)
+    for g in range(ng):
+        live = _visible_slots(inp, g)
+        for s in range(w):
+            if s not in live:
+                inp.ring_k[g, s] = np.nan
+                inp.ring_v[g, s] = np.nan
+    # the full ring's oldest entry is evicted for every row
+    assert np.isnan(inp.ring_k[0, 17]).all()
+    ref = oracle.window_chunk(inp)
+    nh = ng * hpg
+    n = rows * nh * d
+    guard = 64
+    buf = torch.full((n + 2 * guard,), 7.25, dtype=torch.float32, device=DEV)
+    out = buf[guard:guard + n].view(rows, nh, d)
+    need = B.chunk_workspace_bytes(rows, ng, hpg, d, w, ns)
+    ws = B.Workspace(DEV)
+    ws.buf = torch.zeros(need + 4096, dtype=torch.uint8, device=DEV)
+    ws.buf[need:] = 0xAB
+    gpu_chunk(inp, out=out, workspace=ws)
+    assert_close(out.cpu().numpy(), ref, "poisoned")
+    b = buf.cpu().numpy()
+    assert np.all(b[:guard] == 7.25) and np.all(b[guard + n:] == 7.25), "wrote outside out"
+    assert np.all(ws.buf[need:].cpu().numpy() == 0xAB), "wrote outside the workspace"
+
+
+def test_gated_untouched_slots():
+    _case("gated untouched slots")
+    inp = gen.make_gated(6, 40, 64, 16, 4, 2, 64, seed=5)
+    read_or_written = set()
+    for r in range(inp.rows):
+        pos = inp.pos0 + r
+        for p in range(max(0, pos + 1 - inp.window), pos + 1):
+            read_or_written.add(p % inp.cap)
+    untouched = [s for s in range(inp.cap) if s not in read_or_written]
+    inp.ring_k[untouched] = np.nan
+    inp.ring_v[untouched] = np.nan
+    z, rk, rv = gpu_gated(inp)
+    oz, _, _ = oracle.window_gated(inp)
+    assert_close(z, oz, "gated poisoned")
+    assert np.isnan(rk[untouched]).all() and np.isnan(rv[untouched]).all()
+
+
+# ── invariants on the GPU ────────────────────────────────────────────────────────────────────
+
+def test_ring_rotation_on_gpu():
+    _case("rotation")
+    inp = gen.make_chunk(9, 3, 4, 128, 80, 4, [(80, 11, 0, 0), (30, 70, 0, 0), (20, 5, 0, 40)], seed=3)
+    base = gpu_chunk(inp).cpu().numpy()
+    rot = gen.make_chunk(9, 3, 4, 128, 80, 4, inp.meta.copy(), seed=3)
+    for g in range(3):
+        ln, head, far, ov = (int(x) for x in inp.meta[g])
+        wg = ov if ov else inp.w
+        r = 7 * g + 5
+        idx = (np.arange(wg) + r) % wg
+        rot.ring_k[g, idx] = inp.ring_k[g, :wg]
+        rot.ring_v[g, idx] = inp.ring_v[g, :wg]
+        rot.meta[g] = (ln, (head + r) % wg, far, ov)
+    assert_close(gpu_chunk(rot).cpu().numpy(), base, "rotation")
+
+
+def test_chunk_equals_sequence_of_decodes_on_gpu():
+    _case("chunk vs decodes")
+    import test_oracle_pins as pins
+    inp = gen.make_chunk(12, 2, 4, 128, 10, 2, [(10, 3, 0, 0), (4, 1, 0, 6)], seed=8)
+    full = gpu_chunk(inp).cpu().numpy()
+    state = gen.make_chunk(1, 2, 4, 128, 10, 2, inp.meta.copy(), seed=0)
+    state.ring_k, state.ring_v = inp.ring_k.copy(), inp.ring_v.copy()
+    state.sink_k, state.sink_v = inp.sink_k, inp.sink_v
+    for i in range(inp.rows):
+        state.q = inp.q[i:i + 1].copy()
+        state.chunk_k = inp.chunk_k[i:i + 1].copy()
+        state.chunk_v = inp.chunk_v[i:i + 1].copy()
+        assert_close(gpu_chunk(state).cpu().numpy()[0], full[i], f"decode row {i}")
+        for g in range(inp.ng):
+            pins._push(state, g, inp.chunk_k[i, g], inp.chunk_v[i, g])
+
+
+def test_repeated_calls_and_workspace_reuse():
+    """Split counters reset themselves: back-to-back calls of different shapes on one workspace."""
+    _case("workspace reuse")
+    ws = B.Workspace(DEV)
+    a = gen.make_chunk(1, 8, 4, 128, 2048, 4, [(2048, 100 * g, 0, 0) for g in range(8)], seed=1)
+    b = gen.make_chunk(200, 2, 4, 128, 700, 3, [(700, 3, 0, 0), (300, 9, 0, 0)], seed=2)
+    ra, rb = oracle.window_chunk(a), oracle.window_chunk(b)
+    ws.get(max(B.chunk_workspace_bytes(1, 8, 4, 128, 2048, 4),
+               B.chunk_workspace_bytes(200, 2, 4, 128, 700, 3)))
+    ws.buf[64 * 1024:] = 0x55   # stale bytes everywhere but the counter region
+    c = gen.make_chunk(40, 1, 1, 64, 40, 0, [(40, 7, 0, 0)], seed=3)
+    rc = oracle.window_chunk(c)
+    for it in range(3):
+        assert_close(gpu_chunk(a, workspace=ws).cpu().numpy(), ra, "a")
+        assert_close(gpu_chunk(b, workspace=ws).cpu().numpy(), rb, "b")
+        try:
+            B.tuning_set(B.TUNE_FORCE_KERNEL, 2 if it % 2 else 1)
+            B.tuning_set(B.TUNE_TILES_PER_SPLIT, 1)
+            assert_close(gpu_chunk(c, workspace=ws).cpu().numpy(), rc, "c")
+        finally:
+            B.tuning_set(B.TUNE_FORCE_KERNEL, 0)
+            B.tuning_set(B.TUNE_TILES_PER_SPLIT, 0)
+
+
+def test_degenerate_cases():
+    _case("degenerate")
+    # a window of one key (override 1, no sinks) returns the row's own value
+    inp = gen.make_chunk(5, 2, 4, 64, 8, 0, [(1, 0, 0, 1), (0, 0, 0, 1)], seed=4)
+    got = gpu_chunk(inp).cpu().numpy()
+    for i in range(5):
+        for gh in range(8):
+            np.testing.assert_allclose(got[i, gh], inp.chunk_v[i, gh // 4], rtol=0, atol=1e-6)
+    # an empty ring: plain causal attention over the chunk plus sinks
+    inp = gen.make_chunk(50, 1, 4, 128, 64, 3, [(0, 0, 0, 0)], seed=6)
+    assert_close(gpu_chunk(inp).cpu().numpy(), oracle.window_chunk(inp), "empty ring")
+    # rows = 0 is rejected before any launch
+    t = gen.to_device(inp, DEV)
+    rc = B.load().attn_window_chunk(t["ring_k"].data_ptr(), t["ring_v"].data_ptr(),
+                                    t["meta"].data_ptr(), None, None, t["q"].data_ptr(),
+                                    t["chunk_k"].data_ptr(), t["chunk_v"].data_ptr(),
+                                    t["q"].data_ptr(), 0, 1, 4, 128, 64, 0, 0.1, None, 0, None)
+    assert rc == B.EINVAL

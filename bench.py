@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 F32_PEAK_TFLOPS = 157.3
 METRIC = "KV GB/s and rows/s for windowed GQA attention; % of HBM peak"
+KERNEL_NAMES = {1: "attn_dec_kernel", 2: "attn_mfma_kernel", 3: "attn_valu_kernel"}
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_valu_counters.json")
 
 
@@ -66,24 +67,30 @@ def run_chunk(B, t, scale, out, ws):
 
 
 def time_calls(torch, fn, n_sets, steps, warmup):
-    """(ms per step over the bracketed region, mean per-launch event ms)."""
+    """(ms per step over a bracketed loop, mean and median per-call event ms).
+
+    The step time comes from one pair of events around `steps` back-to-back calls; the per-call
+    times from a second pass with an event pair around each call (both on the stream the
+    library launches on, torch's current stream)."""
     stream = torch.cuda.current_stream()
     for s in range(warmup):
         fn(s % n_sets)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record(stream)
+    for s in range(steps):
+        fn(s % n_sets)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for s in range(steps):
         starts[s].record(stream)
         fn(s % n_sets)
         ends[s].record(stream)
-    t1.record(stream)
     torch.cuda.synchronize()
-    total = t0.elapsed_time(t1)
     per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     return total / steps, float(np.mean(per)), float(np.median(per))
 
@@ -153,7 +160,7 @@ def bench_others(args, torch, B, gen, acct):
                      "rows_per_s": round(inp.rows / ms * 1e3, 1),
                      "tflops": round(flops / ms / 1e9, 3),
                      "tflops_frac_f32_peak": round(flops / ms / 1e9 / F32_PEAK_TFLOPS, 4),
-                     "kernel": "mfma" if kern[0] == 2 else "valu", "splits": kern[2],
+                     "kernel": KERNEL_NAMES[kern[0]], "splits": kern[2],
                      "cache": "hot (inputs resident, reused)"}
         del t, out, ws
         torch.cuda.empty_cache()
@@ -201,6 +208,7 @@ def main():
     inp, ms, ev_mean, ev_med, kv, tot, set_bytes = bench_decode(args, torch, B, gen, acct)
     value = kv / (ms * 1e-3) / 1e9
     plan = B.chunk_plan(inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns)
+    kname = KERNEL_NAMES[plan[0]]
     traffic = measured_traffic()
     line = {
         "metric": METRIC,
@@ -218,7 +226,7 @@ def main():
         "config": {"workload": "decode", "rows": inp.rows, "ng": inp.ng, "hpg": inp.hpg,
                    "nh": inp.nh, "d": inp.d, "w": inp.w, "ns": inp.ns, "ring": "full, seeded heads",
                    "input_sets": args.sets, "rotating_bytes": args.sets * set_bytes,
-                   "kernel": "valu split-K" if plan[0] == 1 else "mfma", "splits": plan[2]},
+                   "kernel": kname, "splits": plan[2], "keys_per_split": plan[3]},
         "rows_per_s": round(inp.rows / (ms * 1e-3), 1),
         "hbm_frac": round(tot / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {
@@ -228,7 +236,7 @@ def main():
             "unit": "GB/s",
             "frac": round(tot / (ev_mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "attn_valu_kernel<128,4,false>",
+            "kernel": f"{kname} (+ split merge launch), one attn_window_chunk call",
             "algorithmic_bytes_per_launch": tot,
             "launch_ms_mean": round(ev_mean, 6),
             "launch_ms_median": round(ev_med, 6),

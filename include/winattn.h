@@ -129,8 +129,9 @@ int attn_workspace_init(void* workspace, size_t bytes, void* stream);
  * valid, WINATTN_EINVAL otherwise (also for a NULL pointer or ng, w < 1). */
 int attn_window_check_meta(const uint32_t* host_meta, int ng, int w);
 
-/* Diagnostics: how attn_window_chunk would run these sizes. kernel = 1 (vector-ALU split-K
- * kernel) or 2 (f32 matrix-core kernel); query_block = query vectors per workgroup; splits =
+/* Diagnostics: how attn_window_chunk would run these sizes. kernel = 1 (register-resident
+ * split-K kernel, up to 8 query vectors per block), 2 (f32 matrix-core kernel) or 3 (LDS-staged
+ * vector-ALU split-K kernel, 16 per block); query_block = query vectors per workgroup; splits =
  * key splits reserved per query block; keys_per_split = keys each split covers at most.
  * Output pointers may be NULL. Returns 0 or WINATTN_EINVAL. */
 int attn_window_chunk_plan(int rows, int ng, int hpg, int d, int w, int ns, int* kernel,
@@ -145,9 +146,10 @@ int attn_mfma_layout_probe(float* out, void* stream);
 /* Tuning knobs for tests and benchmarks (process-wide, not thread-safe; 0 = automatic).
  * They change the launch plan and therefore the workspace size: query the size after setting
  * them. */
-#define WINATTN_TUNE_FORCE_KERNEL 1    /* 1 = vector-ALU kernel, 2 = matrix-core kernel */
+#define WINATTN_TUNE_FORCE_KERNEL 1    /* kernel number as reported by attn_window_chunk_plan */
 #define WINATTN_TUNE_TILES_PER_SPLIT 2 /* key tiles per split */
 #define WINATTN_TUNE_TARGET_BLOCKS 3   /* workgroups the split count aims for */
+#define WINATTN_TUNE_MERGE_KERNEL 4    /* 1 = splits merge in the last split, 2 = separate launch */
 int attn_tuning_set(int knob, int value);
 
 /* A static, human-readable description of a return code. */

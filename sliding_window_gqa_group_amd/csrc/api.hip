@@ -14,9 +14,10 @@ namespace winattn {
 namespace {
 
 // Tuning knobs (attn_tuning_set); 0 = automatic.
-int g_force_kernel = 0;     // 1 VALU, 2 MFMA
+int g_force_kernel = 0;     // 1 register kernel, 2 MFMA, 3 LDS vector kernel
 int g_tiles_per_split = 0;
 int g_target_blocks = 0;
+int g_merge_kernel = -1;    // -1 automatic, 0 merge in the last split, 1 separate merge launch
 
 constexpr int kValuMaxQ = 16;
 // Split counters sit at the start of every workspace, at the same place for every plan, so
@@ -25,7 +26,10 @@ constexpr int kValuMaxQ = 16;
 constexpr size_t kTicketBytes = 64 * 1024;
 constexpr long long kMaxTickets = kTicketBytes / sizeof(unsigned int);
 
+enum Kind { kKindDec = 1, kKindMfma = 2, kKindValu = 3 };
+
 struct Plan {
+    int kind;
     bool mfma;
     int dpad;
     int qb;             // query vectors per block
@@ -33,6 +37,7 @@ struct Plan {
     int tk;             // keys per tile
     int tps;            // tiles per split
     int nsplit;         // splits reserved per block
+    bool merge_kernel;  // merge splits in a separate launch
     size_t off_q, off_pacc, off_pm, off_pl, off_tickets, bytes;
 };
 
@@ -47,14 +52,17 @@ Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_f
     Plan pl{};
     const long long nq_tot = (long long)rows * hpg;
     pl.dpad = pad_d(d);
-    pl.mfma = nq_tot > kValuMaxQ;
-    if (g_force_kernel == 1) pl.mfma = false;
-    if (g_force_kernel == 2) pl.mfma = true;
-    if (pl.mfma) {
+    pl.kind = nq_tot <= 8 ? kKindDec : (nq_tot <= kValuMaxQ ? kKindValu : kKindMfma);
+    if (g_force_kernel >= 1 && g_force_kernel <= 3) pl.kind = g_force_kernel;
+    pl.mfma = pl.kind == kKindMfma;
+    if (pl.kind == kKindMfma) {
         pl.qb = mfma_query_block();
         pl.tk = mfma_tile_keys();
+    } else if (pl.kind == kKindDec) {
+        pl.qb = nq_tot <= 4 ? 4 : 8;
+        pl.tk = dec_tile_keys(pl.dpad);
     } else {
-        pl.qb = nq_tot <= 4 ? 4 : (nq_tot <= 8 ? 8 : 16);
+        pl.qb = 16;
         pl.tk = valu_tile_keys(pl.dpad);
     }
     pl.nqblocks = cdiv(nq_tot, pl.qb);
@@ -64,7 +72,11 @@ Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_f
     const long long keys_max = (long long)wcap + span - 1;
     const int max_tiles = cdiv(keys_max, pl.tk);
     const long long blocks = (long long)pl.nqblocks * ng;
-    const int target = g_target_blocks > 0 ? g_target_blocks : (pl.mfma ? 1024 : 256);
+    // Workgroups the split count aims for: the register kernel runs two per CU, the LDS
+    // vector kernel one, the matrix-core kernel up to two (with two rounds to balance).
+    const int target = g_target_blocks > 0
+                           ? g_target_blocks
+                           : (pl.kind == kKindMfma ? 1024 : (pl.kind == kKindDec ? 512 : 256));
     int s_target = cdiv(target, blocks);
     if (s_target < 1) s_target = 1;
     if (s_target > max_tiles) s_target = max_tiles;
@@ -82,6 +94,11 @@ Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_f
     if (blocks > kMaxTickets) tps = max_tiles;
     pl.tps = tps;
     pl.nsplit = cdiv(max_tiles, tps);
+    // Decode-sized calls finish all their splits at nearly the same moment, so the merge is on
+    // the critical path: a separate launch (coherence at the kernel boundary) is cheaper than
+    // device-scope stores, a counter and an acquire. Wide calls merge in the last split, which
+    // overlaps with other blocks still computing.
+    pl.merge_kernel = g_merge_kernel >= 0 ? g_merge_kernel == 1 : pl.kind == kKindDec;
 
     // Layout: [counters][prepared queries][partials], each region 256-byte aligned.
     const bool split = pl.nsplit > 1;
@@ -109,13 +126,18 @@ Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_f
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The kernels address rows within one group's ring, sinks or chunk with 32-bit offsets:
+// every tensor of a call stays under 2^31 floats (8 GiB).
+constexpr long long kMaxFloats = (1LL << 31) - 1;
+
 bool chunk_shape_ok(int rows, int ng, int hpg, int d, int w, int ns) {
     if (rows < 1 || ng < 1 || hpg < 1 || w < 1 || ns < 0) return false;
     if (d < 4 || d > 256 || d % 4 != 0) return false;
-    // Keep every index the kernels form inside 32 bits.
     if (rows > (1 << 24) || w > (1 << 28) || ns > (1 << 20)) return false;
     if ((long long)ng * hpg > (1 << 16)) return false;
-    if ((long long)rows * ng * hpg > (1LL << 30)) return false;
+    const long long nh = (long long)ng * hpg;
+    if ((long long)ng * w * d > kMaxFloats || (long long)ng * ns * d > kMaxFloats) return false;
+    if ((long long)rows * nh * d > kMaxFloats || (long long)rows * ng * d > kMaxFloats) return false;
     return true;
 }
 
@@ -125,6 +147,7 @@ bool gated_shape_ok(int rows, int pos0, int cap, int window, int nh, int nk, int
     if (rows > (1 << 24) || cap > (1 << 28) || window > (1 << 28) || nh > (1 << 16)) return false;
     if ((long long)pos0 + rows > 0x7ffffff0LL) return false;
     if ((long long)cap < (long long)window + rows - 1) return false;
+    if ((long long)cap * nk * hd > kMaxFloats || (long long)rows * nh * hd > kMaxFloats) return false;
     return true;
 }
 
@@ -138,11 +161,17 @@ int launch_attention(const Plan& pl, AttnParams& p, bool gated, char* ws, hipStr
         p.pl = reinterpret_cast<float*>(ws + pl.off_pl);
         p.tickets = reinterpret_cast<unsigned int*>(ws + pl.off_tickets);
     }
+    p.merge_kernel = pl.merge_kernel && pl.nsplit > 1 ? 1 : 0;
     hipError_t err;
-    if (pl.mfma)
+    const dim3 grid(pl.nsplit, pl.nqblocks, p.ng);
+    if (pl.kind == kKindMfma)
         err = launch_mfma(p, gated, pl.dpad, stream);
+    else if (pl.kind == kKindDec)
+        err = launch_dec(p, gated, pl.dpad, pl.qb, grid, stream);
     else
-        err = launch_valu(p, gated, pl.dpad, pl.qb, dim3(pl.nsplit, pl.nqblocks, p.ng), stream);
+        err = launch_valu(p, gated, pl.dpad, pl.qb, grid, stream);
+    if (err == hipSuccess && p.merge_kernel)
+        err = launch_split_merge(p, gated, pl.qb, pl.dpad, pl.tk, stream);
     return err == hipSuccess ? WINATTN_OK : WINATTN_ELAUNCH;
 }
 
@@ -306,7 +335,7 @@ int attn_window_chunk_plan(int rows, int ng, int hpg, int d, int w, int ns, int*
                            int* query_block, int* splits, int* keys_per_split) {
     if (!chunk_shape_ok(rows, ng, hpg, d, w, ns)) return WINATTN_EINVAL;
     const Plan pl = make_plan(rows, ng, hpg, d, w, ns, 0);
-    if (kernel) *kernel = pl.mfma ? 2 : 1;
+    if (kernel) *kernel = pl.kind;
     if (query_block) *query_block = pl.qb;
     if (splits) *splits = pl.nsplit;
     if (keys_per_split) *keys_per_split = pl.tps * pl.tk;
@@ -323,7 +352,7 @@ int attn_tuning_set(int knob, int value) {
     if (value < 0) return WINATTN_EINVAL;
     switch (knob) {
         case WINATTN_TUNE_FORCE_KERNEL:
-            if (value > 2) return WINATTN_EINVAL;
+            if (value > 3) return WINATTN_EINVAL;
             g_force_kernel = value;
             return WINATTN_OK;
         case WINATTN_TUNE_TILES_PER_SPLIT:
@@ -331,6 +360,10 @@ int attn_tuning_set(int knob, int value) {
             return WINATTN_OK;
         case WINATTN_TUNE_TARGET_BLOCKS:
             g_target_blocks = value;
+            return WINATTN_OK;
+        case WINATTN_TUNE_MERGE_KERNEL:
+            if (value > 2) return WINATTN_EINVAL;
+            g_merge_kernel = value - 1;
             return WINATTN_OK;
         default:
             return WINATTN_EINVAL;

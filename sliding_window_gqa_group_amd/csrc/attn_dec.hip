@@ -1,0 +1,334 @@
+// Split-K windowed attention for decode-sized chunks (at most 8 query vectors per KV group per
+// workgroup), computed entirely in registers.
+//
+// Prior art on the o1c page ("A sealed layer's attention for a chunk of rows, on Metal"): the
+// token path `o1c_tok_near` gives each simdgroup a stripe of the window's keys, keeps the row's
+// queries in registers and updates a running (max, sum, accumulator) per head, and
+// `o1c_tok_merge` combines the partials. The gfx950 design:
+//
+//  - A lane group of TPK = D*NQ/32 adjacent lanes owns one key per pass: lane sl of the group
+//    holds float4 columns sl, sl + TPK, ... of that key's K and V row (TPK lanes read TPK*16
+//    consecutive bytes, so each load instruction is fully coalesced) and the same columns of
+//    every query (32 floats per lane).
+//  - Scores are partial dot products reduced across the group with DPP, which leaves the full
+//    score in every lane of the group, exactly where the value update needs it.
+//  - Each lane group is its own split: it keeps a running max, sum and accumulator per query
+//    over the keys it owns. No LDS and no barrier inside the tile loop; the groups are merged
+//    once at the end through LDS, and the workgroup's splits in the last-arriving workgroup.
+//  - Two register buffers of K/V tiles: a split's first two tiles are requested at once, and a
+//    buffer is refilled as soon as its tile has been consumed.
+#include "winattn_dev.h"
+#include "launch.h"
+
+namespace winattn {
+
+template <int D, int NQ>
+struct DecShape {
+    static constexpr int TPK = D * NQ / 32;     // lanes per key
+    static constexpr int F4 = D / (4 * TPK);    // float4 columns of a key per lane
+    static constexpr int KPP = kThreads / TPK;  // keys per pass of the block = lane groups
+    static constexpr int TK = 4096 / D;         // keys per tile: 4 float4 per lane per tensor
+    static constexpr int PASSES = TK / KPP;
+    static_assert(TPK >= 4 && TPK <= 64 && F4 >= 1 && PASSES >= 1, "unsupported shape");
+    static_assert(PASSES * F4 == 4, "four float4 of K and of V per lane per tile");
+};
+
+// Sum over the TPK lanes of a group, result in every lane of the group.
+template <int TPK>
+__device__ inline float lane_group_sum(float v) {
+    if constexpr (TPK <= 16) {
+        return group_sum<TPK>(v);
+    } else {
+        v = group_sum<16>(v);
+        v += dpp<kDppBcast15, 0xA>(v, 0.0f);   // rows 1 and 3 now hold row pairs
+        if constexpr (TPK == 32) {
+            const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+            const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+            return (threadIdx.x & 32) ? hi : lo;
+        } else {
+            v += dpp<kDppBcast31, 0xC>(v, 0.0f);
+            return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+        }
+    }
+}
+
+template <int D, int NQ, bool GATED>
+__global__ __launch_bounds__(kThreads, 2) void attn_dec_kernel(const AttnParams p) {
+    using S = DecShape<D, NQ>;
+    constexpr int TPK = S::TPK, F4 = S::F4, KPP = S::KPP, TK = S::TK, PASSES = S::PASSES;
+
+    __shared__ __align__(16) float s_red[KPP * NQ * D];   // group accumulators at the end
+    __shared__ float s_gm[KPP * NQ], s_gl[KPP * NQ];
+    __shared__ float s_m[NQ], s_l[NQ];
+    __shared__ int s_flag;
+    static_assert(KPP * NQ * D >= kMergeScratch, "merge scratch reuses the reduction area");
+
+    const int tid = threadIdx.x;
+    const int split = blockIdx.x, qb = blockIdx.y, g = blockIdx.z;
+    const int gi = tid / TPK, sl = tid % TPK;   // lane group (key slot), lane within the group
+    const int nq_tot = p.rows * p.hpg;
+    const int q0 = qb * NQ;
+    const int nq = min(NQ, nq_tot - q0);
+    const GroupWin gw = resolve_group<GATED>(p, g);
+    const int r_first = q0 / p.hpg, r_last = (q0 + nq - 1) / p.hpg;
+    const int xlo = window_lo(gw.hi0 + r_first, gw.wcap);
+    const int xhi = gw.hi0 + r_last;
+    const Tiles tr = tile_range<TK>(p.ns, xlo, xhi, p.tps, split);
+    const int nsplit = tr.nsplit, nst = tr.nst;
+    if (split >= nsplit) return;
+    const int t_begin = tr.t_begin, t_end = tr.t_end;
+    const int d4 = p.d / 4;
+
+    // ---- tile loads: key of (pass, group) = tile base + pass * KPP + gi; columns sl + TPK f
+    const KVBases b = kv_bases(p);
+    const unsigned long long rk = b.rk + 4ull * (unsigned long long)((long long)g * p.ring_gs);
+    const unsigned long long rv = b.rv + 4ull * (unsigned long long)((long long)g * p.ring_gs);
+    const unsigned long long ck = b.ck + 4ull * (unsigned long long)((long long)g * p.chunk_gs);
+    const unsigned long long cv = b.cv + 4ull * (unsigned long long)((long long)g * p.chunk_gs);
+    const unsigned long long sk = b.sk + 4ull * (unsigned long long)((long long)g * p.ns * p.d);
+    const unsigned long long sv = b.sv + 4ull * (unsigned long long)((long long)g * p.ns * p.d);
+    const int ss = (int)p.ring_ss, crs = (int)p.chunk_rs;
+
+    vf4 kA[PASSES][F4], vA[PASSES][F4], kB[PASSES][F4], vB[PASSES][F4];
+    auto load_tile = [&](vf4 (&kr)[PASSES][F4], vf4 (&vr)[PASSES][F4], int t) {
+        if (t < nst) {
+#pragma unroll
+            for (int ps = 0; ps < PASSES; ++ps) {
+                const int si = t * TK + ps * KPP + gi;
+                const bool valid = si < p.ns;
+                const int row = valid ? si * p.d : 0;
+#pragma unroll
+                for (int f = 0; f < F4; ++f) {
+                    const int c = sl + TPK * f;
+                    const int off = (valid && c < d4) ? row + 4 * c : 0;
+                    kr[ps][f] = *reinterpret_cast<gvf4p>((valid ? sk : rk) + 4ull * (unsigned)off);
+                    vr[ps][f] = *reinterpret_cast<gvf4p>((valid ? sv : rv) + 4ull * (unsigned)off);
+                }
+            }
+        } else {
+            const int xt = xlo + (t - nst) * TK + gi;
+#pragma unroll
+            for (int ps = 0; ps < PASSES; ++ps) {
+                const int x = xt + ps * KPP;
+                const bool valid = x < xhi;
+                const bool in_ring = x < gw.xsplit || !valid;
+                int slot = gw.base + x;
+                slot = slot >= gw.mod ? slot - gw.mod : slot;
+                const int row = !valid ? 0 : (in_ring ? slot * ss : (x - gw.xsplit) * crs);
+#pragma unroll
+                for (int f = 0; f < F4; ++f) {
+                    const int c = sl + TPK * f;
+                    const int off = c < d4 ? row + 4 * c : row;
+                    kr[ps][f] = *reinterpret_cast<gvf4p>((in_ring ? rk : ck) + 4ull * (unsigned)off);
+                    vr[ps][f] = *reinterpret_cast<gvf4p>((in_ring ? rv : cv) + 4ull * (unsigned)off);
+                }
+            }
+        }
+    };
+    load_tile(kA, vA, t_begin);
+    if (t_begin + 1 < t_end) load_tile(kB, vB, t_begin + 1);
+
+    // ---- queries: this lane's columns of every query, times scale*log2(e); window bounds
+    vf4 qr[NQ][F4];
+    int qlo[NQ], qhi[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        const int qi = q0 + min(j, nq - 1);
+        const int row = qi / p.hpg, gh = g * p.hpg + qi % p.hpg;
+        const float* qp = p.q + ((size_t)row * p.nh + gh) * p.d;
+#pragma unroll
+        for (int f = 0; f < F4; ++f) {
+            const int c = sl + TPK * f;
+            vf4 v = {0.f, 0.f, 0.f, 0.f};
+            if (j < nq && c < d4) v = *reinterpret_cast<const vf4*>(qp + 4 * c);
+            qr[j][f] = v * p.scale_log2;
+        }
+        const int hi = gw.hi0 + row;
+        qlo[j] = j < nq ? window_lo(hi, gw.wcap) : 0;
+        qhi[j] = j < nq ? hi : 0;
+    }
+
+    float mrun[NQ], lrun[NQ];
+    vf4 acc[NQ][F4];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        mrun[j] = -INFINITY;
+        lrun[j] = 0.0f;
+#pragma unroll
+        for (int f = 0; f < F4; ++f) acc[j][f] = vf4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // ---- one tile: scores, online softmax of this lane group, value update
+    auto step = [&](vf4 (&kr)[PASSES][F4], vf4 (&vr)[PASSES][F4], int t) {
+        float sc[PASSES][NQ];
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps) {
+            const int k = ps * KPP + gi;
+            bool colok[F4];
+#pragma unroll
+            for (int f = 0; f < F4; ++f) colok[f] = sl + TPK * f < d4;
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                float s = 0.0f;
+#pragma unroll
+                for (int f = 0; f < F4; ++f) {
+                    const vf4 kv = colok[f] ? kr[ps][f] : vf4{0.f, 0.f, 0.f, 0.f};
+                    const vf4 pr = kv * qr[j][f];
+                    s += (pr.x + pr.y) + (pr.z + pr.w);
+                }
+                s = lane_group_sum<TPK>(s);
+                const bool vis = key_visible<TK>(p.ns, xlo, nst, t, k, qlo[j], qhi[j], j < nq);
+                sc[ps][j] = vis ? s : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            float tmax = sc[0][j];
+#pragma unroll
+            for (int ps = 1; ps < PASSES; ++ps) tmax = fmaxf(tmax, sc[ps][j]);
+            const float m_new = fmaxf(mrun[j], tmax);
+            const float mu = safe_max(m_new);
+            const float corr = __builtin_amdgcn_exp2f(mrun[j] - mu);
+            mrun[j] = m_new;
+            float lsum = 0.0f;
+#pragma unroll
+            for (int f = 0; f < F4; ++f) acc[j][f] *= corr;
+#pragma unroll
+            for (int ps = 0; ps < PASSES; ++ps) {
+                const float pv = __builtin_amdgcn_exp2f(sc[ps][j] - mu);
+                lsum += pv;
+#pragma unroll
+                for (int f = 0; f < F4; ++f) {
+                    // a padding key has score -inf, weight 0; select, never multiply, its value
+                    const vf4 vv = pv != 0.0f ? vr[ps][f] : vf4{0.f, 0.f, 0.f, 0.f};
+                    acc[j][f] += pv * vv;
+                }
+            }
+            lrun[j] = lrun[j] * corr + lsum;
+        }
+        if (t + 2 < t_end) load_tile(kr, vr, t + 2);
+    };
+    for (int t = t_begin; t < t_end; t += 2) {
+        step(kA, vA, t);
+        if (t + 1 < t_end) step(kB, vB, t + 1);
+    }
+
+    // ---- merge the lane groups (each group's state is uniform across its lanes)
+    if (sl == 0) {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            s_gm[gi * NQ + j] = mrun[j];
+            s_gl[gi * NQ + j] = lrun[j];
+        }
+    }
+    __syncthreads();
+    if (tid < NQ) {
+        float m = -INFINITY;
+        for (int u = 0; u < KPP; ++u) m = fmaxf(m, s_gm[u * NQ + tid]);
+        const float mu = safe_max(m);
+        float l = 0.0f;
+        for (int u = 0; u < KPP; ++u) l += s_gl[u * NQ + tid] * __builtin_amdgcn_exp2f(s_gm[u * NQ + tid] - mu);
+        s_m[tid] = m;
+        s_l[tid] = l;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        const float f = __builtin_amdgcn_exp2f(mrun[j] - safe_max(s_m[j]));
+#pragma unroll
+        for (int fc = 0; fc < F4; ++fc)
+            *reinterpret_cast<vf4*>(s_red + (gi * NQ + j) * D + 4 * (sl + TPK * fc)) = acc[j][fc] * f;
+    }
+    __syncthreads();
+
+    const int blk = g * p.nqblocks + qb;
+    constexpr int D4 = D / 4;
+    for (int item = tid; item < NQ * D4; item += kThreads) {
+        const int j = item / D4, c = item % D4;
+        if (j >= nq || c >= d4) continue;
+        vf4 o = {0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < KPP; ++u) o += *reinterpret_cast<const vf4*>(s_red + (u * NQ + j) * D + 4 * c);
+        if (nsplit == 1) {
+            o *= 1.0f / fmaxf(s_l[j], 1e-30f);
+            store_out<GATED>(p, q0 + j, g, 4 * c, make_float4(o.x, o.y, o.z, o.w));
+        } else {
+            const size_t at = ((size_t)blk * p.nsplit_grid + split) * NQ + j;
+            store_part4(p, p.pacc + at * D + 4 * c, make_float4(o.x, o.y, o.z, o.w));
+            if (c == 0) {
+                store_part(p, p.pm + at, s_m[j]);
+                store_part(p, p.pl + at, s_l[j]);
+            }
+        }
+    }
+    if (nsplit > 1) {
+        __syncthreads();   // s_red is reused as merge scratch
+        merge_if_last<NQ, D, GATED>(p, blk, nsplit, q0, nq, g, &s_flag, s_red);
+    }
+}
+
+// Separate merge launch: one workgroup per query block, grid = (query blocks, groups).
+template <int QB, int D, bool GATED>
+__global__ __launch_bounds__(kThreads) void split_merge_kernel(const AttnParams p, int tk) {
+    __shared__ __align__(16) float scratch[kMergeScratch];
+    const int qb = blockIdx.x, g = blockIdx.y;
+    const int nq_tot = p.rows * p.hpg;
+    const int q0 = qb * QB;
+    const int nq = min(QB, nq_tot - q0);
+    const GroupWin gw = resolve_group<GATED>(p, g);
+    const int r_first = q0 / p.hpg, r_last = (q0 + nq - 1) / p.hpg;
+    const int xlo = window_lo(gw.hi0 + r_first, gw.wcap);
+    const int xhi = gw.hi0 + r_last;
+    const int nstream = (xhi - xlo + tk - 1) / tk;
+    const int nsplit = (nstream + p.tps - 1) / p.tps;
+    if (nsplit <= 1) return;   // that block wrote its output directly
+    merge_block<QB, D, GATED>(p, g * p.nqblocks + qb, nsplit, q0, nq, g, scratch);
+}
+
+template <int D, int NQ, bool GATED>
+static hipError_t launch_dec_t(const AttnParams& p, dim3 grid, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_dec_kernel<D, NQ, GATED>), grid, dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <bool GATED>
+static hipError_t launch_dec_g(const AttnParams& p, int dpad, int nq, dim3 grid, hipStream_t s) {
+    if (dpad == 64 && nq == 4) return launch_dec_t<64, 4, GATED>(p, grid, s);
+    if (dpad == 64 && nq == 8) return launch_dec_t<64, 8, GATED>(p, grid, s);
+    if (dpad == 128 && nq == 4) return launch_dec_t<128, 4, GATED>(p, grid, s);
+    if (dpad == 128 && nq == 8) return launch_dec_t<128, 8, GATED>(p, grid, s);
+    if (dpad == 256 && nq == 4) return launch_dec_t<256, 4, GATED>(p, grid, s);
+    if (dpad == 256 && nq == 8) return launch_dec_t<256, 8, GATED>(p, grid, s);
+    return hipErrorInvalidValue;
+}
+
+template <bool GATED>
+static hipError_t launch_merge_g(const AttnParams& p, int qb, int dpad, int tk, hipStream_t s) {
+    const dim3 grid(p.nqblocks, p.ng);
+#define WINATTN_MERGE_CASE(QQ, DD)                                                                  \
+    if (qb == QQ && dpad == DD) {                                                                   \
+        hipLaunchKernelGGL((split_merge_kernel<QQ, DD, GATED>), grid, dim3(kThreads), 0, s, p, tk); \
+        return hipGetLastError();                                                                   \
+    }
+    WINATTN_MERGE_CASE(4, 64) WINATTN_MERGE_CASE(4, 128) WINATTN_MERGE_CASE(4, 256)
+    WINATTN_MERGE_CASE(8, 64) WINATTN_MERGE_CASE(8, 128) WINATTN_MERGE_CASE(8, 256)
+    WINATTN_MERGE_CASE(16, 64) WINATTN_MERGE_CASE(16, 128) WINATTN_MERGE_CASE(16, 256)
+    WINATTN_MERGE_CASE(128, 64) WINATTN_MERGE_CASE(128, 128) WINATTN_MERGE_CASE(128, 256)
+#undef WINATTN_MERGE_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_merge(const AttnParams& p, bool gated, int qb, int dpad, int tk,
+                              hipStream_t stream) {
+    return gated ? launch_merge_g<true>(p, qb, dpad, tk, stream)
+                 : launch_merge_g<false>(p, qb, dpad, tk, stream);
+}
+
+hipError_t launch_dec(const AttnParams& p, bool gated, int dpad, int nq, dim3 grid,
+                      hipStream_t stream) {
+    return gated ? launch_dec_g<true>(p, dpad, nq, grid, stream)
+                 : launch_dec_g<false>(p, dpad, nq, grid, stream);
+}
+
+int dec_tile_keys(int dpad) { return 4096 / dpad; }
+
+}  // namespace winattn

@@ -77,23 +77,10 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
     const int lo = window_lo(hi, gw.wcap);
 
     float4 kreg[LPT], vreg[LPT];
+    unsigned kmask = 0u;
+    const KVBases kvb = kv_bases(p);
     auto load_tile = [&](int t) {
-#pragma unroll
-        for (int j = 0; j < LPT; ++j) {
-            const int f = tid + kThreads * j;
-            const int key = f / D4, c = f % D4;
-            long long off = 0;
-            const int src = key_offset<TK>(p, gw, g, xlo, xhi, nst, t, key, off);
-            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-            if (src >= 0 && c < d4) {
-                const float *kp, *vp;
-                key_ptrs(p, src, off, kp, vp);
-                kv = *reinterpret_cast<const float4*>(kp + 4 * c);
-                vv = *reinterpret_cast<const float4*>(vp + 4 * c);
-            }
-            kreg[j] = kv;
-            vreg[j] = vv;
-        }
+        kmask = load_tile_regs<TK, D, LPT>(p, kvb, gw, g, xlo, xhi, nst, t, d4, kreg, vreg);
     };
 
     load_tile(t_begin);   // first tile in flight while the queries load
@@ -127,8 +114,9 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
         for (int j = 0; j < LPT; ++j) {
             const int f = tid + kThreads * j;
             const int key = f / D4, c = f % D4;
-            *reinterpret_cast<float4*>(s_k + key * KST + 4 * c) = kreg[j];
-            *reinterpret_cast<float4*>(s_v + key * VST + 4 * c) = vreg[j];
+            const bool keep = (kmask >> j) & 1u;
+            *reinterpret_cast<float4*>(s_k + key * KST + 4 * c) = zero_unless(keep, kreg[j]);
+            *reinterpret_cast<float4*>(s_v + key * VST + 4 * c) = zero_unless(keep, vreg[j]);
         }
         __syncthreads();
         if (t + 1 < t_end) load_tile(t + 1);
@@ -212,12 +200,12 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int e = 32 * b + 8 * m + 4 * hb;
-                store_dev4(p.pacc + at * D + e, make_float4(oacc[b][4 * m], oacc[b][4 * m + 1],
+                store_part4(p, p.pacc + at * D + e, make_float4(oacc[b][4 * m], oacc[b][4 * m + 1],
                                                             oacc[b][4 * m + 2], oacc[b][4 * m + 3]));
             }
         if (hb == 0) {
-            store_dev(p.pm + at, mrun);
-            store_dev(p.pl + at, lrun);
+            store_part(p, p.pm + at, mrun);
+            store_part(p, p.pl + at, lrun);
         }
     }
     merge_if_last<QB, D, GATED>(p, blk, nsplit, q0, nq, g, &s_flag, s_k);

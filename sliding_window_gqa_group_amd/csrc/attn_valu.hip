@@ -37,6 +37,7 @@ struct ValuShape {
     static_assert(SL % 4 == 0, "score slice must be whole float4s");
     static_assert(KS * D4 == kThreads && KPT * KS == TK, "value phase must tile the block");
     static_assert(NQ % 4 == 0, "four waves share the softmax");
+    static_assert(TPK == 4 || TPK == 8, "a key's lanes reduce within a row");
     static_assert(UNION_FLOATS >= kMergeScratch, "merge scratch reuses the tile area");
 };
 
@@ -77,27 +78,14 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(const AttnParams p)
     // Two register tile buffers: both of a split's first tiles are requested at once, and a
     // buffer is refilled as soon as its tile has been copied to LDS.
     float4 kA[LPT], vA[LPT], kB[LPT], vB[LPT];
-    auto load_tile = [&](float4 (&kr)[LPT], float4 (&vr)[LPT], int t) {
-#pragma unroll
-        for (int j = 0; j < LPT; ++j) {
-            const int f = tid + kThreads * j;
-            const int key = f / D4, c = f % D4;
-            long long off = 0;
-            const int src = key_offset<TK>(p, gw, g, xlo, xhi, nst, t, key, off);
-            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-            if (src >= 0 && c < d4) {
-                const float *kp, *vp;
-                key_ptrs(p, src, off, kp, vp);
-                kv = *reinterpret_cast<const float4*>(kp + 4 * c);
-                vv = *reinterpret_cast<const float4*>(vp + 4 * c);
-            }
-            kr[j] = kv;
-            vr[j] = vv;
-        }
+    unsigned mA = 0u, mB = 0u;
+    const KVBases kvb = kv_bases(p);
+    auto load_tile = [&](float4 (&kr)[LPT], float4 (&vr)[LPT], unsigned& m, int t) {
+        m = load_tile_regs<TK, D, LPT>(p, kvb, gw, g, xlo, xhi, nst, t, d4, kr, vr);
     };
 
-    load_tile(kA, vA, t_begin);   // first tiles in flight while the queries are staged
-    if (t_begin + 1 < t_end) load_tile(kB, vB, t_begin + 1);
+    load_tile(kA, vA, mA, t_begin);   // first tiles in flight while the queries are staged
+    if (t_begin + 1 < t_end) load_tile(kB, vB, mB, t_begin + 1);
 
     // Per-query window in key-index space, and the scaled queries.
     if (tid < NQ) {
@@ -139,17 +127,18 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(const AttnParams p)
     const int skey = tid / TPK, sl = tid % TPK;       // score role
     const int vc = tid % D4, vks = tid / D4;          // value role
 
-    auto step = [&](float4 (&kr)[LPT], float4 (&vr)[LPT], int t) {
+    auto step = [&](float4 (&kr)[LPT], float4 (&vr)[LPT], unsigned& m, int t) {
         __syncthreads();   // the previous tile's readers are done with s_k, s_v, s_p
 #pragma unroll
         for (int j = 0; j < LPT; ++j) {
             const int f = tid + kThreads * j;
             const int key = f / D4, c = f % D4;
-            *reinterpret_cast<float4*>(s_k + key * KST + 4 * c) = kr[j];
-            *reinterpret_cast<float4*>(s_v + key * D + 4 * c) = vr[j];
+            const bool keep = (m >> j) & 1u;
+            *reinterpret_cast<float4*>(s_k + key * KST + 4 * c) = zero_unless(keep, kr[j]);
+            *reinterpret_cast<float4*>(s_v + key * D + 4 * c) = zero_unless(keep, vr[j]);
         }
         __syncthreads();
-        if (t + 2 < t_end) load_tile(kr, vr, t + 2);   // refill this buffer two tiles ahead
+        if (t + 2 < t_end) load_tile(kr, vr, m, t + 2);   // refill this buffer two tiles ahead
 
         // Scores: lanes sl of key skey hold slices; reduce over the TPK adjacent lanes.
         {
@@ -170,9 +159,7 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(const AttnParams p)
                 }
             }
 #pragma unroll
-            for (int o = 1; o < TPK; o <<= 1)
-#pragma unroll
-                for (int j = 0; j < NQ; ++j) acc[j] += __shfl_xor(acc[j], o);
+            for (int j = 0; j < NQ; ++j) acc[j] = group_sum<TPK>(acc[j]);
 #pragma unroll
             for (int j = 0; j < NQ; ++j) {
                 if (j % TPK == sl) {
@@ -226,8 +213,8 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(const AttnParams p)
         }
     };
     for (int t = t_begin; t < t_end; t += 2) {
-        step(kA, vA, t);
-        if (t + 1 < t_end) step(kB, vB, t + 1);
+        step(kA, vA, mA, t);
+        if (t + 1 < t_end) step(kB, vB, mB, t + 1);
     }
 
     // Sum the key sets through LDS, then write the output or this split's partial.
@@ -261,10 +248,10 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(const AttnParams p)
             store_out<GATED>(p, q0 + j, g, 4 * c, o);
         } else {
             const size_t at = ((size_t)blk * p.nsplit_grid + split) * NQ + j;
-            store_dev4(p.pacc + at * D + 4 * c, o);
+            store_part4(p, p.pacc + at * D + 4 * c, o);
             if (c == 0) {
-                store_dev(p.pm + at, s_m[j]);
-                store_dev(p.pl + at, s_l[j]);
+                store_part(p, p.pm + at, s_m[j]);
+                store_part(p, p.pl + at, s_l[j]);
             }
         }
     }

@@ -13,6 +13,17 @@ hipError_t launch_valu(const AttnParams& p, bool gated, int dpad, int nq, dim3 g
                        hipStream_t stream);
 int valu_tile_keys(int dpad);
 
+// Register-resident split-K kernel for <= 8 query vectors per block; grid as the VALU kernel;
+// nq in {4, 8}.
+hipError_t launch_dec(const AttnParams& p, bool gated, int dpad, int nq, dim3 grid,
+                      hipStream_t stream);
+int dec_tile_keys(int dpad);
+
+// Separate launch that merges the split partials of every query block (qb query vectors per
+// block, tk keys per tile of the attention kernel that wrote them).
+hipError_t launch_split_merge(const AttnParams& p, bool gated, int qb, int dpad, int tk,
+                              hipStream_t stream);
+
 // Split-K MFMA kernel; 1-D grid over (group, split, query block) items, XCD-aware.
 hipError_t launch_mfma(const AttnParams& p, bool gated, int dpad, hipStream_t stream);
 int mfma_query_block();

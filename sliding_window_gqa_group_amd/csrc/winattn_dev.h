@@ -48,6 +48,7 @@ struct AttnParams {
     int nqblocks;                // query blocks per group
     float scale_log2;            // scale * log2(e): scores live in the log2 domain
     int g_base, g_mod, g_hi0, g_wcap;   // gated call's ring descriptor
+    int merge_kernel;            // 1: splits are merged by a separate kernel launch
 };
 
 struct GroupWin {
@@ -104,27 +105,87 @@ __device__ inline Tiles tile_range(int ns, int xlo, int xhi, int tps, int split)
     return r;
 }
 
-// Offset (floats) of the K/V row of key k of tile t. Returns the source tensor (0 sink, 1 ring,
-// 2 chunk) or -1 for a padding key (past the sinks or past the block's stream range).
-template <int TK>
-__device__ inline int key_offset(const AttnParams& p, const GroupWin& gw, int g, int xlo,
-                                 int xhi, int nst, int t, int k, long long& off) {
+// K and V rows of key k of tile t, chosen with selects rather than branches so that a thread's
+// tile loads issue back to back. Padding keys (past the sinks or past the block's stream
+// range) get the group ring's first row, a valid address, and `valid` = false: the caller
+// loads unconditionally and zeroes the value by select.
+// K/V base addresses held as integers in registers. Selecting between pointer fields of the
+// argument struct makes the compiler fetch the chosen field from memory (or spill the choice
+// to scratch) before every K/V load; integer selects plus an explicit global address space
+// keep the loads as plain global loads that issue back to back.
+typedef float vf4 __attribute__((ext_vector_type(4)));
+typedef const vf4 __attribute__((address_space(1)))* gvf4p;
+
+struct KVBases {
+    unsigned long long rk, rv, sk, sv, ck, cv;
+};
+
+__device__ inline KVBases kv_bases(const AttnParams& p) {
+    return KVBases{(unsigned long long)p.ring_k, (unsigned long long)p.ring_v,
+                   (unsigned long long)p.sink_k, (unsigned long long)p.sink_v,
+                   (unsigned long long)p.chunk_k, (unsigned long long)p.chunk_v};
+}
+
+__device__ inline float4 ld4(unsigned long long base, int off_floats) {
+    const vf4 v = *reinterpret_cast<gvf4p>(base + 4ull * (unsigned int)off_floats);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ inline float4 zero_unless(bool keep, float4 v) {
+    return make_float4(keep ? v.x : 0.0f, keep ? v.y : 0.0f, keep ? v.z : 0.0f, keep ? v.w : 0.0f);
+}
+
+// Loads a K/V tile into registers: thread t takes float4 column t % (D/4) of keys
+// t / (D/4) + j * (256 / (D/4)), j < LPT. Sink tiles and stream tiles take separate
+// (tile-uniform) paths; within a stream tile a row is in the ring (slot (base + x) mod mod,
+// one conditional subtraction) or in the chunk. Offsets within a group are 32-bit (the host
+// keeps every tensor under 2^31 floats). Padding keys (past the sinks, past the block's stream
+// range, or columns beyond d) load the group's first ring row, a valid address; the returned
+// mask has bit j set for real keys, and the caller zeroes the others by select when it copies
+// the tile to LDS, so the loads issue back to back with nothing waiting on them.
+template <int TK, int D, int LPT>
+__device__ inline unsigned load_tile_regs(const AttnParams& p, const KVBases b,
+                                          const GroupWin& gw, int g, int xlo, int xhi, int nst,
+                                          int t, int d4, float4 (&kr)[LPT], float4 (&vr)[LPT]) {
+    static_assert(LPT <= 32, "validity mask holds 32 loads");
+    unsigned mask = 0u;
+    constexpr int D4 = D / 4;
+    constexpr int KPP = kThreads / D4;   // keys per pass of the block
+    const int key0 = threadIdx.x / D4, c = threadIdx.x % D4;
+    const bool col_ok = c < d4;
+    const unsigned long long rk = b.rk + 4ull * (unsigned long long)((long long)g * p.ring_gs);
+    const unsigned long long rv = b.rv + 4ull * (unsigned long long)((long long)g * p.ring_gs);
     if (t < nst) {
-        const int si = t * TK + k;
-        if (si >= p.ns) return -1;
-        off = ((long long)g * p.ns + si) * p.d;
-        return 0;
+        const unsigned long long sk = b.sk + 4ull * (unsigned long long)((long long)g * p.ns * p.d);
+        const unsigned long long sv = b.sv + 4ull * (unsigned long long)((long long)g * p.ns * p.d);
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) {
+            const int si = t * TK + key0 + KPP * j;
+            const bool valid = si < p.ns && col_ok;
+            const int off = valid ? si * p.d + 4 * c : 0;
+            kr[j] = ld4(valid ? sk : rk, off);
+            vr[j] = ld4(valid ? sv : rv, off);
+            mask |= valid ? 1u << j : 0u;
+        }
+    } else {
+        const unsigned long long ck = b.ck + 4ull * (unsigned long long)((long long)g * p.chunk_gs);
+        const unsigned long long cv = b.cv + 4ull * (unsigned long long)((long long)g * p.chunk_gs);
+        const int ss = (int)p.ring_ss, crs = (int)p.chunk_rs;
+        const int x0 = xlo + (t - nst) * TK + key0;
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) {
+            const int x = x0 + KPP * j;
+            const bool valid = x < xhi && col_ok;
+            const bool in_ring = x < gw.xsplit || !valid;
+            int slot = gw.base + x;
+            slot = slot >= gw.mod ? slot - gw.mod : slot;
+            const int off = !valid ? 0 : (in_ring ? slot * ss : (x - gw.xsplit) * crs) + 4 * c;
+            kr[j] = ld4(in_ring ? rk : ck, off);
+            vr[j] = ld4(in_ring ? rv : cv, off);
+            mask |= valid ? 1u << j : 0u;
+        }
     }
-    const int x = xlo + (t - nst) * TK + k;
-    if (x >= xhi) return -1;
-    if (x < gw.xsplit) {
-        int slot = gw.base + x;
-        if (slot >= gw.mod) slot -= gw.mod;
-        off = (long long)g * p.ring_gs + (long long)slot * p.ring_ss;
-        return 1;
-    }
-    off = (long long)(x - gw.xsplit) * p.chunk_rs + (long long)g * p.chunk_gs;
-    return 2;
+    return mask;
 }
 
 // Whether key k of tile t is visible to a query whose stream window is [lo, hi); `sinks` is
@@ -137,30 +198,55 @@ __device__ inline bool key_visible(int ns, int xlo, int nst, int t, int k, int l
     return x >= lo && x < hi;
 }
 
-__device__ inline void key_ptrs(const AttnParams& p, int src, long long off, const float*& kp,
-                                const float*& vp) {
-    if (src == 0) {
-        kp = p.sink_k + off;
-        vp = p.sink_v + off;
-    } else if (src == 1) {
-        kp = p.ring_k + off;
-        vp = p.ring_v + off;
-    } else {
-        kp = p.chunk_k + off;
-        vp = p.chunk_v + off;
-    }
+// Cross-lane steps on DPP (data-parallel primitives: a VALU operand read from another lane of
+// the same row of 16 or broadcast across rows), not on the LDS crossbar.
+enum : int {
+    kDppXor1 = 0xB1,          // quad_perm [1,0,3,2]
+    kDppXor2 = 0x4E,          // quad_perm [2,3,0,1]
+    kDppHalfMirror = 0x141,   // lane i <-> 7 - i within each half row
+    kDppMirror = 0x140,       // lane i <-> 15 - i within each row
+    kDppBcast15 = 0x142,      // lane 15 of each row to the whole next row
+    kDppBcast31 = 0x143,      // lane 31 to rows 2 and 3
+};
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ inline float dpp(float v, float fill) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(v), CTRL,
+                                                      ROW_MASK, 0xF, false));
 }
 
-__device__ inline float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+// Max / sum over groups of N adjacent lanes (N in 2, 4, 8, 16), result in every lane of a group.
+template <int N>
+__device__ inline float group_max(float v) {
+    if constexpr (N >= 2) v = fmaxf(v, dpp<kDppXor1>(v, -INFINITY));
+    if constexpr (N >= 4) v = fmaxf(v, dpp<kDppXor2>(v, -INFINITY));
+    if constexpr (N >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v, -INFINITY));
+    if constexpr (N >= 16) v = fmaxf(v, dpp<kDppMirror>(v, -INFINITY));
     return v;
+}
+
+template <int N>
+__device__ inline float group_sum(float v) {
+    if constexpr (N >= 2) v += dpp<kDppXor1>(v, 0.0f);
+    if constexpr (N >= 4) v += dpp<kDppXor2>(v, 0.0f);
+    if constexpr (N >= 8) v += dpp<kDppHalfMirror>(v, 0.0f);
+    if constexpr (N >= 16) v += dpp<kDppMirror>(v, 0.0f);
+    return v;
+}
+
+// Max / sum over the whole wave, returned uniform (every lane).
+__device__ inline float wave_max(float v) {
+    v = group_max<16>(v);
+    v = fmaxf(v, dpp<kDppBcast15, 0xA>(v, -INFINITY));
+    v = fmaxf(v, dpp<kDppBcast31, 0xC>(v, -INFINITY));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    v = group_sum<16>(v);
+    v += dpp<kDppBcast15, 0xA>(v, 0.0f);
+    v += dpp<kDppBcast31, 0xC>(v, 0.0f);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Numerically safe online-softmax step in the log2 domain. Given the running max m_old and the
@@ -187,10 +273,11 @@ __device__ inline void store_out(const AttnParams& p, int qi, int g, int e, floa
     *reinterpret_cast<float4*>(p.out + ((size_t)row * p.nh + gh) * p.d + e) = o;
 }
 
-// Split partials cross XCDs, whose L2 caches are not coherent with each other. Rather than
-// agent-scope fences (which write back and invalidate a whole L2 from every workgroup), the
-// partials are written and read with device-scope accesses: relaxed agent-scope atomics,
-// which the compiler emits as stores/loads carrying the device-scope cache bit.
+// Split partials cross XCDs, whose L2 caches are not coherent with each other. Rather than a
+// release fence in every workgroup (which writes back a whole L2), the partials are stored
+// with device-scope stores (relaxed agent-scope atomics, emitted with the device-scope cache
+// bit, acknowledged once visible device-wide); only the one merging workgroup per block then
+// performs an agent-scope acquire before reading them.
 __device__ inline void store_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -242,41 +329,30 @@ __device__ inline void fold_splits(const AttnParams& p, size_t base, int j, int 
     for (int s = s0; s < nsplit; s += kMergeUnroll * stride) {
         float m[kMergeUnroll], l[kMergeUnroll];
         float4 a[kMergeUnroll];
+        // Unconditional loads (a split index past the end reads the last split again) so that
+        // the whole batch issues back to back; the extra entries are dropped by select.
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
-            const int su = s + u * stride;
-            m[u] = -INFINITY;
-            l[u] = 0.0f;
-            a[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (su < nsplit) {
-                const size_t at = base + (size_t)su * QB + j;
-                m[u] = load_dev(p.pm + at);
-                l[u] = load_dev(p.pl + at);
-                a[u] = load_dev4(p.pacc + at * D + 4 * c);
-            }
+            const int su = min(s + u * stride, nsplit - 1);
+            const size_t at = base + (size_t)su * QB + j;
+            m[u] = p.pm[at];
+            l[u] = p.pl[at];
+            a[u] = *reinterpret_cast<const float4*>(p.pacc + at * D + 4 * c);
         }
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) part_fold(x, m[u], l[u], a[u]);
+        for (int u = 0; u < kMergeUnroll; ++u) {
+            const bool real = s + u * stride < nsplit;
+            part_fold(x, real ? m[u] : -INFINITY, real ? l[u] : 0.0f,
+                      real ? a[u] : make_float4(0.f, 0.f, 0.f, 0.f));
+        }
     }
 }
 
+// Combines the nsplit partials of query block `blk` into the output (all threads of the block
+// call it). `scratch` is free LDS of at least kMergeScratch floats.
 template <int QB, int D, bool GATED>
-__device__ inline void merge_if_last(const AttnParams& p, int blk, int nsplit, int q0, int nq,
-                                     int g, int* s_flag, float* scratch) {
-    static_assert(QB <= kThreads && kThreads % QB == 0, "query block must divide the block");
-    // Every thread's device-scope partial stores are acknowledged before the counter moves.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned int prev =
-            __hip_atomic_fetch_add(p.tickets + blk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int last = (prev == (unsigned int)(nsplit - 1));
-        if (last) __hip_atomic_store(p.tickets + blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_flag = last;
-    }
-    __syncthreads();
-    if (!*s_flag) return;
-
+__device__ inline void merge_block(const AttnParams& p, int blk, int nsplit, int q0, int nq, int g,
+                                   float* scratch) {
     constexpr int D4 = D / 4;
     const int d4 = p.d / 4;
     const size_t base = (size_t)blk * p.nsplit_grid * QB;
@@ -318,6 +394,40 @@ __device__ inline void merge_if_last(const AttnParams& p, int blk, int nsplit, i
                              make_float4(x.a.x * inv, x.a.y * inv, x.a.z * inv, x.a.w * inv));
         }
     }
+}
+
+// After every split of a query block has written its partial, the last one to arrive merges
+// them. When the plan uses a separate merge kernel (p.merge_kernel), this returns at once.
+template <int QB, int D, bool GATED>
+__device__ inline void merge_if_last(const AttnParams& p, int blk, int nsplit, int q0, int nq,
+                                     int g, int* s_flag, float* scratch) {
+    static_assert(QB <= kThreads && kThreads % QB == 0, "query block must divide the block");
+    if (p.merge_kernel) return;
+    // Every thread's device-scope partial stores are acknowledged before the counter moves.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned int prev =
+            __hip_atomic_fetch_add(p.tickets + blk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = (prev == (unsigned int)(nsplit - 1));
+        if (last) __hip_atomic_store(p.tickets + blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = last;
+    }
+    __syncthreads();
+    if (!*s_flag) return;
+    // Acquire at agent scope: drop this XCD's L2 copies of lines other XCDs have written, so the
+    // plain vector loads below read the partials the other splits stored at device scope.
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    merge_block<QB, D, GATED>(p, blk, nsplit, q0, nq, g, scratch);
+}
+
+// Partial stores: device scope for the in-kernel merge; plain when a separate merge kernel
+// reads them after the kernel boundary.
+__device__ inline void store_part(const AttnParams& p, float* dst, float v) {
+    if (p.merge_kernel) *dst = v; else store_dev(dst, v);
+}
+__device__ inline void store_part4(const AttnParams& p, float* dst, float4 v) {
+    if (p.merge_kernel) *reinterpret_cast<float4*>(dst) = v; else store_dev4(dst, v);
 }
 
 }  // namespace winattn

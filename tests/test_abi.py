@@ -98,7 +98,8 @@ def test_workspace_queries(lib):
 
 
 def test_plans_of_the_named_workloads(lib):
-    assert B.chunk_plan(1, 8, 4, 128, 4096, 4)[0] == 1          # decode: vector-ALU split-K
+    assert B.chunk_plan(1, 8, 4, 128, 4096, 4)[0] == 1          # decode: register split-K
+    assert B.chunk_plan(4, 8, 4, 128, 4096, 4)[0] == 3          # 16 queries: LDS vector kernel
     assert B.chunk_plan(512, 8, 4, 128, 4096, 4)[0] == 2        # prefill: matrix cores
     k, qb, splits, kps = B.chunk_plan(2048, 8, 8, 128, 32768, 4)
     assert k == 2 and splits * kps >= 4 + 32768 + 16
@@ -111,7 +112,10 @@ def test_tuning_knobs_change_the_plan(lib):
         B.tuning_set(B.TUNE_FORCE_KERNEL, 1)
         B.tuning_set(B.TUNE_TILES_PER_SPLIT, 1)
         k, qb, splits, kps = B.chunk_plan(512, 8, 4, 128, 4096, 4)
-        assert k == 1 and qb == 16 and kps == 64
+        assert k == 1 and qb == 8 and kps == 32
+        B.tuning_set(B.TUNE_FORCE_KERNEL, 3)
+        k, qb, splits, kps = B.chunk_plan(512, 8, 4, 128, 4096, 4)
+        assert k == 3 and qb == 16 and kps == 64
     finally:
         B.tuning_set(B.TUNE_FORCE_KERNEL, 0)
         B.tuning_set(B.TUNE_TILES_PER_SPLIT, 0)

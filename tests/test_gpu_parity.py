@@ -26,7 +26,8 @@ def _gpu():
         pytest.skip("no GPU")
     B.load()   # fail loudly if the HIP library is missing
     yield
-    for knob in (B.TUNE_FORCE_KERNEL, B.TUNE_TILES_PER_SPLIT, B.TUNE_TARGET_BLOCKS):
+    for knob in (B.TUNE_FORCE_KERNEL, B.TUNE_TILES_PER_SPLIT, B.TUNE_TARGET_BLOCKS,
+                 B.TUNE_MERGE_KERNEL):
         B.tuning_set(knob, 0)
 
 
@@ -170,8 +171,13 @@ SWEEP = [
 
 VARIANTS = {
     "auto": {},
-    "valu_many_splits": {B.TUNE_FORCE_KERNEL: 1, B.TUNE_TILES_PER_SPLIT: 1},
+    "register_many_splits": {B.TUNE_FORCE_KERNEL: 1, B.TUNE_TILES_PER_SPLIT: 1},
     "mfma_many_splits": {B.TUNE_FORCE_KERNEL: 2, B.TUNE_TILES_PER_SPLIT: 1},
+    "lds_vector_many_splits": {B.TUNE_FORCE_KERNEL: 3, B.TUNE_TILES_PER_SPLIT: 1},
+    "register_merge_launch": {B.TUNE_FORCE_KERNEL: 1, B.TUNE_TILES_PER_SPLIT: 1,
+                              B.TUNE_MERGE_KERNEL: 2},
+    "mfma_merge_launch": {B.TUNE_FORCE_KERNEL: 2, B.TUNE_TILES_PER_SPLIT: 1,
+                          B.TUNE_MERGE_KERNEL: 2},
 }
 
 

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libwinattn.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "winattn.h")
 
 OK, EINVAL, EWORKSPACE, ELAUNCH, EUNSUPPORTED = 0, -1, -2, -3, -4
-TUNE_FORCE_KERNEL, TUNE_TILES_PER_SPLIT, TUNE_TARGET_BLOCKS, TUNE_MERGE_KERNEL = 1, 2, 3, 4
+TUNE_FORCE_KERNEL, TUNE_TILES_PER_SPLIT, TUNE_TARGET_BLOCKS, TUNE_MERGE_KERNEL, TUNE_XCD_MAP = 1, 2, 3, 4, 5
 
 _lib = None
 _vp = ctypes.c_void_p

@@ -18,6 +18,7 @@ int g_force_kernel = 0;     // 1 register kernel, 2 MFMA, 3 LDS vector kernel
 int g_tiles_per_split = 0;
 int g_target_blocks = 0;
 int g_merge_kernel = -1;    // -1 automatic, 0 merge in the last split, 1 separate merge launch
+int g_xcd_map = -1;         // -1 automatic, else the matrix-core work order
 
 constexpr int kValuMaxQ = 16;
 // Split counters sit at the start of every workspace, at the same place for every plan, so
@@ -38,6 +39,7 @@ struct Plan {
     int tps;            // tiles per split
     int nsplit;         // splits reserved per block
     bool merge_kernel;  // merge splits in a separate launch
+    int xcd_map;        // matrix-core work order: 1 whole groups per XCD, 0 round-robin
     size_t off_q, off_pacc, off_pm, off_pl, off_tickets, bytes;
 };
 
@@ -94,11 +96,15 @@ Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_f
     if (blocks > kMaxTickets) tps = max_tiles;
     pl.tps = tps;
     pl.nsplit = cdiv(max_tiles, tps);
-    // Decode-sized calls finish all their splits at nearly the same moment, so the merge is on
-    // the critical path: a separate launch (coherence at the kernel boundary) is cheaper than
-    // device-scope stores, a counter and an acquire. Wide calls merge in the last split, which
-    // overlaps with other blocks still computing.
-    pl.merge_kernel = g_merge_kernel >= 0 ? g_merge_kernel == 1 : pl.kind == kKindDec;
+    // Splits merge in a separate launch by default: the kernel boundary makes the partials
+    // visible, so the attention kernel stores them plainly, with no acknowledged device-scope
+    // stores, counter or acquire, and no block's tail carries a merge (measured faster for the
+    // decode, prefill and gated workloads). Merging in the last-arriving split stays available.
+    pl.merge_kernel = g_merge_kernel >= 0 ? g_merge_kernel == 1 : true;
+    // Whole groups per XCD when a group's K/V stream fits comfortably in an XCD's 4 MB L2
+    // (twice that, since neighbouring blocks only touch the part of the window they share).
+    const long long group_bytes = ((long long)wcap + span + ns) * d * 8;
+    pl.xcd_map = g_xcd_map >= 0 ? g_xcd_map : (group_bytes <= (8LL << 20) ? 1 : 0);
 
     // Layout: [counters][prepared queries][partials], each region 256-byte aligned.
     const bool split = pl.nsplit > 1;
@@ -152,6 +158,7 @@ bool gated_shape_ok(int rows, int pos0, int cap, int window, int nh, int nk, int
 }
 
 int launch_attention(const Plan& pl, AttnParams& p, bool gated, char* ws, hipStream_t stream) {
+    p.xcd_map = pl.xcd_map;
     p.tps = pl.tps;
     p.nsplit_grid = pl.nsplit;
     p.nqblocks = pl.nqblocks;
@@ -364,6 +371,10 @@ int attn_tuning_set(int knob, int value) {
         case WINATTN_TUNE_MERGE_KERNEL:
             if (value > 2) return WINATTN_EINVAL;
             g_merge_kernel = value - 1;
+            return WINATTN_OK;
+        case WINATTN_TUNE_XCD_MAP:
+            if (value > 2) return WINATTN_EINVAL;
+            g_xcd_map = value - 1;
             return WINATTN_OK;
         default:
             return WINATTN_EINVAL;

@@ -18,9 +18,7 @@
 // halves, which lets every lane read its K and Q operands as float4s.
 //
 // A workgroup owns 128 consecutive query vectors (row-major over (row, head) of one group),
-// 32 per wave, and one split of the key tiles that the block's rows can see. Work items are
-// mapped XCD-aware: consecutive query blocks of one (group, split) read nearly the same K/V
-// tiles, so they are placed on the same XCD to share its L2.
+// 32 per wave, and one split of the key tiles that the block's rows can see.
 #include "winattn_dev.h"
 #include "launch.h"
 
@@ -42,10 +40,17 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
     __shared__ __align__(16) float s_v[TK * VST];
     __shared__ int s_flag;
 
-    // XCD-aware decode of the work item: hardware deals blocks to the 8 XCDs round-robin.
+    // Work item = (group, split, query block), query block fastest. The hardware deals blocks
+    // to the 8 XCDs round-robin (block b to XCD b % 8). Two orders:
+    //  - xcd_map 1: XCD x takes the x-th contiguous eighth of the items, i.e. whole groups when
+    //    the items divide evenly: all query blocks of a group share that XCD's L2, which holds
+    //    the group's K/V when its window is short (a few MB);
+    //  - xcd_map 0: item = b, every XCD gets a uniform mix of groups and splits, which balances
+    //    groups of very different windows when their K/V cannot stay in L2 anyway.
     const int n_items = p.nsplit_grid * p.nqblocks * p.ng;
     const int per_xcd = (n_items + 7) / 8;
-    const int item = (int)(blockIdx.x % 8u) * per_xcd + (int)(blockIdx.x / 8u);
+    const int item = p.xcd_map ? (int)(blockIdx.x % 8u) * per_xcd + (int)(blockIdx.x / 8u)
+                               : (int)blockIdx.x;
     if (item >= n_items) return;
     const int qb = item % p.nqblocks;
     const int split = (item / p.nqblocks) % p.nsplit_grid;
@@ -121,9 +126,12 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
         __syncthreads();
         if (t + 1 < t_end) load_tile(t + 1);
 
+        // This lane's visible keys of the tile as a range [klo, khi) of key indices.
         const int tx = xlo + (t - nst) * TK;   // first stream entry of a stream tile
-        const bool sees = t < nst || (tx < hi && tx + TK > lo);
-        if (!__any(sees)) continue;   // the whole wave's queries miss this tile
+        const bool sink_tile = t < nst;
+        const int klo = sink_tile ? 0 : lo - tx;
+        const int khi = sink_tile ? p.ns - t * TK : hi - tx;
+        if (!__any(klo < TK && khi > 0 && khi > klo)) continue;   // the whole wave misses it
 
         floatx16 sacc;
 #pragma unroll
@@ -142,12 +150,11 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
         float tmax = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const bool vis = key_visible<TK>(p.ns, xlo, nst, t, 8 * (r >> 2) + 4 * hb + (r & 3),
-                                             lo, hi, true);
-            sacc[r] = vis ? sacc[r] : -INFINITY;
+            const int k = 8 * (r >> 2) + 4 * hb + (r & 3);
+            sacc[r] = (k >= klo && k < khi) ? sacc[r] : -INFINITY;
             tmax = fmaxf(tmax, sacc[r]);
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = half_swap_max(tmax);
         const float m_new = fmaxf(mrun, tmax);
         const float mu = safe_max(m_new);
         const float corr = __builtin_amdgcn_exp2f(mrun - mu);
@@ -157,13 +164,17 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
             sacc[r] = __builtin_amdgcn_exp2f(sacc[r] - mu);
             psum += sacc[r];
         }
-        psum += __shfl_xor(psum, 32);
+        psum = half_swap_sum(psum);
         lrun = lrun * corr + psum;
+        // Rescale the accumulators only when some lane's running max moved (after the first
+        // few tiles of a long window it rarely does).
+        if (__any(m_new != mrun)) {
+#pragma unroll
+            for (int b = 0; b < NDB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[b][r] *= corr;
+        }
         mrun = m_new;
-#pragma unroll
-        for (int b = 0; b < NDB; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[b][r] *= corr;
 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -214,7 +225,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
 template <int D, bool GATED>
 static hipError_t launch_mfma_t(const AttnParams& p, hipStream_t stream) {
     const int n_items = p.nsplit_grid * p.nqblocks * p.ng;
-    const int blocks = 8 * ((n_items + 7) / 8);
+    const int blocks = p.xcd_map ? 8 * ((n_items + 7) / 8) : n_items;
     hipLaunchKernelGGL((attn_mfma_kernel<D, GATED>), dim3(blocks), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }

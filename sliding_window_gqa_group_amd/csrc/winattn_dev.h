@@ -49,6 +49,7 @@ struct AttnParams {
     float scale_log2;            // scale * log2(e): scores live in the log2 domain
     int g_base, g_mod, g_hi0, g_wcap;   // gated call's ring descriptor
     int merge_kernel;            // 1: splits are merged by a separate kernel launch
+    int xcd_map;                 // matrix-core kernel's work order (see attn_mfma.hip)
 };
 
 struct GroupWin {
@@ -232,6 +233,17 @@ __device__ inline float group_sum(float v) {
     if constexpr (N >= 8) v += dpp<kDppHalfMirror>(v, 0.0f);
     if constexpr (N >= 16) v += dpp<kDppMirror>(v, 0.0f);
     return v;
+}
+
+// Max / sum of a lane's value with that of lane l ^ 32 (gfx950 v_permlane32_swap: with the
+// same value in both operands, the two results hold the lane's own and its partner's value).
+__device__ inline float half_swap_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float half_swap_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Max / sum over the whole wave, returned uniform (every lane).

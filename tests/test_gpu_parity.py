@@ -27,7 +27,7 @@ def _gpu():
     B.load()   # fail loudly if the HIP library is missing
     yield
     for knob in (B.TUNE_FORCE_KERNEL, B.TUNE_TILES_PER_SPLIT, B.TUNE_TARGET_BLOCKS,
-                 B.TUNE_MERGE_KERNEL):
+                 B.TUNE_MERGE_KERNEL, B.TUNE_XCD_MAP):
         B.tuning_set(knob, 0)
 
 
@@ -178,6 +178,8 @@ VARIANTS = {
                               B.TUNE_MERGE_KERNEL: 2},
     "mfma_merge_launch": {B.TUNE_FORCE_KERNEL: 2, B.TUNE_TILES_PER_SPLIT: 1,
                           B.TUNE_MERGE_KERNEL: 2},
+    "mfma_in_kernel_merge_other_order": {B.TUNE_FORCE_KERNEL: 2, B.TUNE_TILES_PER_SPLIT: 2,
+                                         B.TUNE_MERGE_KERNEL: 1, B.TUNE_XCD_MAP: 2},
 }
 
 

@@ -28,7 +28,8 @@ HBM_PEAK_GBS = 8000.0
 F32_PEAK_TFLOPS = 157.3
 METRIC = "KV GB/s and rows/s for windowed GQA attention; % of HBM peak"
 KERNEL_NAMES = {1: "attn_dec_kernel", 2: "attn_mfma_kernel", 3: "attn_valu_kernel"}
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_valu_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_dec_kernel_decode_counters.json")
+CALIBRATION_COPY_BYTES = 64 << 20
 
 
 def kernel_source_digest() -> str:
@@ -182,6 +183,43 @@ def bench_others(args, torch, B, gen, acct):
     return res
 
 
+def counter_run(args, torch, B, gen):
+    """A short, untimed run for hardware-counter passes: one device-to-device copy of
+    CALIBRATION_COPY_BYTES (reads and writes exactly that many bytes), then `calls` calls of one
+    workload on rotating input sets, as the timed decode run makes them."""
+    dev = "cuda:0"
+    src = torch.empty(CALIBRATION_COPY_BYTES // 4, dtype=torch.float32, device=dev).normal_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    name = args.counter_run
+    if name == "gated":
+        g = gen.gated()
+        t = gen.to_device(g, dev)
+        out = torch.empty((g.rows, g.nh, g.hd), dtype=torch.float32, device=dev)
+        for _ in range(args.calls):
+            B.attn_window_gated(t["yq"], t["yk"], t["yv"], t["rope"], t["q_scale"], t["gate"],
+                                t["gate_scale"], t["ring_k"], t["ring_v"], g.pos0, g.window,
+                                g.scale, g.eps, out=out)
+    else:
+        inp = {"tiny": gen.tiny, "decode": gen.decode, "prefill": gen.prefill,
+               "large": gen.large}[name]()
+        base = chunk_tensors(inp, torch, dev)
+        n_sets = args.sets if name in ("tiny", "decode") else 1
+        sets = [base] + [{k: (v.clone() if v is not None else None) for k, v in base.items()}
+                         for _ in range(n_sets - 1)]
+        out = torch.empty((inp.rows, inp.nh, inp.d), dtype=torch.float32, device=dev)
+        ws = B.Workspace(dev)
+        ws.get(B.chunk_workspace_bytes(inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns))
+        for i in range(args.calls):
+            run_chunk(B, sets[i % n_sets], inp.scale, out, ws)
+    torch.cuda.synchronize()
+    print(f"counter run: {name}, {args.calls} calls, calibration copy {CALIBRATION_COPY_BYTES} B",
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,6 +229,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-others", action="store_true")
+    ap.add_argument("--counter-run", choices=["tiny", "decode", "prefill", "large", "gated"],
+                    help="untimed calls of one workload for rocprofv3 counter passes; no JSON")
+    ap.add_argument("--calls", type=int, default=20)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only; run with --gpus 1 (the per-GPU "
@@ -205,6 +246,9 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     B.load()
+    if args.counter_run:
+        counter_run(args, torch, B, gen)
+        return
     inp, ms, ev_mean, ev_med, kv, tot, set_bytes = bench_decode(args, torch, B, gen, acct)
     value = kv / (ms * 1e-3) / 1e9
     plan = B.chunk_plan(inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns)

@@ -178,7 +178,7 @@ int launch_attention(const Plan& pl, AttnParams& p, bool gated, char* ws, hipStr
     else
         err = launch_valu(p, gated, pl.dpad, pl.qb, grid, stream);
     if (err == hipSuccess && p.merge_kernel)
-        err = launch_split_merge(p, gated, pl.qb, pl.dpad, pl.tk, stream);
+        err = launch_split_merge(p, gated, pl.qb, pl.dpad, stream);
     return err == hipSuccess ? WINATTN_OK : WINATTN_ELAUNCH;
 }
 

@@ -75,7 +75,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dec_kernel(const AttnParams 
     const int xhi = gw.hi0 + r_last;
     const Tiles tr = tile_range<TK>(p.ns, xlo, xhi, p.tps, split);
     const int nsplit = tr.nsplit, nst = tr.nst;
-    if (split >= nsplit) return;
+    if (split >= nsplit) {
+        mark_split_empty<NQ>(p, g * p.nqblocks + qb, split);
+        return;
+    }
     const int t_begin = tr.t_begin, t_end = tr.t_end;
     const int d4 = p.d / 4;
 
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dec_kernel(const AttnParams 
         if (j >= nq || c >= d4) continue;
         vf4 o = {0.f, 0.f, 0.f, 0.f};
         for (int u = 0; u < KPP; ++u) o += *reinterpret_cast<const vf4*>(s_red + (u * NQ + j) * D + 4 * c);
-        if (nsplit == 1) {
+        if (nsplit == 1 && !p.merge_kernel) {
             o *= 1.0f / fmaxf(s_l[j], 1e-30f);
             store_out<GATED>(p, q0 + j, g, 4 * c, make_float4(o.x, o.y, o.z, o.w));
         } else {
@@ -266,22 +269,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dec_kernel(const AttnParams 
     }
 }
 
-// Separate merge launch: one workgroup per query block, grid = (query blocks, groups).
+// Separate merge launch: one workgroup per (query block, group, 32-column chunk), so that the
+// partials are read by many CUs at once rather than by one per block.
+constexpr int kMergeCols = 32;
+
 template <int QB, int D, bool GATED>
-__global__ __launch_bounds__(kThreads) void split_merge_kernel(const AttnParams p, int tk) {
+__global__ __launch_bounds__(kThreads) void split_merge_kernel(const AttnParams p) {
     __shared__ __align__(16) float scratch[kMergeScratch];
     const int qb = blockIdx.x, g = blockIdx.y;
-    const int nq_tot = p.rows * p.hpg;
     const int q0 = qb * QB;
-    const int nq = min(QB, nq_tot - q0);
-    const GroupWin gw = resolve_group<GATED>(p, g);
-    const int r_first = q0 / p.hpg, r_last = (q0 + nq - 1) / p.hpg;
-    const int xlo = window_lo(gw.hi0 + r_first, gw.wcap);
-    const int xhi = gw.hi0 + r_last;
-    const int nstream = (xhi - xlo + tk - 1) / tk;
-    const int nsplit = (nstream + p.tps - 1) / p.tps;
-    if (nsplit <= 1) return;   // that block wrote its output directly
-    merge_block<QB, D, GATED>(p, g * p.nqblocks + qb, nsplit, q0, nq, g, scratch);
+    const int nq = min(QB, p.rows * p.hpg - q0);
+    // Every split slot of the block holds a partial or an empty mark (see mark_split_empty).
+    merge_block<QB, D, GATED, kMergeCols>(p, g * p.nqblocks + qb, p.nsplit_grid, q0, nq, g,
+                                          scratch, (int)blockIdx.z * (kMergeCols / 4));
 }
 
 template <int D, int NQ, bool GATED>
@@ -302,11 +302,11 @@ static hipError_t launch_dec_g(const AttnParams& p, int dpad, int nq, dim3 grid,
 }
 
 template <bool GATED>
-static hipError_t launch_merge_g(const AttnParams& p, int qb, int dpad, int tk, hipStream_t s) {
-    const dim3 grid(p.nqblocks, p.ng);
+static hipError_t launch_merge_g(const AttnParams& p, int qb, int dpad, hipStream_t s) {
+    const dim3 grid(p.nqblocks, p.ng, dpad / kMergeCols);
 #define WINATTN_MERGE_CASE(QQ, DD)                                                                  \
     if (qb == QQ && dpad == DD) {                                                                   \
-        hipLaunchKernelGGL((split_merge_kernel<QQ, DD, GATED>), grid, dim3(kThreads), 0, s, p, tk); \
+        hipLaunchKernelGGL((split_merge_kernel<QQ, DD, GATED>), grid, dim3(kThreads), 0, s, p);     \
         return hipGetLastError();                                                                   \
     }
     WINATTN_MERGE_CASE(4, 64) WINATTN_MERGE_CASE(4, 128) WINATTN_MERGE_CASE(4, 256)
@@ -317,10 +317,10 @@ static hipError_t launch_merge_g(const AttnParams& p, int qb, int dpad, int tk, 
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_split_merge(const AttnParams& p, bool gated, int qb, int dpad, int tk,
+hipError_t launch_split_merge(const AttnParams& p, bool gated, int qb, int dpad,
                               hipStream_t stream) {
-    return gated ? launch_merge_g<true>(p, qb, dpad, tk, stream)
-                 : launch_merge_g<false>(p, qb, dpad, tk, stream);
+    return gated ? launch_merge_g<true>(p, qb, dpad, stream)
+                 : launch_merge_g<false>(p, qb, dpad, stream);
 }
 
 hipError_t launch_dec(const AttnParams& p, bool gated, int dpad, int nq, dim3 grid,

@@ -69,7 +69,10 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
     const int xhi = gw.hi0 + r_last;
     const Tiles tr = tile_range<TK>(p.ns, xlo, xhi, p.tps, split);
     const int nsplit = tr.nsplit, nst = tr.nst;
-    if (split >= nsplit) return;
+    if (split >= nsplit) {
+        mark_split_empty<QB>(p, g * p.nqblocks + qb, split);
+        return;
+    }
     const int t_begin = tr.t_begin, t_end = tr.t_end;
     const int d4 = p.d / 4;
 
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
 
     // Lane holds, for its query, d = 32b + 8m + 4*hb + (0..3) in oacc[b][4m .. 4m+3].
     const int blk = g * p.nqblocks + qb;
-    if (nsplit == 1) {
+    if (nsplit == 1 && !p.merge_kernel) {
         if (qvalid) {
             const float inv = 1.0f / fmaxf(lrun, 1e-30f);
 #pragma unroll

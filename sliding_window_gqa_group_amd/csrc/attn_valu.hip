@@ -71,7 +71,10 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(const AttnParams p)
     const int xhi = gw.hi0 + r_last;
     const Tiles tr = tile_range<TK>(p.ns, xlo, xhi, p.tps, split);
     const int nsplit = tr.nsplit, nst = tr.nst;
-    if (split >= nsplit) return;
+    if (split >= nsplit) {
+        mark_split_empty<NQ>(p, g * p.nqblocks + qb, split);
+        return;
+    }
     const int t_begin = tr.t_begin, t_end = tr.t_end;
     const int d4 = p.d / 4;
 
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(const AttnParams p)
             const float4 a = *reinterpret_cast<const float4*>(s_red + (ks * NQ + j) * D + 4 * c);
             o.x += a.x; o.y += a.y; o.z += a.z; o.w += a.w;
         }
-        if (nsplit == 1) {
+        if (nsplit == 1 && !p.merge_kernel) {
             const float inv = 1.0f / fmaxf(s_l[j], 1e-30f);
             o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
             store_out<GATED>(p, q0 + j, g, 4 * c, o);

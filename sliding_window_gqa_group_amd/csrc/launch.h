@@ -20,8 +20,8 @@ hipError_t launch_dec(const AttnParams& p, bool gated, int dpad, int nq, dim3 gr
 int dec_tile_keys(int dpad);
 
 // Separate launch that merges the split partials of every query block (qb query vectors per
-// block, tk keys per tile of the attention kernel that wrote them).
-hipError_t launch_split_merge(const AttnParams& p, bool gated, int qb, int dpad, int tk,
+// block); it reads only the partials, never the ring metadata.
+hipError_t launch_split_merge(const AttnParams& p, bool gated, int qb, int dpad,
                               hipStream_t stream);
 
 // Split-K MFMA kernel; 1-D grid over (group, split, query block) items, XCD-aware.

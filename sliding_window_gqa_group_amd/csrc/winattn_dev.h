@@ -353,7 +353,8 @@ __device__ inline void fold_splits(const AttnParams& p, size_t base, int j, int 
         }
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
-            const bool real = s + u * stride < nsplit;
+            // past the end, or a split that marked its slot empty (m = -inf)
+            const bool real = s + u * stride < nsplit && m[u] > -INFINITY;
             part_fold(x, real ? m[u] : -INFINITY, real ? l[u] : 0.0f,
                       real ? a[u] : make_float4(0.f, 0.f, 0.f, 0.f));
         }
@@ -361,11 +362,13 @@ __device__ inline void fold_splits(const AttnParams& p, size_t base, int j, int 
 }
 
 // Combines the nsplit partials of query block `blk` into the output (all threads of the block
-// call it). `scratch` is free LDS of at least kMergeScratch floats.
-template <int QB, int D, bool GATED>
+// call it), for the DC columns starting at column 4 * c0 (DC = D: every column). `scratch` is
+// free LDS of at least kMergeScratch floats.
+template <int QB, int D, bool GATED, int DC = D>
 __device__ inline void merge_block(const AttnParams& p, int blk, int nsplit, int q0, int nq, int g,
-                                   float* scratch) {
-    constexpr int D4 = D / 4;
+                                   float* scratch, int c0 = 0) {
+    static_assert(DC % 4 == 0 && D % DC == 0, "column chunk must divide the padded width");
+    constexpr int D4 = DC / 4;
     const int d4 = p.d / 4;
     const size_t base = (size_t)blk * p.nsplit_grid * QB;
     constexpr int ITEMS = QB * D4;
@@ -374,7 +377,7 @@ __device__ inline void merge_block(const AttnParams& p, int blk, int nsplit, int
 #pragma unroll
         for (int k = 0; k < IPT; ++k) {
             const int item = threadIdx.x + kThreads * k;
-            const int j = item / D4, c = item % D4;
+            const int j = item / D4, c = c0 + item % D4;
             Part x{-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
             fold_splits<QB, D>(p, base, j, c, 0, 1, nsplit, x);
             if (j < nq && c < d4) {
@@ -386,7 +389,7 @@ __device__ inline void merge_block(const AttnParams& p, int blk, int nsplit, int
     } else {
         constexpr int NSUB = kThreads / ITEMS;
         const int item = threadIdx.x % ITEMS, sub = threadIdx.x / ITEMS;
-        const int j = item / D4, c = item % D4;
+        const int j = item / D4, c = c0 + item % D4;
         Part x{-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
         fold_splits<QB, D>(p, base, j, c, sub, NSUB, nsplit, x);
         float* s_m = scratch;
@@ -406,6 +409,15 @@ __device__ inline void merge_block(const AttnParams& p, int blk, int nsplit, int
                              make_float4(x.a.x * inv, x.a.y * inv, x.a.z * inv, x.a.w * inv));
         }
     }
+}
+
+// With a separate merge launch, a split that has no keys for its block marks the block's partial
+// slots empty (m = -inf), and a block with a single split still writes a partial: the merge
+// kernel then folds every split slot of the grid without resolving the group's window.
+template <int QB>
+__device__ inline void mark_split_empty(const AttnParams& p, int blk, int split) {
+    if (p.merge_kernel && threadIdx.x < QB)
+        p.pm[((size_t)blk * p.nsplit_grid + split) * QB + threadIdx.x] = -INFINITY;
 }
 
 // After every split of a query block has written its partial, the last one to arrive merges

@@ -33,22 +33,44 @@ struct DecShape {
     static_assert(PASSES * F4 == 4, "four float4 of K and of V per lane per tile");
 };
 
-// Sum over the TPK lanes of a group, result in every lane of the group.
+// Given per-row sums (every lane of a 16-lane row holds its row's sum), the sum over the
+// TPK = 32 or 64 lanes of the group, in every lane of the group.
 template <int TPK>
-__device__ inline float lane_group_sum(float v) {
-    if constexpr (TPK <= 16) {
-        return group_sum<TPK>(v);
+__device__ inline float lane_group_sum_above16(float v) {
+    static_assert(TPK == 32 || TPK == 64, "groups above 16 lanes are 32 or 64 wide");
+    v += dpp<kDppBcast15, 0xA>(v, 0.0f);   // rows 1 and 3 now hold row pairs
+    if constexpr (TPK == 32) {
+        const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+        const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+        return (threadIdx.x & 32) ? hi : lo;
     } else {
-        v = group_sum<16>(v);
-        v += dpp<kDppBcast15, 0xA>(v, 0.0f);   // rows 1 and 3 now hold row pairs
-        if constexpr (TPK == 32) {
-            const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
-            const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-            return (threadIdx.x & 32) ? hi : lo;
-        } else {
-            v += dpp<kDppBcast31, 0xC>(v, 0.0f);
-            return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-        }
+        v += dpp<kDppBcast31, 0xC>(v, 0.0f);
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+    }
+}
+
+// Sum over the TPK lanes of a group of each of N values, result in every lane of the group.
+// The DPP steps of the N values are interleaved level by level, so that no step waits on the
+// one just before it.
+template <int TPK, int N>
+__device__ inline void lane_group_sum_n(float* v) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp<kDppXor1>(v[i], 0.0f);
+    if constexpr (TPK >= 4) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] += dpp<kDppXor2>(v[i], 0.0f);
+    }
+    if constexpr (TPK >= 8) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] += dpp<kDppHalfMirror>(v[i], 0.0f);
+    }
+    if constexpr (TPK >= 16) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] += dpp<kDppMirror>(v[i], 0.0f);
+    }
+    if constexpr (TPK > 16) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = lane_group_sum_above16<TPK>(v[i]);
     }
 }
 
@@ -93,31 +115,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dec_kernel(const AttnParams 
     const int ss = (int)p.ring_ss, crs = (int)p.chunk_rs;
 
     vf4 kA[PASSES][F4], vA[PASSES][F4], kB[PASSES][F4], vB[PASSES][F4];
+    // Every load reads a live row: a padding key (past the sinks, or past the block's stream
+    // range) loads sink 0 or the block's last stream entry, and a column past d loads the key's
+    // first columns. Its score is masked to -inf, so its weight is exactly 0 and 0 times finite
+    // data adds nothing: no select on K, V or the accumulators is needed.
     auto load_tile = [&](vf4 (&kr)[PASSES][F4], vf4 (&vr)[PASSES][F4], int t) {
         if (t < nst) {
 #pragma unroll
             for (int ps = 0; ps < PASSES; ++ps) {
                 const int si = t * TK + ps * KPP + gi;
-                const bool valid = si < p.ns;
-                const int row = valid ? si * p.d : 0;
+                const int row = si < p.ns ? si * p.d : 0;
 #pragma unroll
                 for (int f = 0; f < F4; ++f) {
                     const int c = sl + TPK * f;
-                    const int off = (valid && c < d4) ? row + 4 * c : 0;
-                    kr[ps][f] = *reinterpret_cast<gvf4p>((valid ? sk : rk) + 4ull * (unsigned)off);
-                    vr[ps][f] = *reinterpret_cast<gvf4p>((valid ? sv : rv) + 4ull * (unsigned)off);
+                    const int off = c < d4 ? row + 4 * c : row;
+                    kr[ps][f] = *reinterpret_cast<gvf4p>(sk + 4ull * (unsigned)off);
+                    vr[ps][f] = *reinterpret_cast<gvf4p>(sv + 4ull * (unsigned)off);
                 }
             }
         } else {
             const int xt = xlo + (t - nst) * TK + gi;
 #pragma unroll
             for (int ps = 0; ps < PASSES; ++ps) {
-                const int x = xt + ps * KPP;
-                const bool valid = x < xhi;
-                const bool in_ring = x < gw.xsplit || !valid;
+                const int x = min(xt + ps * KPP, xhi - 1);
+                const bool in_ring = x < gw.xsplit;
                 int slot = gw.base + x;
                 slot = slot >= gw.mod ? slot - gw.mod : slot;
-                const int row = !valid ? 0 : (in_ring ? slot * ss : (x - gw.xsplit) * crs);
+                const int row = in_ring ? slot * ss : (x - gw.xsplit) * crs;
 #pragma unroll
                 for (int f = 0; f < F4; ++f) {
                     const int c = sl + TPK * f;
@@ -163,32 +187,48 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dec_kernel(const AttnParams 
 
     // ---- one tile: scores, online softmax of this lane group, value update
     auto step = [&](vf4 (&kr)[PASSES][F4], vf4 (&vr)[PASSES][F4], int t) {
-        float sc[PASSES][NQ];
+        // partial dot products over this lane's columns (q is zero past d), then summed over
+        // the lane group
+        float sc[PASSES * NQ];
 #pragma unroll
-        for (int ps = 0; ps < PASSES; ++ps) {
-            const int k = ps * KPP + gi;
-            bool colok[F4];
-#pragma unroll
-            for (int f = 0; f < F4; ++f) colok[f] = sl + TPK * f < d4;
+        for (int ps = 0; ps < PASSES; ++ps)
 #pragma unroll
             for (int j = 0; j < NQ; ++j) {
                 float s = 0.0f;
 #pragma unroll
                 for (int f = 0; f < F4; ++f) {
-                    const vf4 kv = colok[f] ? kr[ps][f] : vf4{0.f, 0.f, 0.f, 0.f};
-                    const vf4 pr = kv * qr[j][f];
-                    s += (pr.x + pr.y) + (pr.z + pr.w);
+                    float h = kr[ps][f].x * qr[j][f].x;
+                    h = __builtin_fmaf(kr[ps][f].y, qr[j][f].y, h);
+                    h = __builtin_fmaf(kr[ps][f].z, qr[j][f].z, h);
+                    h = __builtin_fmaf(kr[ps][f].w, qr[j][f].w, h);
+                    s = f == 0 ? h : s + h;
                 }
-                s = lane_group_sum<TPK>(s);
-                const bool vis = key_visible<TK>(p.ns, xlo, nst, t, k, qlo[j], qhi[j], j < nq);
-                sc[ps][j] = vis ? s : -INFINITY;
+                sc[ps * NQ + j] = s;
+            }
+        constexpr int kSumMax = NQ >= 8 ? 1 : 8;   // eight queries hold too many registers already
+        constexpr int kSumBlock = PASSES * NQ < kSumMax ? PASSES * NQ : kSumMax;
+#pragma unroll
+        for (int b = 0; b < PASSES * NQ; b += kSumBlock) lane_group_sum_n<TPK, kSumBlock>(sc + b);
+        // Visibility, branch free: a stream key at entry x is visible to a query whose window
+        // is [lo, hi) (padding queries have empty windows); a real sink to every real query.
+        const int sink_tile = t < nst;   // uniform over the block
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps) {
+            const int k = ps * KPP + gi;
+            const int x = xlo + (t - nst) * TK + k;
+            const int sink_real = sink_tile & (t * TK + k < p.ns);
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                const int in_win = (x >= qlo[j]) & (x < qhi[j]) & (sink_tile ^ 1);
+                const int vis = in_win | (sink_real & (j < nq));
+                sc[ps * NQ + j] = vis ? sc[ps * NQ + j] : -INFINITY;
             }
         }
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
-            float tmax = sc[0][j];
+            float tmax = sc[j];
 #pragma unroll
-            for (int ps = 1; ps < PASSES; ++ps) tmax = fmaxf(tmax, sc[ps][j]);
+            for (int ps = 1; ps < PASSES; ++ps) tmax = fmaxf(tmax, sc[ps * NQ + j]);
             const float m_new = fmaxf(mrun[j], tmax);
             const float mu = safe_max(m_new);
             const float corr = __builtin_amdgcn_exp2f(mrun[j] - mu);
@@ -198,13 +238,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dec_kernel(const AttnParams 
             for (int f = 0; f < F4; ++f) acc[j][f] *= corr;
 #pragma unroll
             for (int ps = 0; ps < PASSES; ++ps) {
-                const float pv = __builtin_amdgcn_exp2f(sc[ps][j] - mu);
+                const float pv = __builtin_amdgcn_exp2f(sc[ps * NQ + j] - mu);
                 lsum += pv;
 #pragma unroll
                 for (int f = 0; f < F4; ++f) {
-                    // a padding key has score -inf, weight 0; select, never multiply, its value
-                    const vf4 vv = pv != 0.0f ? vr[ps][f] : vf4{0.f, 0.f, 0.f, 0.f};
-                    acc[j][f] += pv * vv;
+                    acc[j][f].x = __builtin_fmaf(pv, vr[ps][f].x, acc[j][f].x);
+                    acc[j][f].y = __builtin_fmaf(pv, vr[ps][f].y, acc[j][f].y);
+                    acc[j][f].z = __builtin_fmaf(pv, vr[ps][f].z, acc[j][f].z);
+                    acc[j][f].w = __builtin_fmaf(pv, vr[ps][f].w, acc[j][f].w);
                 }
             }
             lrun[j] = lrun[j] * corr + lsum;

@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 F32_PEAK_TFLOPS = 157.3
 METRIC = "KV GB/s and rows/s for windowed GQA attention; % of HBM peak"
-KERNEL_NAMES = {1: "attn_dec_kernel", 2: "attn_mfma_kernel", 3: "attn_valu_kernel"}
+KERNEL_NAMES = {1: "attn_dec_kernel", 2: "attn_mfma_kernel", 3: "attn_valu_kernel",
+                4: "attn_mfma16_kernel"}
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_dec_kernel_decode_counters.json")
 CALIBRATION_COPY_BYTES = 64 << 20
 

@@ -130,10 +130,11 @@ int attn_workspace_init(void* workspace, size_t bytes, void* stream);
 int attn_window_check_meta(const uint32_t* host_meta, int ng, int w);
 
 /* Diagnostics: how attn_window_chunk would run these sizes. kernel = 1 (register-resident
- * split-K kernel, up to 8 query vectors per block), 2 (f32 matrix-core kernel) or 3 (LDS-staged
- * vector-ALU split-K kernel, 16 per block); query_block = query vectors per workgroup; splits =
- * key splits reserved per query block; keys_per_split = keys each split covers at most.
- * Output pointers may be NULL. Returns 0 or WINATTN_EINVAL. */
+ * split-K kernel, up to 8 query vectors per block), 2 (f32 matrix-core kernel on 32x32 tiles,
+ * 128 per block), 3 (LDS-staged vector-ALU split-K kernel, 16 per block) or 4 (f32 matrix-core
+ * kernel on 16x16 tiles, 64 per block, used for d > 128); query_block = query vectors per
+ * workgroup; splits = key splits reserved per query block; keys_per_split = keys each split
+ * covers at most. Output pointers may be NULL. Returns 0 or WINATTN_EINVAL. */
 int attn_window_chunk_plan(int rows, int ng, int hpg, int d, int w, int ns, int* kernel,
                            int* query_block, int* splits, int* keys_per_split);
 
@@ -142,6 +143,11 @@ int attn_window_chunk_plan(int rows, int ng, int hpg, int d, int w, int ns, int*
  * A[i][0] = i, A[i][1] = 1, B[0][j] = 1, B[1][j] = 64 j, so element (i, j) holds i + 64 j.
  * out: device [64][16] floats; out[lane*16 + r] = accumulator r of lane `lane`. */
 int attn_mfma_layout_probe(float* out, void* stream);
+
+/* The same self-test for the 16x16x4 f32 product of kernel 4: A[i][0] = i, A[i][1..3] = 1,
+ * B[0][j] = 1, B[1][j] = 64 j, B[2][j] = B[3][j] = 0, so element (i, j) holds i + 64 j.
+ * out: device [64][4] floats; out[lane*4 + r] = accumulator r of lane `lane`. */
+int attn_mfma16_layout_probe(float* out, void* stream);
 
 /* Tuning knobs for tests and benchmarks (process-wide, not thread-safe; 0 = automatic).
  * They change the launch plan and therefore the workspace size: query the size after setting

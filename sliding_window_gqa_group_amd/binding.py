@@ -58,6 +58,8 @@ def load(path: str = LIB_PATH):
     lib.attn_window_chunk_plan.restype = _i
     lib.attn_mfma_layout_probe.argtypes = [_vp, _vp]
     lib.attn_mfma_layout_probe.restype = _i
+    lib.attn_mfma16_layout_probe.argtypes = [_vp, _vp]
+    lib.attn_mfma16_layout_probe.restype = _i
     lib.attn_tuning_set.argtypes = [_i, _i]
     lib.attn_tuning_set.restype = _i
     lib.attn_strerror.argtypes = [_i]
@@ -215,6 +217,15 @@ def mfma_layout_probe(device="cuda", stream=None):
     rc = load().attn_mfma_layout_probe(out.data_ptr(), _stream_ptr(stream, out.device))
     if rc != OK:
         raise WinattnError("attn_mfma_layout_probe", rc)
+    return out
+
+
+def mfma16_layout_probe(device="cuda", stream=None):
+    """[64][4] accumulator map of one 16x16x4 f32 matrix-core product (see the header)."""
+    out = torch.full((64, 4), -1.0, dtype=torch.float32, device=device)
+    rc = load().attn_mfma16_layout_probe(out.data_ptr(), _stream_ptr(stream, out.device))
+    if rc != OK:
+        raise WinattnError("attn_mfma16_layout_probe", rc)
     return out
 
 

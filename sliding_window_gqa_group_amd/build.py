@@ -10,7 +10,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libwinattn.so")
-SOURCES = ["api.hip", "attn_dec.hip", "attn_valu.hip", "attn_mfma.hip", "gated_prep.hip"]
+SOURCES = ["api.hip", "attn_dec.hip", "attn_valu.hip", "attn_mfma.hip", "attn_mfma16.hip",
+           "gated_prep.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

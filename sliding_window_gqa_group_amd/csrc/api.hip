@@ -14,7 +14,7 @@ namespace winattn {
 namespace {
 
 // Tuning knobs (attn_tuning_set); 0 = automatic.
-int g_force_kernel = 0;     // 1 register kernel, 2 MFMA, 3 LDS vector kernel
+int g_force_kernel = 0;     // 1 register, 2 MFMA 32x32, 3 LDS vector, 4 MFMA 16x16 kernel
 int g_tiles_per_split = 0;
 int g_target_blocks = 0;
 int g_merge_kernel = -1;    // -1 automatic, 0 merge in the last split, 1 separate merge launch
@@ -27,7 +27,7 @@ constexpr int kValuMaxQ = 16;
 constexpr size_t kTicketBytes = 64 * 1024;
 constexpr long long kMaxTickets = kTicketBytes / sizeof(unsigned int);
 
-enum Kind { kKindDec = 1, kKindMfma = 2, kKindValu = 3 };
+enum Kind { kKindDec = 1, kKindMfma = 2, kKindValu = 3, kKindMfma16 = 4 };
 
 struct Plan {
     int kind;
@@ -54,12 +54,20 @@ Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_f
     Plan pl{};
     const long long nq_tot = (long long)rows * hpg;
     pl.dpad = pad_d(d);
-    pl.kind = nq_tot <= 8 ? kKindDec : (nq_tot <= kValuMaxQ ? kKindValu : kKindMfma);
-    if (g_force_kernel >= 1 && g_force_kernel <= 3) pl.kind = g_force_kernel;
-    pl.mfma = pl.kind == kKindMfma;
+    // Matrix cores for more than 16 query vectors per group: 32x32 tiles with 32 queries per
+    // wave, or 16x16 tiles with 16 per wave where the 32-wide tiles would not fit in registers
+    // (d = 256).
+    pl.kind = nq_tot <= 8 ? kKindDec
+                          : (nq_tot <= kValuMaxQ ? kKindValu
+                                                 : (pl.dpad == 256 ? kKindMfma16 : kKindMfma));
+    if (g_force_kernel >= 1 && g_force_kernel <= 4) pl.kind = g_force_kernel;
+    pl.mfma = pl.kind == kKindMfma || pl.kind == kKindMfma16;
     if (pl.kind == kKindMfma) {
         pl.qb = mfma_query_block();
         pl.tk = mfma_tile_keys();
+    } else if (pl.kind == kKindMfma16) {
+        pl.qb = mfma16_query_block();
+        pl.tk = mfma16_tile_keys();
     } else if (pl.kind == kKindDec) {
         pl.qb = nq_tot <= 4 ? 4 : 8;
         pl.tk = dec_tile_keys(pl.dpad);
@@ -75,16 +83,18 @@ Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_f
     const int max_tiles = cdiv(keys_max, pl.tk);
     const long long blocks = (long long)pl.nqblocks * ng;
     // Workgroups the split count aims for: the register kernel runs two per CU, the LDS
-    // vector kernel one, the matrix-core kernel up to two (with two rounds to balance).
+    // vector kernel one, the 32x32 matrix-core kernel up to two (with two rounds to balance),
+    // the 16x16 one a single round.
     const int target = g_target_blocks > 0
                            ? g_target_blocks
-                           : (pl.kind == kKindMfma ? 1024 : (pl.kind == kKindDec ? 512 : 256));
+                           : (pl.kind == kKindMfma ? 1024
+                                                   : (pl.kind == kKindDec ? 512 : 256));
     int s_target = cdiv(target, blocks);
     if (s_target < 1) s_target = 1;
     if (s_target > max_tiles) s_target = max_tiles;
     int tps = cdiv(max_tiles, s_target);
     // A matrix-core split should amortise its partial (qb x d floats) over a few tiles.
-    const int tps_min = pl.mfma ? 4 : 1;
+    const int tps_min = pl.kind == kKindMfma ? 4 : (pl.kind == kKindMfma16 ? 2 : 1);
     if (tps < tps_min) tps = tps_min;
     // Long windows: bound a split's work so the blocks of unequal groups balance.
     const int tps_cap = pl.mfma ? 128 : 64;
@@ -173,6 +183,8 @@ int launch_attention(const Plan& pl, AttnParams& p, bool gated, char* ws, hipStr
     const dim3 grid(pl.nsplit, pl.nqblocks, p.ng);
     if (pl.kind == kKindMfma)
         err = launch_mfma(p, gated, pl.dpad, stream);
+    else if (pl.kind == kKindMfma16)
+        err = launch_mfma16(p, gated, pl.dpad, stream);
     else if (pl.kind == kKindDec)
         err = launch_dec(p, gated, pl.dpad, pl.qb, grid, stream);
     else
@@ -355,11 +367,18 @@ int attn_mfma_layout_probe(float* out, void* stream) {
                                                                                   : WINATTN_ELAUNCH;
 }
 
+int attn_mfma16_layout_probe(float* out, void* stream) {
+    if (!out) return WINATTN_EINVAL;
+    return launch_mfma16_probe(out, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? WINATTN_OK
+               : WINATTN_ELAUNCH;
+}
+
 int attn_tuning_set(int knob, int value) {
     if (value < 0) return WINATTN_EINVAL;
     switch (knob) {
         case WINATTN_TUNE_FORCE_KERNEL:
-            if (value > 3) return WINATTN_EINVAL;
+            if (value > 4) return WINATTN_EINVAL;
             g_force_kernel = value;
             return WINATTN_OK;
         case WINATTN_TUNE_TILES_PER_SPLIT:

@@ -353,6 +353,7 @@ static hipError_t launch_merge_g(const AttnParams& p, int qb, int dpad, hipStrea
     WINATTN_MERGE_CASE(4, 64) WINATTN_MERGE_CASE(4, 128) WINATTN_MERGE_CASE(4, 256)
     WINATTN_MERGE_CASE(8, 64) WINATTN_MERGE_CASE(8, 128) WINATTN_MERGE_CASE(8, 256)
     WINATTN_MERGE_CASE(16, 64) WINATTN_MERGE_CASE(16, 128) WINATTN_MERGE_CASE(16, 256)
+    WINATTN_MERGE_CASE(64, 64) WINATTN_MERGE_CASE(64, 128) WINATTN_MERGE_CASE(64, 256)
     WINATTN_MERGE_CASE(128, 64) WINATTN_MERGE_CASE(128, 128) WINATTN_MERGE_CASE(128, 256)
 #undef WINATTN_MERGE_CASE
     return hipErrorInvalidValue;

@@ -30,6 +30,13 @@ int mfma_query_block();
 int mfma_tile_keys();
 hipError_t launch_mfma_probe(float* out, hipStream_t stream);
 
+// Split-K MFMA kernel on 16x16x4 tiles (16 queries per wave) for d = 256 and short chunks;
+// same grid and work order as launch_mfma.
+hipError_t launch_mfma16(const AttnParams& p, bool gated, int dpad, hipStream_t stream);
+int mfma16_query_block();
+int mfma16_tile_keys();
+hipError_t launch_mfma16_probe(float* out, hipStream_t stream);
+
 struct PrepParams {
     const float* yq;
     const float* yk;

@@ -103,6 +103,9 @@ def test_plans_of_the_named_workloads(lib):
     assert B.chunk_plan(512, 8, 4, 128, 4096, 4)[0] == 2        # prefill: matrix cores
     k, qb, splits, kps = B.chunk_plan(2048, 8, 8, 128, 32768, 4)
     assert k == 2 and splits * kps >= 4 + 32768 + 16
+    # wide heads (the gated shape: 64 rows, 4 query heads per KV head, d = 256)
+    k, qb, splits, kps = B.chunk_plan(64, 4, 4, 256, 1024, 0)
+    assert (k, qb) == (4, 64)
 
 
 def test_tuning_knobs_change_the_plan(lib):
@@ -116,11 +119,16 @@ def test_tuning_knobs_change_the_plan(lib):
         B.tuning_set(B.TUNE_FORCE_KERNEL, 3)
         k, qb, splits, kps = B.chunk_plan(512, 8, 4, 128, 4096, 4)
         assert k == 3 and qb == 16 and kps == 64
+        B.tuning_set(B.TUNE_FORCE_KERNEL, 4)
+        k, qb, splits, kps = B.chunk_plan(512, 8, 4, 128, 4096, 4)
+        assert k == 4 and qb == 64 and kps == 32
     finally:
         B.tuning_set(B.TUNE_FORCE_KERNEL, 0)
         B.tuning_set(B.TUNE_TILES_PER_SPLIT, 0)
     with pytest.raises(B.WinattnError):
         B.tuning_set(99, 1)
+    with pytest.raises(B.WinattnError):
+        B.tuning_set(B.TUNE_FORCE_KERNEL, 5)
 
 
 def test_check_meta(lib):

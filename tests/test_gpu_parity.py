@@ -81,6 +81,16 @@ def test_mfma_layout_probe():
             assert out[lane, r] == i + 64 * j, (lane, r, out[lane, r])
 
 
+def test_mfma16_layout_probe():
+    _case("mfma16 layout probe")
+    out = B.mfma16_layout_probe(DEV).cpu().numpy()
+    for lane in range(64):
+        for r in range(4):
+            i = 4 * (lane // 16) + r
+            j = lane % 16
+            assert out[lane, r] == i + 64 * j, (lane, r, out[lane, r])
+
+
 # ── the named workloads ──────────────────────────────────────────────────────────────────────
 
 def test_tiny():
@@ -179,6 +189,9 @@ VARIANTS = {
     "mfma_merge_launch": {B.TUNE_FORCE_KERNEL: 2, B.TUNE_TILES_PER_SPLIT: 1,
                           B.TUNE_MERGE_KERNEL: 2},
     "mfma_in_kernel_merge_other_order": {B.TUNE_FORCE_KERNEL: 2, B.TUNE_TILES_PER_SPLIT: 2,
+                                         B.TUNE_MERGE_KERNEL: 1, B.TUNE_XCD_MAP: 2},
+    "mfma16_many_splits": {B.TUNE_FORCE_KERNEL: 4, B.TUNE_TILES_PER_SPLIT: 1},
+    "mfma16_one_split_in_kernel_merge": {B.TUNE_FORCE_KERNEL: 4, B.TUNE_TILES_PER_SPLIT: 3,
                                          B.TUNE_MERGE_KERNEL: 1, B.TUNE_XCD_MAP: 2},
 }
 

@@ -310,9 +310,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dec_kernel(const AttnParams 
     }
 }
 
-// Separate merge launch: one workgroup per (query block, group, 32-column chunk), so that the
-// partials are read by many CUs at once rather than by one per block.
-constexpr int kMergeCols = 32;
+// Separate merge launch: one workgroup per (query block, group, column chunk), so that the
+// partials are read by many CUs at once rather than by one per block. The chunk is 32 columns
+// (128 contiguous bytes of a partial row), except for 64-query blocks, where 16 columns give
+// every thread exactly one (query, column) item (measured faster; for 128-query blocks the
+// shorter 32-byte runs cost more than the extra workgroups gain).
+template <int QB>
+constexpr int merge_cols() { return QB == 64 ? 16 : 32; }
 
 template <int QB, int D, bool GATED>
 __global__ __launch_bounds__(kThreads) void split_merge_kernel(const AttnParams p) {
@@ -321,8 +325,9 @@ __global__ __launch_bounds__(kThreads) void split_merge_kernel(const AttnParams 
     const int q0 = qb * QB;
     const int nq = min(QB, p.rows * p.hpg - q0);
     // Every split slot of the block holds a partial or an empty mark (see mark_split_empty).
-    merge_block<QB, D, GATED, kMergeCols>(p, g * p.nqblocks + qb, p.nsplit_grid, q0, nq, g,
-                                          scratch, (int)blockIdx.z * (kMergeCols / 4));
+    constexpr int MC = merge_cols<QB>();
+    merge_block<QB, D, GATED, MC>(p, g * p.nqblocks + qb, p.nsplit_grid, q0, nq, g, scratch,
+                                  (int)blockIdx.z * (MC / 4));
 }
 
 template <int D, int NQ, bool GATED>
@@ -344,11 +349,11 @@ static hipError_t launch_dec_g(const AttnParams& p, int dpad, int nq, dim3 grid,
 
 template <bool GATED>
 static hipError_t launch_merge_g(const AttnParams& p, int qb, int dpad, hipStream_t s) {
-    const dim3 grid(p.nqblocks, p.ng, dpad / kMergeCols);
-#define WINATTN_MERGE_CASE(QQ, DD)                                                                  \
-    if (qb == QQ && dpad == DD) {                                                                   \
-        hipLaunchKernelGGL((split_merge_kernel<QQ, DD, GATED>), grid, dim3(kThreads), 0, s, p);     \
-        return hipGetLastError();                                                                   \
+#define WINATTN_MERGE_CASE(QQ, DD)                                                               \
+    if (qb == QQ && dpad == DD) {                                                                \
+        const dim3 grid(p.nqblocks, p.ng, DD / merge_cols<QQ>());                                \
+        hipLaunchKernelGGL((split_merge_kernel<QQ, DD, GATED>), grid, dim3(kThreads), 0, s, p);  \
+        return hipGetLastError();                                                                \
     }
     WINATTN_MERGE_CASE(4, 64) WINATTN_MERGE_CASE(4, 128) WINATTN_MERGE_CASE(4, 256)
     WINATTN_MERGE_CASE(8, 64) WINATTN_MERGE_CASE(8, 128) WINATTN_MERGE_CASE(8, 256)

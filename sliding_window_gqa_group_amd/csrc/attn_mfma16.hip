@@ -78,17 +78,18 @@ __device__ inline DirectSrc direct_src(const AttnParams& p, const KVBases& b, co
     return s;
 }
 
-// Wave w loads rows w, w + 4, ... of key tile t straight into the LDS tile (kb, vb), one
+// Wave w of NW loads rows w, w + NW, ... of key tile t straight into the LDS tile (kb, vb), one
 // 64-lane row per instruction. Every row read is a live one (a padding key reads sink 0 or the
 // block's last stream entry; lanes past d read the row's first columns), so no LDS slot holds
 // non-finite padding: a masked key gets weight 0 and 0 times finite data adds nothing.
-template <int TK, int KST, int VST>
+template <int TK, int KST, int VST, int NW>
 __device__ __attribute__((always_inline)) inline void issue_direct(const DirectSrc s, int t,
                                                                    float* kb, float* vb) {
+    static_assert(TK % NW == 0, "every wave loads the same number of rows");
     const bool sink_t = t < s.nst;
 #pragma unroll
-    for (int i = 0; i < TK / 4; ++i) {
-        const int key = s.wave + 4 * i;
+    for (int i = 0; i < TK / NW; ++i) {
+        const int key = s.wave + NW * i;
         const int si = t * TK + key;
         const int x = min(s.xlo + (t - s.nst) * TK + key, s.xhi - 1);
         const bool in_ring = x < s.xsplit;
@@ -104,20 +105,32 @@ __device__ __attribute__((always_inline)) inline void issue_direct(const DirectS
     }
 }
 
+// d = 256: a key row is one wave-wide 16-byte-per-lane load, which gfx950 writes straight into
+// LDS (global_load_lds_dwordx4); two LDS tile buffers then replace the register staging of the
+// next tile, and the workgroup runs 8 waves, two per SIMD: waves w and w + 4 own the same 16
+// queries and take one 16-key block of every tile each, so that one wave's softmax overlaps
+// the other's matrix products. Their two online-softmax states are combined at the end.
+// Narrower rows stage through registers with 4 waves.
+template <int D>
+constexpr int m16_key_split() { return D == 256 ? 2 : 1; }
+
 template <int D, bool GATED>
-__global__ __launch_bounds__(kThreads, 1) void attn_mfma16_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kThreads * m16_key_split<D>(), 1) void attn_mfma16_kernel(const AttnParams p) {
     constexpr int TK = kM16TK, QB = kM16QB;
+    constexpr int KS = m16_key_split<D>();    // waves per query set (key blocks split among them)
+    constexpr int NT = kThreads * KS;         // threads per workgroup
+    constexpr int NW = NT / 64;
     constexpr int D4 = D / 4, KST = D + 4, VST = D + 4;
     constexpr int LPT = TK * D4 / kThreads;   // float4 loads per thread per tensor per tile
     constexpr int NDB = D / 16;               // 16-wide d blocks of the output
     constexpr int NKB = TK / 16;              // 16-key blocks of a tile
-    // d = 256: a key row is one wave-wide 16-byte-per-lane load, which gfx950 writes straight
-    // into LDS (global_load_lds_dwordx4); two LDS tile buffers then replace the register
-    // staging of the next tile. Narrower rows stage through registers.
+    constexpr int NKBW = NKB / KS;            // key blocks per wave
     constexpr bool DIRECT = D == 256;
     static_assert(LPT >= 1 && TK * D4 == LPT * kThreads, "tile load must cover the tile");
-    static_assert(TK * KST >= kMergeScratch, "merge scratch reuses the K tile area");
+    static_assert(TK * KST >= 6 * NT, "merge scratch reuses the K tile area");
     static_assert(!DIRECT || D4 == 64, "direct loads move one 64-lane row per instruction");
+    static_assert(KS == 1 || DIRECT, "the key split runs on the direct-load path");
+    static_assert(NKBW * KS == NKB, "key blocks divide among the waves of a query set");
 
     // Each LDS tile buffer is its own array, so that the compiler sees that reading one buffer
     // never conflicts with the direct loads still filling the other, and leaves them in flight.
@@ -139,6 +152,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma16_kernel(const AttnPara
     const int g = item / (p.nqblocks * p.nsplit_grid);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int qw = wave & 3, kh = wave >> 2;   // query set of the wave, its part of the keys
     const int qcol = lane & 15, kr4 = lane >> 4;
     const int nq_tot = p.rows * p.hpg;
     const int q0 = qb * QB;
@@ -158,7 +172,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma16_kernel(const AttnPara
     const int d4 = p.d / 4;
 
     // This lane's query (column qcol of its wave's 16) and its window in key-index space.
-    const int jq = wave * 16 + qcol;
+    const int jq = qw * 16 + qcol;
     const bool qvalid = jq < nq;
     const int qi = q0 + (qvalid ? jq : nq - 1);
     const int row = qi / p.hpg, gh = g * p.hpg + qi % p.hpg;
@@ -175,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma16_kernel(const AttnPara
             kmask = load_tile_regs<TK, D, LPT>(p, kvb, gw, g, xlo, xhi, nst, t, d4, kreg, vreg);
     };
     if constexpr (DIRECT)
-        issue_direct<TK, KST, VST>(dsrc, t_begin, s_k, s_v);
+        issue_direct<TK, KST, VST, NW>(dsrc, t_begin, s_k, s_v);
     else
         load_tile(t_begin);   // first tile in flight while the queries load
 
@@ -209,30 +223,57 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma16_kernel(const AttnPara
         const int khi = sink_tile ? p.ns - t * TK : hi - tx;
         if (!__any(klo < TK && khi > 0 && khi > klo)) return;   // the whole wave misses it
 
-        floatx4 sacc[NKB];
+        // This wave's key blocks of the tile: kb = kh * NKBW + kw. Software-pipelined: the K
+        // fragments of step m + 2 are read while step m's products run (scheduling barriers
+        // keep the compiler from moving the reads back next to their uses).
+        constexpr int NM = D / 16;
+        constexpr int PF = 2;
+        floatx4 sacc[NKBW];
+        float4 kbuf[PF + 1][NKBW];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            sacc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-            const float* kp = tk_ + (16 * kb + qcol) * KST + 4 * kr4;
+        for (int kw = 0; kw < NKBW; ++kw) sacc[kw] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < D / 16; ++m) {
-                const float4 k4 = *reinterpret_cast<const float4*>(kp + 16 * m);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.x, qreg[4 * m + 0], sacc[kb], 0, 0, 0);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.y, qreg[4 * m + 1], sacc[kb], 0, 0, 0);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.z, qreg[4 * m + 2], sacc[kb], 0, 0, 0);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.w, qreg[4 * m + 3], sacc[kb], 0, 0, 0);
+        for (int m = 0; m < PF; ++m)
+#pragma unroll
+            for (int kw = 0; kw < NKBW; ++kw)
+                kbuf[m][kw] = *reinterpret_cast<const float4*>(
+                    tk_ + (16 * (kh * NKBW + kw) + qcol) * KST + 4 * kr4 + 16 * m);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            if (m + PF < NM) {
+#pragma unroll
+                for (int kw = 0; kw < NKBW; ++kw)
+                    kbuf[(m + PF) % (PF + 1)][kw] = *reinterpret_cast<const float4*>(
+                        tk_ + (16 * (kh * NKBW + kw) + qcol) * KST + 4 * kr4 + 16 * (m + PF));
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kw = 0; kw < NKBW; ++kw) {
+                const float4 k4 = kbuf[m % (PF + 1)][kw];
+                sacc[kw] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.x, qreg[4 * m + 0], sacc[kw], 0, 0, 0);
+                sacc[kw] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.y, qreg[4 * m + 1], sacc[kw], 0, 0, 0);
+                sacc[kw] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.z, qreg[4 * m + 2], sacc[kw], 0, 0, 0);
+                sacc[kw] = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.w, qreg[4 * m + 3], sacc[kw], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // The first V^T operands of the value product, read now so that their latency hides
+        // under the softmax (step st = 4 kw + kk covers keys 16 kb + 4 kr4 + kk).
+        constexpr int NST = NKBW * 4;
+        float vbuf[2][NDB];
+#pragma unroll
+        for (int b = 0; b < NDB; ++b)
+            vbuf[0][b] = tv_[(16 * (kh * NKBW) + 4 * kr4) * VST + qcol + 16 * b];
 
         // Mask by select (never multiply: masked slots may hold anything), online softmax.
         float tmax = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int kw = 0; kw < NKBW; ++kw)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int k = 16 * kb + 4 * kr4 + r;
-                sacc[kb][r] = (k >= klo && k < khi) ? sacc[kb][r] : -INFINITY;
-                tmax = fmaxf(tmax, sacc[kb][r]);
+                const int k = 16 * (kh * NKBW + kw) + 4 * kr4 + r;
+                sacc[kw][r] = (k >= klo && k < khi) ? sacc[kw][r] : -INFINITY;
+                tmax = fmaxf(tmax, sacc[kw][r]);
             }
         tmax = half_swap_max(quarter_swap_max(tmax));
         const float m_new = fmaxf(mrun, tmax);
@@ -240,11 +281,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma16_kernel(const AttnPara
         const float corr = __builtin_amdgcn_exp2f(mrun - mu);
         float psum = 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int kw = 0; kw < NKBW; ++kw)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                sacc[kb][r] = __builtin_amdgcn_exp2f(sacc[kb][r] - mu);
-                psum += sacc[kb][r];
+                sacc[kw][r] = __builtin_amdgcn_exp2f(sacc[kw][r] - mu);
+                psum += sacc[kw][r];
             }
         psum = half_swap_sum(quarter_swap_sum(psum));
         lrun = lrun * corr + psum;
@@ -256,14 +297,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma16_kernel(const AttnPara
         mrun = m_new;
 
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int st = 0; st < NST; ++st) {
+            if (st + 1 < NST) {
+                const int kw1 = (st + 1) / 4, kk1 = (st + 1) % 4;
+                const float* vp = tv_ + (16 * (kh * NKBW + kw1) + 4 * kr4 + kk1) * VST + qcol;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const float* vp = tv_ + (16 * kb + 4 * kr4 + kk) * VST + qcol;
-#pragma unroll
-                for (int b = 0; b < NDB; ++b)
-                    oacc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(vp[16 * b], sacc[kb][kk], oacc[b], 0, 0, 0);
+                for (int b = 0; b < NDB; ++b) vbuf[(st + 1) & 1][b] = vp[16 * b];
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int b = 0; b < NDB; ++b)
+                oacc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(vbuf[st & 1][b], sacc[st / 4][st % 4],
+                                                               oacc[b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     if constexpr (DIRECT) {
@@ -272,12 +319,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma16_kernel(const AttnPara
         for (int t = t_begin; t < t_end; t += 2) {
             __builtin_amdgcn_s_waitcnt(kVmcntZero);
             __syncthreads();
-            if (t + 1 < t_end) issue_direct<TK, KST, VST>(dsrc, t + 1, s_k1, s_v1);
+            if (t + 1 < t_end) issue_direct<TK, KST, VST, NW>(dsrc, t + 1, s_k1, s_v1);
             compute_tile(t, s_k, s_v);
             if (t + 1 < t_end) {
                 __builtin_amdgcn_s_waitcnt(kVmcntZero);
                 __syncthreads();
-                if (t + 2 < t_end) issue_direct<TK, KST, VST>(dsrc, t + 2, s_k, s_v);
+                if (t + 2 < t_end) issue_direct<TK, KST, VST, NW>(dsrc, t + 2, s_k, s_v);
                 compute_tile(t + 1, s_k1, s_v1);
             }
         }
@@ -298,10 +345,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma16_kernel(const AttnPara
         }
     }
 
-    // Lane holds, for its query, d = 16b + 4*kr4 + (0..3) in oacc[b].
+    if constexpr (KS == 2) {
+        // Fold the second key half's (m, l, O) into the first: waves 4..7 publish theirs in the
+        // (now free) tile buffers, waves 0..3 combine. O goes as [b][lane of the query set]
+        // float4s, columns 0..127 in s_k and 128..255 in s_v.
+        static_assert(NDB == 16 && 2 * 128 * 4 * 8 <= TK * KST, "combine area");
+        __syncthreads();
+        const int li = qw * 64 + lane;
+        if (kh == 1) {
+#pragma unroll
+            for (int b = 0; b < NDB; ++b) {
+                float* dst = (b < 8 ? s_k : s_v) + ((b & 7) * 256 + li) * 4;
+                *reinterpret_cast<floatx4*>(dst) = oacc[b];
+            }
+            s_k1[li] = mrun;
+            s_k1[256 + li] = lrun;
+        }
+        __syncthreads();
+        if (kh == 0) {
+            const float m1 = s_k1[li], l1 = s_k1[256 + li];
+            const float mt = fmaxf(mrun, m1), mu = safe_max(mt);
+            const float f0 = __builtin_amdgcn_exp2f(mrun - mu), f1 = __builtin_amdgcn_exp2f(m1 - mu);
+            lrun = lrun * f0 + l1 * f1;
+            mrun = mt;
+#pragma unroll
+            for (int b = 0; b < NDB; ++b) {
+                const float* src = (b < 8 ? s_k : s_v) + ((b & 7) * 256 + li) * 4;
+                oacc[b] = oacc[b] * f0 + *reinterpret_cast<const floatx4*>(src) * f1;
+            }
+        }
+    }
+
+    // Lane holds, for its query, d = 16b + 4*kr4 + (0..3) in oacc[b] (waves of key half 0).
     const int blk = g * p.nqblocks + qb;
     if (nsplit == 1 && !p.merge_kernel) {
-        if (qvalid) {
+        if (qvalid && kh == 0) {
             const float inv = 1.0f / fmaxf(lrun, 1e-30f);
 #pragma unroll
             for (int b = 0; b < NDB; ++b) {
@@ -314,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma16_kernel(const AttnPara
         }
         return;
     }
-    if (qvalid) {
+    if (qvalid && kh == 0) {
         const size_t at = ((size_t)blk * p.nsplit_grid + split) * QB + jq;
 #pragma unroll
         for (int b = 0; b < NDB; ++b)
@@ -326,14 +404,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma16_kernel(const AttnPara
         }
     }
     if constexpr (DIRECT) __syncthreads();   // no wave still reads the last tile's buffer
-    merge_if_last<QB, D, GATED>(p, blk, nsplit, q0, nq, g, &s_flag, s_k);
+    merge_if_last<QB, D, GATED, NT>(p, blk, nsplit, q0, nq, g, &s_flag, s_k);
 }
 
 template <int D, bool GATED>
 static hipError_t launch_mfma16_t(const AttnParams& p, hipStream_t stream) {
     const int n_items = p.nsplit_grid * p.nqblocks * p.ng;
     const int blocks = p.xcd_map ? 8 * ((n_items + 7) / 8) : n_items;
-    hipLaunchKernelGGL((attn_mfma16_kernel<D, GATED>), dim3(blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_mfma16_kernel<D, GATED>), dim3(blocks), dim3(kThreads * m16_key_split<D>()),
+                       0, stream, p);
     return hipGetLastError();
 }
 

@@ -361,10 +361,10 @@ __device__ inline void fold_splits(const AttnParams& p, size_t base, int j, int 
     }
 }
 
-// Combines the nsplit partials of query block `blk` into the output (all threads of the block
-// call it), for the DC columns starting at column 4 * c0 (DC = D: every column). `scratch` is
-// free LDS of at least kMergeScratch floats.
-template <int QB, int D, bool GATED, int DC = D>
+// Combines the nsplit partials of query block `blk` into the output (all NT threads of the
+// block call it), for the DC columns starting at column 4 * c0 (DC = D: every column).
+// `scratch` is free LDS of at least 6 * NT floats (kMergeScratch for 256 threads).
+template <int QB, int D, bool GATED, int DC = D, int NT = kThreads>
 __device__ inline void merge_block(const AttnParams& p, int blk, int nsplit, int q0, int nq, int g,
                                    float* scratch, int c0 = 0) {
     static_assert(DC % 4 == 0 && D % DC == 0, "column chunk must divide the padded width");
@@ -372,11 +372,11 @@ __device__ inline void merge_block(const AttnParams& p, int blk, int nsplit, int
     const int d4 = p.d / 4;
     const size_t base = (size_t)blk * p.nsplit_grid * QB;
     constexpr int ITEMS = QB * D4;
-    if constexpr (ITEMS >= kThreads) {
-        constexpr int IPT = ITEMS / kThreads;
+    if constexpr (ITEMS >= NT) {
+        constexpr int IPT = ITEMS / NT;
 #pragma unroll
         for (int k = 0; k < IPT; ++k) {
-            const int item = threadIdx.x + kThreads * k;
+            const int item = threadIdx.x + NT * k;
             const int j = item / D4, c = c0 + item % D4;
             Part x{-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
             fold_splits<QB, D>(p, base, j, c, 0, 1, nsplit, x);
@@ -387,14 +387,14 @@ __device__ inline void merge_block(const AttnParams& p, int blk, int nsplit, int
             }
         }
     } else {
-        constexpr int NSUB = kThreads / ITEMS;
+        constexpr int NSUB = NT / ITEMS;
         const int item = threadIdx.x % ITEMS, sub = threadIdx.x / ITEMS;
         const int j = item / D4, c = c0 + item % D4;
         Part x{-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
         fold_splits<QB, D>(p, base, j, c, sub, NSUB, nsplit, x);
         float* s_m = scratch;
-        float* s_l = scratch + kThreads;
-        float4* s_a = reinterpret_cast<float4*>(scratch + 2 * kThreads);
+        float* s_l = scratch + NT;
+        float4* s_a = reinterpret_cast<float4*>(scratch + 2 * NT);
         s_m[threadIdx.x] = x.m;
         s_l[threadIdx.x] = x.l;
         s_a[threadIdx.x] = x.a;
@@ -422,10 +422,10 @@ __device__ inline void mark_split_empty(const AttnParams& p, int blk, int split)
 
 // After every split of a query block has written its partial, the last one to arrive merges
 // them. When the plan uses a separate merge kernel (p.merge_kernel), this returns at once.
-template <int QB, int D, bool GATED>
+template <int QB, int D, bool GATED, int NT = kThreads>
 __device__ inline void merge_if_last(const AttnParams& p, int blk, int nsplit, int q0, int nq,
                                      int g, int* s_flag, float* scratch) {
-    static_assert(QB <= kThreads && kThreads % QB == 0, "query block must divide the block");
+    static_assert(QB <= NT && NT % QB == 0, "query block must divide the block");
     if (p.merge_kernel) return;
     // Every thread's device-scope partial stores are acknowledged before the counter moves.
     __builtin_amdgcn_s_waitcnt(0);
@@ -442,7 +442,7 @@ __device__ inline void merge_if_last(const AttnParams& p, int blk, int nsplit, i
     // Acquire at agent scope: drop this XCD's L2 copies of lines other XCDs have written, so the
     // plain vector loads below read the partials the other splits stored at device scope.
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    merge_block<QB, D, GATED>(p, blk, nsplit, q0, nq, g, scratch);
+    merge_block<QB, D, GATED, D, NT>(p, blk, nsplit, q0, nq, g, scratch);
 }
 
 // Partial stores: device scope for the in-kernel merge; plain when a separate merge kernel

@@ -58,8 +58,10 @@ def load_library(path: str):
     lib.oracle_window_gated.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
                                         _f32p, _f32p, _f32p, i, i, i, i, i, i, i, f, f]
     lib.oracle_meta_ok.argtypes = [_u32p, i, i]
+    lib.oracle_window_commit.argtypes = [_f32p, _f32p, _u32p, _f32p, _f32p, i, i, i, i]
     for name in ("oracle_window_chunk", "oracle_window_chunk_select",
-                 "oracle_window_chunk_weights", "oracle_window_gated", "oracle_meta_ok"):
+                 "oracle_window_chunk_weights", "oracle_window_gated", "oracle_meta_ok",
+                 "oracle_window_commit"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -159,6 +161,23 @@ def window_gated(inp):
     if rc != 0:
         raise ValueError(f"oracle_window_gated rejected its arguments (rc={rc})")
     return out, rk, rv
+
+
+def window_commit(inp):
+    """(ring_k, ring_v, meta) after pushing the chunk's K/V rows into the rings of a
+    ChunkInputs-like object (inputs untouched)."""
+    lib = _load()
+    rk = np.array(inp.ring_k, dtype=np.float32, copy=True, order="C")
+    rv = np.array(inp.ring_v, dtype=np.float32, copy=True, order="C")
+    meta = np.array(inp.meta, dtype=np.uint32, copy=True, order="C")
+    ck, pck = _f32(inp.chunk_k)
+    cv, pcv = _f32(inp.chunk_v)
+    rc = lib.oracle_window_commit(rk.ctypes.data_as(_f32p), rv.ctypes.data_as(_f32p),
+                                  meta.ctypes.data_as(_u32p), pck, pcv, inp.rows, inp.ng, inp.d,
+                                  inp.w)
+    if rc != 0:
+        raise ValueError(f"oracle_window_commit rejected its arguments (rc={rc})")
+    return rk, rv, meta
 
 
 def meta_ok(meta, ng: int, w: int) -> bool:

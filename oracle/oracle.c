@@ -283,6 +283,47 @@ int oracle_window_gated(const float *yq, const float *yk, const float *yv, const
     return 0;
 }
 
+/*
+ * The state after a chunk (o1c page: `o1c_ring_commit` writes the chunk's K/V rows into the
+ * ring, `o1c_meta` advances length, head and the far count; `o1c_tok_commit` is the one-row
+ * form). Written here as its plain definition: the rows are pushed one at a time, oldest first.
+ * A push lands in slot (head + len) mod wg; while the ring is not full its length grows,
+ * otherwise the oldest entry is evicted: the slot is the head's, the head moves on by one and
+ * the far count (meta field 2) grows by one. Reading for a chunk longer than the window: the
+ * pushes are sequential, so only the chunk's last wg rows remain.
+ * ring_k, ring_v [ng][w][d] and meta [ng][4] are updated in place.
+ */
+int oracle_window_commit(float *ring_k, float *ring_v, uint32_t *meta, const float *chunk_k,
+                         const float *chunk_v, int rows, int ng, int d, int w) {
+    if (!ring_k || !ring_v || !meta || !chunk_k || !chunk_v) return -1;
+    if (rows < 1 || ng < 1 || d < 1 || w < 1) return -1;
+    if (!meta_ok(meta, ng, w)) return -1;
+    for (int g = 0; g < ng; ++g) {
+        const uint32_t wg = group_window(meta, g, w);
+        uint32_t len = meta[4 * g], head = meta[4 * g + 1], far = meta[4 * g + 2];
+        if (len == 0) head %= wg;
+        for (int j = 0; j < rows; ++j) {
+            const uint32_t slot = (uint32_t)(((uint64_t)head + len) % wg);
+            const float *ks = chunk_k + ((size_t)j * ng + g) * d;
+            const float *vs = chunk_v + ((size_t)j * ng + g) * d;
+            float *kd = ring_k + ((size_t)g * w + slot) * d;
+            float *vd = ring_v + ((size_t)g * w + slot) * d;
+            memcpy(kd, ks, sizeof(float) * (size_t)d);
+            memcpy(vd, vs, sizeof(float) * (size_t)d);
+            if (len < wg) {
+                len += 1;
+            } else {
+                head = (head + 1) % wg;
+                far += 1;
+            }
+        }
+        meta[4 * g] = len;
+        meta[4 * g + 1] = head;
+        meta[4 * g + 2] = far;
+    }
+    return 0;
+}
+
 /* Host-side meta validation with the same rules the oracle enforces (1 = valid). */
 int oracle_meta_ok(const uint32_t *meta, int ng, int w) {
     if (!meta || ng < 1 || w < 1) return 0;

@@ -44,6 +44,12 @@ MUTANTS = [
     ("query scale dropped", "for (int e = 0; e < hd; ++e) qd[e] *= (double)q_scale[(size_t)a * hd + e];",
      "for (int e = 0; e < hd; ++e) qd[e] *= 1.0;"),
     ("ring value not written", "vd[e] = vs[e];", "vd[e] = vd[e];"),
+    ("commit slot ignores the head", "const uint32_t slot = (uint32_t)(((uint64_t)head + len) % wg);",
+     "const uint32_t slot = (uint32_t)(((uint64_t)len) % wg);"),
+    ("full ring keeps its head", "head = (head + 1) % wg;", "head = head % wg;"),
+    ("far count not advanced", "far += 1;", "far += 0;"),
+    ("commit takes the wrong group's row", "const float *ks = chunk_k + ((size_t)j * ng + g) * d;",
+     "const float *ks = chunk_k + ((size_t)j * ng + (ng - 1 - g)) * d;"),
 ]
 
 PIN_TESTS = [getattr(pins, n) for n in dir(pins) if n.startswith("test_")]

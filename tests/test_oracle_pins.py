@@ -260,24 +260,93 @@ def _push(inp, g, k, v):
         inp.meta[g] = (wg, (head + 1) % wg, far + 1, ov)
 
 
+def _decode_state(inp):
+    """A one-row call sharing inp's rings (copied), meta (copied) and sinks."""
+    state = gen.make_chunk(1, inp.ng, inp.hpg, inp.d, inp.w, inp.ns, inp.meta.copy(), 0,
+                           scale=inp.scale)
+    state.ring_k = inp.ring_k.copy()
+    state.ring_v = inp.ring_v.copy()
+    state.sink_k, state.sink_v = inp.sink_k, inp.sink_v
+    return state
+
+
+def _row_of(state, inp, i):
+    state.q = inp.q[i:i + 1].copy()
+    state.chunk_k = inp.chunk_k[i:i + 1].copy()
+    state.chunk_v = inp.chunk_v[i:i + 1].copy()
+
+
 def test_chunk_equals_sequence_of_decodes():
+    """Row i of a chunk call == a one-row call after the rows before it were pushed: by the
+    push rule written out here, and by the oracle's commit (row by row, and all rows before i
+    in one commit)."""
     rng = np.random.default_rng(41)
     for _ in range(25):
         inp = _random_case(rng)
         full = oracle.window_chunk(inp)
-        state = gen.make_chunk(1, inp.ng, inp.hpg, inp.d, inp.w, inp.ns, inp.meta.copy(), 0,
-                               scale=inp.scale)
-        state.ring_k = inp.ring_k.copy()
-        state.ring_v = inp.ring_v.copy()
-        state.sink_k, state.sink_v = inp.sink_k, inp.sink_v
+        pushed, committed = _decode_state(inp), _decode_state(inp)
         for i in range(inp.rows):
-            state.q = inp.q[i:i + 1].copy()
-            state.chunk_k = inp.chunk_k[i:i + 1].copy()
-            state.chunk_v = inp.chunk_v[i:i + 1].copy()
-            one = oracle.window_chunk(state)
-            np.testing.assert_allclose(one[0], full[i], rtol=1e-7, atol=1e-9)
+            for state in (pushed, committed):
+                _row_of(state, inp, i)
+                np.testing.assert_allclose(oracle.window_chunk(state)[0], full[i], rtol=1e-7,
+                                           atol=1e-9)
             for g in range(inp.ng):
-                _push(state, g, inp.chunk_k[i, g], inp.chunk_v[i, g])
+                _push(pushed, g, inp.chunk_k[i, g], inp.chunk_v[i, g])
+            committed.ring_k, committed.ring_v, committed.meta = oracle.window_commit(committed)
+            np.testing.assert_array_equal(committed.meta, pushed.meta)
+            np.testing.assert_array_equal(committed.ring_k, pushed.ring_k)
+            # the rows before i + 1 in a single commit reach the same state
+            if i >= 1:
+                many = gen.make_chunk(i + 1, inp.ng, inp.hpg, inp.d, inp.w, inp.ns,
+                                      inp.meta.copy(), 0, scale=inp.scale)
+                many.ring_k, many.ring_v = inp.ring_k.copy(), inp.ring_v.copy()
+                many.chunk_k = inp.chunk_k[:i + 1].copy()
+                many.chunk_v = inp.chunk_v[:i + 1].copy()
+                rk, rv, meta = oracle.window_commit(many)
+                np.testing.assert_array_equal(meta, pushed.meta)
+                np.testing.assert_array_equal(rk, pushed.ring_k)
+                np.testing.assert_array_equal(rv, pushed.ring_v)
+
+
+def _live_entries(ring_g, meta_g, w):
+    """A group's ring entries oldest first, read as the attention reads them: entry x at slot
+    (head + x) mod wg."""
+    ln, head, _, ov = (int(x) for x in meta_g)
+    wg = ov if ov else w
+    return [ring_g[(head + x) % wg] for x in range(ln)]
+
+
+def test_commit_matches_stream_bruteforce():
+    """After a commit the ring, read through the attention's slot rule, holds the last
+    min(wg, len + rows) entries of [old entries, chunk rows] (a bounded deque); length and far
+    count follow; slots that hold no entry and slots past the group window keep their data."""
+    from collections import deque
+    rng = np.random.default_rng(77)
+    for _ in range(300):
+        inp = _random_case(rng, rows=int(rng.integers(1, 14)))
+        rk, rv, meta = oracle.window_commit(inp)
+        for g in range(inp.ng):
+            ln0, head0, far0, ov = (int(x) for x in inp.meta[g])
+            wg = ov if ov else inp.w
+            ks = deque(_live_entries(inp.ring_k[g], inp.meta[g], inp.w), maxlen=wg)
+            vs = deque(_live_entries(inp.ring_v[g], inp.meta[g], inp.w), maxlen=wg)
+            for j in range(inp.rows):
+                ks.append(inp.chunk_k[j, g])
+                vs.append(inp.chunk_v[j, g])
+            assert int(meta[g, 0]) == len(ks) == min(wg, ln0 + inp.rows)
+            assert int(meta[g, 2]) == far0 + max(0, ln0 + inp.rows - wg)
+            assert int(meta[g, 3]) == ov
+            got_k = _live_entries(rk[g], meta[g], inp.w)
+            got_v = _live_entries(rv[g], meta[g], inp.w)
+            for a, b in zip(got_k, ks):
+                np.testing.assert_array_equal(a, b)
+            for a, b in zip(got_v, vs):
+                np.testing.assert_array_equal(a, b)
+            live = {(int(meta[g, 1]) + x) % wg for x in range(int(meta[g, 0]))}
+            for slot in range(inp.w):
+                if slot >= wg or slot not in live:
+                    np.testing.assert_array_equal(rk[g, slot], inp.ring_k[g, slot])
+                    np.testing.assert_array_equal(rv[g, slot], inp.ring_v[g, slot])
 
 
 def test_group_override_equals_group_alone_restrided():

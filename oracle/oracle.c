@@ -301,7 +301,8 @@ int oracle_window_commit(float *ring_k, float *ring_v, uint32_t *meta, const flo
     for (int g = 0; g < ng; ++g) {
         const uint32_t wg = group_window(meta, g, w);
         uint32_t len = meta[4 * g], head = meta[4 * g + 1], far = meta[4 * g + 2];
-        if (len == 0) head %= wg;
+        if (len == 0) head %= wg;   /* an empty ring's head may be any value */
+        int evicted = 0;
         for (int j = 0; j < rows; ++j) {
             const uint32_t slot = (uint32_t)(((uint64_t)head + len) % wg);
             const float *ks = chunk_k + ((size_t)j * ng + g) * d;
@@ -315,11 +316,14 @@ int oracle_window_commit(float *ring_k, float *ring_v, uint32_t *meta, const flo
             } else {
                 head = (head + 1) % wg;
                 far += 1;
+                evicted = 1;
             }
         }
         meta[4 * g] = len;
-        meta[4 * g + 1] = head;
-        meta[4 * g + 2] = far;
+        if (evicted) {   /* as `o1c_meta`: the head and far count change only on eviction */
+            meta[4 * g + 1] = head;
+            meta[4 * g + 2] = far;
+        }
     }
     return 0;
 }

@@ -119,6 +119,25 @@ int attn_window_gated(const float* yq, const float* yk, const float* yv, const f
                       int window, int nh, int nk, int hd, float scale, float eps,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* The state after a chunk, for the next call of a decode loop (o1c page, "A sealed layer's
+ * attention for a chunk of rows, on Metal": `o1c_ring_commit` and `o1c_meta`; one-row form
+ * `o1c_tok_commit`). Pushes the chunk's K/V rows into each group's ring and advances its meta:
+ * row j lands in slot (head + len + j) mod wg (wg = the group's window: meta field 3 if
+ * non-zero, else w); if len + rows <= wg, len grows by rows; otherwise len = wg, head moves on by
+ * ev = len + rows - wg (mod wg) and the far count (field 2) grows by ev. Head and far count are
+ * written only when entries are evicted. A chunk longer than wg leaves only its last wg rows
+ * (pushes are sequential; the earlier rows are not written).
+ *   ring_k, ring_v  device [ng][w][d] f32, updated in place (only the pushed slots)
+ *   meta            device [ng][4] u32, updated in place (same rules as attn_window_chunk)
+ *   chunk_k, chunk_v device [rows][ng][d] f32, the rows just attended (read only)
+ * Sizes as attn_window_chunk (rows, ng, w >= 1; d % 4 == 0, 4 <= d <= 256); 16-byte aligned
+ * float pointers, 4-byte aligned meta. Asynchronous on `stream`, allocates nothing; run it after
+ * the chunk's attention call on the same stream (that call reads the slots this one
+ * overwrites). Invalid device meta is clamped as in attn_window_chunk. Returns 0,
+ * WINATTN_EINVAL (nothing launched) or WINATTN_ELAUNCH. */
+int attn_window_commit(float* ring_k, float* ring_v, uint32_t* meta, const float* chunk_k,
+                       const float* chunk_v, int rows, int ng, int d, int w, void* stream);
+
 /* Workspace bytes attn_window_gated needs for these sizes (0 if the sizes are invalid). */
 size_t attn_window_gated_workspace(int rows, int nh, int nk, int hd, int window);
 

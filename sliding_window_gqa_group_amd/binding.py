@@ -58,6 +58,8 @@ def load(path: str = LIB_PATH):
     lib.attn_window_chunk_plan.restype = _i
     lib.attn_mfma_layout_probe.argtypes = [_vp, _vp]
     lib.attn_mfma_layout_probe.restype = _i
+    lib.attn_window_commit.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]
+    lib.attn_window_commit.restype = _i
     lib.attn_mfma16_layout_probe.argtypes = [_vp, _vp]
     lib.attn_mfma16_layout_probe.restype = _i
     lib.attn_tuning_set.argtypes = [_i, _i]
@@ -218,6 +220,22 @@ def mfma_layout_probe(device="cuda", stream=None):
     if rc != OK:
         raise WinattnError("attn_mfma_layout_probe", rc)
     return out
+
+
+def attn_window_commit(ring_k, ring_v, meta, chunk_k, chunk_v, stream=None) -> None:
+    """Push the chunk's K/V rows [rows][ng][d] into the rings [ng][w][d] and advance meta
+    [ng][4] in place (see attn_window_commit in include/winattn.h)."""
+    ng, w, d = ring_k.shape
+    rows = chunk_k.shape[0]
+    if (tuple(ring_v.shape) != (ng, w, d) or tuple(chunk_k.shape) != (rows, ng, d)
+            or tuple(chunk_v.shape) != (rows, ng, d) or tuple(meta.shape) != (ng, 4)):
+        raise ValueError("attn_window_commit: rings [ng][w][d], chunk [rows][ng][d], meta [ng][4]")
+    rc = load().attn_window_commit(
+        _ptr(ring_k, "ring_k"), _ptr(ring_v, "ring_v"),
+        _ptr(meta, "meta", (torch.int32, torch.uint32)), _ptr(chunk_k, "chunk_k"),
+        _ptr(chunk_v, "chunk_v"), rows, ng, d, w, _stream_ptr(stream, ring_k.device))
+    if rc != OK:
+        raise WinattnError("attn_window_commit", rc)
 
 
 def mfma16_layout_probe(device="cuda", stream=None):

@@ -226,6 +226,18 @@ int attn_window_check_meta(const uint32_t* host_meta, int ng, int w) {
     return WINATTN_OK;
 }
 
+int attn_window_commit(float* ring_k, float* ring_v, uint32_t* meta, const float* chunk_k,
+                       const float* chunk_v, int rows, int ng, int d, int w, void* stream) {
+    if (!chunk_shape_ok(rows, ng, 1, d, w, 0)) return WINATTN_EINVAL;
+    if (!ring_k || !ring_v || !meta || !chunk_k || !chunk_v) return WINATTN_EINVAL;
+    if (!aligned16(ring_k) || !aligned16(ring_v) || !aligned16(chunk_k) || !aligned16(chunk_v) ||
+        ((uintptr_t)meta & 3u) != 0)
+        return WINATTN_EINVAL;
+    const CommitParams p{ring_k, ring_v, meta, chunk_k, chunk_v, rows, ng, d, w};
+    return launch_ring_commit(p, static_cast<hipStream_t>(stream)) == hipSuccess ? WINATTN_OK
+                                                                                 : WINATTN_ELAUNCH;
+}
+
 size_t attn_window_chunk_workspace(int rows, int ng, int hpg, int d, int w, int ns) {
     if (!chunk_shape_ok(rows, ng, hpg, d, w, ns)) return 0;
     return make_plan(rows, ng, hpg, d, w, ns, 0).bytes;

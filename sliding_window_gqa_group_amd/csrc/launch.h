@@ -53,4 +53,15 @@ hipError_t launch_gated_prep(const PrepParams& p, hipStream_t stream);
 
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
 
+struct CommitParams {
+    float* ring_k;          // [ng][w][d]
+    float* ring_v;
+    uint32_t* meta;         // [ng][4], updated in place
+    const float* chunk_k;   // [rows][ng][d]
+    const float* chunk_v;
+    int rows, ng, d, w;
+};
+// Ring commit and meta advance after a chunk; one workgroup per group.
+hipError_t launch_ring_commit(const CommitParams& p, hipStream_t stream);
+
 }  // namespace winattn

@@ -86,6 +86,23 @@ def test_gated_rejects_small_workspace(lib):
     assert _gated(lib, wsb=need - 1) == B.EWORKSPACE
 
 
+def _commit(lib, **kw):
+    a = dict(ring_k=FAKE, ring_v=FAKE, meta=FAKE, chunk_k=FAKE, chunk_v=FAKE, rows=1, ng=1,
+             d=64, w=16, stream=None)
+    a.update(kw)
+    return lib.attn_window_commit(a["ring_k"], a["ring_v"], a["meta"], a["chunk_k"],
+                                  a["chunk_v"], a["rows"], a["ng"], a["d"], a["w"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(rows=0), dict(ng=0), dict(w=0), dict(d=0), dict(d=6), dict(d=260), dict(ring_k=None),
+    dict(meta=None), dict(chunk_v=None), dict(ring_v=FAKE + 4), dict(chunk_k=FAKE + 8),
+    dict(meta=FAKE + 2),
+])
+def test_commit_rejects_invalid_arguments(lib, kw):
+    assert _commit(lib, **kw) == B.EINVAL
+
+
 def test_workspace_queries(lib):
     assert B.chunk_workspace_bytes(0, 1, 1, 64, 16, 0) == 0
     assert B.gated_workspace_bytes(1, 5, 2, 64, 8) == 0

@@ -335,6 +335,59 @@ def test_chunk_equals_sequence_of_decodes_on_gpu():
             pins._push(state, g, inp.chunk_k[i, g], inp.chunk_v[i, g])
 
 
+# ── ring commit + meta advance (the state a decode loop carries) ───────────────────────────
+
+COMMIT_CASES = [
+    # rows, ng, d, w, meta
+    (1, 8, 128, 4096, "full"),
+    (3, 3, 64, 20, "mix"),
+    (25, 2, 128, 16, "mix"),        # chunk longer than the window
+    (7, 4, 36, 9, "partial"),
+    (40, 1, 256, 100, "override"),
+    (1, 2, 4, 1, "full"),            # window of one
+]
+
+
+@pytest.mark.parametrize("shape", COMMIT_CASES, ids=[f"r{c[0]}g{c[1]}d{c[2]}w{c[3]}{c[4]}" for c in COMMIT_CASES])
+def test_commit_matches_oracle(shape):
+    rows, ng, d, w, kind = shape
+    _case(f"commit {shape}")
+    rng = np.random.default_rng(zlib.crc32(repr(shape).encode()))
+    inp = gen.make_chunk(rows, ng, 1, d, w, 0, _rand_meta(rng, ng, w, kind),
+                         seed=int(rng.integers(1 << 30)))
+    inp.meta[:, 2] = rng.integers(0, 1000, size=ng)   # far counts carry through
+    rk, rv, meta = oracle.window_commit(inp)
+    t = gen.to_device(inp, DEV)
+    B.attn_window_commit(t["ring_k"], t["ring_v"], t["meta"], t["chunk_k"], t["chunk_v"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(t["meta"].cpu().numpy().astype(np.uint32), meta)
+    np.testing.assert_array_equal(t["ring_k"].cpu().numpy(), rk)
+    np.testing.assert_array_equal(t["ring_v"].cpu().numpy(), rv)
+
+
+def test_decode_loop_with_commit_on_gpu():
+    """A stateful loop entirely on the GPU: attend one row, commit it, next row. Every row's
+    output equals the oracle's chunk call on the starting state, and the final rings and meta
+    equal the oracle's commit of the whole chunk."""
+    _case("decode loop with commit")
+    inp = gen.make_chunk(20, 3, 4, 128, 12, 2, [(12, 5, 3, 0), (2, 1, 0, 7), (0, 9, 0, 0)], seed=9)
+    ref = oracle.window_chunk(inp)
+    rk, rv, meta = oracle.window_commit(inp)
+    t = gen.to_device(inp, DEV)
+    out = torch.empty((1, inp.nh, inp.d), dtype=torch.float32, device=DEV)
+    for i in range(inp.rows):
+        B.attn_window_chunk(t["ring_k"], t["ring_v"], t["meta"], t["sink_k"], t["sink_v"],
+                            t["q"][i:i + 1], t["chunk_k"][i:i + 1], t["chunk_v"][i:i + 1],
+                            inp.scale, out=out)
+        assert_close(out.cpu().numpy()[0], ref[i], f"decode row {i}")
+        B.attn_window_commit(t["ring_k"], t["ring_v"], t["meta"], t["chunk_k"][i:i + 1],
+                             t["chunk_v"][i:i + 1])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(t["meta"].cpu().numpy().astype(np.uint32), meta)
+    np.testing.assert_array_equal(t["ring_k"].cpu().numpy(), rk)
+    np.testing.assert_array_equal(t["ring_v"].cpu().numpy(), rv)
+
+
 def test_repeated_calls_and_workspace_reuse():
     """Split counters reset themselves: back-to-back calls of different shapes on one workspace."""
     _case("workspace reuse")

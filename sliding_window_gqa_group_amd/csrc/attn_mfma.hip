@@ -136,18 +136,33 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
         const int khi = sink_tile ? p.ns - t * TK : hi - tx;
         if (!__any(klo < TK && khi > 0 && khi > klo)) continue;   // the whole wave misses it
 
+        // Scores, software-pipelined: the K fragment of step c + 2 is read while step c's
+        // products run (scheduling barriers keep the reads from sinking next to their uses).
+        constexpr int NC = D / 8, PF = 2;
         floatx16 sacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
         const float* kr = s_k + qcol * KST + 4 * hb;
+        float4 kbuf[PF + 1];
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) {
-            const float4 k4 = *reinterpret_cast<const float4*>(kr + 8 * c);
+        for (int c = 0; c < PF; ++c) kbuf[c] = *reinterpret_cast<const float4*>(kr + 8 * c);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            if (c + PF < NC)
+                kbuf[(c + PF) % (PF + 1)] = *reinterpret_cast<const float4*>(kr + 8 * (c + PF));
+            __builtin_amdgcn_sched_barrier(0);
+            const float4 k4 = kbuf[c % (PF + 1)];
             sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.x, qreg[4 * c + 0], sacc, 0, 0, 0);
             sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.y, qreg[4 * c + 1], sacc, 0, 0, 0);
             sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.z, qreg[4 * c + 2], sacc, 0, 0, 0);
             sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(k4.w, qreg[4 * c + 3], sacc, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // The first V^T operands, read now so their latency hides under the softmax:
+        // vbuf[r & 1][b] = V[8 (r / 4) + 4 hb + r % 4][32 b + qcol].
+        float vbuf[2][NDB];
+#pragma unroll
+        for (int b = 0; b < NDB; ++b) vbuf[0][b] = s_v[(4 * hb) * VST + qcol + 32 * b];
 
         // Mask by select (never multiply: masked slots may hold anything), online softmax.
         float tmax = -INFINITY;
@@ -181,10 +196,16 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float* vr = s_v + (8 * (r >> 2) + 4 * hb + (r & 3)) * VST + qcol;
+            if (r + 1 < 16) {
+                const float* vr = s_v + (8 * ((r + 1) >> 2) + 4 * hb + ((r + 1) & 3)) * VST + qcol;
+#pragma unroll
+                for (int b = 0; b < NDB; ++b) vbuf[(r + 1) & 1][b] = vr[32 * b];
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int b = 0; b < NDB; ++b)
-                oacc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[32 * b], sacc[r], oacc[b], 0, 0, 0);
+                oacc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(vbuf[r & 1][b], sacc[r], oacc[b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 

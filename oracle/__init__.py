@@ -59,9 +59,14 @@ def load_library(path: str):
                                         _f32p, _f32p, _f32p, i, i, i, i, i, i, i, f, f]
     lib.oracle_meta_ok.argtypes = [_u32p, i, i]
     lib.oracle_window_commit.argtypes = [_f32p, _f32p, _u32p, _f32p, _f32p, i, i, i, i]
+    lib.oracle_window_chunk_far.argtypes = [_f32p, _f32p, _u32p, _f32p, _f32p, _f32p, _f32p,
+                                            _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
+                                            i, i, i, i, i, i, i, f]
+    lib.oracle_window_commit_far.argtypes = [_f32p, _f32p, _u32p, _f32p, _f32p, _f32p, _f32p,
+                                             _f32p, i, i, i, i, i, i, f]
     for name in ("oracle_window_chunk", "oracle_window_chunk_select",
                  "oracle_window_chunk_weights", "oracle_window_gated", "oracle_meta_ok",
-                 "oracle_window_commit"):
+                 "oracle_window_commit", "oracle_window_chunk_far", "oracle_window_commit_far"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -178,6 +183,41 @@ def window_commit(inp):
     if rc != 0:
         raise ValueError(f"oracle_window_commit rejected its arguments (rc={rc})")
     return rk, rv, meta
+
+
+def window_chunk_far(inp, far) -> np.ndarray:
+    """out [rows][nh][d] of a chunk call with the far field `far` (a FarState-like object)."""
+    lib = _load()
+    keep, ptrs = _chunk_ptrs(inp)
+    fk = [_f32(a) for a in (far.k_tilde, far.q_tilde, far.mu, far.mz, far.t_hat)]
+    out = np.zeros((inp.rows, inp.ng * inp.hpg, inp.d), dtype=np.float32)
+    rc = lib.oracle_window_chunk_far(*ptrs, *[p for _, p in fk], out.ctypes.data_as(_f32p),
+                                     inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns, far.m,
+                                     inp.scale)
+    if rc != 0:
+        raise ValueError(f"oracle_window_chunk_far rejected its arguments (rc={rc})")
+    return out
+
+
+def window_commit_far(inp, far):
+    """(ring_k, ring_v, meta, mz, t_hat) after committing the chunk with its far state (inputs
+    untouched)."""
+    lib = _load()
+    rk = np.array(inp.ring_k, dtype=np.float32, copy=True, order="C")
+    rv = np.array(inp.ring_v, dtype=np.float32, copy=True, order="C")
+    meta = np.array(inp.meta, dtype=np.uint32, copy=True, order="C")
+    mz = np.array(far.mz, dtype=np.float32, copy=True, order="C")
+    th = np.array(far.t_hat, dtype=np.float32, copy=True, order="C")
+    ck, pck = _f32(inp.chunk_k)
+    cv, pcv = _f32(inp.chunk_v)
+    qt, pqt = _f32(far.q_tilde)
+    rc = lib.oracle_window_commit_far(rk.ctypes.data_as(_f32p), rv.ctypes.data_as(_f32p),
+                                      meta.ctypes.data_as(_u32p), pck, pcv, pqt,
+                                      mz.ctypes.data_as(_f32p), th.ctypes.data_as(_f32p),
+                                      inp.rows, inp.ng, inp.hpg, inp.d, inp.w, far.m, inp.scale)
+    if rc != 0:
+        raise ValueError(f"oracle_window_commit_far rejected its arguments (rc={rc})")
+    return rk, rv, meta, mz, th
 
 
 def meta_ok(meta, ng: int, w: int) -> bool:

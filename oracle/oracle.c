@@ -328,6 +328,249 @@ int oracle_window_commit(float *ring_k, float *ring_v, uint32_t *meta, const flo
     return 0;
 }
 
+/*
+ * The far field (o1c page: `o1c_far_e`, `o1c_land`, `o1c_far`, `o1c_soft`, `o1c_add`,
+ * `o1c_far_commit`; token path `o1c_tok_far`, `o1c_tok_merge`). Keys that have left a group's
+ * window are summarised per query head gh by m landmarks: landmark b keeps a far max mx_b and
+ * a far mass z_b (mz [gh][2m]: maxima then masses) and a far numerator t_hat_b [d], the sums of
+ * exp(s - mx_b) and exp(s - mx_b) V over the evicted keys, s = scale <q_tilde_b, K> with the
+ * landmark's own query q_tilde [gh][m][d]. A row's query reads them through landmark keys
+ * k_tilde [g][m][d] and a mixing matrix mu [gh][m][m] (row a, column b).
+ *
+ * Evictions inside the chunk: chunk row j >= j0 = wg - len0 pushes out the oldest entry, the
+ * group's logical entry x = j - j0 (ring slot (head0 + x) mod wg while x < len0; reading for a
+ * chunk longer than the window: a later entry x >= len0 is chunk row x - len0).
+ */
+
+/* Evicted entry of chunk row j (j >= j0): its K and V rows. */
+static void evicted_entry(const float *ring_k, const float *ring_v, const float *chunk_k,
+                          const float *chunk_v, uint32_t len0, uint32_t head0, uint32_t wg,
+                          int ng, int d, int w, int g, uint32_t x, const float **k,
+                          const float **v) {
+    if (x < len0) {
+        const size_t slot = (size_t)(head0 + x) % (size_t)wg;
+        *k = ring_k + ((size_t)g * w + slot) * d;
+        *v = ring_v + ((size_t)g * w + slot) * d;
+    } else {
+        size_t row = (size_t)(x - len0);
+        *k = chunk_k + (row * ng + g) * d;
+        *v = chunk_v + (row * ng + g) * d;
+    }
+}
+
+/*
+ * Eviction scores of one landmark (`o1c_far_e`): for the chunk's evicting rows j in [j0, rows),
+ * e[j] = exp(fe_j - mx) with fe_j = scale <q_tilde, K_ev(j)>, mx = max(old max, fe_j), the
+ * rescale r = exp(old max - mx) of the old mass and numerator (1 if the max did not move: an
+ * empty far field starts at -inf), and z[i] = old mass r + sum_{j0 <= j <= i} e[j], the far mass
+ * as of row i. e[j] = 0 for j < j0.
+ */
+static void far_evict(const float *ring_k, const float *ring_v, const float *chunk_k,
+                      const float *chunk_v, uint32_t len0, uint32_t head0, uint32_t wg, int ng,
+                      int d, int w, int g, int rows, const float *qt, double m_old, double mass,
+                      double scale, double *e, double *z, double *mx_out, double *r_out) {
+    const long j0 = (long)wg - (long)len0;
+    double mx = m_old;
+    for (long j = 0; j < rows; ++j) {
+        e[j] = -INFINITY;
+        if (j < j0) continue;
+        const float *k, *v;
+        evicted_entry(ring_k, ring_v, chunk_k, chunk_v, len0, head0, wg, ng, d, w, g,
+                      (uint32_t)(j - j0), &k, &v);
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += (double)qt[c] * (double)k[c];
+        e[j] = scale * dot;
+        if (e[j] > mx) mx = e[j];
+    }
+    const double r = mx == m_old ? 1.0 : exp(m_old - mx);
+    double acc = mass * r;
+    for (long j = 0; j < rows; ++j) {
+        e[j] = j >= j0 ? exp(e[j] - mx) : 0.0;
+        acc += e[j];
+        z[j] = acc;
+    }
+    *mx_out = mx;
+    *r_out = r;
+}
+
+static int far_args_ok(const float *k_tilde, const float *q_tilde, const float *mu,
+                       const float *mz, const float *t_hat, int m) {
+    return k_tilde && q_tilde && mu && mz && t_hat && m >= 1;
+}
+
+/*
+ * Chunk attention with the far field: out [rows][nh][d]. Row i of head gh (`o1c_far`,
+ * `o1c_soft`, `o1c_add`): the near scores over its sinks and window; if the far field is
+ * non-empty as of the row (far_len plus the chunk's evictions up to row i), landmark scores
+ * fl_a = scale <q, k_tilde_a>, f = max fl, weights w_b = sum_a exp(fl_a - f) mu[a][b], the
+ * common max c = max(near max, f + mx_b), gains g_b = w_b exp(f + mx_b - c), far mass
+ * F = sum_b g_b z_b(i); if F < 0 the far part is dropped. Then
+ * out = (sum_near exp(s - c) V + sum_b g_b r_b t_hat_b + sum_{j0<=j<=i} (sum_b g_b e_b(j)) V_ev(j))
+ *       / (sum_near exp(s - c) + F).
+ */
+int oracle_window_chunk_far(const float *ring_k, const float *ring_v, const uint32_t *meta,
+                            const float *sink_k, const float *sink_v, const float *q,
+                            const float *chunk_k, const float *chunk_v, const float *k_tilde,
+                            const float *q_tilde, const float *mu, const float *mz,
+                            const float *t_hat, float *out, int rows, int ng, int hpg, int d,
+                            int w, int ns, int m, float scale) {
+    if (!out || !chunk_args_ok(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v, rows,
+                               ng, hpg, d, w, ns))
+        return -1;
+    if (!far_args_ok(k_tilde, q_tilde, mu, mz, t_hat, m)) return -1;
+    const int nh = ng * hpg;
+    const double sc = (double)scale;
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int g = 0; g < ng; ++g) {
+        for (int h = 0; h < hpg; ++h) {
+            const uint32_t wg = group_window(meta, g, w);
+            const uint32_t len0 = meta[4 * g], head0 = meta[4 * g + 1], far0 = meta[4 * g + 2];
+            const long j0 = (long)wg - (long)len0;
+            const int gh = g * hpg + h;
+            const size_t nmax = (size_t)ns + wg;
+            const float **kp = malloc(sizeof(*kp) * nmax);
+            const float **vp = malloc(sizeof(*vp) * nmax);
+            double *s = malloc(sizeof(double) * nmax);
+            double *acc = malloc(sizeof(double) * (size_t)d);
+            double *qd = malloc(sizeof(double) * (size_t)d);
+            double *e = malloc(sizeof(double) * (size_t)m * rows);
+            double *z = malloc(sizeof(double) * (size_t)m * rows);
+            double *mx = malloc(sizeof(double) * (size_t)m);
+            double *r = malloc(sizeof(double) * (size_t)m);
+            double *fl = malloc(sizeof(double) * (size_t)m);
+            double *wb = malloc(sizeof(double) * (size_t)m);
+            double *gb = malloc(sizeof(double) * (size_t)m);
+            if (!kp || !vp || !s || !acc || !qd || !e || !z || !mx || !r || !fl || !wb || !gb) {
+#pragma omp atomic write
+                bad = 1;
+            } else {
+                for (int b = 0; b < m; ++b)
+                    far_evict(ring_k, ring_v, chunk_k, chunk_v, len0, head0, wg, ng, d, w, g,
+                              rows, q_tilde + ((size_t)gh * m + b) * d,
+                              (double)mz[(size_t)gh * 2 * m + b],
+                              (double)mz[(size_t)gh * 2 * m + m + b], sc, e + (size_t)b * rows,
+                              z + (size_t)b * rows, &mx[b], &r[b]);
+                for (int i = 0; i < rows; ++i) {
+                    const float *qrow = q + ((size_t)i * nh + gh) * d;
+                    for (int c = 0; c < d; ++c) qd[c] = (double)qrow[c];
+                    const int n = key_list(ring_k, ring_v, meta, sink_k, sink_v, chunk_k,
+                                           chunk_v, ng, d, w, ns, g, i, kp, vp);
+                    double cmax = -INFINITY;
+                    for (int j = 0; j < n; ++j) {
+                        double dot = 0.0;
+                        for (int c = 0; c < d; ++c) dot += qd[c] * (double)kp[j][c];
+                        s[j] = sc * dot;
+                        if (s[j] > cmax) cmax = s[j];
+                    }
+                    const long farl = (long)far0 + (i >= j0 ? i - j0 + 1 : 0);
+                    double far_den = 0.0;
+                    int have = 0;
+                    if (farl > 0) {
+                        double f = -INFINITY;
+                        for (int a = 0; a < m; ++a) {
+                            const float *kt = k_tilde + ((size_t)g * m + a) * d;
+                            double dot = 0.0;
+                            for (int c = 0; c < d; ++c) dot += qd[c] * (double)kt[c];
+                            fl[a] = sc * dot;
+                            if (fl[a] > f) f = fl[a];
+                        }
+                        for (int b = 0; b < m; ++b) wb[b] = 0.0;
+                        for (int a = 0; a < m; ++a) {
+                            const double ea = exp(fl[a] - f);
+                            for (int b = 0; b < m; ++b)
+                                wb[b] += ea * (double)mu[((size_t)gh * m + a) * m + b];
+                        }
+                        for (int b = 0; b < m; ++b)
+                            if (f + mx[b] > cmax) cmax = f + mx[b];
+                        for (int b = 0; b < m; ++b) {
+                            gb[b] = wb[b] * exp(f + mx[b] - cmax);
+                            far_den += gb[b] * z[(size_t)b * rows + i];
+                        }
+                        if (far_den >= 0.0) have = 1; else far_den = 0.0;
+                    }
+                    double den = far_den;
+                    for (int c = 0; c < d; ++c) acc[c] = 0.0;
+                    for (int j = 0; j < n; ++j) {
+                        const double p = exp(s[j] - cmax);
+                        den += p;
+                        for (int c = 0; c < d; ++c) acc[c] += p * (double)vp[j][c];
+                    }
+                    if (have) {
+                        for (int b = 0; b < m; ++b) {
+                            const float *th = t_hat + ((size_t)gh * m + b) * d;
+                            for (int c = 0; c < d; ++c) acc[c] += gb[b] * r[b] * (double)th[c];
+                        }
+                        for (long j = j0 < 0 ? 0 : j0; j <= i; ++j) {
+                            double cf = 0.0;
+                            for (int b = 0; b < m; ++b) cf += gb[b] * e[(size_t)b * rows + j];
+                            const float *kk, *vv;
+                            evicted_entry(ring_k, ring_v, chunk_k, chunk_v, len0, head0, wg, ng,
+                                          d, w, g, (uint32_t)(j - j0), &kk, &vv);
+                            for (int c = 0; c < d; ++c) acc[c] += cf * (double)vv[c];
+                        }
+                    }
+                    if (den < 1e-30) den = 1e-30;
+                    float *o = out + ((size_t)i * nh + gh) * d;
+                    for (int c = 0; c < d; ++c) o[c] = (float)(acc[c] / den);
+                }
+            }
+            free(kp); free(vp); free(s); free(acc); free(qd); free(e); free(z); free(mx);
+            free(r); free(fl); free(wb); free(gb);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * The far state after the chunk (`o1c_far_commit`), then the ring commit and meta advance:
+ * for every head gh and landmark b with evictions in the chunk, t_hat_b <- t_hat_b r_b +
+ * sum_{j >= j0} e_b(j) V_ev(j), far max <- mx_b, far mass <- z_b(rows - 1). mz and t_hat are
+ * updated in place; then oracle_window_commit (which also adds the evictions to far_len).
+ */
+int oracle_window_commit_far(float *ring_k, float *ring_v, uint32_t *meta, const float *chunk_k,
+                             const float *chunk_v, const float *q_tilde, float *mz,
+                             float *t_hat, int rows, int ng, int hpg, int d, int w, int m,
+                             float scale) {
+    if (!ring_k || !ring_v || !meta || !chunk_k || !chunk_v || !q_tilde || !mz || !t_hat)
+        return -1;
+    if (rows < 1 || ng < 1 || hpg < 1 || d < 1 || w < 1 || m < 1) return -1;
+    if (!meta_ok(meta, ng, w)) return -1;
+    double *e = malloc(sizeof(double) * (size_t)rows);
+    double *z = malloc(sizeof(double) * (size_t)rows);
+    double *acc = malloc(sizeof(double) * (size_t)d);
+    if (!e || !z || !acc) { free(e); free(z); free(acc); return -1; }
+    for (int g = 0; g < ng; ++g) {
+        const uint32_t wg = group_window(meta, g, w);
+        const uint32_t len0 = meta[4 * g], head0 = meta[4 * g + 1];
+        const long j0 = (long)wg - (long)len0;
+        if (j0 >= rows) continue;   /* nothing evicted */
+        for (int h = 0; h < hpg; ++h) {
+            const int gh = g * hpg + h;
+            for (int b = 0; b < m; ++b) {
+                double mx, r;
+                float *mzb = mz + (size_t)gh * 2 * m;
+                far_evict(ring_k, ring_v, chunk_k, chunk_v, len0, head0, wg, ng, d, w, g, rows,
+                          q_tilde + ((size_t)gh * m + b) * d, (double)mzb[b],
+                          (double)mzb[m + b], (double)scale, e, z, &mx, &r);
+                float *th = t_hat + ((size_t)gh * m + b) * d;
+                for (int c = 0; c < d; ++c) acc[c] = (double)th[c] * r;
+                for (long j = j0 < 0 ? 0 : j0; j < rows; ++j) {
+                    const float *kk, *vv;
+                    evicted_entry(ring_k, ring_v, chunk_k, chunk_v, len0, head0, wg, ng, d, w,
+                                  g, (uint32_t)(j - j0), &kk, &vv);
+                    for (int c = 0; c < d; ++c) acc[c] += e[j] * (double)vv[c];
+                }
+                for (int c = 0; c < d; ++c) th[c] = (float)acc[c];
+                mzb[b] = (float)mx;
+                mzb[m + b] = (float)z[rows - 1];
+            }
+        }
+    }
+    free(e); free(z); free(acc);
+    return oracle_window_commit(ring_k, ring_v, meta, chunk_k, chunk_v, rows, ng, d, w);
+}
+
 /* Host-side meta validation with the same rules the oracle enforces (1 = valid). */
 int oracle_meta_ok(const uint32_t *meta, int ng, int w) {
     if (!meta || ng < 1 || w < 1) return 0;

@@ -185,6 +185,48 @@ CHUNK_CONFIGS = {"tiny": tiny, "decode": decode, "prefill": prefill, "large": la
 GATED_CONFIGS = {"gated": gated}
 
 
+@dataclass
+class FarState:
+    """Synthetic far-field state of a chunk call: m landmarks per query head.
+
+    k_tilde [ng][m][d] landmark keys, q_tilde [nh][m][d] landmark queries, mu [nh][m][m]
+    mixing weights (row a, column b), mz [nh][2m] far maxima then far masses, t_hat [nh][m][d]
+    far numerators. A group whose meta far_len is 0 has an empty far field (maxima -inf, masses
+    and numerators 0)."""
+    m: int
+    k_tilde: np.ndarray
+    q_tilde: np.ndarray
+    mu: np.ndarray
+    mz: np.ndarray
+    t_hat: np.ndarray
+
+
+def make_far(inp: ChunkInputs, m: int, seed: int, mu_kind: str = "positive") -> FarState:
+    """Draw a far state for `inp` (its meta's far_len says which groups have one). Landmark
+    keys and queries are N(0,1); mu is U(0,1) ("positive") or N(0,1) ("signed"); a non-empty
+    field has maxima N(0,1), masses U(0.5, 4) and numerators N(0,1) scaled by the mass."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ng, hpg, d = inp.ng, inp.hpg, inp.d
+    nh = ng * hpg
+    k_tilde = rng.standard_normal((ng, m, d), dtype=np.float32)
+    q_tilde = rng.standard_normal((nh, m, d), dtype=np.float32)
+    if mu_kind == "signed":
+        mu = rng.standard_normal((nh, m, m), dtype=np.float32)
+    else:
+        mu = rng.random((nh, m, m), dtype=np.float32)
+    mz = np.zeros((nh, 2 * m), dtype=np.float32)
+    mz[:, :m] = rng.standard_normal((nh, m), dtype=np.float32)
+    mz[:, m:] = rng.uniform(0.5, 4.0, (nh, m)).astype(np.float32)
+    t_hat = rng.standard_normal((nh, m, d), dtype=np.float32) * mz[:, m:, None]
+    for g in range(ng):
+        if int(inp.meta[g, 2]) == 0:
+            sl = slice(g * hpg, (g + 1) * hpg)
+            mz[sl, :m] = -np.inf
+            mz[sl, m:] = 0.0
+            t_hat[sl] = 0.0
+    return FarState(m, k_tilde, q_tilde, mu, mz, np.ascontiguousarray(t_hat, dtype=np.float32))
+
+
 def to_device(inp, device="cuda"):
     """The arrays of a ChunkInputs / GatedInputs as contiguous torch tensors on `device`."""
     import torch

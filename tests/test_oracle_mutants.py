@@ -50,6 +50,22 @@ MUTANTS = [
     ("far count not advanced", "far += 1;", "far += 0;"),
     ("commit takes the wrong group's row", "const float *ks = chunk_k + ((size_t)j * ng + g) * d;",
      "const float *ks = chunk_k + ((size_t)j * ng + (ng - 1 - g)) * d;"),
+    ("far numerator not rescaled", "acc[c] += gb[b] * r[b] * (double)th[c];",
+     "acc[c] += gb[b] * (double)th[c];"),
+    ("mixing matrix transposed", "wb[b] += ea * (double)mu[((size_t)gh * m + a) * m + b];",
+     "wb[b] += ea * (double)mu[((size_t)gh * m + b) * m + a];"),
+    ("far mass one row behind", "far_den += gb[b] * z[(size_t)b * rows + i];",
+     "far_den += gb[b] * z[(size_t)b * rows + (i > 0 ? i - 1 : 0)];"),
+    ("negative far mass kept", "if (far_den >= 0.0) have = 1; else far_den = 0.0;", "have = 1;"),
+    ("row's own eviction left out", "for (long j = j0 < 0 ? 0 : j0; j <= i; ++j) {",
+     "for (long j = j0 < 0 ? 0 : j0; j < i; ++j) {"),
+    ("old far mass not rescaled", "double acc = mass * r;", "double acc = mass;"),
+    ("gain ignores the landmark max", "gb[b] = wb[b] * exp(f + mx[b] - cmax);",
+     "gb[b] = wb[b] * exp(f - cmax);"),
+    ("far-field call: query of the wrong row", "const float *qrow = q + ((size_t)i * nh + gh) * d;",
+     "const float *qrow = q + ((size_t)0 * nh + gh) * d;"),
+    ("far commit numerator not rescaled", "for (int c = 0; c < d; ++c) acc[c] = (double)th[c] * r;",
+     "for (int c = 0; c < d; ++c) acc[c] = (double)th[c];"),
 ]
 
 PIN_TESTS = [getattr(pins, n) for n in dir(pins) if n.startswith("test_")]

@@ -524,3 +524,205 @@ def test_golden_gated_unit():
     np.testing.assert_allclose(z, np.array(gd["expected_z"]), rtol=gd["rtol"], atol=gd["atol"])
     np.testing.assert_allclose(rk, np.array(gd["expected_ring_k"]), rtol=1e-7, atol=1e-8)
     np.testing.assert_array_equal(rv, np.array(gd["expected_ring_v"], dtype=np.float32))
+
+
+# ── the far field (landmark summaries of evicted keys) ──────────────────────────────────────
+
+def _far_case(rng, rows, m=1, hpg=1, far_len=None, d=8):
+    ng = int(rng.integers(1, 4))
+    w = int(rng.integers(2, 9))
+    meta = []
+    for _ in range(ng):
+        ov = int(rng.integers(1, w + 1)) if rng.random() < 0.3 else 0
+        wg = ov if ov else w
+        ln = int(rng.integers(0, wg + 1))
+        head = int(rng.integers(0, wg))
+        fl = int(far_len if far_len is not None else rng.integers(0, 4))
+        meta.append((ln, head, fl, ov))
+    return gen.make_chunk(rows, ng, hpg, d, w, int(rng.choice([0, 2])), meta,
+                          seed=int(rng.integers(1 << 30)), scale=float(rng.choice([0.3, 0.6])))
+
+
+def _stream_entries(inp, g):
+    """K, V of every entry a group has held so far, oldest first: its ring entries then chunk
+    rows (the history before them is passed separately)."""
+    ln, head, _, ov = (int(x) for x in inp.meta[g])
+    wg = ov if ov else inp.w
+    ks = [inp.ring_k[g, (head + x) % wg] for x in range(ln)]
+    vs = [inp.ring_v[g, (head + x) % wg] for x in range(ln)]
+    return ks, vs
+
+
+def _exact_far_state(q, hist_k, hist_v, scale):
+    """f64 summary (max, mass, numerator) of a key history against one landmark query."""
+    if len(hist_k) == 0:
+        return -np.inf, 0.0, np.zeros(q.shape[0])
+    s = scale * (np.asarray(hist_k, np.float64) @ q.astype(np.float64))
+    mx = s.max()
+    e = np.exp(s - mx)
+    return mx, e.sum(), e @ np.asarray(hist_v, np.float64)
+
+
+def _history_setup(rng, inp, m=1):
+    """Give each group a history of far_len evicted keys, every head one query shared by all
+    rows, and an exact landmark 0 (q_tilde = that query). Returns (far, history per group)."""
+    far = gen.make_far(inp, m, seed=int(rng.integers(1 << 30)))
+    hist = []
+    for g in range(inp.ng):
+        n0 = int(inp.meta[g, 2])
+        hk = rng.standard_normal((n0, inp.d)).astype(np.float32)
+        hv = rng.standard_normal((n0, inp.d)).astype(np.float32)
+        hist.append((hk, hv))
+        for h in range(inp.hpg):
+            gh = g * inp.hpg + h
+            qh = rng.standard_normal(inp.d).astype(np.float32)
+            inp.q[:, gh] = qh
+            far.q_tilde[gh, 0] = qh
+            mx, z, th = _exact_far_state(qh, hk, hv, inp.scale)
+            far.mz[gh, 0], far.mz[gh, m] = mx, z
+            far.t_hat[gh, 0] = th
+    return far, hist
+
+
+def _full_history_attention(inp, hist, i, gh):
+    """Plain softmax of row i's query over every key its group has seen: sinks, the far
+    history, all ring entries and chunk rows 0..i."""
+    g = gh // inp.hpg
+    ks, vs = _stream_entries(inp, g)
+    keys = list(inp.sink_k[g]) + list(hist[g][0]) + ks + [inp.chunk_k[j, g] for j in range(i + 1)]
+    vals = list(inp.sink_v[g]) + list(hist[g][1]) + vs + [inp.chunk_v[j, g] for j in range(i + 1)]
+    q = inp.q[i, gh].astype(np.float64)
+    s = inp.scale * (np.asarray(keys, np.float64) @ q)
+    p = np.exp(s - s.max())
+    return (p @ np.asarray(vals, np.float64)) / p.sum()
+
+
+def test_far_empty_equals_near_attention():
+    rng = np.random.default_rng(601)
+    done = 0
+    while done < 40:
+        inp = _far_case(rng, rows=int(rng.integers(1, 5)), m=int(rng.integers(1, 4)),
+                        hpg=int(rng.integers(1, 3)), far_len=0)
+        wgs = [int(inp.meta[g, 3]) or inp.w for g in range(inp.ng)]
+        if inp.rows > min(wgs):
+            continue   # a chunk longer than a window evicts its own rows
+        done += 1
+        for g in range(inp.ng):   # no evictions: the chunk fits into every ring
+            ov = int(inp.meta[g, 3])
+            wg = ov if ov else inp.w
+            inp.meta[g, 0] = min(int(inp.meta[g, 0]), max(0, wg - inp.rows))
+        far = gen.make_far(inp, int(rng.integers(1, 4)), seed=int(rng.integers(1 << 30)))
+        np.testing.assert_allclose(oracle.window_chunk_far(inp, far), oracle.window_chunk(inp),
+                                   rtol=1e-6, atol=1e-7)
+
+
+def test_far_exact_landmarks_give_full_history_attention():
+    """One landmark whose query is the row's query summarises the evicted keys exactly. A row
+    weighs landmark b by sum_a exp(scale <q, k_tilde_a>) mu[a][b] (not normalised), so with a
+    zero landmark key and a mixing weight of 1 the weight is exactly 1: windowed attention plus
+    the far field is then plain attention over everything the group has seen, evictions inside
+    the chunk included."""
+    rng = np.random.default_rng(602)
+    for _ in range(60):
+        inp = _far_case(rng, rows=int(rng.integers(1, 12)), hpg=int(rng.integers(1, 3)))
+        far, hist = _history_setup(rng, inp)
+        far.mu[:] = 1.0
+        far.k_tilde[:] = 0.0
+        got = oracle.window_chunk_far(inp, far)
+        for i in range(inp.rows):
+            for gh in range(inp.nh):
+                np.testing.assert_allclose(got[i, gh], _full_history_attention(inp, hist, i, gh),
+                                           rtol=2e-5, atol=2e-6)
+
+
+def test_far_mixing_selects_the_landmark_its_row_names():
+    """Landmark key 0 scores 0 and key 1 scores -400 against the row's query, so only row 0 of
+    mu counts; mu[0] = (0, 1) routes the whole weight to landmark 1, which holds the exact
+    history (mu is not symmetric: mu[1][0] = 0.7, so reading it transposed would weigh the
+    exact state by 0.7 and landmark 0's unrelated state by 1)."""
+    rng = np.random.default_rng(603)
+    for _ in range(30):
+        inp = _far_case(rng, rows=int(rng.integers(1, 6)), m=2, far_len=int(rng.integers(1, 4)))
+        far, hist = _history_setup(rng, inp, m=2)
+        for gh in range(inp.nh):   # move the exact summary to landmark 1
+            far.q_tilde[gh, 1] = far.q_tilde[gh, 0]
+            far.mz[gh, 1], far.mz[gh, 3] = far.mz[gh, 0], far.mz[gh, 2]
+            far.t_hat[gh, 1] = far.t_hat[gh, 0]
+            far.q_tilde[gh, 0] = rng.standard_normal(inp.d)
+            far.mz[gh, 0] = far.mz[gh, 1] - 1.0
+            far.mz[gh, 2] = 3.0
+            far.t_hat[gh, 0] = rng.standard_normal(inp.d)
+            far.mu[gh] = [[0.0, 1.0], [0.7, 0.0]]
+        for g in range(inp.ng):
+            q0 = inp.q[0, g * inp.hpg].astype(np.float64)
+            far.k_tilde[g, 0] = 0.0
+            far.k_tilde[g, 1] = -400.0 * q0 / (inp.scale * float(q0 @ q0))
+        got = oracle.window_chunk_far(inp, far)
+        for i in range(inp.rows):
+            for gh in range(inp.nh):
+                np.testing.assert_allclose(got[i, gh], _full_history_attention(inp, hist, i, gh),
+                                           rtol=2e-5, atol=2e-6)
+
+
+def test_far_negative_mass_is_dropped():
+    """A negative far mass (mixing weight -1) drops the far part, evictions inside the chunk
+    included: the result is the windowed attention alone."""
+    rng = np.random.default_rng(604)
+    for _ in range(30):
+        inp = _far_case(rng, rows=int(rng.integers(1, 8)), far_len=int(rng.integers(1, 4)))
+        far = gen.make_far(inp, 1, seed=int(rng.integers(1 << 30)))
+        far.mu[:] = -1.0
+        np.testing.assert_allclose(oracle.window_chunk_far(inp, far), oracle.window_chunk(inp),
+                                   rtol=1e-6, atol=1e-7)
+
+
+def test_far_commit_summarises_the_evicted_keys_exactly():
+    rng = np.random.default_rng(605)
+    for _ in range(60):
+        inp = _far_case(rng, rows=int(rng.integers(1, 12)), m=2, hpg=int(rng.integers(1, 3)))
+        far, hist = _history_setup(rng, inp, m=2)
+        rk, rv, meta, mz, th = oracle.window_commit_far(inp, far)
+        rk0, rv0, meta0 = oracle.window_commit(inp)
+        np.testing.assert_array_equal(rk, rk0)
+        np.testing.assert_array_equal(meta, meta0)
+        for g in range(inp.ng):
+            ks, vs = _stream_entries(inp, g)
+            ks += [inp.chunk_k[j, g] for j in range(inp.rows)]
+            vs += [inp.chunk_v[j, g] for j in range(inp.rows)]
+            ov = int(inp.meta[g, 3])
+            wg = ov if ov else inp.w
+            nev = max(0, len(ks) - wg)   # the oldest entries leave the window
+            hk = list(hist[g][0]) + ks[:nev]
+            hv = list(hist[g][1]) + vs[:nev]
+            assert int(meta[g, 2]) == int(inp.meta[g, 2]) + nev
+            for h in range(inp.hpg):
+                gh = g * inp.hpg + h
+                mx, z, t = _exact_far_state(far.q_tilde[gh, 0], hk, hv, inp.scale)
+                if nev == 0:   # untouched
+                    np.testing.assert_array_equal(mz[gh], far.mz[gh])
+                    np.testing.assert_array_equal(th[gh], far.t_hat[gh])
+                    continue
+                np.testing.assert_allclose(mz[gh, 0], mx, rtol=1e-6, atol=1e-6)
+                np.testing.assert_allclose(mz[gh, 2], z, rtol=2e-6)
+                np.testing.assert_allclose(th[gh, 0], t, rtol=2e-5, atol=2e-6)
+
+
+def test_far_chunk_equals_sequence_of_decodes():
+    """Row i of a chunk call with a far field == a one-row call on the state after the rows
+    before it were committed with their far updates (any mixing, any landmark queries)."""
+    rng = np.random.default_rng(606)
+    for _ in range(25):
+        inp = _far_case(rng, rows=int(rng.integers(1, 8)), m=int(rng.integers(1, 4)),
+                        hpg=int(rng.integers(1, 3)))
+        far = gen.make_far(inp, int(rng.integers(1, 4)), seed=int(rng.integers(1 << 30)),
+                           mu_kind="positive")
+        full = oracle.window_chunk_far(inp, far)
+        state = _decode_state(inp)
+        sfar = gen.FarState(far.m, far.k_tilde, far.q_tilde, far.mu, far.mz.copy(),
+                            far.t_hat.copy())
+        for i in range(inp.rows):
+            _row_of(state, inp, i)
+            np.testing.assert_allclose(oracle.window_chunk_far(state, sfar)[0], full[i],
+                                       rtol=2e-5, atol=2e-6)
+            state.ring_k, state.ring_v, state.meta, sfar.mz, sfar.t_hat = \
+                oracle.window_commit_far(state, sfar)

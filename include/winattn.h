@@ -46,8 +46,9 @@ extern "C" {
 #define WINATTN_EUNSUPPORTED (-4)
 
 /* Ring metadata of one KV group, four u32 per group, laid out as the o1c page's header comment
- * gives it: entries held, slot of the oldest entry, far-field count (ignored here), and a
- * per-group window override (0 = the call's default w; `wgf`). */
+ * gives it: entries held, slot of the oldest entry, far-field count (the number of keys that
+ * have left the window; read only by the far-field calls), and a per-group window override
+ * (0 = the call's default w; `wgf`). */
 typedef struct {
     uint32_t len;
     uint32_t head;
@@ -137,6 +138,61 @@ int attn_window_gated(const float* yq, const float* yk, const float* yv, const f
  * WINATTN_EINVAL (nothing launched) or WINATTN_ELAUNCH. */
 int attn_window_commit(float* ring_k, float* ring_v, uint32_t* meta, const float* chunk_k,
                        const float* chunk_v, int rows, int ng, int d, int w, void* stream);
+
+/*
+ * attn_window_chunk_far — attn_window_chunk plus the far field: landmark summaries of the keys
+ * that have left each group's window (o1c page: `o1c_far_e`, `o1c_land`, `o1c_far`, `o1c_soft`,
+ * `o1c_add`; token path `o1c_tok_far`, `o1c_tok_merge`).
+ *
+ * State, per query head gh = g*hpg + h and landmark b < m:
+ *   mz     [nh][2m]    mz[gh][b] = far max mx_b, mz[gh][m+b] = far mass z_b (-inf and 0 while
+ *                      the field is empty)
+ *   t_hat  [nh][m][d]  far numerator: sum over evicted keys of exp(s - mx_b) V,
+ *                      s = scale <q_tilde[gh][b], K>; z_b is the same sum of exp(s - mx_b)
+ *   q_tilde [nh][m][d] landmark queries; k_tilde [ng][m][d] landmark keys;
+ *   mu     [nh][m][m]  mixing matrix, row a, column b
+ * Chunk row j >= j0 = wg - len evicts the group's oldest entry x = j - j0 (ring slot
+ * (head + x) mod wg while x < len, else chunk row x - len); with e_b(j) = exp(s_b(j) - mx'_b),
+ * mx'_b = max(mx_b, s_b(j) over the chunk's evictions), r_b = exp(mx_b - mx'_b) (1 if the max
+ * did not move) and z_b(i) = z_b r_b + sum_{j0<=j<=i} e_b(j), row i of head gh with near scores
+ * s over its attn_window_chunk key set takes, when far_len + (evictions up to row i) > 0:
+ *   fl_a = scale <q, k_tilde[g][a]>, f = max fl, w_b = sum_a exp(fl_a - f) mu[gh][a][b],
+ *   c = max(max s, f + mx'_b), G_b = w_b exp(f + mx'_b - c), F = sum_b G_b z_b(i);
+ *   out = (sum exp(s - c) V + sum_b G_b (r_b t_hat_b + sum_{j0<=j<=i} e_b(j) V_ev(j)))
+ *         / (sum exp(s - c) + F),
+ * and drops the far terms (F and the numerator) when F < 0 or the field is empty.
+ *
+ * Arguments as attn_window_chunk plus the state above (device pointers, read only here), and
+ * m, the landmark count: 1 <= m <= 64. rows <= 64 (the far path works on chunks of at most 64
+ * rows; larger chunks or m return WINATTN_EUNSUPPORTED). The workspace is required (see
+ * attn_window_chunk_far_workspace) and follows the convention above.
+ */
+int attn_window_chunk_far(const float* ring_k, const float* ring_v, const uint32_t* meta,
+                          const float* sink_k, const float* sink_v, const float* q,
+                          const float* chunk_k, const float* chunk_v, const float* k_tilde,
+                          const float* q_tilde, const float* mu, const float* mz,
+                          const float* t_hat, float* out, int rows, int ng, int hpg, int d, int w,
+                          int ns, int m, float scale, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Workspace bytes attn_window_chunk_far needs for these sizes (0 if invalid or unsupported). */
+size_t attn_window_chunk_far_workspace(int rows, int ng, int hpg, int d, int w, int ns, int m);
+
+/*
+ * attn_window_commit_far — the far state and ring after a chunk (o1c page: `o1c_far_commit`,
+ * then `o1c_ring_commit` and `o1c_meta`). For every group with evictions in the chunk and every
+ * head gh and landmark b: t_hat_b <- r_b t_hat_b + sum_{j>=j0} e_b(j) V_ev(j), mz[gh][b] <- mx'_b,
+ * mz[gh][m+b] <- z_b(rows - 1) (notation of attn_window_chunk_far); groups without evictions
+ * keep their state. Then exactly attn_window_commit. mz and t_hat [nh] as above, updated in
+ * place; q_tilde read only. Sizes as attn_window_chunk_far with hpg = heads per group (no
+ * sinks). Asynchronous on `stream`; allocates nothing and needs no workspace. Run it after the
+ * chunk's attention call on the same stream. Returns 0, WINATTN_EINVAL, WINATTN_EUNSUPPORTED
+ * (nothing launched) or WINATTN_ELAUNCH.
+ */
+int attn_window_commit_far(float* ring_k, float* ring_v, uint32_t* meta, const float* chunk_k,
+                           const float* chunk_v, const float* q_tilde, float* mz, float* t_hat,
+                           int rows, int ng, int hpg, int d, int w, int m, float scale,
+                           void* stream);
 
 /* Workspace bytes attn_window_gated needs for these sizes (0 if the sizes are invalid). */
 size_t attn_window_gated_workspace(int rows, int nh, int nk, int hd, int window);

@@ -62,6 +62,12 @@ def load(path: str = LIB_PATH):
     lib.attn_window_commit.restype = _i
     lib.attn_mfma16_layout_probe.argtypes = [_vp, _vp]
     lib.attn_mfma16_layout_probe.restype = _i
+    lib.attn_window_chunk_far.argtypes = [_vp] * 14 + [_i] * 7 + [_f, _vp, _sz, _vp]
+    lib.attn_window_chunk_far.restype = _i
+    lib.attn_window_chunk_far_workspace.argtypes = [_i] * 7
+    lib.attn_window_chunk_far_workspace.restype = _sz
+    lib.attn_window_commit_far.argtypes = [_vp] * 8 + [_i] * 6 + [_f, _vp]
+    lib.attn_window_commit_far.restype = _i
     lib.attn_tuning_set.argtypes = [_i, _i]
     lib.attn_tuning_set.restype = _i
     lib.attn_strerror.argtypes = [_i]
@@ -99,6 +105,10 @@ def chunk_workspace_bytes(rows, ng, hpg, d, w, ns) -> int:
 
 def gated_workspace_bytes(rows, nh, nk, hd, window) -> int:
     return int(load().attn_window_gated_workspace(rows, nh, nk, hd, window))
+
+
+def chunk_far_workspace_bytes(rows, ng, hpg, d, w, ns, m) -> int:
+    return load().attn_window_chunk_far_workspace(rows, ng, hpg, d, w, ns, m)
 
 
 def chunk_plan(rows, ng, hpg, d, w, ns):
@@ -236,6 +246,62 @@ def attn_window_commit(ring_k, ring_v, meta, chunk_k, chunk_v, stream=None) -> N
         _ptr(chunk_v, "chunk_v"), rows, ng, d, w, _stream_ptr(stream, ring_k.device))
     if rc != OK:
         raise WinattnError("attn_window_commit", rc)
+
+
+def _far_shapes(ring_k, q_tilde, mz, t_hat):
+    ng, w, d = ring_k.shape
+    nh, m, dq = q_tilde.shape
+    if dq != d or nh % ng or tuple(mz.shape) != (nh, 2 * m) or tuple(t_hat.shape) != (nh, m, d):
+        raise ValueError("far state: q_tilde [nh][m][d], mz [nh][2m], t_hat [nh][m][d]")
+    return ng, w, d, nh, m
+
+
+def attn_window_chunk_far(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v, k_tilde,
+                          q_tilde, mu, mz, t_hat, scale, out=None, workspace=None, stream=None):
+    """out[rows][nh][d] = windowed GQA attention of a chunk plus the far field of landmark
+    summaries (see attn_window_chunk_far in include/winattn.h). k_tilde [ng][m][d],
+    q_tilde [nh][m][d], mu [nh][m][m], mz [nh][2m], t_hat [nh][m][d]."""
+    ng, w, d, nh, m = _far_shapes(ring_k, q_tilde, mz, t_hat)
+    rows = q.shape[0]
+    if tuple(q.shape) != (rows, nh, d) or tuple(k_tilde.shape) != (ng, m, d) \
+            or tuple(mu.shape) != (nh, m, m):
+        raise ValueError("attn_window_chunk_far: q [rows][nh][d], k_tilde [ng][m][d], mu [nh][m][m]")
+    ns = 0 if sink_k is None else sink_k.shape[1]
+    if out is None:
+        out = torch.empty((rows, nh, d), dtype=torch.float32, device=q.device)
+    st = _stream_ptr(stream, q.device)
+    need = chunk_far_workspace_bytes(rows, ng, nh // ng, d, w, ns, m)
+    ws = workspace if workspace is not None else _default_workspace(q.device, st)
+    wp, wb = ws.get(need)
+    rc = load().attn_window_chunk_far(
+        _ptr(ring_k, "ring_k"), _ptr(ring_v, "ring_v"),
+        _ptr(meta, "meta", (torch.int32, torch.uint32)), _ptr(sink_k, "sink_k"),
+        _ptr(sink_v, "sink_v"), _ptr(q, "q"), _ptr(chunk_k, "chunk_k"), _ptr(chunk_v, "chunk_v"),
+        _ptr(k_tilde, "k_tilde"), _ptr(q_tilde, "q_tilde"), _ptr(mu, "mu"), _ptr(mz, "mz"),
+        _ptr(t_hat, "t_hat"), _ptr(out, "out"), rows, ng, nh // ng, d, w, ns, m, float(scale),
+        wp, wb, st)
+    if rc != OK:
+        raise WinattnError("attn_window_chunk_far", rc)
+    return out
+
+
+def attn_window_commit_far(ring_k, ring_v, meta, chunk_k, chunk_v, q_tilde, mz, t_hat, scale,
+                           stream=None) -> None:
+    """Update the far state (mz, t_hat) with the chunk's evictions, then push the chunk into
+    the rings and advance meta, all in place (see attn_window_commit_far in
+    include/winattn.h)."""
+    ng, w, d, nh, m = _far_shapes(ring_k, q_tilde, mz, t_hat)
+    rows = chunk_k.shape[0]
+    if (tuple(ring_v.shape) != (ng, w, d) or tuple(chunk_k.shape) != (rows, ng, d)
+            or tuple(chunk_v.shape) != (rows, ng, d) or tuple(meta.shape) != (ng, 4)):
+        raise ValueError("attn_window_commit_far: rings [ng][w][d], chunk [rows][ng][d], meta [ng][4]")
+    rc = load().attn_window_commit_far(
+        _ptr(ring_k, "ring_k"), _ptr(ring_v, "ring_v"),
+        _ptr(meta, "meta", (torch.int32, torch.uint32)), _ptr(chunk_k, "chunk_k"),
+        _ptr(chunk_v, "chunk_v"), _ptr(q_tilde, "q_tilde"), _ptr(mz, "mz"), _ptr(t_hat, "t_hat"),
+        rows, ng, nh // ng, d, w, m, float(scale), _stream_ptr(stream, ring_k.device))
+    if rc != OK:
+        raise WinattnError("attn_window_commit_far", rc)
 
 
 def mfma16_layout_probe(device="cuda", stream=None):

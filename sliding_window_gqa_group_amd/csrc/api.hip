@@ -38,6 +38,7 @@ struct Plan {
     int tk;             // keys per tile
     int tps;            // tiles per split
     int nsplit;         // splits reserved per block
+    int slots;          // partial slots per block: nsplit plus extra (the far field's)
     bool merge_kernel;  // merge splits in a separate launch
     int xcd_map;        // matrix-core work order: 1 whole groups per XCD, 0 round-robin
     size_t off_q, off_pacc, off_pm, off_pl, off_tickets, bytes;
@@ -50,7 +51,8 @@ int pad_d(int d) { return d <= 64 ? 64 : (d <= 128 ? 128 : 256); }
 
 // rows/hpg/d: the call's shape; wcap: the largest window any row can have; qbuf_floats: extra
 // workspace for the gated call's prepared queries.
-Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_floats) {
+Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_floats,
+               int extra_slots = 0) {
     Plan pl{};
     const long long nq_tot = (long long)rows * hpg;
     pl.dpad = pad_d(d);
@@ -117,7 +119,9 @@ Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_f
     pl.xcd_map = g_xcd_map >= 0 ? g_xcd_map : (group_bytes <= (8LL << 20) ? 1 : 0);
 
     // Layout: [counters][prepared queries][partials], each region 256-byte aligned.
-    const bool split = pl.nsplit > 1;
+    pl.slots = pl.nsplit + extra_slots;
+    if (extra_slots > 0) pl.merge_kernel = true;   // the extra partials merge in the merge launch
+    const bool split = pl.nsplit > 1 || extra_slots > 0;
     if (!split && qbuf_floats == 0) {
         pl.bytes = 0;
         return pl;
@@ -128,7 +132,7 @@ Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_f
     pl.off_q = off;
     off = align_up(off + qbuf_floats * sizeof(float), 256);
     if (split) {
-        const size_t slots = (size_t)blocks * pl.nsplit * pl.qb;
+        const size_t slots = (size_t)blocks * pl.slots * pl.qb;
         pl.off_pacc = off;
         off = align_up(off + slots * pl.dpad * sizeof(float), 256);
         pl.off_pm = off;
@@ -171,14 +175,15 @@ int launch_attention(const Plan& pl, AttnParams& p, bool gated, char* ws, hipStr
     p.xcd_map = pl.xcd_map;
     p.tps = pl.tps;
     p.nsplit_grid = pl.nsplit;
+    p.slot_stride = pl.slots;
     p.nqblocks = pl.nqblocks;
-    if (pl.nsplit > 1) {
+    if (pl.slots > 1) {
         p.pacc = reinterpret_cast<float*>(ws + pl.off_pacc);
         p.pm = reinterpret_cast<float*>(ws + pl.off_pm);
         p.pl = reinterpret_cast<float*>(ws + pl.off_pl);
         p.tickets = reinterpret_cast<unsigned int*>(ws + pl.off_tickets);
     }
-    p.merge_kernel = pl.merge_kernel && pl.nsplit > 1 ? 1 : 0;
+    p.merge_kernel = pl.merge_kernel && pl.slots > 1 ? 1 : 0;
     hipError_t err;
     const dim3 grid(pl.nsplit, pl.nqblocks, p.ng);
     if (pl.kind == kKindMfma)
@@ -283,6 +288,160 @@ int attn_window_chunk(const float* ring_k, const float* ring_v, const uint32_t* 
     p.scale_log2 = scale * kLog2e;
     return launch_attention(pl, p, false, static_cast<char*>(workspace),
                             static_cast<hipStream_t>(stream));
+}
+
+namespace {
+
+// Far-field workspace: the attention plan with one extra partial slot per query block, then the
+// f64 eviction arrays [nh][m][rows] (weights, prefix masses) and [nh][m] (max, rescale).
+struct FarPlan {
+    Plan pl;
+    size_t off_e, off_z, off_mx, off_r, bytes;
+};
+
+FarPlan make_far_plan(int rows, int ng, int hpg, int d, int w, int ns, int m) {
+    FarPlan f{};
+    f.pl = make_plan(rows, ng, hpg, d, w, ns, 0, 1);
+    const size_t nhm = (size_t)ng * hpg * m;
+    size_t off = f.pl.bytes;
+    f.off_e = off;
+    off = align_up(off + nhm * rows * sizeof(double), 256);
+    f.off_z = off;
+    off = align_up(off + nhm * rows * sizeof(double), 256);
+    f.off_mx = off;
+    off = align_up(off + nhm * sizeof(double), 256);
+    f.off_r = off;
+    off = align_up(off + nhm * sizeof(double), 256);
+    f.bytes = off;
+    return f;
+}
+
+bool far_shape_ok(int rows, int m) { return m >= 1 && m <= kFarMaxLandmarks && rows <= kFarMaxRows; }
+
+}  // namespace
+
+size_t attn_window_chunk_far_workspace(int rows, int ng, int hpg, int d, int w, int ns, int m) {
+    if (!chunk_shape_ok(rows, ng, hpg, d, w, ns) || !far_shape_ok(rows, m)) return 0;
+    return make_far_plan(rows, ng, hpg, d, w, ns, m).bytes;
+}
+
+int attn_window_chunk_far(const float* ring_k, const float* ring_v, const uint32_t* meta,
+                          const float* sink_k, const float* sink_v, const float* q,
+                          const float* chunk_k, const float* chunk_v, const float* k_tilde,
+                          const float* q_tilde, const float* mu, const float* mz,
+                          const float* t_hat, float* out, int rows, int ng, int hpg, int d, int w,
+                          int ns, int m, float scale, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    if (!chunk_shape_ok(rows, ng, hpg, d, w, ns) || !std::isfinite(scale)) return WINATTN_EINVAL;
+    if (m < 1) return WINATTN_EINVAL;
+    if (!far_shape_ok(rows, m)) return WINATTN_EUNSUPPORTED;
+    const void* ptrs[] = {ring_k, ring_v, q, chunk_k, chunk_v, k_tilde, q_tilde, mu, mz, t_hat, out};
+    for (const void* ptr : ptrs)
+        if (!ptr || !aligned16(ptr)) return WINATTN_EINVAL;
+    if (!meta || ((uintptr_t)meta & 3u) != 0) return WINATTN_EINVAL;
+    if (ns > 0 && (!sink_k || !sink_v || !aligned16(sink_k) || !aligned16(sink_v)))
+        return WINATTN_EINVAL;
+    if ((long long)ng * hpg * m * d > kMaxFloats) return WINATTN_EINVAL;
+    const FarPlan fp = make_far_plan(rows, ng, hpg, d, w, ns, m);
+    if (!workspace || workspace_bytes < fp.bytes) return WINATTN_EWORKSPACE;
+    if (!aligned16(workspace)) return WINATTN_EINVAL;
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Plan& pl = fp.pl;
+
+    FarParams f{};
+    f.ring_k = ring_k;
+    f.ring_v = ring_v;
+    f.meta = meta;
+    f.chunk_k = chunk_k;
+    f.chunk_v = chunk_v;
+    f.q = q;
+    f.k_tilde = k_tilde;
+    f.q_tilde = q_tilde;
+    f.mu = mu;
+    f.mz = const_cast<float*>(mz);        // read only on this path
+    f.t_hat = const_cast<float*>(t_hat);
+    f.ev_e = reinterpret_cast<double*>(ws + fp.off_e);
+    f.ev_z = reinterpret_cast<double*>(ws + fp.off_z);
+    f.ev_mx = reinterpret_cast<double*>(ws + fp.off_mx);
+    f.ev_r = reinterpret_cast<double*>(ws + fp.off_r);
+    f.pacc = reinterpret_cast<float*>(ws + pl.off_pacc);
+    f.pm = reinterpret_cast<float*>(ws + pl.off_pm);
+    f.pl = reinterpret_cast<float*>(ws + pl.off_pl);
+    f.rows = rows;
+    f.ng = ng;
+    f.hpg = hpg;
+    f.nh = ng * hpg;
+    f.d = d;
+    f.w = w;
+    f.m = m;
+    f.qb = pl.qb;
+    f.nqblocks = pl.nqblocks;
+    f.slot_stride = pl.slots;
+    f.far_slot = pl.nsplit;
+    f.dpad = pl.dpad;
+    f.scale = scale;
+    if (launch_far_evict(f, st) != hipSuccess || launch_far_part(f, st) != hipSuccess)
+        return WINATTN_ELAUNCH;
+
+    AttnParams p{};
+    p.ring_k = ring_k;
+    p.ring_v = ring_v;
+    p.meta = meta;
+    p.sink_k = ns > 0 ? sink_k : nullptr;
+    p.sink_v = ns > 0 ? sink_v : nullptr;
+    p.q = q;
+    p.chunk_k = chunk_k;
+    p.chunk_v = chunk_v;
+    p.out = out;
+    p.ring_gs = (long long)w * d;
+    p.ring_ss = d;
+    p.chunk_rs = (long long)ng * d;
+    p.chunk_gs = d;
+    p.rows = rows;
+    p.ng = ng;
+    p.hpg = hpg;
+    p.nh = ng * hpg;
+    p.d = d;
+    p.w = w;
+    p.ns = ns;
+    p.scale_log2 = scale * kLog2e;
+    return launch_attention(pl, p, false, ws, st);
+}
+
+int attn_window_commit_far(float* ring_k, float* ring_v, uint32_t* meta, const float* chunk_k,
+                           const float* chunk_v, const float* q_tilde, float* mz, float* t_hat,
+                           int rows, int ng, int hpg, int d, int w, int m, float scale,
+                           void* stream) {
+    if (!chunk_shape_ok(rows, ng, hpg, d, w, 0) || !std::isfinite(scale)) return WINATTN_EINVAL;
+    if (m < 1) return WINATTN_EINVAL;
+    if (!far_shape_ok(rows, m)) return WINATTN_EUNSUPPORTED;
+    const void* ptrs[] = {ring_k, ring_v, chunk_k, chunk_v, q_tilde, mz, t_hat};
+    for (const void* ptr : ptrs)
+        if (!ptr || !aligned16(ptr)) return WINATTN_EINVAL;
+    if (!meta || ((uintptr_t)meta & 3u) != 0) return WINATTN_EINVAL;
+    if ((long long)ng * hpg * m * d > kMaxFloats) return WINATTN_EINVAL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    FarParams f{};
+    f.ring_k = ring_k;
+    f.ring_v = ring_v;
+    f.meta = meta;
+    f.chunk_k = chunk_k;
+    f.chunk_v = chunk_v;
+    f.q_tilde = q_tilde;
+    f.mz = mz;
+    f.t_hat = t_hat;
+    f.rows = rows;
+    f.ng = ng;
+    f.hpg = hpg;
+    f.nh = ng * hpg;
+    f.d = d;
+    f.w = w;
+    f.m = m;
+    f.scale = scale;
+    if (launch_far_commit(f, st) != hipSuccess) return WINATTN_ELAUNCH;
+    const CommitParams c{ring_k, ring_v, meta, chunk_k, chunk_v, rows, ng, d, w};
+    return launch_ring_commit(c, st) == hipSuccess ? WINATTN_OK : WINATTN_ELAUNCH;
 }
 
 size_t attn_window_gated_workspace(int rows, int nh, int nk, int hd, int window) {

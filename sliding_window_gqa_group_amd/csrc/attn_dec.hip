@@ -296,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dec_kernel(const AttnParams 
             o *= 1.0f / fmaxf(s_l[j], 1e-30f);
             store_out<GATED>(p, q0 + j, g, 4 * c, make_float4(o.x, o.y, o.z, o.w));
         } else {
-            const size_t at = ((size_t)blk * p.nsplit_grid + split) * NQ + j;
+            const size_t at = ((size_t)blk * p.slot_stride + split) * NQ + j;
             store_part4(p, p.pacc + at * D + 4 * c, make_float4(o.x, o.y, o.z, o.w));
             if (c == 0) {
                 store_part(p, p.pm + at, s_m[j]);
@@ -324,9 +324,10 @@ __global__ __launch_bounds__(kThreads) void split_merge_kernel(const AttnParams 
     const int qb = blockIdx.x, g = blockIdx.y;
     const int q0 = qb * QB;
     const int nq = min(QB, p.rows * p.hpg - q0);
-    // Every split slot of the block holds a partial or an empty mark (see mark_split_empty).
+    // Every slot of the block holds a partial or an empty mark (see mark_split_empty): the
+    // splits, and the far field's partial when the call has one.
     constexpr int MC = merge_cols<QB>();
-    merge_block<QB, D, GATED, MC>(p, g * p.nqblocks + qb, p.nsplit_grid, q0, nq, g, scratch,
+    merge_block<QB, D, GATED, MC>(p, g * p.nqblocks + qb, p.slot_stride, q0, nq, g, scratch,
                                   (int)blockIdx.z * (MC / 4));
 }
 

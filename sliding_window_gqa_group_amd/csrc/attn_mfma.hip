@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
         return;
     }
     if (qvalid) {
-        const size_t at = ((size_t)blk * p.nsplit_grid + split) * QB + jq;
+        const size_t at = ((size_t)blk * p.slot_stride + split) * QB + jq;
 #pragma unroll
         for (int b = 0; b < NDB; ++b)
 #pragma unroll

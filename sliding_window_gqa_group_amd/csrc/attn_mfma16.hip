@@ -393,7 +393,7 @@ __global__ __launch_bounds__(kThreads * m16_key_split<D>(), 1) void attn_mfma16_
         return;
     }
     if (qvalid && kh == 0) {
-        const size_t at = ((size_t)blk * p.nsplit_grid + split) * QB + jq;
+        const size_t at = ((size_t)blk * p.slot_stride + split) * QB + jq;
 #pragma unroll
         for (int b = 0; b < NDB; ++b)
             store_part4(p, p.pacc + at * D + 16 * b + 4 * kr4,

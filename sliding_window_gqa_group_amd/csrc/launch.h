@@ -64,4 +64,36 @@ struct CommitParams {
 // Ring commit and meta advance after a chunk; one workgroup per group.
 hipError_t launch_ring_commit(const CommitParams& p, hipStream_t stream);
 
+struct FarParams {
+    const float* ring_k;    // [ng][w][d]
+    const float* ring_v;
+    const uint32_t* meta;   // [ng][4], as before the chunk
+    const float* chunk_k;   // [rows][ng][d]
+    const float* chunk_v;
+    const float* q;         // [rows][nh][d] (chunk call only)
+    const float* k_tilde;   // [ng][m][d] landmark keys (chunk call only)
+    const float* q_tilde;   // [nh][m][d] landmark queries
+    const float* mu;        // [nh][m][m] mixing matrix (chunk call only)
+    float* mz;              // [nh][2m] far maxima then far masses (written by the commit)
+    float* t_hat;           // [nh][m][d] far numerators (written by the commit)
+    double* ev_e;           // workspace [nh][m][rows]: eviction weights
+    double* ev_z;           // workspace [nh][m][rows]: far mass as of each row
+    double* ev_mx;          // workspace [nh][m]: far max after the chunk
+    double* ev_r;           // workspace [nh][m]: rescale of the old state
+    float* pacc;            // the attention's split partials; the far part is slot far_slot
+    float* pm;
+    float* pl;
+    int rows, ng, hpg, nh, d, w, m;
+    int qb, nqblocks, slot_stride, far_slot, dpad;
+    float scale;
+};
+// Far field of a chunk (rows <= 64, m <= 64): eviction scores per (head, landmark), then the
+// far partial of every (row, head) into the partial buffer, merged by the merge launch.
+hipError_t launch_far_evict(const FarParams& p, hipStream_t stream);
+hipError_t launch_far_part(const FarParams& p, hipStream_t stream);
+// Far state after a chunk; runs before the ring commit, which overwrites the evicted rows.
+hipError_t launch_far_commit(const FarParams& p, hipStream_t stream);
+constexpr int kFarMaxRows = 64;
+constexpr int kFarMaxLandmarks = 64;
+
 }  // namespace winattn

@@ -36,15 +36,17 @@ struct AttnParams {
     float* out;                  // [rows][nh][d]
     const float* gate;           // gated call only: [rows][nh*d]
     const float* gate_scale;     // gated call only: [nh*d]
-    float* pacc;                 // split partials: [blocks][nsplit_grid][QB][D]
-    float* pm;                   // [blocks][nsplit_grid][QB] running max (log2 domain)
-    float* pl;                   // [blocks][nsplit_grid][QB] running sum
+    float* pacc;                 // split partials: [blocks][slot_stride][QB][D]
+    float* pm;                   // [blocks][slot_stride][QB] running max (log2 domain)
+    float* pl;                   // [blocks][slot_stride][QB] running sum
     unsigned int* tickets;       // [blocks]
     long long ring_gs, ring_ss;  // ring strides in floats: per group, per slot
     long long chunk_rs, chunk_gs;
     int rows, ng, hpg, nh, d, w, ns;
     int tps;                     // key tiles per split
     int nsplit_grid;             // splits reserved per query block
+    int slot_stride;             // partial slots per query block: the splits, plus one for the
+                                 // far field when the call has one
     int nqblocks;                // query blocks per group
     float scale_log2;            // scale * log2(e): scores live in the log2 domain
     int g_base, g_mod, g_hi0, g_wcap;   // gated call's ring descriptor
@@ -370,7 +372,7 @@ __device__ inline void merge_block(const AttnParams& p, int blk, int nsplit, int
     static_assert(DC % 4 == 0 && D % DC == 0, "column chunk must divide the padded width");
     constexpr int D4 = DC / 4;
     const int d4 = p.d / 4;
-    const size_t base = (size_t)blk * p.nsplit_grid * QB;
+    const size_t base = (size_t)blk * p.slot_stride * QB;
     constexpr int ITEMS = QB * D4;
     if constexpr (ITEMS >= NT) {
         constexpr int IPT = ITEMS / NT;
@@ -417,7 +419,7 @@ __device__ inline void merge_block(const AttnParams& p, int blk, int nsplit, int
 template <int QB>
 __device__ inline void mark_split_empty(const AttnParams& p, int blk, int split) {
     if (p.merge_kernel && threadIdx.x < QB)
-        p.pm[((size_t)blk * p.nsplit_grid + split) * QB + threadIdx.x] = -INFINITY;
+        p.pm[((size_t)blk * p.slot_stride + split) * QB + threadIdx.x] = -INFINITY;
 }
 
 // After every split of a query block has written its partial, the last one to arrive merges

@@ -103,6 +103,63 @@ def test_commit_rejects_invalid_arguments(lib, kw):
     assert _commit(lib, **kw) == B.EINVAL
 
 
+def _chunk_far(lib, **kw):
+    a = dict(ring_k=FAKE, ring_v=FAKE, meta=FAKE, sink_k=None, sink_v=None, q=FAKE,
+             chunk_k=FAKE, chunk_v=FAKE, k_tilde=FAKE, q_tilde=FAKE, mu=FAKE, mz=FAKE,
+             t_hat=FAKE, out=FAKE, rows=4, ng=2, hpg=2, d=64, w=16, ns=0, m=8, scale=0.125,
+             ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.attn_window_chunk_far(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(rows=0), dict(m=0), dict(d=6), dict(k_tilde=None), dict(q_tilde=None), dict(mu=None),
+    dict(mz=None), dict(t_hat=None), dict(mu=FAKE + 4), dict(t_hat=FAKE + 8),
+    dict(ns=2), dict(scale=float("nan")), dict(meta=FAKE + 1),
+])
+def test_chunk_far_rejects_invalid_arguments(lib, kw):
+    assert _chunk_far(lib, **kw) == B.EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(rows=65), dict(m=65)])
+def test_chunk_far_rejects_unsupported_sizes(lib, kw):
+    assert _chunk_far(lib, **kw) == B.EUNSUPPORTED
+
+
+def test_chunk_far_needs_its_workspace(lib):
+    need = B.chunk_far_workspace_bytes(4, 2, 2, 64, 16, 0, 8)
+    assert need > 0
+    # the far call keeps one more partial slot per query block and its eviction arrays
+    assert need > B.chunk_workspace_bytes(4, 2, 2, 64, 16, 0) + 2 * 4 * 8 * 4 * 4
+    assert _chunk_far(lib, ws=None) == B.EWORKSPACE
+    assert _chunk_far(lib, wsb=need - 1) == B.EWORKSPACE
+    assert B.chunk_far_workspace_bytes(65, 2, 2, 64, 16, 0, 8) == 0
+    assert B.chunk_far_workspace_bytes(4, 2, 2, 64, 16, 0, 65) == 0
+    assert B.chunk_far_workspace_bytes(4, 2, 2, 64, 16, 0, 0) == 0
+
+
+def _commit_far(lib, **kw):
+    a = dict(ring_k=FAKE, ring_v=FAKE, meta=FAKE, chunk_k=FAKE, chunk_v=FAKE, q_tilde=FAKE,
+             mz=FAKE, t_hat=FAKE, rows=4, ng=2, hpg=2, d=64, w=16, m=8, scale=0.125,
+             stream=None)
+    a.update(kw)
+    return lib.attn_window_commit_far(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(rows=0), dict(ng=0), dict(hpg=0), dict(m=0), dict(d=6), dict(q_tilde=None),
+    dict(mz=None), dict(t_hat=None), dict(mz=FAKE + 4), dict(meta=None),
+    dict(scale=float("inf")),
+])
+def test_commit_far_rejects_invalid_arguments(lib, kw):
+    assert _commit_far(lib, **kw) == B.EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(rows=65), dict(m=65)])
+def test_commit_far_rejects_unsupported_sizes(lib, kw):
+    assert _commit_far(lib, **kw) == B.EUNSUPPORTED
+
+
 def test_workspace_queries(lib):
     assert B.chunk_workspace_bytes(0, 1, 1, 64, 16, 0) == 0
     assert B.gated_workspace_bytes(1, 5, 2, 64, 8) == 0

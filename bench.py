@@ -169,6 +169,31 @@ def bench_others(args, torch, B, gen, acct):
                      "cache": "hot (inputs resident, reused)"}
         del t, out, ws
         torch.cuda.empty_cache()
+    for name, rows in (("decode_far_m32", 1), ("chunk64_far_m32", 64)):
+        # the decode shapes with a far field of 32 landmarks per head in every group (full
+        # rings, so every row evicts); the near-only call on the same inputs is timed beside it
+        inp = gen.make_chunk(rows, 8, 4, 128, 4096, 4, gen.decode().meta.copy(), seed=7)
+        inp.meta[:, 2] = 1000
+        far = gen.make_far(inp, 32, seed=8)
+        t = chunk_tensors(inp, torch, dev)
+        f = gen.to_device(far, dev)
+        out = torch.empty((inp.rows, inp.nh, inp.d), dtype=torch.float32, device=dev)
+        ws = B.Workspace(dev)
+        ws.get(B.chunk_far_workspace_bytes(inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns, 32))
+
+        def far_call(i):
+            B.attn_window_chunk_far(t["ring_k"], t["ring_v"], t["meta"], t["sink_k"],
+                                    t["sink_v"], t["q"], t["chunk_k"], t["chunk_v"],
+                                    f["k_tilde"], f["q_tilde"], f["mu"], f["mz"], f["t_hat"],
+                                    inp.scale, out=out, workspace=ws)
+        ms, _, _ = time_calls(torch, far_call, 1, 20, 3)
+        near_ms, _, _ = time_calls(torch, lambda i: run_chunk(B, t, inp.scale, out, ws), 1, 20, 3)
+        res[name] = {"ms": round(ms, 5), "near_only_ms": round(near_ms, 5),
+                     "kv_gbs": round(acct.unique_kv_bytes(inp) / ms / 1e6, 2),
+                     "rows_per_s": round(inp.rows / ms * 1e3, 1), "landmarks": 32,
+                     "cache": "hot (inputs resident, reused)"}
+        del t, f, out, ws
+        torch.cuda.empty_cache()
     g = gen.gated()
     t = gen.to_device(g, dev)
     out = torch.empty((g.rows, g.nh, g.hd), dtype=torch.float32, device=dev)

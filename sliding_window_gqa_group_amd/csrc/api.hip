@@ -381,8 +381,9 @@ int attn_window_chunk_far(const float* ring_k, const float* ring_v, const uint32
     f.far_slot = pl.nsplit;
     f.dpad = pl.dpad;
     f.scale = scale;
-    if (launch_far_evict(f, st) != hipSuccess || launch_far_part(f, st) != hipSuccess)
-        return WINATTN_ELAUNCH;
+    // A one-row call scores its own eviction inside the far-part kernel.
+    if (rows > 1 && launch_far_evict(f, st) != hipSuccess) return WINATTN_ELAUNCH;
+    if (launch_far_part(f, rows > 1 ? 0 : 1, st) != hipSuccess) return WINATTN_ELAUNCH;
 
     AttnParams p{};
     p.ring_k = ring_k;

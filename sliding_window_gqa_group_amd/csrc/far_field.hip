@@ -15,8 +15,9 @@
 //   far_evict_kernel   one wave per (head, landmark), lane = chunk row: eviction scores, far
 //                      max, rescale of the old state and the prefix far mass, into workspace
 //                      (f64);
-//   far_part_kernel    one wave per (row, head), lane = landmark: landmark scores, weights
-//                      through mu, gains, far mass and numerator -> the far partial;
+//   far_part_kernel    one workgroup per (row, head): landmark scores, weights through mu,
+//                      gains, far mass and numerator -> the far partial (a one-row call
+//                      scores its own eviction here instead of in far_evict_kernel);
 //   far_commit_kernel  one wave per (head, landmark), lane = chunk row: the far state after
 //                      the chunk (before the ring commit overwrites the evicted rows).
 // A chunk with a far field has at most 64 rows and at most 64 landmarks (one wave's lanes; the
@@ -151,83 +152,272 @@ __global__ __launch_bounds__(64) void far_evict_kernel(const FarParams p) {
     }
 }
 
-// One wave per (row i, head gh); lane a is landmark a for the scores and weights, lane j is
-// chunk row j for the evicted rows' weights, then lane c owns float4 column c of the numerator.
-__global__ __launch_bounds__(64) void far_part_kernel(const FarParams p) {
-    __shared__ double s_ea[64], s_gain[64], s_gn[64], s_cf[64];
+// Far-part modes: where a row's per-landmark far max, rescale, mass and eviction weights come
+// from.
+enum FarMode {
+    kFarFromWorkspace = 0,   // the chunk's evictions, scored by far_evict_kernel
+    kFarFusedOneRow = 1,     // one-row call: the row's own eviction is scored here
+    kFarCurrent = 2,         // no evictions in the call: the state in mz is current
+};
+
+// The far partial of one (row i, head gh): a workgroup of 256 threads. Every operand is loaded
+// in a few wide rounds (mu and t_hat are prefetched at the start), dot products and landmark
+// sums are split across lanes, and the per-landmark scalars live in wave 0, lane b.
+// DP = padded head width (64, 128, 256): the partial row has DP floats.
+template <int DP, int MODE>
+__global__ __launch_bounds__(256) void far_part_kernel(const FarParams p) {
+    constexpr int NT = 256;
+    constexpr int D4P = DP / 4;             // float4 columns of a partial row
+    constexpr int S = NT / D4P;             // column slices in the numerator phase
+    constexpr int TH = (kFarMaxLandmarks + S - 1) / S;   // landmarks per slice, at most
+    constexpr int EV = (kFarMaxRows + S - 1) / S;        // evicted rows per slice, at most
+    constexpr int MU = kFarMaxLandmarks * kFarMaxLandmarks / NT;   // mu entries per thread
+    __shared__ double s_fl[64], s_fe[64], s_ea[64], s_gn[64], s_gain[64];
+    __shared__ double s_up[NT], s_cfp[NT];
+    __shared__ double s_acc[NT * 4];
+    __shared__ int s_have;
+    __shared__ float s_pm, s_F;
+
+    const int t = threadIdx.x, lane = t & 63;
     const int i = blockIdx.x / p.nh, gh = blockIdx.x % p.nh;
-    const int g = gh / p.hpg, lane = threadIdx.x;
-    const GroupState s = group_state(p, g);
-    const int m = p.m, d4 = p.d / 4;
+    const int g = gh / p.hpg, m = p.m, d4 = p.d / 4;
+    const GroupState gs = group_state(p, g);
+    const int j0 = MODE == kFarCurrent ? 0x7fffffff : gs.j0;
 
     // This (row, head)'s slot in the partial buffer.
     const int qi = i * p.hpg + gh % p.hpg;   // query index within the group, row-major
-    const int blk = g * p.nqblocks + qi / p.qb, j = qi % p.qb;
-    const size_t at = ((size_t)blk * p.slot_stride + p.far_slot) * p.qb + j;
-    float* acc_out = p.pacc + at * p.dpad;
+    const int blk = g * p.nqblocks + qi / p.qb;
+    const size_t at = ((size_t)blk * p.slot_stride + p.far_slot) * p.qb + qi % p.qb;
+    float4* acc_out = reinterpret_cast<float4*>(p.pacc + at * DP);
 
-    const long long farl = (long long)s.far0 + (i >= s.j0 ? i - s.j0 + 1 : 0);
-    float pm = -INFINITY;
-    double far_den = 0.0;
-    bool have = false;
-    if (farl > 0) {
-        const size_t lb = (size_t)gh * m + lane;
-        // landmark scores of the row's query
-        double fl = -INFINITY;
-        if (lane < m)
-            fl = (double)p.scale * dot_f64(p.q + ((size_t)i * p.nh + gh) * p.d,
-                                           p.k_tilde + ((size_t)g * m + lane) * p.d, p.d);
-        const double f = far_wave_max(fl);
-        s_ea[lane] = lane < m ? exp(fl - f) : 0.0;
-        // The far partial's max, rounded to f32 as the merge reads it; the gains are taken
-        // against that rounded value, so the merge's rescale of this partial is exact.
-        const double Mb = lane < m ? f + p.ev_mx[lb] : -INFINITY;
-        pm = (float)(far_wave_max(Mb) * kLog2eD);
-        const double M = (double)pm / kLog2eD;
-        __syncthreads();
-        // weight of landmark b (lane b): sum_a exp(fl_a - f) mu[a][b]
-        double wb = 0.0;
-        if (lane < m)
-            for (int a = 0; a < m; ++a)
-                wb = fma(s_ea[a], (double)p.mu[((size_t)gh * m + a) * m + lane], wb);
-        const double gain = lane < m ? wb * exp(Mb - M) : 0.0;
-        far_den = far_wave_sum(lane < m ? gain * p.ev_z[lb * p.rows + i] : 0.0);
-        have = far_den >= 0.0 && pm > -INFINITY;
-        s_gain[lane] = gain;
-        s_gn[lane] = lane < m ? gain * p.ev_r[lb] : 0.0;
-        __syncthreads();
-        // weight of each evicted row j0 <= jj <= i: sum_b gain_b e_b(jj) (lane jj)
-        double cf = 0.0;
-        if (lane <= i && lane >= s.j0)
-            for (int bb = 0; bb < m; ++bb)
-                cf = fma(s_gain[bb], p.ev_e[((size_t)gh * m + bb) * p.rows + lane], cf);
-        s_cf[lane] = cf;
-        __syncthreads();
-    }
-    if (!have) {   // empty field, or a negative far mass: the far part is dropped
-        for (int c = lane; c < p.dpad / 4; c += 64)
-            reinterpret_cast<float4*>(acc_out)[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (lane == 0) {
+    const long long farl = (long long)gs.far0 + (i >= j0 ? i - j0 + 1 : 0);
+    if (farl <= 0) {   // empty far field: an empty partial
+        if (t < D4P) acc_out[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t == 0) {
             p.pm[at] = -INFINITY;
             p.pl[at] = 0.0f;
         }
         return;
     }
-    for (int c = lane; c < p.dpad / 4; c += 64) {
-        Acc4 a{0.0, 0.0, 0.0, 0.0};
-        if (c < d4) {
-            for (int bb = 0; bb < m; ++bb)
-                acc4_fma(a, s_gn[bb],
-                         reinterpret_cast<const float4*>(p.t_hat + ((size_t)gh * m + bb) * p.d)[c]);
-            for (int jj = s.j0; jj <= i; ++jj)
-                acc4_fma(a, s_cf[jj], reinterpret_cast<const float4*>(evicted_row(p, s, g, jj, true))[c]);
-        }
-        reinterpret_cast<float4*>(acc_out)[c] =
-            make_float4((float)a.x, (float)a.y, (float)a.z, (float)a.w);
+
+    int mp = 4;
+    while (mp < m) mp <<= 1;
+    const int tpl = NT / mp;   // threads per landmark in the dot phase (4 .. 64)
+
+    // Every operand is loaded up front from an address clamped into range, so that no load
+    // sits behind a branch whose join would wait for it; the predicates apply where the values
+    // are used. This thread's mu entries: landmark b = t % mp, rows a = t / mp + k tpl; t_hat
+    // rows: column c = t % D4P, landmarks b = t / D4P + k S.
+    const int bm = t % mp, am = t / mp;
+    const int bmc = bm < m ? bm : m - 1;
+    float mu_r[MU];
+#pragma unroll
+    for (int k = 0; k < MU; ++k) {
+        const int a = min(am + k * tpl, m - 1);
+        mu_r[k] = p.mu[((size_t)gh * m + a) * m + bmc];
     }
-    if (lane == 0) {
-        p.pm[at] = pm;   // the merge works in the log2 domain
-        p.pl[at] = (float)far_den;
+    const int cc = t % D4P, sl = t / D4P;
+    const int ccc = cc < d4 ? cc : d4 - 1;
+    float4 th_r[TH];
+#pragma unroll
+    for (int k = 0; k < TH; ++k) {
+        const int b = min(sl + k * S, m - 1);
+        th_r[k] = reinterpret_cast<const float4*>(p.t_hat + ((size_t)gh * m + b) * p.d)[ccc];
+    }
+    // Per-landmark state for wave 0, lane b (lanes b >= m load landmark m - 1 and ignore it).
+    const size_t lb = (size_t)gh * m + (t < m ? t : m - 1);
+    double MX, R = 1.0, Z, m_old = 0.0, mass = 0.0;
+    if constexpr (MODE == kFarFromWorkspace) {
+        MX = p.ev_mx[lb];
+        R = p.ev_r[lb];
+        Z = p.ev_z[lb * p.rows + i];
+    } else {
+        m_old = p.mz[(size_t)gh * 2 * m + (lb - (size_t)gh * m)];
+        mass = p.mz[(size_t)gh * 2 * m + m + (lb - (size_t)gh * m)];
+        MX = m_old;
+        Z = mass;
+    }
+    const bool evicts1 = MODE == kFarFusedOneRow && j0 == 0;   // the one row evicts an entry
+    // The one-row call's evicted value row, column cc (slice 0 uses it).
+    const float* v1row = evicts1 ? evicted_row(p, gs, g, 0, true) : p.ring_v + (size_t)g * p.w * p.d;
+    const float4 v_ev1 = reinterpret_cast<const float4*>(v1row)[ccc];
+
+    // Landmark scores fl_a = scale <q, k_tilde_a> (and for the fused one-row mode the eviction
+    // scores fe_a = scale <q_tilde_a, K_ev>): tpl consecutive lanes per landmark.
+    {
+        const int a = t / tpl, sp = t % tpl;
+        double v = 0.0, v2 = 0.0;
+        if (a < m) {
+            const float4* qv = reinterpret_cast<const float4*>(p.q + ((size_t)i * p.nh + gh) * p.d);
+            const float4* kt = reinterpret_cast<const float4*>(p.k_tilde + ((size_t)g * m + a) * p.d);
+            for (int c = sp; c < d4; c += tpl) {
+                const float4 x = qv[c], y = kt[c];
+                v = fma((double)x.x, (double)y.x, v);
+                v = fma((double)x.y, (double)y.y, v);
+                v = fma((double)x.z, (double)y.z, v);
+                v = fma((double)x.w, (double)y.w, v);
+            }
+            if (evicts1) {
+                const float4* qt = reinterpret_cast<const float4*>(p.q_tilde + ((size_t)gh * m + a) * p.d);
+                const float4* kv = reinterpret_cast<const float4*>(evicted_row(p, gs, g, 0, false));
+                for (int c = sp; c < d4; c += tpl) {
+                    const float4 x = qt[c], y = kv[c];
+                    v2 = fma((double)x.x, (double)y.x, v2);
+                    v2 = fma((double)x.y, (double)y.y, v2);
+                    v2 = fma((double)x.z, (double)y.z, v2);
+                    v2 = fma((double)x.w, (double)y.w, v2);
+                }
+            }
+        }
+        for (int k = tpl >> 1; k >= 1; k >>= 1) {
+            v += __shfl_xor(v, k);
+            v2 += __shfl_xor(v2, k);
+        }
+        if (sp == 0 && a < m) {
+            s_fl[a] = (double)p.scale * v;
+            s_fe[a] = (double)p.scale * v2;
+        }
+    }
+    __syncthreads();
+
+    // Wave 0: f = max fl, exp(fl_a - f); the fused mode's eviction of landmark b.
+    double f = 0.0, E = 0.0;
+    if (t < 64) {
+        const double fl = lane < m ? s_fl[lane] : -INFINITY;
+        f = far_wave_max(fl);
+        s_ea[lane] = lane < m ? exp(fl - f) : 0.0;
+        if (evicts1 && lane < m) {
+            const double fe = s_fe[lane];
+            MX = fmax(m_old, fe);
+            R = MX == m_old ? 1.0 : exp(m_old - MX);
+            E = exp(fe - MX);
+            Z = mass * R + E;
+        }
+    }
+    __syncthreads();
+
+    // Weights u_b = sum_a exp(fl_a - f) mu[a][b]: partial sums over this thread's rows a.
+    {
+        double u = 0.0;
+#pragma unroll
+        for (int k = 0; k < MU; ++k) {
+            const int a = am + k * tpl;
+            if (a < m) u = fma(s_ea[a], (double)mu_r[k], u);
+        }
+        s_up[t] = u;   // index am * mp + bm == t
+    }
+    __syncthreads();
+
+    // Wave 0, lane b: u_b, the optional clamp, the gains against the partial's rounded max,
+    // the far mass F, and (fused mode) the weight of the row's own eviction.
+    if (t < 64) {
+        double u = 0.0;
+        if (lane < m)
+            for (int a = 0; a < tpl; ++a) u += s_up[a * mp + lane];
+        if (p.rect && u < 0.0) u = 0.0;
+        const double Mb = lane < m ? f + MX : -INFINITY;   // lanes >= m hold landmark m - 1
+        const float pm = (float)(far_wave_max(Mb) * kLog2eD);
+        const double Mr = (double)pm / kLog2eD;
+        const double gain = lane < m ? u * exp(Mb - Mr) : 0.0;
+        const double F = far_wave_sum(lane < m ? gain * Z : 0.0);
+        s_gain[lane] = gain;
+        s_gn[lane] = lane < m ? gain * R : 0.0;
+        if (MODE == kFarFusedOneRow) {
+            const double cf0 = far_wave_sum(lane < m ? gain * E : 0.0);
+            if (lane == 0) s_cfp[0] = cf0;
+        }
+        if (lane == 0) {
+            s_have = F >= 0.0 && pm > -INFINITY;
+            s_pm = pm;
+            s_F = (float)F;
+        }
+    }
+    __syncthreads();
+    if (!s_have) {   // negative far mass: the far part is dropped
+        if (t < D4P) acc_out[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t == 0) {
+            p.pm[at] = -INFINITY;
+            p.pl[at] = 0.0f;
+        }
+        return;
+    }
+
+    // Weights of the evicted rows j0 <= j <= i: cf_j = sum_b gain_b e_b(j), four partial sums
+    // per row (wave w takes landmarks b = w mod 4).
+    const int jlo = j0 > 0 ? j0 : 0;
+    if constexpr (MODE == kFarFromWorkspace) {
+        const int j = lane, w = t >> 6;
+        const int jc = min(j, p.rows - 1);
+        double e_r[kFarMaxLandmarks / 4];
+#pragma unroll
+        for (int k = 0; k < kFarMaxLandmarks / 4; ++k)
+            e_r[k] = p.ev_e[((size_t)gh * m + min(w + 4 * k, m - 1)) * p.rows + jc];
+        double cf = 0.0;
+#pragma unroll
+        for (int k = 0; k < kFarMaxLandmarks / 4; ++k)
+            if (w + 4 * k < m) cf = fma(s_gain[w + 4 * k], e_r[k], cf);
+        s_cfp[t] = j >= jlo && j <= i ? cf : 0.0;   // index w * 64 + j
+        __syncthreads();
+    }
+
+    // Numerator, column cc, slice sl: landmarks b = sl + k S and evicted rows j = jlo + sl + k S.
+    double ax = 0.0, ay = 0.0, az = 0.0, aw = 0.0;
+#pragma unroll
+    for (int k = 0; k < TH; ++k) {
+        const int b = sl + k * S;
+        const double gn = b < m ? s_gn[b] : 0.0;
+        ax = fma(gn, (double)th_r[k].x, ax);
+        ay = fma(gn, (double)th_r[k].y, ay);
+        az = fma(gn, (double)th_r[k].z, az);
+        aw = fma(gn, (double)th_r[k].w, aw);
+    }
+    if (MODE == kFarFusedOneRow && evicts1 && sl == 0) {
+        const double cf = s_cfp[0];
+        ax = fma(cf, (double)v_ev1.x, ax);
+        ay = fma(cf, (double)v_ev1.y, ay);
+        az = fma(cf, (double)v_ev1.z, az);
+        aw = fma(cf, (double)v_ev1.w, aw);
+    }
+    if (MODE == kFarFromWorkspace && i >= jlo) {
+        // rows past i load row i and are dropped at use
+        float4 vr[EV];
+#pragma unroll
+        for (int k = 0; k < EV; ++k) {
+            const int j = min(jlo + sl + k * S, i);
+            vr[k] = reinterpret_cast<const float4*>(evicted_row(p, gs, g, j, true))[ccc];
+        }
+#pragma unroll
+        for (int k = 0; k < EV; ++k) {
+            const int j = jlo + sl + k * S;
+            if (j <= i) {
+                const double cf = s_cfp[j] + s_cfp[64 + j] + s_cfp[128 + j] + s_cfp[192 + j];
+                ax = fma(cf, (double)vr[k].x, ax);
+                ay = fma(cf, (double)vr[k].y, ay);
+                az = fma(cf, (double)vr[k].z, az);
+                aw = fma(cf, (double)vr[k].w, aw);
+            }
+        }
+    }
+    s_acc[4 * t + 0] = ax;
+    s_acc[4 * t + 1] = ay;
+    s_acc[4 * t + 2] = az;
+    s_acc[4 * t + 3] = aw;
+    __syncthreads();
+    if (t < D4P) {
+        double x = 0.0, y = 0.0, z = 0.0, w = 0.0;
+        for (int k = 0; k < S; ++k) {
+            const int u = 4 * (k * D4P + t);
+            x += s_acc[u];
+            y += s_acc[u + 1];
+            z += s_acc[u + 2];
+            w += s_acc[u + 3];
+        }
+        acc_out[t] = t < d4 ? make_float4((float)x, (float)y, (float)z, (float)w)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (t == 0) {
+        p.pm[at] = s_pm;   // the merge works in the log2 domain
+        p.pl[at] = s_F;
     }
 }
 
@@ -265,8 +455,24 @@ hipError_t launch_far_evict(const FarParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_far_part(const FarParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL(far_part_kernel, dim3(p.rows * p.nh), dim3(64), 0, stream, p);
+template <int DP>
+static void launch_far_part_dp(const FarParams& p, int mode, hipStream_t stream) {
+    const dim3 grid(p.rows * p.nh), block(256);
+    if (mode == kFarFromWorkspace)
+        hipLaunchKernelGGL((far_part_kernel<DP, kFarFromWorkspace>), grid, block, 0, stream, p);
+    else if (mode == kFarFusedOneRow)
+        hipLaunchKernelGGL((far_part_kernel<DP, kFarFusedOneRow>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((far_part_kernel<DP, kFarCurrent>), grid, block, 0, stream, p);
+}
+
+hipError_t launch_far_part(const FarParams& p, int mode, hipStream_t stream) {
+    if (p.dpad == 64)
+        launch_far_part_dp<64>(p, mode, stream);
+    else if (p.dpad == 128)
+        launch_far_part_dp<128>(p, mode, stream);
+    else
+        launch_far_part_dp<256>(p, mode, stream);
     return hipGetLastError();
 }
 

@@ -85,12 +85,15 @@ struct FarParams {
     float* pl;
     int rows, ng, hpg, nh, d, w, m;
     int qb, nqblocks, slot_stride, far_slot, dpad;
+    int rect;               // clamp the landmark weights at zero (gated one-row form)
     float scale;
 };
 // Far field of a chunk (rows <= 64, m <= 64): eviction scores per (head, landmark), then the
 // far partial of every (row, head) into the partial buffer, merged by the merge launch.
 hipError_t launch_far_evict(const FarParams& p, hipStream_t stream);
-hipError_t launch_far_part(const FarParams& p, hipStream_t stream);
+// mode 0: evictions scored by launch_far_evict; 1: a one-row call that scores its own
+// eviction; 2: no evictions in the call (the state is current).
+hipError_t launch_far_part(const FarParams& p, int mode, hipStream_t stream);
 // Far state after a chunk; runs before the ring commit, which overwrites the evicted rows.
 hipError_t launch_far_commit(const FarParams& p, hipStream_t stream);
 constexpr int kFarMaxRows = 64;

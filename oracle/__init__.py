@@ -64,9 +64,13 @@ def load_library(path: str):
                                             i, i, i, i, i, i, i, f]
     lib.oracle_window_commit_far.argtypes = [_f32p, _f32p, _u32p, _f32p, _f32p, _f32p, _f32p,
                                              _f32p, i, i, i, i, i, i, f]
+    lib.oracle_window_gated_far.argtypes = [_f32p, _f32p, _f32p, _u32p, _f32p, _f32p, _f32p,
+                                            _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
+                                            i, i, i, i, i, i, f, i]
     for name in ("oracle_window_chunk", "oracle_window_chunk_select",
                  "oracle_window_chunk_weights", "oracle_window_gated", "oracle_meta_ok",
-                 "oracle_window_commit", "oracle_window_chunk_far", "oracle_window_commit_far"):
+                 "oracle_window_commit", "oracle_window_chunk_far", "oracle_window_commit_far",
+                 "oracle_window_gated_far"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -218,6 +222,30 @@ def window_commit_far(inp, far):
     if rc != 0:
         raise ValueError(f"oracle_window_commit_far rejected its arguments (rc={rc})")
     return rk, rv, meta, mz, th
+
+
+def window_gated_far(inp) -> np.ndarray:
+    """z [nh][hd] of the gated one-row call with the far field, for a GatedFarInputs-like
+    object (q [nh][hd], ring_k/ring_v [nk][w][hd], meta [nk][4], sinks [nk][ns][hd] or empty,
+    k_tilde [nk][m][hd], mu [nh][m][m], mz [nh][2m], t_hat [nh][m][hd], gate and gate_scale
+    [nh*hd], scale, rect)."""
+    lib = _load()
+    nk, w, hd = inp.ring_k.shape
+    nh = inp.q.shape[0]
+    ns = inp.sink_k.shape[1] if inp.sink_k is not None else 0
+    m = inp.mu.shape[1]
+    keep = [_f32(a) for a in (inp.q, inp.ring_k, inp.ring_v)]
+    meta = np.ascontiguousarray(inp.meta, dtype=np.uint32)
+    sk = _f32(inp.sink_k) if ns else (None, None)
+    sv = _f32(inp.sink_v) if ns else (None, None)
+    rest = [_f32(a) for a in (inp.k_tilde, inp.mu, inp.mz, inp.t_hat, inp.gate, inp.gate_scale)]
+    out = np.zeros((nh, hd), dtype=np.float32)
+    rc = lib.oracle_window_gated_far(*[p for _, p in keep], meta.ctypes.data_as(_u32p), sk[1],
+                                     sv[1], *[p for _, p in rest], out.ctypes.data_as(_f32p),
+                                     nh, nk, hd, w, ns, m, inp.scale, int(inp.rect))
+    if rc != 0:
+        raise ValueError(f"oracle_window_gated_far rejected its arguments (rc={rc})")
+    return out
 
 
 def meta_ok(meta, ng: int, w: int) -> bool:

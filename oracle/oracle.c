@@ -12,10 +12,14 @@
  *  - o1c page ("A sealed layer's attention for a chunk of rows, on Metal", crate cortiq-engine
  *    0.8.79): the layout header comment; `wgf` (per-group window override); `o1c_score` (a row's
  *    window over the ring then the chunk's rows up to its own); `o1c_max`, `o1c_soft`, `o1c_sum`,
- *    `o1c_add` (max, exp, 1/sum, value sum). The far-field landmark terms are taken with zero
- *    landmarks, so the far mass and far numerators vanish and the near softmax is the result.
+ *    `o1c_add` (max, exp, 1/sum, value sum). oracle_window_chunk takes the far-field landmark
+ *    terms with zero landmarks, so the far mass and far numerators vanish and the near softmax
+ *    is its result.
  *  - dory page ("Dory's token path", crate cortiq-engine 0.8.57): `dory_prep` (rotation, unit
- *    heads, query scale, ring write), `low_key`, `dory_score`, `dory_soft`, `dory_sum`, `dory_gate`.
+ *    heads, query scale, ring write), `low_key`, `dory_score`, `dory_soft`, `dory_sum`, `dory_gate`;
+ *    the one-row far-field form `dory_os` .. `dory_ogate` (oracle_window_gated_far).
+ *  - o1c far field and commits (oracle_window_commit, oracle_window_chunk_far,
+ *    oracle_window_commit_far): see the comments at those functions.
  *
  * Readings where the pages leave a step open are listed in the design notes; the ones that
  * matter here: a window of wg keys ends at and includes the row itself; the RoPE table is an
@@ -569,6 +573,117 @@ int oracle_window_commit_far(float *ring_k, float *ring_v, uint32_t *meta, const
     }
     free(e); free(z); free(acc);
     return oracle_window_commit(ring_k, ring_v, meta, chunk_k, chunk_v, rows, ng, d, w);
+}
+
+/*
+ * The gated one-row call with the far field (dory page: `dory_os`, `dory_ol`, `dory_omax`,
+ * `dory_ofar`, `dory_osoft`, `dory_osum`, `dory_ogate`). The row's own key is already in the
+ * ring, so query head gh (KV head kh = gh / hpg) attends over the ns sinks of kh and ring slots
+ * 0 .. len-1 of kh (len = meta[kh] field 0; storage order does not matter), with scores
+ * s = scale <q, K>. When the far count (meta field 2) is non-zero, the landmark part joins:
+ * fl_a = scale <q, k_tilde[kh][a]>, f = max fl, u_b = sum_a exp(fl_a - f) mu[gh][a][b] (clamped
+ * at 0 when rect is non-zero), c = max(max s, f + mx_b) with mx_b = mz[gh][b], gains
+ * G_b = u_b exp(f + mx_b - c), far mass F = sum_b G_b mz[gh][m + b]; the far terms are kept when
+ * F >= 0. Then
+ *   out = (sum exp(s - c) V + sum_b G_b t_hat_b) / max(sum exp(s - c) + F, 1e-30)
+ *         / (1 + exp(-gate * gate_scale)).
+ * Layouts: q [nh][hd]; ring_k, ring_v [nk][w][hd]; sink_k, sink_v [nk][ns][hd]; meta [nk][4];
+ * k_tilde [nk][m][hd]; mu [nh][m][m]; mz [nh][2m]; t_hat [nh][m][hd]; gate, gate_scale
+ * [nh * hd]; out [nh][hd].
+ */
+int oracle_window_gated_far(const float *q, const float *ring_k, const float *ring_v,
+                            const uint32_t *meta, const float *sink_k, const float *sink_v,
+                            const float *k_tilde, const float *mu, const float *mz,
+                            const float *t_hat, const float *gate, const float *gate_scale,
+                            float *out, int nh, int nk, int hd, int w, int ns, int m, float scale,
+                            int rect) {
+    if (!q || !ring_k || !ring_v || !meta || !k_tilde || !mu || !mz || !t_hat || !gate ||
+        !gate_scale || !out)
+        return -1;
+    if (nh < 1 || nk < 1 || nh % nk != 0 || hd < 1 || w < 1 || ns < 0 || m < 1) return -1;
+    if (ns > 0 && (!sink_k || !sink_v)) return -1;
+    for (int kh = 0; kh < nk; ++kh)
+        if (meta[4 * kh] > (uint32_t)w) return -1;
+    const int hpg = nh / nk;
+    const double sc = (double)scale;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int gh = 0; gh < nh; ++gh) {
+        const int kh = gh / hpg;
+        const int len = (int)meta[4 * kh], far = (int)meta[4 * kh + 2];
+        const int n = ns + len;
+        double *s = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        double *acc = malloc(sizeof(double) * (size_t)hd);
+        double *fl = malloc(sizeof(double) * (size_t)m);
+        double *u = malloc(sizeof(double) * (size_t)m);
+        double *gb = malloc(sizeof(double) * (size_t)m);
+        if (!s || !acc || !fl || !u || !gb) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+            const float *qv = q + (size_t)gh * hd;
+            double cmax = -INFINITY;
+            for (int j = 0; j < n; ++j) {
+                const float *k = j < ns ? sink_k + ((size_t)kh * ns + j) * hd
+                                        : ring_k + ((size_t)kh * w + (j - ns)) * hd;
+                double dot = 0.0;
+                for (int e = 0; e < hd; ++e) dot += (double)qv[e] * (double)k[e];
+                s[j] = sc * dot;
+                if (s[j] > cmax) cmax = s[j];
+            }
+            double far_den = 0.0;
+            int have = 0;
+            if (far > 0) {
+                double f = -INFINITY;
+                for (int a = 0; a < m; ++a) {
+                    const float *kt = k_tilde + ((size_t)kh * m + a) * hd;
+                    double dot = 0.0;
+                    for (int e = 0; e < hd; ++e) dot += (double)qv[e] * (double)kt[e];
+                    fl[a] = sc * dot;
+                    if (fl[a] > f) f = fl[a];
+                }
+                for (int b = 0; b < m; ++b) u[b] = 0.0;
+                for (int a = 0; a < m; ++a) {
+                    const double ea = exp(fl[a] - f);
+                    for (int b = 0; b < m; ++b) u[b] += ea * (double)mu[((size_t)gh * m + a) * m + b];
+                }
+                if (rect)
+                    for (int b = 0; b < m; ++b) if (u[b] < 0.0) u[b] = 0.0;
+                const float *mzh = mz + (size_t)gh * 2 * m;
+                for (int b = 0; b < m; ++b)
+                    if (f + (double)mzh[b] > cmax) cmax = f + (double)mzh[b];
+                for (int b = 0; b < m; ++b) {
+                    gb[b] = u[b] * exp(f + (double)mzh[b] - cmax);
+                    far_den += gb[b] * (double)mzh[m + b];
+                }
+                have = far_den >= 0.0;   /* a negative far mass drops the far terms */
+                if (!have) far_den = 0.0;
+            }
+            double den = far_den;
+            for (int e = 0; e < hd; ++e) acc[e] = 0.0;
+            for (int j = 0; j < n; ++j) {
+                const float *v = j < ns ? sink_v + ((size_t)kh * ns + j) * hd
+                                        : ring_v + ((size_t)kh * w + (j - ns)) * hd;
+                const double p = exp(s[j] - cmax);
+                den += p;
+                for (int e = 0; e < hd; ++e) acc[e] += p * (double)v[e];
+            }
+            if (have)
+                for (int b = 0; b < m; ++b) {
+                    const float *th = t_hat + ((size_t)gh * m + b) * hd;
+                    for (int e = 0; e < hd; ++e) acc[e] += gb[b] * (double)th[e];
+                }
+            if (den < 1e-30) den = 1e-30;
+            float *z = out + (size_t)gh * hd;
+            for (int e = 0; e < hd; ++e) {
+                const size_t ge = (size_t)gh * hd + e;
+                const double gs = (double)gate[ge] * (double)gate_scale[ge];
+                z[e] = (float)(acc[e] / den / (1.0 + exp(-gs)));
+            }
+        }
+        free(s); free(acc); free(fl); free(u); free(gb);
+    }
+    return bad ? -1 : 0;
 }
 
 /* Host-side meta validation with the same rules the oracle enforces (1 = valid). */

@@ -227,6 +227,94 @@ def make_far(inp: ChunkInputs, m: int, seed: int, mu_kind: str = "positive") -> 
     return FarState(m, k_tilde, q_tilde, mu, mz, np.ascontiguousarray(t_hat, dtype=np.float32))
 
 
+@dataclass
+class GatedFarInputs:
+    """The gated one-row call with the far field: one query per head, the ring after the row's
+    own push, sinks, and a far state per query head."""
+    q: np.ndarray            # [nh][hd]
+    ring_k: np.ndarray       # [nk][w][hd]
+    ring_v: np.ndarray       # [nk][w][hd]
+    meta: np.ndarray         # [nk][4] u32: len, head (unused), far count, window (unused)
+    sink_k: np.ndarray       # [nk][ns][hd]
+    sink_v: np.ndarray
+    k_tilde: np.ndarray      # [nk][m][hd]
+    mu: np.ndarray           # [nh][m][m]
+    mz: np.ndarray           # [nh][2m]
+    t_hat: np.ndarray        # [nh][m][hd]
+    gate: np.ndarray         # [nh*hd]
+    gate_scale: np.ndarray   # [nh*hd]
+    scale: float
+    rect: int
+
+    @property
+    def nh(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def nk(self) -> int:
+        return self.ring_k.shape[0]
+
+    @property
+    def hd(self) -> int:
+        return self.q.shape[1]
+
+    @property
+    def w(self) -> int:
+        return self.ring_k.shape[1]
+
+    @property
+    def ns(self) -> int:
+        return self.sink_k.shape[1]
+
+    @property
+    def m(self) -> int:
+        return self.mu.shape[1]
+
+
+def _unit_rows(rng, shape) -> np.ndarray:
+    x = rng.standard_normal(shape, dtype=np.float32).astype(np.float64)
+    x /= np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x.astype(np.float32)
+
+
+def make_gated_far(nh: int, nk: int, hd: int, w: int, ns: int, m: int, meta, seed: int,
+                   scale: float, rect: int = 0, mu_kind: str = "positive") -> GatedFarInputs:
+    """Seeded inputs of the gated one-row far call, shaped like the gated path's prepped heads:
+    ring, sink and landmark keys are unit vectors, the query is a unit vector times U(0.5, 1.5)
+    per component (the learned query scale), values N(0,1); mu U(0,1) ("positive") or N(0,1)
+    ("signed"); a head whose KV head has a far count gets far maxima N(0,1) * scale, masses
+    U(0.5, 4) and numerators N(0,1) times the mass, the others the empty field (-inf, 0, 0);
+    gate and gate_scale N(0,1). `meta` lists (len, head, far count, window) per KV head."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    meta = np.asarray(meta, dtype=np.uint32).reshape(nk, 4)
+    q = _unit_rows(rng, (nh, hd)) * rng.uniform(0.5, 1.5, (nh, hd)).astype(np.float32)
+    ring_k = _unit_rows(rng, (nk, w, hd))
+    ring_v = rng.standard_normal((nk, w, hd), dtype=np.float32)
+    sink_k = _unit_rows(rng, (nk, ns, hd)) if ns else np.zeros((nk, 0, hd), np.float32)
+    sink_v = rng.standard_normal((nk, ns, hd), dtype=np.float32)
+    k_tilde = _unit_rows(rng, (nk, m, hd))
+    if mu_kind == "signed":
+        mu = rng.standard_normal((nh, m, m), dtype=np.float32)
+    else:
+        mu = rng.random((nh, m, m), dtype=np.float32)
+    mz = np.zeros((nh, 2 * m), dtype=np.float32)
+    mz[:, :m] = rng.standard_normal((nh, m), dtype=np.float32) * np.float32(scale)
+    mz[:, m:] = rng.uniform(0.5, 4.0, (nh, m)).astype(np.float32)
+    t_hat = rng.standard_normal((nh, m, hd), dtype=np.float32) * mz[:, m:, None]
+    gate = rng.standard_normal(nh * hd, dtype=np.float32)
+    gate_scale = rng.standard_normal(nh * hd, dtype=np.float32)
+    hpg = nh // nk
+    for kh in range(nk):
+        if int(meta[kh, 2]) == 0:
+            sl = slice(kh * hpg, (kh + 1) * hpg)
+            mz[sl, :m] = -np.inf
+            mz[sl, m:] = 0.0
+            t_hat[sl] = 0.0
+    return GatedFarInputs(q.astype(np.float32), ring_k, ring_v, meta, sink_k, sink_v, k_tilde,
+                          mu, mz, np.ascontiguousarray(t_hat, dtype=np.float32), gate,
+                          gate_scale, float(np.float32(scale)), int(rect))
+
+
 def to_device(inp, device="cuda"):
     """The arrays of a ChunkInputs / GatedInputs as contiguous torch tensors on `device`."""
     import torch

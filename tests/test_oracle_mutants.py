@@ -66,6 +66,20 @@ MUTANTS = [
      "const float *qrow = q + ((size_t)0 * nh + gh) * d;"),
     ("far commit numerator not rescaled", "for (int c = 0; c < d; ++c) acc[c] = (double)th[c] * r;",
      "for (int c = 0; c < d; ++c) acc[c] = (double)th[c];"),
+    ("gated far: rect ignored", "for (int b = 0; b < m; ++b) if (u[b] < 0.0) u[b] = 0.0;",
+     "for (int b = 0; b < m; ++b) if (u[b] < 0.0) u[b] = u[b];"),
+    ("gated far: empty far field read", "if (far > 0) {", "if (far >= 0) {"),
+    ("gated far: one ring slot short", "const int n = ns + len;", "const int n = ns + len - (len > 1);"),
+    ("gated far: landmark keys of KV head 0", "const float *kt = k_tilde + ((size_t)kh * m + a) * hd;",
+     "const float *kt = k_tilde + ((size_t)0 * m + a) * hd;"),
+    ("gated far: gate sign", "z[e] = (float)(acc[e] / den / (1.0 + exp(-gs)));",
+     "z[e] = (float)(acc[e] / den / (1.0 + exp(gs)));"),
+    ("gated far: far numerator dropped", "for (int e = 0; e < hd; ++e) acc[e] += gb[b] * (double)th[e];",
+     "for (int e = 0; e < hd; ++e) acc[e] += 0.0 * gb[b] * (double)th[e];"),
+    ("gated far: negative far mass kept", "have = far_den >= 0.0;   /* a negative far mass drops the far terms */",
+     "have = 1;"),
+    ("gated far: mu transposed", "u[b] += ea * (double)mu[((size_t)gh * m + a) * m + b];",
+     "u[b] += ea * (double)mu[((size_t)gh * m + b) * m + a];"),
 ]
 
 PIN_TESTS = [getattr(pins, n) for n in dir(pins) if n.startswith("test_")]

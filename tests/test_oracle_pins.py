@@ -726,3 +726,158 @@ def test_far_chunk_equals_sequence_of_decodes():
                                        rtol=2e-5, atol=2e-6)
             state.ring_k, state.ring_v, state.meta, sfar.mz, sfar.t_hat = \
                 oracle.window_commit_far(state, sfar)
+
+
+# ── the gated one-row call with the far field (dory page, `dory_os` .. `dory_ogate`) ─────────
+
+def _gated_far_case(rng, nk=2, hpg=2, hd=16, w=12, ns=2, m=1, far=3, scale=0.5):
+    lens = [int(rng.integers(1, w + 1)) for _ in range(nk)]
+    meta = [(lens[kh], int(rng.integers(0, w)), far, 0) for kh in range(nk)]
+    return gen.make_gated_far(nk * hpg, nk, hd, w, ns, m, meta, seed=int(rng.integers(1 << 30)),
+                              scale=scale)
+
+
+def _gated_bruteforce(inp, extra=None):
+    """sigmoid(gate * gate_scale) times f64 softmax attention (torch SDPA) of each head's query
+    over its KV head's sinks, ring slots 0..len-1 and, if given, extra (K, V) rows per head."""
+    out = np.zeros((inp.nh, inp.hd))
+    hpg = inp.nh // inp.nk
+    for gh in range(inp.nh):
+        kh = gh // hpg
+        ln = int(inp.meta[kh, 0])
+        ks = [inp.sink_k[kh], inp.ring_k[kh, :ln]]
+        vs = [inp.sink_v[kh], inp.ring_v[kh, :ln]]
+        if extra is not None:
+            ks.append(extra[gh][0])
+            vs.append(extra[gh][1])
+        k = torch.from_numpy(np.concatenate(ks).astype(np.float64))[None, None]
+        v = torch.from_numpy(np.concatenate(vs).astype(np.float64))[None, None]
+        q = torch.from_numpy(inp.q[gh].astype(np.float64))[None, None, None]
+        o = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=inp.scale)[0, 0, 0]
+        g = torch.from_numpy((inp.gate[gh * inp.hd:(gh + 1) * inp.hd].astype(np.float64) *
+                              inp.gate_scale[gh * inp.hd:(gh + 1) * inp.hd].astype(np.float64)))
+        out[gh] = (o * torch.sigmoid(g)).numpy()
+    return out
+
+
+def _gated_exact_landmark(rng, inp, b=0, n_hist=None):
+    """Landmark b of every head summarises a history of keys exactly for that head's query:
+    returns the history per head."""
+    hist = []
+    m = inp.m
+    for gh in range(inp.nh):
+        n0 = n_hist if n_hist is not None else int(rng.integers(1, 6))
+        hk = gen._unit_rows(rng, (n0, inp.hd))
+        hv = rng.standard_normal((n0, inp.hd)).astype(np.float32)
+        mx, z, th = _exact_far_state(inp.q[gh], hk, hv, inp.scale)
+        inp.mz[gh, b], inp.mz[gh, m + b] = mx, z
+        inp.t_hat[gh, b] = th
+        hist.append((hk, hv))
+    return hist
+
+
+def test_gated_far_empty_field_is_gated_softmax():
+    """No far count: the far state is never read and the result is the gated softmax over the
+    sinks and the ring's slots 0..len-1. The state holds NaN on one pass and, on another, a
+    finite state with positive weights and masses that would change the result if read."""
+    rng = np.random.default_rng(701)
+    for _ in range(20):
+        inp = _gated_far_case(rng, nk=int(rng.integers(1, 4)), hpg=int(rng.integers(1, 4)),
+                              ns=int(rng.integers(0, 3)), m=int(rng.integers(1, 4)), far=0,
+                              scale=float(rng.choice([0.25, 4.0])))
+        ref = _gated_bruteforce(inp)
+        m = inp.m
+        inp.mz[:, :m] = 3.0
+        inp.mz[:, m:] = 2.0
+        inp.t_hat[...] = 5.0
+        np.testing.assert_allclose(oracle.window_gated_far(inp), ref, rtol=2e-6, atol=1e-7)
+        for a in (inp.k_tilde, inp.mu, inp.mz, inp.t_hat):
+            a[...] = np.nan
+        np.testing.assert_allclose(oracle.window_gated_far(inp), ref, rtol=2e-6, atol=1e-7)
+
+
+def test_gated_far_exact_landmark_gives_full_attention():
+    """One landmark whose summary is exact for the head's query (zero landmark key, mixing
+    weight 1): the gated call equals gated softmax over sinks, ring and the whole history."""
+    rng = np.random.default_rng(702)
+    for _ in range(20):
+        inp = _gated_far_case(rng, nk=int(rng.integers(1, 4)), hpg=int(rng.integers(1, 4)),
+                              ns=int(rng.integers(0, 3)), scale=float(rng.choice([0.25, 4.0])))
+        inp.k_tilde[:] = 0.0
+        inp.mu[:] = 1.0
+        hist = _gated_exact_landmark(rng, inp)
+        np.testing.assert_allclose(oracle.window_gated_far(inp), _gated_bruteforce(inp, hist),
+                                   rtol=2e-5, atol=2e-6)
+
+
+def test_gated_far_rect_clamps_negative_weights():
+    """Landmark 0 is exact, landmark 1 gets weight -3 (mu row 0 = (1, -3), zero landmark keys)
+    and a large mass. With rect the weight is clamped to 0: full attention with the history.
+    Without it the far mass is negative and the far part is dropped: the near result."""
+    rng = np.random.default_rng(703)
+    for _ in range(20):
+        inp = _gated_far_case(rng, m=2, scale=float(rng.choice([0.25, 4.0])))
+        inp.k_tilde[:] = 0.0
+        inp.mu[:] = 0.0
+        inp.mu[:, 0, 0], inp.mu[:, 0, 1] = 1.0, -3.0
+        hist = _gated_exact_landmark(rng, inp, b=0, n_hist=2)
+        inp.mz[:, 1] = inp.mz[:, 0] + 2.0      # landmark 1: larger max and mass
+        inp.mz[:, 3] = inp.mz[:, 2] * 5.0 + 1.0
+        inp.rect = 1
+        np.testing.assert_allclose(oracle.window_gated_far(inp), _gated_bruteforce(inp, hist),
+                                   rtol=2e-5, atol=2e-6)
+        inp.rect = 0
+        np.testing.assert_allclose(oracle.window_gated_far(inp), _gated_bruteforce(inp),
+                                   rtol=2e-6, atol=1e-7)
+
+
+def test_gated_far_landmark_keys_of_the_rows_kv_head():
+    """KV head kh's queries point along basis vector kh; its landmark key 1 is -200 times that
+    vector (score -200 * |q| * scale) and key 0 is zero, so only row 0 of mu counts; mu[0] =
+    (0, 1) routes the weight to landmark 1, which is exact; mu[1] = (0.7, 0) makes mu
+    non-symmetric. Another KV head's landmark keys score 0 and would mix in landmark 0's
+    unrelated state."""
+    rng = np.random.default_rng(704)
+    for _ in range(20):
+        nk, hpg, hd = int(rng.integers(2, 4)), int(rng.integers(1, 3)), 16
+        inp = _gated_far_case(rng, nk=nk, hpg=hpg, hd=hd, m=2, scale=1.0)
+        for gh in range(inp.nh):
+            kh = gh // hpg
+            inp.q[gh] = 0.0
+            inp.q[gh, kh] = float(rng.uniform(0.5, 1.5))
+        inp.k_tilde[:] = 0.0
+        for kh in range(nk):
+            inp.k_tilde[kh, 1, kh] = -200.0
+        inp.mu[:] = 0.0
+        inp.mu[:, 0, 1] = 1.0
+        inp.mu[:, 1, 0] = 0.7
+        hist = _gated_exact_landmark(rng, inp, b=1)
+        np.testing.assert_allclose(oracle.window_gated_far(inp), _gated_bruteforce(inp, hist),
+                                   rtol=2e-5, atol=2e-6)
+
+
+def test_gated_far_gate_zero_halves_the_ungated_result():
+    """gate = 0 multiplies by sigmoid(0) = 1/2 exactly; a gate of 1e4 multiplies by 1."""
+    rng = np.random.default_rng(705)
+    for _ in range(10):
+        inp = _gated_far_case(rng, nk=2, hpg=2, m=3, scale=2.0)
+        inp.gate[:] = 0.0
+        half = oracle.window_gated_far(inp)
+        inp.gate[:] = 1e4
+        inp.gate_scale[:] = 1.0
+        full = oracle.window_gated_far(inp)
+        np.testing.assert_array_equal(half, full * np.float32(0.5))
+
+
+def test_gated_far_ring_storage_order_is_irrelevant():
+    """The ring's live slots are a set: permuting slots 0..len-1 leaves the result unchanged."""
+    rng = np.random.default_rng(706)
+    for _ in range(10):
+        inp = _gated_far_case(rng, nk=2, hpg=2, m=2, ns=1, scale=4.0)
+        base = oracle.window_gated_far(inp)
+        for kh in range(inp.nk):
+            ln = int(inp.meta[kh, 0])
+            perm = rng.permutation(ln)
+            inp.ring_k[kh, :ln] = inp.ring_k[kh, perm]
+            inp.ring_v[kh, :ln] = inp.ring_v[kh, perm]
+        np.testing.assert_allclose(oracle.window_gated_far(inp), base, rtol=1e-6, atol=1e-7)

@@ -194,6 +194,28 @@ def bench_others(args, torch, B, gen, acct):
                      "cache": "hot (inputs resident, reused)"}
         del t, f, out, ws
         torch.cuda.empty_cache()
+    # the gated one-row call with 32 landmarks per head, at the gated workload's head shapes
+    # (16 query / 4 KV heads, hd 256, full 1024-slot rings); the same call with every far
+    # count 0 (far part skipped) is timed beside it
+    gf = gen.make_gated_far(16, 4, 256, 1024, 0, 32, [(1024, 0, 5000, 0)] * 4, seed=9,
+                            scale=1 / 16)
+    t = gen.to_device(gf, dev)
+    out = torch.empty((16, 256), dtype=torch.float32, device=dev)
+    ws = B.Workspace(dev)
+
+    def gated_far_call(i, meta):
+        B.attn_window_gated_far(t["q"], t["ring_k"], t["ring_v"], meta, None, None,
+                                t["k_tilde"], t["mu"], t["mz"], t["t_hat"], t["gate"],
+                                t["gate_scale"], gf.scale, out=out, workspace=ws)
+    ms, _, _ = time_calls(torch, lambda i: gated_far_call(i, t["meta"]), 1, 20, 3)
+    empty = t["meta"].clone()
+    empty[:, 2] = 0
+    near_ms, _, _ = time_calls(torch, lambda i: gated_far_call(i, empty), 1, 20, 3)
+    res["gated_far_m32"] = {"ms": round(ms, 5), "far_empty_ms": round(near_ms, 5),
+                            "kv_gbs": round(4 * 1024 * 256 * 8 / ms / 1e6, 2),
+                            "landmarks": 32, "cache": "hot (inputs resident, reused)"}
+    del t, out, ws
+    torch.cuda.empty_cache()
     g = gen.gated()
     t = gen.to_device(g, dev)
     out = torch.empty((g.rows, g.nh, g.hd), dtype=torch.float32, device=dev)

@@ -194,6 +194,36 @@ int attn_window_commit_far(float* ring_k, float* ring_v, uint32_t* meta, const f
                            int rows, int ng, int hpg, int d, int w, int m, float scale,
                            void* stream);
 
+/*
+ * attn_window_gated_far — the gated one-row call with the far field (dory page: `dory_os`,
+ * `dory_ol`, `dory_omax`, `dory_ofar`, `dory_osoft`, `dory_osum`, `dory_ogate`). The row's own
+ * key and value are already in the ring (pushed by the caller), so query head gh (KV head
+ * kh = gh / (nh/nk)) attends over the ns sinks of kh and ring slots 0 .. len-1 of kh, with
+ * len = meta[kh].len (storage order is irrelevant: the ring holds exactly the window) and
+ * scores scale * <q, K>. When meta[kh].far_len > 0 the landmark part joins: fl_a =
+ * scale <q, k_tilde[kh][a]>, f = max fl, u_b = sum_a exp(fl_a - f) mu[gh][a][b] (clamped at 0
+ * when rect = 1), c = max(max s, f + mz[gh][b]), G_b = u_b exp(f + mz[gh][b] - c), far mass
+ * F = sum_b G_b mz[gh][m+b]; when F >= 0,
+ *   out = (sum exp(s - c) V + sum_b G_b t_hat[gh][b]) / (sum exp(s - c) + F),
+ * else the far terms are dropped; then out[gh][e] /= 1 + exp(-gate[gh*hd+e] * gate_scale[gh*hd+e]).
+ *
+ * Arguments (device pointers): q [nh][hd]; ring_k, ring_v [nk][w][hd]; meta [nk][4] u32
+ * (fields 0 and 2 are read; len <= w, larger values are clamped to w); sink_k, sink_v
+ * [nk][ns][hd] (NULL iff ns == 0); k_tilde [nk][m][hd]; mu [nh][m][m]; mz [nh][2m]; t_hat
+ * [nh][m][hd]; gate, gate_scale [nh*hd]; out [nh][hd] fully overwritten. nh a multiple of nk,
+ * hd % 4 == 0, 4 <= hd <= 256, w >= 1, ns >= 0, 1 <= m <= 64 (larger: WINATTN_EUNSUPPORTED),
+ * rect 0 or 1. Workspace as attn_window_gated_far_workspace returns (always non-zero).
+ */
+int attn_window_gated_far(const float* q, const float* ring_k, const float* ring_v,
+                          const uint32_t* meta, const float* sink_k, const float* sink_v,
+                          const float* k_tilde, const float* mu, const float* mz,
+                          const float* t_hat, const float* gate, const float* gate_scale,
+                          float* out, int nh, int nk, int hd, int w, int ns, int m, float scale,
+                          int rect, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_window_gated_far needs for these sizes (0 if invalid or unsupported). */
+size_t attn_window_gated_far_workspace(int nh, int nk, int hd, int w, int ns, int m);
+
 /* Workspace bytes attn_window_gated needs for these sizes (0 if the sizes are invalid). */
 size_t attn_window_gated_workspace(int rows, int nh, int nk, int hd, int window);
 

@@ -68,6 +68,10 @@ def load(path: str = LIB_PATH):
     lib.attn_window_chunk_far_workspace.restype = _sz
     lib.attn_window_commit_far.argtypes = [_vp] * 8 + [_i] * 6 + [_f, _vp]
     lib.attn_window_commit_far.restype = _i
+    lib.attn_window_gated_far.argtypes = [_vp] * 13 + [_i] * 6 + [_f, _i, _vp, _sz, _vp]
+    lib.attn_window_gated_far.restype = _i
+    lib.attn_window_gated_far_workspace.argtypes = [_i] * 6
+    lib.attn_window_gated_far_workspace.restype = _sz
     lib.attn_tuning_set.argtypes = [_i, _i]
     lib.attn_tuning_set.restype = _i
     lib.attn_strerror.argtypes = [_i]
@@ -109,6 +113,10 @@ def gated_workspace_bytes(rows, nh, nk, hd, window) -> int:
 
 def chunk_far_workspace_bytes(rows, ng, hpg, d, w, ns, m) -> int:
     return load().attn_window_chunk_far_workspace(rows, ng, hpg, d, w, ns, m)
+
+
+def gated_far_workspace_bytes(nh, nk, hd, w, ns, m) -> int:
+    return load().attn_window_gated_far_workspace(nh, nk, hd, w, ns, m)
 
 
 def chunk_plan(rows, ng, hpg, d, w, ns):
@@ -302,6 +310,38 @@ def attn_window_commit_far(ring_k, ring_v, meta, chunk_k, chunk_v, q_tilde, mz, 
         rows, ng, nh // ng, d, w, m, float(scale), _stream_ptr(stream, ring_k.device))
     if rc != OK:
         raise WinattnError("attn_window_commit_far", rc)
+
+
+def attn_window_gated_far(q, ring_k, ring_v, meta, sink_k, sink_v, k_tilde, mu, mz, t_hat,
+                          gate, gate_scale, scale, rect=0, out=None, workspace=None, stream=None):
+    """z [nh][hd] of the gated one-row call with the far field (see attn_window_gated_far in
+    include/winattn.h): q [nh][hd], rings [nk][w][hd], meta [nk][4], sinks [nk][ns][hd] or
+    None, k_tilde [nk][m][hd], mu [nh][m][m], mz [nh][2m], t_hat [nh][m][hd], gate and
+    gate_scale [nh*hd]."""
+    nk, w, hd = ring_k.shape
+    nh = q.shape[0]
+    m = mu.shape[1]
+    if (tuple(q.shape) != (nh, hd) or nh % nk or tuple(k_tilde.shape) != (nk, m, hd)
+            or tuple(mu.shape) != (nh, m, m) or tuple(mz.shape) != (nh, 2 * m)
+            or tuple(t_hat.shape) != (nh, m, hd) or gate.numel() != nh * hd
+            or gate_scale.numel() != nh * hd or tuple(meta.shape) != (nk, 4)):
+        raise ValueError("attn_window_gated_far: inconsistent shapes")
+    ns = 0 if sink_k is None else sink_k.shape[1]
+    if out is None:
+        out = torch.empty((nh, hd), dtype=torch.float32, device=q.device)
+    st = _stream_ptr(stream, q.device)
+    need = gated_far_workspace_bytes(nh, nk, hd, w, ns, m)
+    ws = workspace if workspace is not None else _default_workspace(q.device, st)
+    wp, wb = ws.get(need)
+    rc = load().attn_window_gated_far(
+        _ptr(q, "q"), _ptr(ring_k, "ring_k"), _ptr(ring_v, "ring_v"),
+        _ptr(meta, "meta", (torch.int32, torch.uint32)), _ptr(sink_k, "sink_k"),
+        _ptr(sink_v, "sink_v"), _ptr(k_tilde, "k_tilde"), _ptr(mu, "mu"), _ptr(mz, "mz"),
+        _ptr(t_hat, "t_hat"), _ptr(gate, "gate"), _ptr(gate_scale, "gate_scale"),
+        _ptr(out, "out"), nh, nk, hd, w, ns, m, float(scale), int(rect), wp, wb, st)
+    if rc != OK:
+        raise WinattnError("attn_window_gated_far", rc)
+    return out
 
 
 def mfma16_layout_probe(device="cuda", stream=None):

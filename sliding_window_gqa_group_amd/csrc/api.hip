@@ -445,6 +445,88 @@ int attn_window_commit_far(float* ring_k, float* ring_v, uint32_t* meta, const f
     return launch_ring_commit(c, st) == hipSuccess ? WINATTN_OK : WINATTN_ELAUNCH;
 }
 
+size_t attn_window_gated_far_workspace(int nh, int nk, int hd, int w, int ns, int m) {
+    if (nh < 1 || nk < 1 || nh % nk != 0 || !chunk_shape_ok(1, nk, nh / nk, hd, w, ns) ||
+        !far_shape_ok(1, m))
+        return 0;
+    return make_plan(1, nk, nh / nk, hd, w, ns, 0, 1).bytes;
+}
+
+int attn_window_gated_far(const float* q, const float* ring_k, const float* ring_v,
+                          const uint32_t* meta, const float* sink_k, const float* sink_v,
+                          const float* k_tilde, const float* mu, const float* mz,
+                          const float* t_hat, const float* gate, const float* gate_scale,
+                          float* out, int nh, int nk, int hd, int w, int ns, int m, float scale,
+                          int rect, void* workspace, size_t workspace_bytes, void* stream) {
+    if (nh < 1 || nk < 1 || nh % nk != 0 || !chunk_shape_ok(1, nk, nh / nk, hd, w, ns))
+        return WINATTN_EINVAL;
+    if (!std::isfinite(scale) || m < 1 || (rect != 0 && rect != 1)) return WINATTN_EINVAL;
+    if (!far_shape_ok(1, m)) return WINATTN_EUNSUPPORTED;
+    const void* ptrs[] = {q, ring_k, ring_v, k_tilde, mu, mz, t_hat, gate, gate_scale, out};
+    for (const void* ptr : ptrs)
+        if (!ptr || !aligned16(ptr)) return WINATTN_EINVAL;
+    if (!meta || ((uintptr_t)meta & 3u) != 0) return WINATTN_EINVAL;
+    if (ns > 0 && (!sink_k || !sink_v || !aligned16(sink_k) || !aligned16(sink_v)))
+        return WINATTN_EINVAL;
+    if ((long long)nh * m * hd > kMaxFloats) return WINATTN_EINVAL;
+    const int hpg = nh / nk;
+    const Plan pl = make_plan(1, nk, hpg, hd, w, ns, 0, 1);
+    if (!workspace || workspace_bytes < pl.bytes) return WINATTN_EWORKSPACE;
+    if (!aligned16(workspace)) return WINATTN_EINVAL;
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    FarParams f{};
+    f.ring_k = ring_k;
+    f.ring_v = ring_v;
+    f.meta = meta;
+    f.q = q;
+    f.k_tilde = k_tilde;
+    f.mu = mu;
+    f.mz = const_cast<float*>(mz);        // read only on this path
+    f.t_hat = const_cast<float*>(t_hat);
+    f.pacc = reinterpret_cast<float*>(ws + pl.off_pacc);
+    f.pm = reinterpret_cast<float*>(ws + pl.off_pm);
+    f.pl = reinterpret_cast<float*>(ws + pl.off_pl);
+    f.rows = 1;
+    f.ng = nk;
+    f.hpg = hpg;
+    f.nh = nh;
+    f.d = hd;
+    f.w = w;
+    f.m = m;
+    f.qb = pl.qb;
+    f.nqblocks = pl.nqblocks;
+    f.slot_stride = pl.slots;
+    f.far_slot = pl.nsplit;
+    f.dpad = pl.dpad;
+    f.rect = rect;
+    f.scale = scale;
+    if (launch_far_part(f, 2, st) != hipSuccess) return WINATTN_ELAUNCH;
+
+    AttnParams p{};
+    p.ring_k = ring_k;
+    p.ring_v = ring_v;
+    p.meta = meta;
+    p.sink_k = ns > 0 ? sink_k : nullptr;
+    p.sink_v = ns > 0 ? sink_v : nullptr;
+    p.q = q;
+    p.out = out;
+    p.gate = gate;
+    p.gate_scale = gate_scale;
+    p.ring_gs = (long long)w * hd;
+    p.ring_ss = hd;
+    p.rows = 1;
+    p.ng = nk;
+    p.hpg = hpg;
+    p.nh = nh;
+    p.d = hd;
+    p.w = w;
+    p.ns = ns;
+    p.scale_log2 = scale * kLog2e;
+    return launch_attention(pl, p, true, ws, st);
+}
+
 size_t attn_window_gated_workspace(int rows, int nh, int nk, int hd, int window) {
     if (rows < 1 || nh < 1 || nk < 1 || window < 1 || nh % nk != 0 || hd < 8 || hd > 256 ||
         hd % 8 != 0)

@@ -27,7 +27,7 @@ constexpr int kThreads = 256;
 struct AttnParams {
     const float* ring_k;
     const float* ring_v;
-    const uint32_t* meta;        // chunk call only
+    const uint32_t* meta;        // chunk calls, and the gated one-row call (else NULL)
     const float* sink_k;
     const float* sink_v;
     const float* q;              // [rows][nh][d]
@@ -62,11 +62,23 @@ template <bool GATED>
 __device__ inline GroupWin resolve_group(const AttnParams& p, int g) {
     GroupWin r;
     if constexpr (GATED) {
-        r.base = p.g_base;
-        r.mod = p.g_mod;
-        r.xsplit = 0x7fffffff;
-        r.hi0 = p.g_hi0;
-        r.wcap = p.g_wcap;
+        if (p.meta) {
+            // The gated one-row call: the row's own key is already in the ring, which holds
+            // exactly the window, so ring slots 0 .. len-1 are the keys (storage order is
+            // irrelevant to the softmax). len is clamped to w.
+            const uint32_t len = p.meta[4 * g] < (uint32_t)p.w ? p.meta[4 * g] : (uint32_t)p.w;
+            r.base = 0;
+            r.mod = p.w;
+            r.xsplit = (int)len;
+            r.hi0 = (int)len;
+            r.wcap = p.w;
+        } else {
+            r.base = p.g_base;
+            r.mod = p.g_mod;
+            r.xsplit = 0x7fffffff;
+            r.hi0 = p.g_hi0;
+            r.wcap = p.g_wcap;
+        }
     } else {
         // Out-of-range meta is clamped so that no access leaves the group's ring.
         const uint32_t* m = p.meta + 4 * g;

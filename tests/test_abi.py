@@ -160,6 +160,34 @@ def test_commit_far_rejects_unsupported_sizes(lib, kw):
     assert _commit_far(lib, **kw) == B.EUNSUPPORTED
 
 
+def _gated_far(lib, **kw):
+    a = dict(q=FAKE, ring_k=FAKE, ring_v=FAKE, meta=FAKE, sink_k=None, sink_v=None,
+             k_tilde=FAKE, mu=FAKE, mz=FAKE, t_hat=FAKE, gate=FAKE, gate_scale=FAKE, out=FAKE,
+             nh=8, nk=2, hd=64, w=16, ns=0, m=8, scale=0.125, rect=0, ws=FAKE, wsb=1 << 30,
+             stream=None)
+    a.update(kw)
+    return lib.attn_window_gated_far(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(nh=0), dict(nk=3), dict(hd=6), dict(hd=260), dict(w=0), dict(m=0), dict(rect=2),
+    dict(q=None), dict(gate=None), dict(gate_scale=FAKE + 4), dict(t_hat=None), dict(ns=1),
+    dict(meta=FAKE + 2), dict(scale=float("nan")),
+])
+def test_gated_far_rejects_invalid_arguments(lib, kw):
+    assert _gated_far(lib, **kw) == B.EINVAL
+
+
+def test_gated_far_limits_and_workspace(lib):
+    assert _gated_far(lib, m=65) == B.EUNSUPPORTED
+    need = B.gated_far_workspace_bytes(8, 2, 64, 16, 0, 8)
+    assert need > 0
+    assert _gated_far(lib, ws=None) == B.EWORKSPACE
+    assert _gated_far(lib, wsb=need - 1) == B.EWORKSPACE
+    assert B.gated_far_workspace_bytes(8, 2, 64, 16, 0, 65) == 0
+    assert B.gated_far_workspace_bytes(8, 3, 64, 16, 0, 8) == 0
+
+
 def test_workspace_queries(lib):
     assert B.chunk_workspace_bytes(0, 1, 1, 64, 16, 0) == 0
     assert B.gated_workspace_bytes(1, 5, 2, 64, 8) == 0

@@ -67,7 +67,9 @@ def load_library(path: str):
     lib.oracle_window_gated_far.argtypes = [_f32p, _f32p, _f32p, _u32p, _f32p, _f32p, _f32p,
                                             _f32p, _f32p, _f32p, _f32p, _f32p, _f32p,
                                             i, i, i, i, i, i, f, i]
-    for name in ("oracle_window_chunk", "oracle_window_chunk_select",
+    lib.oracle_encoder_attention.argtypes = [_f32p, _f32p, _f32p, _f32p, _u32p, i, i, i, i, i,
+                                             i, i, i, i, f]
+    for name in ("oracle_encoder_attention", "oracle_window_chunk", "oracle_window_chunk_select",
                  "oracle_window_chunk_weights", "oracle_window_gated", "oracle_meta_ok",
                  "oracle_window_commit", "oracle_window_chunk_far", "oracle_window_commit_far",
                  "oracle_window_gated_far"):
@@ -245,6 +247,26 @@ def window_gated_far(inp) -> np.ndarray:
                                      nh, nk, hd, w, ns, m, inp.scale, int(inp.rect))
     if rc != 0:
         raise ValueError(f"oracle_window_gated_far rejected its arguments (rc={rc})")
+    return out
+
+
+def encoder_attention(inp, out=None) -> np.ndarray:
+    """out [tokens][ldo] of encoder attention for an EncoderInputs-like object (q, k, v row
+    arrays [tokens][ld*], segs [nseg][2] u32, nh, nk, hd, window, scale). Rows outside every
+    sequence keep the values of `out` (zeros if not given)."""
+    lib = _load()
+    keep = [_f32(a) for a in (inp.q, inp.k, inp.v)]
+    if out is None:
+        out = np.zeros((inp.q.shape[0], inp.nh * inp.hd), dtype=np.float32)
+    out = np.array(out, dtype=np.float32, copy=True, order="C")
+    segs = np.ascontiguousarray(inp.segs, dtype=np.uint32)
+    rc = lib.oracle_encoder_attention(*[p for _, p in keep], out.ctypes.data_as(_f32p),
+                                      segs.ctypes.data_as(_u32p), segs.shape[0],
+                                      inp.q.shape[1], inp.k.shape[1], inp.v.shape[1],
+                                      out.shape[1], inp.nh, inp.nk, inp.hd, inp.window,
+                                      inp.scale)
+    if rc != 0:
+        raise ValueError(f"oracle_encoder_attention rejected its arguments (rc={rc})")
     return out
 
 

@@ -20,6 +20,8 @@
  *    the one-row far-field form `dory_os` .. `dory_ogate` (oracle_window_gated_far).
  *  - o1c far field and commits (oracle_window_commit, oracle_window_chunk_far,
  *    oracle_window_commit_far): see the comments at those functions.
+ *  - egemma2 page (`eg_flash_body`, `eg_softmax`): encoder attention over packed sequences
+ *    (oracle_encoder_attention).
  *
  * Readings where the pages leave a step open are listed in the design notes; the ones that
  * matter here: a window of wg keys ends at and includes the row itself; the RoPE table is an
@@ -682,6 +684,69 @@ int oracle_window_gated_far(const float *q, const float *ring_k, const float *ri
             }
         }
         free(s); free(acc); free(fl); free(u); free(gb);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Encoder attention over packed variable-length sequences (egemma2 page: `eg_flash_body`,
+ * `eg_flash64`, `eg_flash64s` for whole sequences, `EgAtt` / `eg_softmax` for the symmetric
+ * window). Sequence s holds tokens start_s .. start_s + len_s - 1 (segs[2s], segs[2s+1]); the
+ * token at position i of its sequence attends, with query head h, to the keys and values of KV
+ * head h / (nh / nk) at positions j of the same sequence with |i - j| <= window (window 0: all
+ * positions), scores scale <q, k>, no causal mask. Row t of q, k, v, out starts at t * ldq,
+ * t * ldk, t * ldv, t * ldo floats; head h's hd values follow at h * hd. Rows of out outside
+ * every sequence are not written.
+ */
+int oracle_encoder_attention(const float *q, const float *k, const float *v, float *out,
+                             const uint32_t *segs, int nseg, int ldq, int ldk, int ldv,
+                             int ldo, int nh, int nk, int hd, int window, float scale) {
+    if (!q || !k || !v || !out || !segs || nseg < 0 || nh < 1 || nk < 1 || nh % nk != 0 ||
+        hd < 1 || window < 0)
+        return -1;
+    if (ldq < nh * hd || ldk < nk * hd || ldv < nk * hd || ldo < nh * hd) return -1;
+    const int group = nh / nk;
+    long total = 0;
+    for (int s = 0; s < nseg; ++s) total += (long)segs[2 * s + 1] * nh;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (long it = 0; it < total; ++it) {
+        /* item -> (sequence, position, head) */
+        long rem = it;
+        int s = 0;
+        while (rem >= (long)segs[2 * s + 1] * nh) {
+            rem -= (long)segs[2 * s + 1] * nh;
+            ++s;
+        }
+        const long start = segs[2 * s], len = segs[2 * s + 1];
+        const long i = rem / nh;
+        const int h = (int)(rem % nh), kvh = h / group;
+        long lo = 0, hi = len;
+        if (window > 0) {
+            lo = i > window ? i - window : 0;
+            hi = i + window + 1 < len ? i + window + 1 : len;
+        }
+        const int n = (int)(hi - lo);
+        const float **kp = malloc(sizeof(*kp) * (size_t)n);
+        const float **vp = malloc(sizeof(*vp) * (size_t)n);
+        double *sc = malloc(sizeof(double) * (size_t)n);
+        double *acc = malloc(sizeof(double) * (size_t)hd);
+        double *qd = malloc(sizeof(double) * (size_t)hd);
+        if (!kp || !vp || !sc || !acc || !qd) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+            for (int j = 0; j < n; ++j) {
+                kp[j] = k + (size_t)(start + lo + j) * ldk + (size_t)kvh * hd;
+                vp[j] = v + (size_t)(start + lo + j) * ldv + (size_t)kvh * hd;
+            }
+            const float *qv = q + (size_t)(start + i) * ldq + (size_t)h * hd;
+            for (int e = 0; e < hd; ++e) qd[e] = (double)qv[e];
+            attend(qd, kp, vp, n, hd, (double)scale, sc, acc, NULL);
+            float *o = out + (size_t)(start + i) * ldo + (size_t)h * hd;
+            for (int e = 0; e < hd; ++e) o[e] = (float)acc[e];
+        }
+        free(kp); free(vp); free(sc); free(acc); free(qd);
     }
     return bad ? -1 : 0;
 }

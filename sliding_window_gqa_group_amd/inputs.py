@@ -315,6 +315,40 @@ def make_gated_far(nh: int, nk: int, hd: int, w: int, ns: int, m: int, meta, see
                           gate_scale, float(np.float32(scale)), int(rect))
 
 
+@dataclass
+class EncoderInputs:
+    """Encoder attention over packed sequences: q [tokens][ldq], k [tokens][ldk], v
+    [tokens][ldv] (head h's values at h*hd of a row), segs [nseg][2] u32 (start, len)."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    segs: np.ndarray
+    nh: int
+    nk: int
+    hd: int
+    window: int
+    scale: float
+
+
+def make_encoder(lens, nh: int, nk: int, hd: int, window: int, seed: int, gap: int = 0,
+                 pad: int = 0, scale: float | None = None) -> EncoderInputs:
+    """Sequences of the given lengths packed one after another (`gap` unused rows between
+    them), q/k/v rows N(0,1) with `pad` extra floats per row (row strides nh*hd + pad and
+    nk*hd + pad); scale 1/sqrt(hd) unless given."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    segs, t = [], 0
+    for ln in lens:
+        segs.append((t, int(ln)))
+        t += int(ln) + gap
+    tokens = max(t, 1)
+    q = rng.standard_normal((tokens, nh * hd + pad), dtype=np.float32)
+    k = rng.standard_normal((tokens, nk * hd + pad), dtype=np.float32)
+    v = rng.standard_normal((tokens, nk * hd + pad), dtype=np.float32)
+    sc = float(np.float32(1.0 / np.sqrt(hd) if scale is None else scale))
+    return EncoderInputs(q, k, v, np.asarray(segs, dtype=np.uint32).reshape(-1, 2), nh, nk, hd,
+                         int(window), sc)
+
+
 def to_device(inp, device="cuda"):
     """The arrays of a ChunkInputs / GatedInputs as contiguous torch tensors on `device`."""
     import torch

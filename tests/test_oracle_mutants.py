@@ -78,6 +78,18 @@ MUTANTS = [
      "for (int e = 0; e < hd; ++e) acc[e] += 0.0 * gb[b] * (double)th[e];"),
     ("gated far: negative far mass kept", "have = far_den >= 0.0;   /* a negative far mass drops the far terms */",
      "have = 1;"),
+    ("encoder: window one short on the right", "hi = i + window + 1 < len ? i + window + 1 : len;",
+     "hi = i + window < len ? i + window : len;"),
+    ("encoder: window one wide on the left", "lo = i > window ? i - window : 0;",
+     "lo = i > window + 1 ? i - window - 1 : 0;"),
+    ("encoder: KV heads interleaved", "h = (int)(rem % nh), kvh = h / group;",
+     "h = (int)(rem % nh), kvh = h % nk;"),
+    ("encoder: causal mask", "long lo = 0, hi = len;", "long lo = 0, hi = i + 1;"),
+    ("encoder: keys from the start of the buffer",
+     "kp[j] = k + (size_t)(start + lo + j) * ldk + (size_t)kvh * hd;",
+     "kp[j] = k + (size_t)(lo + j) * ldk + (size_t)kvh * hd;"),
+    ("encoder: values from the query row", "vp[j] = v + (size_t)(start + lo + j) * ldv + (size_t)kvh * hd;",
+     "vp[j] = v + (size_t)(start + i) * ldv + (size_t)kvh * hd;"),
     ("gated far: mu transposed", "u[b] += ea * (double)mu[((size_t)gh * m + a) * m + b];",
      "u[b] += ea * (double)mu[((size_t)gh * m + b) * m + a];"),
 ]

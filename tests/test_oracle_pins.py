@@ -881,3 +881,98 @@ def test_gated_far_ring_storage_order_is_irrelevant():
             inp.ring_k[kh, :ln] = inp.ring_k[kh, perm]
             inp.ring_v[kh, :ln] = inp.ring_v[kh, perm]
         np.testing.assert_allclose(oracle.window_gated_far(inp), base, rtol=1e-6, atol=1e-7)
+
+
+# ── encoder attention over packed sequences (egemma2 page, `eg_flash_body`, `eg_softmax`) ──
+
+def _encoder_sdpa(inp, s, mask_fn=None):
+    """f64 torch SDPA (non-causal, K/V heads repeated per group) of sequence s, optionally with
+    a boolean keep-mask from mask_fn(len) -> [len][len]."""
+    st, ln = int(inp.segs[s, 0]), int(inp.segs[s, 1])
+    nh, nk, hd = inp.nh, inp.nk, inp.hd
+    q = torch.from_numpy(inp.q[st:st + ln, :nh * hd].astype(np.float64)).view(ln, nh, hd)
+    k = torch.from_numpy(inp.k[st:st + ln, :nk * hd].astype(np.float64)).view(ln, nk, hd)
+    v = torch.from_numpy(inp.v[st:st + ln, :nk * hd].astype(np.float64)).view(ln, nk, hd)
+    k = k.repeat_interleave(nh // nk, dim=1)
+    v = v.repeat_interleave(nh // nk, dim=1)
+    mask = None if mask_fn is None else torch.from_numpy(mask_fn(ln))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        q.transpose(0, 1), k.transpose(0, 1).contiguous(), v.transpose(0, 1).contiguous(),
+        attn_mask=mask, scale=inp.scale)
+    return o.transpose(0, 1).reshape(ln, nh * hd).numpy()
+
+
+def _band(window):
+    def fn(n):
+        i = np.arange(n)
+        return np.abs(i[:, None] - i[None, :]) <= window
+    return fn
+
+
+def test_encoder_full_attention_matches_sdpa():
+    rng = np.random.default_rng(801)
+    for _ in range(12):
+        nk = int(rng.integers(1, 4))
+        nh = nk * int(rng.choice([1, 2, 4]))
+        inp = gen.make_encoder([int(rng.integers(1, 80))], nh, nk, int(rng.choice([8, 16, 36])),
+                               0, seed=int(rng.integers(1 << 30)), pad=int(rng.integers(0, 5)))
+        got = oracle.encoder_attention(inp)
+        np.testing.assert_allclose(got[:, :nh * inp.hd], _encoder_sdpa(inp, 0), rtol=2e-6, atol=1e-7)
+
+
+def test_encoder_symmetric_window_matches_masked_sdpa():
+    rng = np.random.default_rng(802)
+    for _ in range(12):
+        nk = int(rng.integers(1, 3))
+        nh = nk * int(rng.choice([1, 3]))
+        ln = int(rng.integers(2, 90))
+        win = int(rng.integers(1, ln + 2))
+        inp = gen.make_encoder([ln], nh, nk, 16, win, seed=int(rng.integers(1 << 30)))
+        got = oracle.encoder_attention(inp)
+        np.testing.assert_allclose(got[:, :nh * 16], _encoder_sdpa(inp, 0, _band(win)),
+                                   rtol=2e-6, atol=1e-7)
+
+
+def test_encoder_sequences_are_independent_and_gaps_untouched():
+    """A packed call equals each sequence alone; rows between sequences keep their values."""
+    rng = np.random.default_rng(803)
+    for _ in range(8):
+        lens = [int(x) for x in rng.integers(1, 40, size=int(rng.integers(1, 5)))]
+        win = int(rng.choice([0, 1, 4]))
+        inp = gen.make_encoder(lens, 4, 2, 8, win, seed=int(rng.integers(1 << 30)), gap=3, pad=2)
+        sentinel = np.full((inp.q.shape[0], inp.nh * inp.hd + 1), 7.5, np.float32)
+        got = oracle.encoder_attention(inp, out=sentinel)
+        covered = np.zeros(inp.q.shape[0], bool)
+        for s in range(len(lens)):
+            st, ln = int(inp.segs[s, 0]), int(inp.segs[s, 1])
+            covered[st:st + ln] = True
+            mask = None if win == 0 else _band(win)
+            np.testing.assert_allclose(got[st:st + ln, :inp.nh * inp.hd],
+                                       _encoder_sdpa(inp, s, mask), rtol=2e-6, atol=1e-7)
+        assert np.all(got[~covered] == 7.5)
+        assert np.all(got[:, inp.nh * inp.hd:] == 7.5)
+
+
+def test_encoder_uniform_weights_give_the_window_mean():
+    """q = 0: every visible key weighs the same, so the output is the mean of the window's
+    values: positions max(0, i - w) .. min(len, i + w + 1) - 1."""
+    rng = np.random.default_rng(804)
+    for win in (0, 1, 3, 50):
+        inp = gen.make_encoder([23], 2, 1, 8, win, seed=int(rng.integers(1 << 30)))
+        inp.q[:] = 0.0
+        got = oracle.encoder_attention(inp)
+        for i in range(23):
+            lo, hi = (0, 23) if win == 0 else (max(0, i - win), min(23, i + win + 1))
+            ref = inp.v[lo:hi, :8].astype(np.float64).mean(axis=0)
+            for h in range(2):
+                np.testing.assert_allclose(got[i, h * 8:(h + 1) * 8], ref, rtol=1e-6, atol=1e-7)
+
+
+def test_encoder_key_order_is_irrelevant_without_a_window():
+    rng = np.random.default_rng(805)
+    inp = gen.make_encoder([37], 4, 2, 16, 0, seed=5)
+    base = oracle.encoder_attention(inp)
+    perm = rng.permutation(37)
+    inp.k[:] = inp.k[perm]
+    inp.v[:] = inp.v[perm]
+    np.testing.assert_allclose(oracle.encoder_attention(inp), base, rtol=1e-6, atol=1e-7)

@@ -216,6 +216,30 @@ def bench_others(args, torch, B, gen, acct):
                             "landmarks": 32, "cache": "hot (inputs resident, reused)"}
     del t, out, ws
     torch.cuda.empty_cache()
+    # encoder attention: one 9801-position sequence with 16 heads of 64 and no window (the
+    # vision tower's shape), and 16 packed sequences of seeded lengths U[64, 1024] with 16
+    # query / 4 KV heads of 64 and a symmetric window of 128
+    rng = np.random.default_rng(11)
+    for name, lens, nh, nk, win in (
+            ("encoder_full_9801", [9801], 16, 16, 0),
+            ("encoder_varlen_window128", [int(x) for x in rng.integers(64, 1025, size=16)], 16, 4, 128)):
+        e = gen.make_encoder(lens, nh, nk, 64, win, seed=12)
+        q = torch.from_numpy(e.q).to(dev)
+        k = torch.from_numpy(e.k).to(dev)
+        v = torch.from_numpy(e.v).to(dev)
+        segs = torch.from_numpy(e.segs.view(np.int32).copy()).to(dev)
+        out = torch.empty((e.q.shape[0], nh * 64), dtype=torch.float32, device=dev)
+        mx = max(lens)
+        ms, _, _ = time_calls(torch, lambda i: B.attn_encoder(q, k, v, segs, nh, nk, 64, e.scale,
+                                                               window=win, max_len=mx, out=out),
+                              1, 5 if name.endswith("9801") else 20, 2)
+        flops = acct.encoder_flops(e)
+        res[name] = {"ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 3),
+                     "tflops_frac_f32_peak": round(flops / ms / 1e9 / F32_PEAK_TFLOPS, 4),
+                     "tokens": int(sum(lens)), "kernel": "enc_attn_kernel",
+                     "cache": "hot (inputs resident, reused)"}
+        del q, k, v, segs, out
+        torch.cuda.empty_cache()
     g = gen.gated()
     t = gen.to_device(g, dev)
     out = torch.empty((g.rows, g.nh, g.hd), dtype=torch.float32, device=dev)

@@ -224,6 +224,30 @@ int attn_window_gated_far(const float* q, const float* ring_k, const float* ring
 /* Workspace bytes attn_window_gated_far needs for these sizes (0 if invalid or unsupported). */
 size_t attn_window_gated_far_workspace(int nh, int nk, int hd, int w, int ns, int m);
 
+/*
+ * attn_encoder — encoder attention over packed variable-length sequences (egemma2 page,
+ * "EmbeddingGemma 2 encoder": `eg_flash_body` / `eg_flash64` / `eg_flash64s` for whole
+ * sequences with segments [start, len] and K/V heads shared by groups of query heads;
+ * `EgAtt` / `eg_softmax` for the symmetric window). Sequence s holds rows start .. start+len-1
+ * (segs[2s], segs[2s+1]); the row at position i of its sequence attends with query head h to
+ * the rows at positions j of the same sequence with |i - j| <= window (window 0: every
+ * position), reading KV head h / (nh/nk), with scores scale * <q, k> and no causal mask:
+ *   out[row][h*hd .. h*hd+hd) = sum_j softmax_j(scale <q_i, k_j>) v_j.
+ *
+ * Arguments (device pointers, f32 rows): q row t at q + t*ldq, head h's hd values at h*hd;
+ * k, v rows at t*ldk, t*ldv, KV head kvh at kvh*hd; out rows at t*ldo (only the hd-wide head
+ * slices of rows inside some sequence are written). The page's packed q|k|v rows are
+ * q = QKV + q_off, k = QKV + k_off, v = QKV + v_off with one row stride. segs: device
+ * [nseg][2] u32, disjoint sequences. max_len: an upper bound on every len (rows of a longer
+ * sequence past max_len are not written). nh a multiple of nk; hd % 4 == 0, 4 <= hd <= 128
+ * (hd > 128: WINATTN_EUNSUPPORTED); every ld* a multiple of 4 and at least the row's heads
+ * (nh*hd for q and out, nk*hd for k and v); pointers 16-byte aligned; window >= 0. nseg == 0
+ * or max_len == 0 launches nothing. No workspace; asynchronous on `stream`.
+ */
+int attn_encoder(const float* q, const float* k, const float* v, float* out,
+                 const uint32_t* segs, int nseg, int max_len, int ldq, int ldk, int ldv, int ldo,
+                 int nh, int nk, int hd, int window, float scale, void* stream);
+
 /* Workspace bytes attn_window_gated needs for these sizes (0 if the sizes are invalid). */
 size_t attn_window_gated_workspace(int rows, int nh, int nk, int hd, int window);
 

@@ -63,3 +63,18 @@ def gated_counts(inp):
     keys = np.minimum(inp.window, pos + 1)
     flops = int(np.sum(keys)) * inp.nh * 4 * inp.hd
     return kv_read, total, flops
+
+
+def encoder_flops(inp) -> int:
+    """4 * hd flops (score and value products) per visible (position, query head, key) of an
+    encoder call: a window of w keeps positions max(0, i - w) .. min(len, i + w + 1) - 1."""
+    total = 0
+    for _, ln in inp.segs:
+        ln = int(ln)
+        if inp.window == 0:
+            keys = ln * ln
+        else:
+            i = np.arange(ln)
+            keys = int(np.sum(np.minimum(ln, i + inp.window + 1) - np.maximum(0, i - inp.window)))
+        total += keys
+    return 4 * inp.hd * inp.nh * total

@@ -72,6 +72,8 @@ def load(path: str = LIB_PATH):
     lib.attn_window_gated_far.restype = _i
     lib.attn_window_gated_far_workspace.argtypes = [_i] * 6
     lib.attn_window_gated_far_workspace.restype = _sz
+    lib.attn_encoder.argtypes = [_vp] * 5 + [_i] * 10 + [_f, _vp]
+    lib.attn_encoder.restype = _i
     lib.attn_tuning_set.argtypes = [_i, _i]
     lib.attn_tuning_set.restype = _i
     lib.attn_strerror.argtypes = [_i]
@@ -341,6 +343,41 @@ def attn_window_gated_far(q, ring_k, ring_v, meta, sink_k, sink_v, k_tilde, mu, 
         _ptr(out, "out"), nh, nk, hd, w, ns, m, float(scale), int(rect), wp, wb, st)
     if rc != OK:
         raise WinattnError("attn_window_gated_far", rc)
+    return out
+
+
+def _rows(t, name):
+    if not isinstance(t, torch.Tensor) or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D row-major view (rows, columns) with unit column stride")
+    if not t.is_cuda or t.dtype != torch.float32:
+        raise ValueError(f"{name} must be a float32 device tensor")
+    return t.data_ptr(), t.stride(0)
+
+
+def attn_encoder(q, k, v, segs, nh, nk, hd, scale, window=0, max_len=None, out=None,
+                 stream=None):
+    """Encoder attention over packed sequences (see attn_encoder in include/winattn.h).
+
+    q [tokens][>= nh*hd], k and v [tokens][>= nk*hd], out [tokens][>= nh*hd]: 2-D row views
+    (strided rows allowed, e.g. column slices of one packed q|k|v buffer); segs [nseg][2]
+    int32/uint32 device tensor of (start, len); max_len defaults to the largest len (read
+    from segs on the host)."""
+    qp, ldq = _rows(q, "q")
+    kp, ldk = _rows(k, "k")
+    vp, ldv = _rows(v, "v")
+    if out is None:
+        out = torch.zeros((q.shape[0], nh * hd), dtype=torch.float32, device=q.device)
+    op, ldo = _rows(out, "out")
+    if tuple(segs.shape[1:]) != (2,) or not segs.is_contiguous():
+        raise ValueError("segs must be a contiguous [nseg][2] tensor")
+    nseg = segs.shape[0]
+    if max_len is None:
+        max_len = int(segs[:, 1].max().item()) if nseg else 0
+    rc = load().attn_encoder(qp, kp, vp, op, _ptr(segs, "segs", (torch.int32, torch.uint32)),
+                             nseg, int(max_len), ldq, ldk, ldv, ldo, nh, nk, hd, int(window),
+                             float(scale), _stream_ptr(stream, q.device))
+    if rc != OK:
+        raise WinattnError("attn_encoder", rc)
     return out
 
 

@@ -11,7 +11,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libwinattn.so")
 SOURCES = ["api.hip", "attn_dec.hip", "attn_valu.hip", "attn_mfma.hip", "attn_mfma16.hip",
-           "gated_prep.hip", "ring_commit.hip", "far_field.hip"]
+           "gated_prep.hip", "ring_commit.hip", "far_field.hip",
+           "enc_attn.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -527,6 +527,48 @@ int attn_window_gated_far(const float* q, const float* ring_k, const float* ring
     return launch_attention(pl, p, true, ws, st);
 }
 
+int attn_encoder(const float* q, const float* k, const float* v, float* out,
+                 const uint32_t* segs, int nseg, int max_len, int ldq, int ldk, int ldv, int ldo,
+                 int nh, int nk, int hd, int window, float scale, void* stream) {
+    if (nseg < 0 || max_len < 0 || nh < 1 || nk < 1 || nh % nk != 0 || window < 0)
+        return WINATTN_EINVAL;
+    if (hd < 4 || hd % 4 != 0 || !std::isfinite(scale)) return WINATTN_EINVAL;
+    if (hd > 128) return WINATTN_EUNSUPPORTED;
+    if (ldq < nh * hd || ldk < nk * hd || ldv < nk * hd || ldo < nh * hd) return WINATTN_EINVAL;
+    if (ldq % 4 || ldk % 4 || ldv % 4 || ldo % 4) return WINATTN_EINVAL;
+    if (nseg == 0 || max_len == 0) return WINATTN_OK;
+    const void* ptrs[] = {q, k, v, out};
+    for (const void* ptr : ptrs)
+        if (!ptr || !aligned16(ptr)) return WINATTN_EINVAL;
+    if (!segs || ((uintptr_t)segs & 3u) != 0) return WINATTN_EINVAL;
+    const int group = nh / nk;
+    const long long qblocks = ((long long)max_len * group + enc_query_block() - 1) / enc_query_block();
+    if ((long long)max_len > (1 << 28) || (long long)nseg * nk * qblocks > (1LL << 30))
+        return WINATTN_EINVAL;
+    EncParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = out;
+    p.segs = segs;
+    p.ldq = ldq;
+    p.ldk = ldk;
+    p.ldv = ldv;
+    p.ldo = ldo;
+    p.nh = nh;
+    p.nk = nk;
+    p.group = group;
+    p.hd = hd;
+    p.window = window;
+    p.nseg = nseg;
+    p.max_len = max_len;
+    p.max_qblocks = (int)qblocks;
+    p.scale_log2 = scale * kLog2e;
+    return launch_enc_attn(p, hd <= 64 ? 64 : 128, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? WINATTN_OK
+               : WINATTN_ELAUNCH;
+}
+
 size_t attn_window_gated_workspace(int rows, int nh, int nk, int hd, int window) {
     if (rows < 1 || nh < 1 || nk < 1 || window < 1 || nh % nk != 0 || hd < 8 || hd > 256 ||
         hd % 8 != 0)

@@ -96,6 +96,23 @@ hipError_t launch_far_evict(const FarParams& p, hipStream_t stream);
 hipError_t launch_far_part(const FarParams& p, int mode, hipStream_t stream);
 // Far state after a chunk; runs before the ring commit, which overwrites the evicted rows.
 hipError_t launch_far_commit(const FarParams& p, hipStream_t stream);
+struct EncParams {
+    const float* q;           // row t at t * ldq; head h's hd values at h * hd
+    const float* k;           // row t at t * ldk; KV head kvh at kvh * hd
+    const float* v;
+    float* out;               // row t at t * ldo; head h at h * hd
+    const uint32_t* segs;     // [nseg][2]: start, len
+    int ldq, ldk, ldv, ldo;
+    int nh, nk, group, hd;
+    int window;               // 0: the whole sequence, else |i - j| <= window
+    int nseg, max_len;        // sequences; the longest length the grid covers
+    int max_qblocks;          // query blocks per (sequence, KV head) the grid reserves
+    float scale_log2;
+};
+// Encoder attention over packed sequences on the f32 matrix cores; dpad in {64, 128}.
+hipError_t launch_enc_attn(const EncParams& p, int dpad, hipStream_t stream);
+int enc_query_block();
+
 constexpr int kFarMaxRows = 64;
 constexpr int kFarMaxLandmarks = 64;
 

@@ -188,6 +188,29 @@ def test_gated_far_limits_and_workspace(lib):
     assert B.gated_far_workspace_bytes(8, 3, 64, 16, 0, 8) == 0
 
 
+def _encoder(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, segs=FAKE, nseg=2, max_len=100, ldq=512,
+             ldk=128, ldv=128, ldo=512, nh=8, nk=2, hd=64, window=0, scale=0.125, stream=None)
+    a.update(kw)
+    return lib.attn_encoder(*a.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(nh=6, nk=4), dict(nk=0), dict(hd=6), dict(hd=0), dict(window=-1), dict(nseg=-1),
+    dict(ldq=508), dict(ldk=126), dict(ldv=100), dict(ldo=500), dict(q=None), dict(out=FAKE + 4),
+    dict(segs=None), dict(segs=FAKE + 2), dict(scale=float("inf")), dict(max_len=-1),
+])
+def test_encoder_rejects_invalid_arguments(lib, kw):
+    assert _encoder(lib, **kw) == B.EINVAL
+
+
+def test_encoder_limits(lib):
+    assert _encoder(lib, hd=132, ldq=8 * 132, ldk=2 * 132, ldv=2 * 132, ldo=8 * 132) == B.EUNSUPPORTED
+    # nothing to do: no launch, success, even with no pointers at all
+    assert _encoder(lib, nseg=0, q=None, segs=None) == B.OK
+    assert _encoder(lib, max_len=0, q=None) == B.OK
+
+
 def test_workspace_queries(lib):
     assert B.chunk_workspace_bytes(0, 1, 1, 64, 16, 0) == 0
     assert B.gated_workspace_bytes(1, 5, 2, 64, 8) == 0

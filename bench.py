@@ -270,7 +270,26 @@ def counter_run(args, torch, B, gen):
     torch.cuda.synchronize()
     del src, dst
     name = args.counter_run
-    if name == "gated":
+    if name == "encoder":
+        e = gen.make_encoder([9801], 16, 16, 64, 0, seed=12)
+        q, k, v = (torch.from_numpy(a).to(dev) for a in (e.q, e.k, e.v))
+        segs = torch.from_numpy(e.segs.view(np.int32).copy()).to(dev)
+        out = torch.empty((9801, 16 * 64), dtype=torch.float32, device=dev)
+        for _ in range(args.calls):
+            B.attn_encoder(q, k, v, segs, 16, 16, 64, e.scale, max_len=9801, out=out)
+    elif name == "decode_far":
+        inp = gen.make_chunk(1, 8, 4, 128, 4096, 4, gen.decode().meta.copy(), seed=7)
+        inp.meta[:, 2] = 1000
+        far = gen.make_far(inp, 32, seed=8)
+        t = chunk_tensors(inp, torch, dev)
+        f = gen.to_device(far, dev)
+        out = torch.empty((inp.rows, inp.nh, inp.d), dtype=torch.float32, device=dev)
+        for _ in range(args.calls):
+            B.attn_window_chunk_far(t["ring_k"], t["ring_v"], t["meta"], t["sink_k"],
+                                    t["sink_v"], t["q"], t["chunk_k"], t["chunk_v"],
+                                    f["k_tilde"], f["q_tilde"], f["mu"], f["mz"], f["t_hat"],
+                                    inp.scale, out=out)
+    elif name == "gated":
         g = gen.gated()
         t = gen.to_device(g, dev)
         out = torch.empty((g.rows, g.nh, g.hd), dtype=torch.float32, device=dev)
@@ -304,7 +323,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-others", action="store_true")
-    ap.add_argument("--counter-run", choices=["tiny", "decode", "prefill", "large", "gated"],
+    ap.add_argument("--counter-run", choices=["tiny", "decode", "prefill", "large", "gated",
+                                              "encoder", "decode_far"],
                     help="untimed calls of one workload for rocprofv3 counter passes; no JSON")
     ap.add_argument("--calls", type=int, default=20)
     args = ap.parse_args()

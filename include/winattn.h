@@ -239,8 +239,8 @@ size_t attn_window_gated_far_workspace(int nh, int nk, int hd, int w, int ns, in
  * slices of rows inside some sequence are written). The page's packed q|k|v rows are
  * q = QKV + q_off, k = QKV + k_off, v = QKV + v_off with one row stride. segs: device
  * [nseg][2] u32, disjoint sequences. max_len: an upper bound on every len (rows of a longer
- * sequence past max_len are not written). nh a multiple of nk; hd % 4 == 0, 4 <= hd <= 128
- * (hd > 128: WINATTN_EUNSUPPORTED); every ld* a multiple of 4 and at least the row's heads
+ * sequence past max_len are not written). nh a multiple of nk; hd % 4 == 0, 4 <= hd <= 256;
+ * every ld* a multiple of 4 and at least the row's heads
  * (nh*hd for q and out, nk*hd for k and v); pointers 16-byte aligned; window >= 0. nseg == 0
  * or max_len == 0 launches nothing. No workspace; asynchronous on `stream`.
  */

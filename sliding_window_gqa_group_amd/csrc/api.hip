@@ -532,8 +532,7 @@ int attn_encoder(const float* q, const float* k, const float* v, float* out,
                  int nh, int nk, int hd, int window, float scale, void* stream) {
     if (nseg < 0 || max_len < 0 || nh < 1 || nk < 1 || nh % nk != 0 || window < 0)
         return WINATTN_EINVAL;
-    if (hd < 4 || hd % 4 != 0 || !std::isfinite(scale)) return WINATTN_EINVAL;
-    if (hd > 128) return WINATTN_EUNSUPPORTED;
+    if (hd < 4 || hd > 256 || hd % 4 != 0 || !std::isfinite(scale)) return WINATTN_EINVAL;
     if (ldq < nh * hd || ldk < nk * hd || ldv < nk * hd || ldo < nh * hd) return WINATTN_EINVAL;
     if (ldq % 4 || ldk % 4 || ldv % 4 || ldo % 4) return WINATTN_EINVAL;
     if (nseg == 0 || max_len == 0) return WINATTN_OK;
@@ -564,7 +563,7 @@ int attn_encoder(const float* q, const float* k, const float* v, float* out,
     p.max_len = max_len;
     p.max_qblocks = (int)qblocks;
     p.scale_log2 = scale * kLog2e;
-    return launch_enc_attn(p, hd <= 64 ? 64 : 128, static_cast<hipStream_t>(stream)) == hipSuccess
+    return launch_enc_attn(p, pad_d(hd), static_cast<hipStream_t>(stream)) == hipSuccess
                ? WINATTN_OK
                : WINATTN_ELAUNCH;
 }

@@ -28,7 +28,7 @@ __device__ inline int enc_lo(int i, int win) { return win > 0 ? max(0, i - win) 
 __device__ inline int enc_hi(int i, int win, int len) { return win > 0 ? min(len, i + win + 1) : len; }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void enc_attn_kernel(const EncParams p) {
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void enc_attn_kernel(const EncParams p) {
     constexpr int TK = kEncTK, QB = kEncQB;
     constexpr int D4 = D / 4, KST = D + 4, VST = D + 8;
     constexpr int LPT = TK * D4 / kThreads;   // float4 loads per thread per tensor per tile
@@ -91,7 +91,10 @@ __global__ __launch_bounds__(kThreads, 2) void enc_attn_kernel(const EncParams p
             kmask |= (ok ? 1u : 0u) << j;
         }
     };
-    if (ntiles > 0) load_tile(0);
+    // At d = 256 the next tile's registers do not fit beside Q and O: each tile is loaded
+    // right before it is stored to LDS instead of one tile ahead.
+    constexpr bool PREFETCH = D != 256;
+    if (PREFETCH && ntiles > 0) load_tile(0);
 
     // Q^T operand: qreg[4c + r] = scale*log2e * q[8c + 4*hb + r].
     float qreg[D / 2];
@@ -118,6 +121,7 @@ __global__ __launch_bounds__(kThreads, 2) void enc_attn_kernel(const EncParams p
 
     for (int t = 0; t < ntiles; ++t) {
         __syncthreads();
+        if (!PREFETCH) load_tile(t);
 #pragma unroll
         for (int j = 0; j < LPT; ++j) {
             const int key = key0 + j * (kThreads / D4);
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 2) void enc_attn_kernel(const EncParams p
             *reinterpret_cast<float4*>(s_v + key * VST + 4 * col) = zero_unless(keep, vreg[j]);
         }
         __syncthreads();
-        if (t + 1 < ntiles) load_tile(t + 1);
+        if (PREFETCH && t + 1 < ntiles) load_tile(t + 1);
 
         // This lane's visible keys of the tile as a range [klo, khi) of key indices.
         const int tx = xlo + t * TK;
@@ -230,7 +234,8 @@ int enc_query_block() { return kEncQB; }
 
 hipError_t launch_enc_attn(const EncParams& p, int dpad, hipStream_t stream) {
     if (dpad == 64) return launch_enc_t<64>(p, stream);
-    return launch_enc_t<128>(p, stream);
+    if (dpad == 128) return launch_enc_t<128>(p, stream);
+    return launch_enc_t<256>(p, stream);
 }
 
 }  // namespace winattn

@@ -109,7 +109,7 @@ struct EncParams {
     int max_qblocks;          // query blocks per (sequence, KV head) the grid reserves
     float scale_log2;
 };
-// Encoder attention over packed sequences on the f32 matrix cores; dpad in {64, 128}.
+// Encoder attention over packed sequences on the f32 matrix cores; dpad in {64, 128, 256}.
 hipError_t launch_enc_attn(const EncParams& p, int dpad, hipStream_t stream);
 int enc_query_block();
 

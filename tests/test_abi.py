@@ -205,7 +205,7 @@ def test_encoder_rejects_invalid_arguments(lib, kw):
 
 
 def test_encoder_limits(lib):
-    assert _encoder(lib, hd=132, ldq=8 * 132, ldk=2 * 132, ldv=2 * 132, ldo=8 * 132) == B.EUNSUPPORTED
+    assert _encoder(lib, hd=260, ldq=8 * 260, ldk=2 * 260, ldv=2 * 260, ldo=8 * 260) == B.EINVAL
     # nothing to do: no launch, success, even with no pointers at all
     assert _encoder(lib, nseg=0, q=None, segs=None) == B.OK
     assert _encoder(lib, max_len=0, q=None) == B.OK

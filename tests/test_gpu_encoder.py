@@ -55,6 +55,8 @@ CASES = [
     ([150], 4, 2, 100, 1000, 0, 4),        # window wider than the sequence
     ([40, 41, 42], 8, 4, 128, 1, 2, 0),
     ([1, 1, 2, 3], 2, 1, 8, 0, 1, 0),
+    ([96, 130], 8, 2, 256, 0, 1, 4),       # wide heads
+    ([200], 4, 4, 200, 17, 0, 0),          # padded to 256
 ]
 
 

@@ -285,7 +285,7 @@ int attn_mfma16_layout_probe(float* out, void* stream);
 #define WINATTN_TUNE_TILES_PER_SPLIT 2 /* key tiles per split */
 #define WINATTN_TUNE_TARGET_BLOCKS 3   /* workgroups the split count aims for */
 #define WINATTN_TUNE_MERGE_KERNEL 4    /* 1 = splits merge in the last split, 2 = separate launch */
-#define WINATTN_TUNE_XCD_MAP 5         /* matrix-core work order: 1 = round-robin, 2 = groups per XCD */
+#define WINATTN_TUNE_XCD_MAP 5         /* matrix-core and encoder work order: 1 = round-robin, 2 = groups per XCD */
 int attn_tuning_set(int knob, int value);
 
 /* A static, human-readable description of a return code. */

@@ -562,6 +562,9 @@ int attn_encoder(const float* q, const float* k, const float* v, float* out,
     p.nseg = nseg;
     p.max_len = max_len;
     p.max_qblocks = (int)qblocks;
+    // One sequence: its KV heads are alike, so whole heads per XCD; several sequences of
+    // unknown (device-side) lengths: round-robin, so no XCD holds all the long ones.
+    p.xcd_map = g_xcd_map >= 0 ? (g_xcd_map == 1 ? 1 : 0) : (nseg == 1 ? 1 : 0);
     p.scale_log2 = scale * kLog2e;
     return launch_enc_attn(p, pad_d(hd), static_cast<hipStream_t>(stream)) == hipSuccess
                ? WINATTN_OK

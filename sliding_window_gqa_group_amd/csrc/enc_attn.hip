@@ -38,11 +38,15 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void enc_attn_kernel(co
     __shared__ __align__(16) float s_k[TK * KST];
     __shared__ __align__(16) float s_v[TK * VST];
 
-    // Work item = (sequence, KV head, query block), query block fastest; whole (sequence, KV
-    // head) runs of items go to one XCD so that its L2 serves their shared K/V stream.
+    // Work item = (sequence, KV head, query block), query block fastest. The hardware deals
+    // blocks to the 8 XCDs round-robin. xcd_map 1: whole (sequence, KV head) runs of items go to
+    // one XCD, whose L2 then serves their shared K/V stream (even work when the runs are alike);
+    // xcd_map 0: item = block, every XCD gets a slice of every run (even work when sequence
+    // lengths differ).
     const int n_items = p.nseg * p.nk * p.max_qblocks;
     const int per_xcd = (n_items + 7) / 8;
-    const int item = (int)(blockIdx.x % 8u) * per_xcd + (int)(blockIdx.x / 8u);
+    const int item = p.xcd_map ? (int)(blockIdx.x % 8u) * per_xcd + (int)(blockIdx.x / 8u)
+                               : (int)blockIdx.x;
     if (item >= n_items) return;
     const int qb = item % p.max_qblocks;
     const int kvh = (item / p.max_qblocks) % p.nk;
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void enc_attn_kernel(co
 template <int D>
 hipError_t launch_enc_t(const EncParams& p, hipStream_t stream) {
     const long long n_items = (long long)p.nseg * p.nk * p.max_qblocks;
-    const int blocks = (int)(8 * ((n_items + 7) / 8));
+    const int blocks = (int)(p.xcd_map ? 8 * ((n_items + 7) / 8) : n_items);
     hipLaunchKernelGGL((enc_attn_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }

@@ -107,6 +107,7 @@ struct EncParams {
     int window;               // 0: the whole sequence, else |i - j| <= window
     int nseg, max_len;        // sequences; the longest length the grid covers
     int max_qblocks;          // query blocks per (sequence, KV head) the grid reserves
+    int xcd_map;              // work order: 1 whole (sequence, KV head) runs per XCD, 0 round-robin
     float scale_log2;
 };
 // Encoder attention over packed sequences on the f32 matrix cores; dpad in {64, 128, 256}.

@@ -101,3 +101,19 @@ def test_encoder_max_len_above_every_length():
     ref = oracle.encoder_attention(inp, out=np.full((inp.q.shape[0], inp.nh * inp.hd + 4),
                                                      SENTINEL, np.float32))
     assert_close(gpu_encoder(inp, max_len=1000), ref, "max_len 1000")
+
+
+@pytest.mark.parametrize("order", [1, 2], ids=["round_robin", "runs_per_xcd"])
+def test_encoder_work_orders(order):
+    """Both XCD work orders give the oracle's result (the automatic one picks by sequence
+    count)."""
+    _case(f"encoder work order {order}")
+    inp = gen.make_encoder([300, 17, 129, 64], 8, 2, 64, 0, seed=61, gap=1)
+    try:
+        B.tuning_set(B.TUNE_XCD_MAP, order)
+        got = gpu_encoder(inp)
+    finally:
+        B.tuning_set(B.TUNE_XCD_MAP, 0)
+    ref = oracle.encoder_attention(inp, out=np.full((inp.q.shape[0], inp.nh * inp.hd + 4),
+                                                     SENTINEL, np.float32))
+    assert_close(got, ref, f"work order {order}")

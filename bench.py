@@ -71,13 +71,24 @@ def run_chunk(B, t, scale, out, ws):
                                t["q"], t["chunk_k"], t["chunk_v"], scale, out=out, workspace=ws)
 
 
+WARM_MS = 50.0
+
+
 def time_calls(torch, fn, n_sets, steps, warmup):
     """(ms per step over a bracketed loop, mean and median per-call event ms).
 
-    The step time comes from one pair of events around `steps` back-to-back calls; the per-call
-    times from a second pass with an event pair around each call (both on the stream the
-    library launches on, torch's current stream)."""
+    Untimed first: calls for at least WARM_MS of wall time (the GPU leaves its idle clocks;
+    this workload's code and buffers are touched), then `warmup` calls. The step time comes
+    from one pair of events around `steps` back-to-back calls; the per-call times from a second
+    pass with an event pair around each call (both on the stream the library launches on,
+    torch's current stream)."""
     stream = torch.cuda.current_stream()
+    t0w, s = time.perf_counter(), 0
+    while (time.perf_counter() - t0w) * 1e3 < WARM_MS:
+        fn(s % n_sets)
+        s += 1
+        if s % 8 == 0:
+            torch.cuda.synchronize()
     for s in range(warmup):
         fn(s % n_sets)
     torch.cuda.synchronize()

@@ -85,11 +85,12 @@ Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_f
     const int max_tiles = cdiv(keys_max, pl.tk);
     const long long blocks = (long long)pl.nqblocks * ng;
     // Workgroups the split count aims for: the register kernel runs two per CU, the LDS
-    // vector kernel one, the 32x32 matrix-core kernel up to two (with two rounds to balance),
-    // the 16x16 one a single round.
+    // vector kernel one, the 32x32 matrix-core kernel two per CU in three rounds (its blocks'
+    // key ranges differ along a causal chunk; finer splits balance them: the 512-row prefill
+    // chunk measured 284 us at 12 splits against 316 us at 8), the 16x16 one a single round.
     const int target = g_target_blocks > 0
                            ? g_target_blocks
-                           : (pl.kind == kKindMfma ? 1024
+                           : (pl.kind == kKindMfma ? 1536
                                                    : (pl.kind == kKindDec ? 512 : 256));
     int s_target = cdiv(target, blocks);
     if (s_target < 1) s_target = 1;

@@ -32,23 +32,62 @@ namespace {
 // far numerator are sums of terms of both signs that can cancel by orders of magnitude, and in
 // f32 the rounding of every term (scores, exponentials, products) would be amplified by that
 // cancellation. The near partials and the far partial itself stay f32.
+// f64 cross-lane steps on DPP: both 32-bit halves move with the same control (lanes whose
+// source is outside the row, or rows outside ROW_MASK, take `fill`).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ inline double dpp64(double v, double fill) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const unsigned long long f = (unsigned long long)__double_as_longlong(fill);
+    const int lo = __builtin_amdgcn_update_dpp((int)(unsigned)f, (int)(unsigned)b, CTRL, ROW_MASK,
+                                               0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp((int)(unsigned)(f >> 32), (int)(unsigned)(b >> 32),
+                                               CTRL, ROW_MASK, 0xF, false);
+    return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+__device__ inline double readlane64(double v, int lane) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, lane);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), lane);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Max / sum over the whole wave, returned in every lane.
 __device__ inline double far_wave_max(double v) {
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) v = fmax(v, __shfl_xor(v, k));
-    return v;
+    v = fmax(v, dpp64<kDppXor1>(v, -INFINITY));
+    v = fmax(v, dpp64<kDppXor2>(v, -INFINITY));
+    v = fmax(v, dpp64<kDppHalfMirror>(v, -INFINITY));
+    v = fmax(v, dpp64<kDppMirror>(v, -INFINITY));
+    v = fmax(v, dpp64<kDppBcast15, 0xA>(v, -INFINITY));
+    v = fmax(v, dpp64<kDppBcast31, 0xC>(v, -INFINITY));
+    return readlane64(v, 63);
 }
 __device__ inline double far_wave_sum(double v) {
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k);
+    v += dpp64<kDppXor1>(v, 0.0);
+    v += dpp64<kDppXor2>(v, 0.0);
+    v += dpp64<kDppHalfMirror>(v, 0.0);
+    v += dpp64<kDppMirror>(v, 0.0);
+    v += dpp64<kDppBcast15, 0xA>(v, 0.0);
+    v += dpp64<kDppBcast31, 0xC>(v, 0.0);
+    return readlane64(v, 63);
+}
+// Sum over each aligned group of N lanes (N = 4, 8 or 16), in every lane of the group.
+template <int N>
+__device__ inline double far_group_sum(double v) {
+    v += dpp64<kDppXor1>(v, 0.0);
+    v += dpp64<kDppXor2>(v, 0.0);
+    if constexpr (N >= 8) v += dpp64<kDppHalfMirror>(v, 0.0);
+    if constexpr (N >= 16) v += dpp64<kDppMirror>(v, 0.0);
     return v;
 }
-// Inclusive prefix sum over the wave's lanes.
-__device__ inline double far_wave_scan(double v, int lane) {
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) {
-        const double u = __shfl_up(v, k);
-        if (lane >= k) v += u;
-    }
+// Inclusive prefix sum over the wave's lanes: shifts of 1, 2, 4, 8 within each row of 16,
+// then each row adds the totals of the rows before it.
+__device__ inline double far_wave_scan(double v) {
+    v += dpp64<0x111>(v, 0.0);   // row_shr:1
+    v += dpp64<0x112>(v, 0.0);   // row_shr:2
+    v += dpp64<0x114>(v, 0.0);   // row_shr:4
+    v += dpp64<0x118>(v, 0.0);   // row_shr:8
+    v += dpp64<kDppBcast15, 0xA>(v, 0.0);
+    v += dpp64<kDppBcast31, 0xC>(v, 0.0);
     return v;
 }
 
@@ -132,7 +171,7 @@ __device__ inline Eviction evict_landmark(const FarParams& p, const GroupState& 
     // eviction rescales the zero mass by exp(-inf) = 0.
     ev.r = ev.mx == m_old ? 1.0 : exp(m_old - ev.mx);
     ev.e = evicts ? exp(fe - ev.mx) : 0.0;
-    ev.z = mass * ev.r + far_wave_scan(ev.e, lane);
+    ev.z = mass * ev.r + far_wave_scan(ev.e);
     return ev;
 }
 
@@ -269,9 +308,20 @@ __global__ __launch_bounds__(256) void far_part_kernel(const FarParams p) {
                 }
             }
         }
-        for (int k = tpl >> 1; k >= 1; k >>= 1) {
-            v += __shfl_xor(v, k);
-            v2 += __shfl_xor(v2, k);
+        if (tpl == 4) {
+            v = far_group_sum<4>(v);
+            v2 = far_group_sum<4>(v2);
+        } else if (tpl == 8) {
+            v = far_group_sum<8>(v);
+            v2 = far_group_sum<8>(v2);
+        } else if (tpl == 16) {
+            v = far_group_sum<16>(v);
+            v2 = far_group_sum<16>(v2);
+        } else {   // 32 or 64 threads per landmark (at most 8 landmarks)
+            for (int k = tpl >> 1; k >= 1; k >>= 1) {
+                v += __shfl_xor(v, k);
+                v2 += __shfl_xor(v2, k);
+            }
         }
         if (sp == 0 && a < m) {
             s_fl[a] = (double)p.scale * v;

@@ -1,41 +1,65 @@
-"""Compile the HIP library libwinattn.so for gfx950 (in-tree, next to this file)."""
+"""Compile the HIP library libwinattn.so for gfx950 (in-tree, next to this file).
+
+Each source is compiled to its own object in parallel, then the objects are linked into one
+shared library (no relocatable device code: every kernel lives with its launcher).
+"""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libwinattn.so")
+OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "attn_dec.hip", "attn_valu.hip", "attn_mfma.hip", "attn_mfma16.hip",
            "gated_prep.hip", "ring_commit.hip", "far_field.hip",
            "enc_attn.hip"]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 instructions are kept out of generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+_NOISE = "packed-fp32-ops' is not a recognized feature"
+
+
+def _run(cmd):
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if _NOISE not in ln]
+    return res.returncode, msgs
 
 
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    os.makedirs(OBJDIR, exist_ok=True)
+    jobs = []
+    for s in SOURCES:
+        obj = os.path.join(OBJDIR, os.path.splitext(s)[0] + ".o")
+        jobs.append((obj, [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
+                           os.path.join(CSRC, s), "-o", obj]))
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(workers) as ex:
+        results = list(ex.map(lambda j: _run(j[1]), jobs))
+    for (obj, cmd), (rc, msgs) in zip(jobs, results):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        if rc != 0:
+            raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
+        if verbose and msgs:
+            print("\n".join(msgs))
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+    link = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in jobs], "-o", tmp]
+    rc, msgs = _run(link)
     if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines()
-            if "packed-fp32-ops' is not a recognized feature" not in ln]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs))
+        print(" ".join(link), flush=True)
+    if rc != 0:
+        raise RuntimeError("link failed:\n" + "\n".join(msgs))
     os.replace(tmp, LIB)
     return LIB
 

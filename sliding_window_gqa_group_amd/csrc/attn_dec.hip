@@ -17,6 +17,8 @@
 //    once at the end through LDS, and the workgroup's splits in the last-arriving workgroup.
 //  - Two register buffers of K/V tiles: a split's first two tiles are requested at once, and a
 //    buffer is refilled as soon as its tile has been consumed.
+#include <type_traits>
+
 #include "winattn_dev.h"
 #include "launch.h"
 
@@ -74,7 +76,11 @@ __device__ inline void lane_group_sum_n(float* v) {
     }
 }
 
-template <int D, int NQ, bool GATED>
+// SHORT: every split of the launch has at most three tiles (the host picks it when the tiles
+// per split plus the sink tiles are at most 3), run as straight-line code; otherwise a loop with
+// two register buffers. Two instances rather than one with both paths: together they would not
+// fit the register budget of two workgroups per CU.
+template <int D, int NQ, bool GATED, bool SHORT>
 __global__ __launch_bounds__(kThreads, 2) void attn_dec_kernel(const AttnParams p) {
     using S = DecShape<D, NQ>;
     constexpr int TPK = S::TPK, F4 = S::F4, KPP = S::KPP, TK = S::TK, PASSES = S::PASSES;
@@ -91,6 +97,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dec_kernel(const AttnParams 
     const int nq_tot = p.rows * p.hpg;
     const int q0 = qb * NQ;
     const int nq = min(NQ, nq_tot - q0);
+    // ---- queries first: this lane's columns of every query, times scale*log2(e). They are
+    // requested before the key tiles, so that the first tile's arithmetic waits only for that
+    // tile and overlaps the arrival of the next one (vector loads return in issue order). The
+    // addresses are clamped to a live element of the query and padding is scaled by 0.
+    vf4 qr[NQ][F4];
+    {
+        const int d4q = p.d / 4;
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const int qi = q0 + min(j, nq - 1);
+            const int row = qi / p.hpg, gh = g * p.hpg + qi % p.hpg;
+            const float* qp = p.q + ((size_t)row * p.nh + gh) * p.d;
+#pragma unroll
+            for (int f = 0; f < F4; ++f) {
+                const int c = sl + TPK * f;
+                const bool live = (j < nq) & (c < d4q);
+                const vf4 v = *reinterpret_cast<const vf4*>(qp + 4 * (c < d4q ? c : 0));
+                // a select on the loaded value lets the compiler move the load behind a branch
+                // (and wait on it there); a factor of 0 keeps the load unconditional
+                qr[j][f] = v * (live ? p.scale_log2 : 0.0f);
+            }
+        }
+    }
     const GroupWin gw = resolve_group<GATED>(p, g);
     const int r_first = q0 / p.hpg, r_last = (q0 + nq - 1) / p.hpg;
     const int xlo = window_lo(gw.hi0 + r_first, gw.wcap);
@@ -119,58 +148,49 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dec_kernel(const AttnParams 
     // range) loads sink 0 or the block's last stream entry, and a column past d loads the key's
     // first columns. Its score is masked to -inf, so its weight is exactly 0 and 0 times finite
     // data adds nothing: no select on K, V or the accumulators is needed.
+    // Sink and stream tiles share one set of loads: the base and row are selected, not
+    // branched on, so each buffer's loads are straight-line code and the waits before a tile's
+    // arithmetic count only the loads issued after it.
+    const unsigned long long dkc = ck - rk, dks = sk - rk, dvc = cv - rv, dvs = sv - rv;
     auto load_tile = [&](vf4 (&kr)[PASSES][F4], vf4 (&vr)[PASSES][F4], int t) {
-        if (t < nst) {
+        const bool sink_tile = t < nst;   // uniform over the block
+        const int xt = xlo + (t - nst) * TK + gi;
 #pragma unroll
-            for (int ps = 0; ps < PASSES; ++ps) {
-                const int si = t * TK + ps * KPP + gi;
-                const int row = si < p.ns ? si * p.d : 0;
+        for (int ps = 0; ps < PASSES; ++ps) {
+            const int si = t * TK + ps * KPP + gi;
+            const int x = min(xt + ps * KPP, xhi - 1);
+            const bool in_ring = x < gw.xsplit;
+            int slot = gw.base + x;
+            slot = slot >= gw.mod ? slot - gw.mod : slot;
+            const int srow = si < p.ns ? si * p.d : 0;
+            const int xrow = in_ring ? slot * ss : (x - gw.xsplit) * crs;
+            const int row = sink_tile ? srow : xrow;
+            // base = ring + (chunk - ring if a chunk row) + (sink - ring if a sink tile): two
+            // independent selects of uniform differences (a select chain of the three bases
+            // becomes a lookup table in private memory)
+            const bool chunk_key = !in_ring & !sink_tile;
+            const unsigned long long bk = rk + (chunk_key ? dkc : 0ull) + (sink_tile ? dks : 0ull);
+            const unsigned long long bv = rv + (chunk_key ? dvc : 0ull) + (sink_tile ? dvs : 0ull);
 #pragma unroll
-                for (int f = 0; f < F4; ++f) {
-                    const int c = sl + TPK * f;
-                    const int off = c < d4 ? row + 4 * c : row;
-                    kr[ps][f] = *reinterpret_cast<gvf4p>(sk + 4ull * (unsigned)off);
-                    vr[ps][f] = *reinterpret_cast<gvf4p>(sv + 4ull * (unsigned)off);
-                }
-            }
-        } else {
-            const int xt = xlo + (t - nst) * TK + gi;
-#pragma unroll
-            for (int ps = 0; ps < PASSES; ++ps) {
-                const int x = min(xt + ps * KPP, xhi - 1);
-                const bool in_ring = x < gw.xsplit;
-                int slot = gw.base + x;
-                slot = slot >= gw.mod ? slot - gw.mod : slot;
-                const int row = in_ring ? slot * ss : (x - gw.xsplit) * crs;
-#pragma unroll
-                for (int f = 0; f < F4; ++f) {
-                    const int c = sl + TPK * f;
-                    const int off = c < d4 ? row + 4 * c : row;
-                    kr[ps][f] = *reinterpret_cast<gvf4p>((in_ring ? rk : ck) + 4ull * (unsigned)off);
-                    vr[ps][f] = *reinterpret_cast<gvf4p>((in_ring ? rv : cv) + 4ull * (unsigned)off);
-                }
+            for (int f = 0; f < F4; ++f) {
+                const int c = sl + TPK * f;
+                const int off = c < d4 ? row + 4 * c : row;
+                kr[ps][f] = *reinterpret_cast<gvf4p>(bk + 4ull * (unsigned)off);
+                vr[ps][f] = *reinterpret_cast<gvf4p>(bv + 4ull * (unsigned)off);
             }
         }
     };
+    // The second buffer is always filled (a one-tile split loads its tile twice), so that the
+    // first tile's arithmetic waits only for the first tile's loads on every path.
+    const int nt = t_end - t_begin;
     load_tile(kA, vA, t_begin);
-    if (t_begin + 1 < t_end) load_tile(kB, vB, t_begin + 1);
+    load_tile(kB, vB, min(t_begin + 1, t_end - 1));
 
-    // ---- queries: this lane's columns of every query, times scale*log2(e); window bounds
-    vf4 qr[NQ][F4];
+    // ---- window bounds of every query
     int qlo[NQ], qhi[NQ];
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-        const int qi = q0 + min(j, nq - 1);
-        const int row = qi / p.hpg, gh = g * p.hpg + qi % p.hpg;
-        const float* qp = p.q + ((size_t)row * p.nh + gh) * p.d;
-#pragma unroll
-        for (int f = 0; f < F4; ++f) {
-            const int c = sl + TPK * f;
-            vf4 v = {0.f, 0.f, 0.f, 0.f};
-            if (j < nq && c < d4) v = *reinterpret_cast<const vf4*>(qp + 4 * c);
-            qr[j][f] = v * p.scale_log2;
-        }
-        const int hi = gw.hi0 + row;
+        const int hi = gw.hi0 + (q0 + min(j, nq - 1)) / p.hpg;
         qlo[j] = j < nq ? window_lo(hi, gw.wcap) : 0;
         qhi[j] = j < nq ? hi : 0;
     }
@@ -186,7 +206,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dec_kernel(const AttnParams 
     }
 
     // ---- one tile: scores, online softmax of this lane group, value update
-    auto step = [&](vf4 (&kr)[PASSES][F4], vf4 (&vr)[PASSES][F4], int t) {
+    auto step = [&](vf4 (&kr)[PASSES][F4], vf4 (&vr)[PASSES][F4], int t, auto refill) {
         // partial dot products over this lane's columns (q is zero past d), then summed over
         // the lane group
         float sc[PASSES * NQ];
@@ -250,11 +270,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dec_kernel(const AttnParams 
             }
             lrun[j] = lrun[j] * corr + lsum;
         }
-        if (t + 2 < t_end) load_tile(kr, vr, t + 2);
+        if constexpr (decltype(refill)::value) {
+            if (t + 2 < t_end) load_tile(kr, vr, t + 2);
+        }
     };
-    for (int t = t_begin; t < t_end; t += 2) {
-        step(kA, vA, t);
-        if (t + 1 < t_end) step(kB, vB, t + 1);
+    if constexpr (SHORT) {
+        // Straight line for splits of up to three tiles (decode): no loop-carried buffers, so
+        // the compiler has no register copies to make, and a copy would wait for every load.
+        // A three-tile split (split 0 of a decode call: the sink tile, whose few rows arrive
+        // early, then two stream tiles) refills the first buffer as soon as it is consumed.
+        step(kA, vA, t_begin, std::false_type{});
+        if (nt == 3) load_tile(kA, vA, t_begin + 2);
+        if (nt >= 2) step(kB, vB, t_begin + 1, std::false_type{});
+        if (nt == 3) step(kA, vA, t_begin + 2, std::false_type{});
+    } else {
+        for (int t = t_begin; t < t_end; t += 2) {
+            step(kA, vA, t, std::true_type{});
+            if (t + 1 < t_end) step(kB, vB, t + 1, std::true_type{});
+        }
     }
 
     // ---- merge the lane groups (each group's state is uniform across its lanes)
@@ -333,7 +366,12 @@ __global__ __launch_bounds__(kThreads) void split_merge_kernel(const AttnParams 
 
 template <int D, int NQ, bool GATED>
 static hipError_t launch_dec_t(const AttnParams& p, dim3 grid, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_dec_kernel<D, NQ, GATED>), grid, dim3(kThreads), 0, stream, p);
+    constexpr int TK = DecShape<D, NQ>::TK;
+    const bool short_splits = p.tps + (p.ns + TK - 1) / TK <= 3;
+    if (short_splits)
+        hipLaunchKernelGGL((attn_dec_kernel<D, NQ, GATED, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((attn_dec_kernel<D, NQ, GATED, false>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -215,6 +215,45 @@ def test_sweep(shape, variant):
     assert_close(got, ref, f"{shape} {variant}")
 
 
+# The register kernel runs splits of at most three tiles (sink tiles included) as a straight-line
+# instance and longer ones as a two-buffer loop: both instances, split 0 carrying one or two sink
+# tiles (the kernel's tile is 4096 / d keys), and both merge paths.
+DEC_INSTANCES = [
+    # rows, ng, hpg, d, w, ns, meta kind, tiles per split, merge (0 auto, 1 in kernel, 2 launch)
+    (1, 2, 4, 128, 300, 40, "mix", 1, 0),      # split 0: two sink tiles + one stream tile
+    (1, 2, 4, 128, 300, 40, "full", 2, 0),     # four tiles in split 0: loop instance
+    (1, 2, 4, 128, 300, 40, "mix", 1, 1),      # three-tile split, in-kernel merge
+    (2, 1, 4, 64, 500, 70, "mix", 1, 0),       # d = 64: 64-key tiles, two sink tiles
+    (2, 3, 4, 256, 100, 17, "partial", 2, 0),  # d = 256: 16-key tiles, 8 queries, loop
+    (1, 3, 8, 256, 100, 17, "override", 1, 2), # 8 queries, three-tile split 0
+    (1, 2, 4, 128, 5000, 3, "full", 3, 0),     # one sink tile + three stream tiles: loop
+    (1, 1, 4, 128, 4096, 4, "full", 2, 0),     # the decode shape at one group
+]
+
+
+@pytest.mark.parametrize("shape", DEC_INSTANCES,
+                         ids=[f"r{s[0]}g{s[1]}h{s[2]}d{s[3]}w{s[4]}s{s[5]}{s[6]}t{s[7]}m{s[8]}"
+                              for s in DEC_INSTANCES])
+def test_register_kernel_instances(shape):
+    rows, ng, hpg, d, w, ns, kind, tps, merge = shape
+    _case(f"register kernel {shape}")
+    rng = np.random.default_rng(zlib.crc32(repr(shape).encode()))
+    inp = gen.make_chunk(rows, ng, hpg, d, w, ns, _rand_meta(rng, ng, w, kind),
+                         seed=int(rng.integers(1 << 30)))
+    ref = oracle.window_chunk(inp)
+    knobs = {B.TUNE_FORCE_KERNEL: 1, B.TUNE_TILES_PER_SPLIT: tps, B.TUNE_MERGE_KERNEL: merge}
+    try:
+        for knob, val in knobs.items():
+            B.tuning_set(knob, val)
+        plan = B.chunk_plan(rows, ng, hpg, d, w, ns)
+        assert plan[0] == 1, plan
+        got = gpu_chunk(inp).cpu().numpy()
+    finally:
+        for knob in knobs:
+            B.tuning_set(knob, 0)
+    assert_close(got, ref, f"{shape}")
+
+
 GATED_SWEEP = [
     # rows, pos0, cap, window, nh, nk, hd
     (1, 5000, 4096, 1024, 8, 2, 128),

@@ -172,7 +172,11 @@ bool gated_shape_ok(int rows, int pos0, int cap, int window, int nh, int nk, int
     return true;
 }
 
-int launch_attention(const Plan& pl, AttnParams& p, bool gated, char* ws, hipStream_t stream) {
+// far1: a one-row far call's far part (far_mode 1 for the chunk call, 2 for the gated call),
+// launched here: inside the register kernel's launch when that launch can carry it, else on
+// its own before the near kernel.
+int launch_attention(const Plan& pl, AttnParams& p, bool gated, char* ws, hipStream_t stream,
+                     const FarParams* far1 = nullptr, int far_mode = 1) {
     p.xcd_map = pl.xcd_map;
     p.tps = pl.tps;
     p.nsplit_grid = pl.nsplit;
@@ -185,9 +189,23 @@ int launch_attention(const Plan& pl, AttnParams& p, bool gated, char* ws, hipStr
         p.tickets = reinterpret_cast<unsigned int*>(ws + pl.off_tickets);
     }
     p.merge_kernel = pl.merge_kernel && pl.slots > 1 ? 1 : 0;
-    hipError_t err;
+    hipError_t err = hipSuccess;
     const dim3 grid(pl.nsplit, pl.nqblocks, p.ng);
-    if (pl.kind == kKindMfma)
+    bool fused = false;
+    if (far1) {
+        if (pl.kind == kKindDec && p.merge_kernel) {
+            err = launch_dec_far(p, *far1, pl.dpad, pl.qb, gated, far_mode, stream);
+            if (err == hipSuccess)
+                fused = true;
+            else if (err != hipErrorNotSupported)
+                return WINATTN_ELAUNCH;
+        }
+        if (!fused && launch_far_part(*far1, far_mode, stream) != hipSuccess) return WINATTN_ELAUNCH;
+        err = hipSuccess;
+    }
+    if (fused)
+        ;   // the near splits ran in the far part's launch
+    else if (pl.kind == kKindMfma)
         err = launch_mfma(p, gated, pl.dpad, stream);
     else if (pl.kind == kKindMfma16)
         err = launch_mfma16(p, gated, pl.dpad, stream);
@@ -382,9 +400,12 @@ int attn_window_chunk_far(const float* ring_k, const float* ring_v, const uint32
     f.far_slot = pl.nsplit;
     f.dpad = pl.dpad;
     f.scale = scale;
-    // A one-row call scores its own eviction inside the far-part kernel.
-    if (rows > 1 && launch_far_evict(f, st) != hipSuccess) return WINATTN_ELAUNCH;
-    if (launch_far_part(f, rows > 1 ? 0 : 1, st) != hipSuccess) return WINATTN_ELAUNCH;
+    // A one-row call scores its own eviction inside the far-part kernel, which then rides in
+    // the near kernel's launch where it can (launch_attention).
+    if (rows > 1) {
+        if (launch_far_evict(f, st) != hipSuccess) return WINATTN_ELAUNCH;
+        if (launch_far_part(f, 0, st) != hipSuccess) return WINATTN_ELAUNCH;
+    }
 
     AttnParams p{};
     p.ring_k = ring_k;
@@ -408,7 +429,7 @@ int attn_window_chunk_far(const float* ring_k, const float* ring_v, const uint32
     p.w = w;
     p.ns = ns;
     p.scale_log2 = scale * kLog2e;
-    return launch_attention(pl, p, false, ws, st);
+    return launch_attention(pl, p, false, ws, st, rows == 1 ? &f : nullptr);
 }
 
 int attn_window_commit_far(float* ring_k, float* ring_v, uint32_t* meta, const float* chunk_k,
@@ -503,7 +524,6 @@ int attn_window_gated_far(const float* q, const float* ring_k, const float* ring
     f.dpad = pl.dpad;
     f.rect = rect;
     f.scale = scale;
-    if (launch_far_part(f, 2, st) != hipSuccess) return WINATTN_ELAUNCH;
 
     AttnParams p{};
     p.ring_k = ring_k;
@@ -525,7 +545,7 @@ int attn_window_gated_far(const float* q, const float* ring_k, const float* ring
     p.w = w;
     p.ns = ns;
     p.scale_log2 = scale * kLog2e;
-    return launch_attention(pl, p, true, ws, st);
+    return launch_attention(pl, p, true, ws, st, &f, 2);
 }
 
 int attn_encoder(const float* q, const float* k, const float* v, float* out,

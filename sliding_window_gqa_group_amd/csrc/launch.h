@@ -94,6 +94,12 @@ hipError_t launch_far_evict(const FarParams& p, hipStream_t stream);
 // mode 0: evictions scored by launch_far_evict; 1: a one-row call that scores its own
 // eviction; 2: no evictions in the call (the state is current).
 hipError_t launch_far_part(const FarParams& p, int mode, hipStream_t stream);
+// A one-row far call in one launch with the register kernel: the far part of every head (mode 1
+// for the chunk call, 2 for the gated call) and the near splits. hipErrorNotSupported (nothing
+// launched) unless the plan is the register kernel with 4 queries per block and splits of at
+// most three tiles.
+hipError_t launch_dec_far(const AttnParams& p, const FarParams& f, int dpad, int qb, bool gated,
+                          int mode, hipStream_t stream);
 // Far state after a chunk; runs before the ring commit, which overwrites the evicted rows.
 hipError_t launch_far_commit(const FarParams& p, hipStream_t stream);
 struct EncParams {

@@ -76,6 +76,7 @@ FAR_CASES = [
     (5, 1, 3, 100, 6, 2, 1, "override", "positive"),      # one landmark
     (64, 4, 4, 256, 64, 0, 64, "full", "signed"),         # 16x16 matrix-core near kernel
     (2, 3, 1, 64, 1, 0, 3, "full", "positive"),           # window of one
+    (1, 2, 2, 256, 70, 3, 12, "mix", "signed"),           # one row at d = 256 (one launch)
 ]
 
 FAR_VARIANTS = {

@@ -340,7 +340,7 @@ def main():
     ap.add_argument("--calls", type=int, default=20)
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only; run with --gpus 1 (the per-GPU "
+        print("bench.py: measures one GPU only; run with --gpus 1 (the per-GPU "
               "sharding by KV group is described in the design notes)", file=sys.stderr)
         sys.exit(2)
 

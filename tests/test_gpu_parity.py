@@ -215,19 +215,23 @@ def test_sweep(shape, variant):
     assert_close(got, ref, f"{shape} {variant}")
 
 
-# The register kernel runs splits of at most three tiles (sink tiles included) as a straight-line
-# instance and longer ones as a two-buffer loop: both instances, split 0 carrying one or two sink
-# tiles (the kernel's tile is 4096 / d keys), and both merge paths.
+# The register kernel runs splits of at most three tiles (split 0 also carries the sink tiles) as
+# a straight-line instance and longer ones as a two-buffer loop (its tile is 4096 / d keys):
+# both instances, one or two sink tiles, and both merge paths.
 DEC_INSTANCES = [
     # rows, ng, hpg, d, w, ns, meta kind, tiles per split, merge (0 auto, 1 in kernel, 2 launch)
     (1, 2, 4, 128, 300, 40, "mix", 1, 0),      # split 0: two sink tiles + one stream tile
-    (1, 2, 4, 128, 300, 40, "full", 2, 0),     # four tiles in split 0: loop instance
-    (1, 2, 4, 128, 300, 40, "mix", 1, 1),      # three-tile split, in-kernel merge
+    (1, 2, 4, 128, 300, 40, "full", 4, 0),     # six tiles in split 0: loop instance
+    (1, 2, 4, 128, 300, 40, "mix", 1, 1),      # three-tile split 0, in-kernel merge
     (2, 1, 4, 64, 500, 70, "mix", 1, 0),       # d = 64: 64-key tiles, two sink tiles
     (2, 3, 4, 256, 100, 17, "partial", 2, 0),  # d = 256: 16-key tiles, 8 queries, loop
-    (1, 3, 8, 256, 100, 17, "override", 1, 2), # 8 queries, three-tile split 0
-    (1, 2, 4, 128, 5000, 3, "full", 3, 0),     # one sink tile + three stream tiles: loop
+    (1, 3, 8, 256, 100, 17, "override", 1, 2), # 8 queries, separate merge launch
+    (1, 2, 4, 128, 5000, 3, "full", 3, 0),     # three-tile stream splits, four in split 0: loop
     (1, 1, 4, 128, 4096, 4, "full", 2, 0),     # the decode shape at one group
+    (1, 2, 4, 128, 90, 5, "full", 8, 0),       # one split of four tiles: loop
+    (1, 2, 4, 128, 60, 40, "mix", 2, 0),       # one split: two sink and two stream tiles
+    (1, 1, 4, 64, 50, 3, "full", 1, 0),        # one split of two tiles
+    (2, 2, 4, 256, 200, 20, "mix", 4, 1),      # loop, in-kernel merge
 ]
 
 

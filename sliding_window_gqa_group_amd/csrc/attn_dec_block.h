@@ -143,6 +143,7 @@ __device__ __forceinline__ void attn_dec_block(const AttnParams& p, const int sp
     const int ss = (int)p.ring_ss, crs = (int)p.chunk_rs;
 
     vf4 kA[PASSES][F4], vA[PASSES][F4], kB[PASSES][F4], vB[PASSES][F4];
+    vf4 kC[PASSES][F4], vC[PASSES][F4];   // third buffer (straight-line instance only)
     // Every load reads a live row: a padding key (past the sinks, or past the block's stream
     // range) loads sink 0 or the block's last stream entry, and a column past d loads the key's
     // first columns. Its score is masked to -inf, so its weight is exactly 0 and 0 times finite
@@ -184,6 +185,12 @@ __device__ __forceinline__ void attn_dec_block(const AttnParams& p, const int sp
     const int nt = t_end - t_begin;
     load_tile(kA, vA, t_begin);
     load_tile(kB, vB, min(t_begin + 1, t_end - 1));
+    // A three-tile split (split 0 of a decode call: the sink tile and two stream tiles) has its
+    // third tile requested up front too, so it does not queue behind the whole ring's traffic
+    // after the first tile's arithmetic.
+    if constexpr (SHORT) {
+        if (nt == 3) load_tile(kC, vC, t_begin + 2);
+    }
 
     // ---- window bounds of every query
     int qlo[NQ], qhi[NQ];
@@ -276,12 +283,9 @@ __device__ __forceinline__ void attn_dec_block(const AttnParams& p, const int sp
     if constexpr (SHORT) {
         // Straight line for splits of up to three tiles (decode): no loop-carried buffers, so
         // the compiler has no register copies to make, and a copy would wait for every load.
-        // A three-tile split (split 0 of a decode call: the sink tile, whose few rows arrive
-        // early, then two stream tiles) refills the first buffer as soon as it is consumed.
         step(kA, vA, t_begin, std::false_type{});
-        if (nt == 3) load_tile(kA, vA, t_begin + 2);
         if (nt >= 2) step(kB, vB, t_begin + 1, std::false_type{});
-        if (nt == 3) step(kA, vA, t_begin + 2, std::false_type{});
+        if (nt == 3) step(kC, vC, t_begin + 2, std::false_type{});
     } else {
         for (int t = t_begin; t < t_end; t += 2) {
             step(kA, vA, t, std::true_type{});

@@ -14,9 +14,12 @@
 //    score in every lane of the group, exactly where the value update needs it.
 //  - Each lane group is its own split: it keeps a running max, sum and accumulator per query
 //    over the keys it owns. No LDS and no barrier inside the tile loop; the groups are merged
-//    once at the end through LDS, and the workgroup's splits in the last-arriving workgroup.
-//  - Two register buffers of K/V tiles: a split's first two tiles are requested at once, and a
-//    buffer is refilled as soon as its tile has been consumed.
+//    once at the end through LDS, and the workgroups' splits by the merge launch (or by the
+//    last-arriving workgroup).
+//  - The queries are requested before the key tiles, and every tile load is straight-line code,
+//    so a tile's arithmetic waits only for that tile's loads. A split of up to three tiles has
+//    all of them requested at once (straight-line instance); a longer split keeps two register
+//    buffers, each refilled as soon as its tile has been consumed (loop instance).
 #pragma once
 #include <type_traits>
 

@@ -180,6 +180,26 @@ def bench_others(args, torch, B, gen, acct):
                      "cache": "hot (inputs resident, reused)"}
         del t, out, ws
         torch.cuda.empty_cache()
+    # decode over a 32768-slot window (268 MB of K/V per call): three input sets at distinct
+    # addresses (805 MB, beyond the 256 MB Infinity Cache), so K/V come from HBM
+    inp = gen.decode_long()
+    base = chunk_tensors(inp, torch, dev)
+    sets = [base] + [{k: (v.clone() if v is not None else None) for k, v in base.items()}
+                     for _ in range(2)]
+    outs = [torch.empty((inp.rows, inp.nh, inp.d), dtype=torch.float32, device=dev) for _ in range(3)]
+    ws = B.Workspace(dev)
+    ws.get(B.chunk_workspace_bytes(inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns))
+    ms, _, _ = time_calls(torch, lambda i: run_chunk(B, sets[i], inp.scale, outs[i], ws), 3, 60, 6)
+    kern = B.chunk_plan(inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns)
+    res["decode_w32768"] = {"ms": round(ms, 5),
+                            "kv_gbs": round(acct.unique_kv_bytes(inp) / ms / 1e6, 2),
+                            "hbm_frac": round(acct.total_bytes(inp) / ms / 1e6 / HBM_PEAK_GBS, 4),
+                            "rows_per_s": round(inp.rows / ms * 1e3, 1),
+                            "kernel": KERNEL_NAMES[kern[0]], "splits": kern[2],
+                            "keys_per_split": kern[3],
+                            "cache": "rotating (3 input sets, 805 MB)"}
+    del base, sets, outs, ws
+    torch.cuda.empty_cache()
     for name, rows in (("decode_far_m32", 1), ("chunk64_far_m32", 64)):
         # the decode shapes with a far field of 32 landmarks per head in every group (full
         # rings, so every row evicts); the near-only call on the same inputs is timed beside it

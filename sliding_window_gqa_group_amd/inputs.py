@@ -162,6 +162,16 @@ def gated() -> GatedInputs:
     return make_gated(64, 20000, 8192, 1024, 16, 4, 256, seed=3, name="gated")
 
 
+def decode_long(seed: int = 5) -> ChunkInputs:
+    """The decode shapes over a long window: 1 row, 8 KV groups x 4 heads, d=128, w=32768 full
+    ring, seeded head offsets, 4 sinks (268 MB of K/V per call)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ng, w = 8, 32768
+    heads = rng.integers(0, w, size=ng)
+    meta = np.array([(w, int(h), 0, 0) for h in heads], dtype=np.uint32)
+    return _fill_chunk(rng, "decode_long", 1, ng, 4, 128, w, 4, meta, seed, None)
+
+
 def large_meta(seed: int = 4, ng: int = 8, w: int = 32768):
     """Per-group (len, head, 0, window override) for the Large workload, plus its generator."""
     rng = np.random.Generator(np.random.PCG64(seed))

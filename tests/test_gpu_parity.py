@@ -105,6 +105,17 @@ def test_decode():
     assert_close(gpu_chunk(inp).cpu().numpy(), oracle.window_chunk(inp), "decode")
 
 
+def test_decode_long_window():
+    """Decode over a 32768-slot full ring (the register kernel's loop instance, 16 tiles per
+    split), and the same row over the large workload's per-group overrides and partial rings."""
+    _case("decode, w = 32768")
+    inp = gen.decode_long()
+    assert_close(gpu_chunk(inp).cpu().numpy(), oracle.window_chunk(inp), "decode w=32768")
+    _, meta = gen.large_meta(seed=6)
+    inp = gen.make_chunk(1, 8, 4, 128, 32768, 4, meta, seed=6)
+    assert_close(gpu_chunk(inp).cpu().numpy(), oracle.window_chunk(inp), "decode, overrides")
+
+
 def _sampled_rows(rows, k, seed):
     rng = np.random.default_rng(seed)
     fixed = {0, 1, 2, 15, 16, 31, 32, 33, 127, 128, rows // 2, rows - 2, rows - 1}

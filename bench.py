@@ -330,9 +330,9 @@ def counter_run(args, torch, B, gen):
                                 g.scale, g.eps, out=out)
     else:
         inp = {"tiny": gen.tiny, "decode": gen.decode, "prefill": gen.prefill,
-               "large": gen.large}[name]()
+               "large": gen.large, "decode_long": gen.decode_long}[name]()
         base = chunk_tensors(inp, torch, dev)
-        n_sets = args.sets if name in ("tiny", "decode") else 1
+        n_sets = {"tiny": args.sets, "decode": args.sets, "decode_long": 3}.get(name, 1)
         sets = [base] + [{k: (v.clone() if v is not None else None) for k, v in base.items()}
                          for _ in range(n_sets - 1)]
         out = torch.empty((inp.rows, inp.nh, inp.d), dtype=torch.float32, device=dev)
@@ -355,7 +355,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--counter-run", choices=["tiny", "decode", "prefill", "large", "gated",
-                                              "encoder", "decode_far"],
+                                              "encoder", "decode_far", "decode_long"],
                     help="untimed calls of one workload for rocprofv3 counter passes; no JSON")
     ap.add_argument("--calls", type=int, default=20)
     args = ap.parse_args()

@@ -224,6 +224,10 @@ def test_workspace_queries(lib):
 
 def test_plans_of_the_named_workloads(lib):
     assert B.chunk_plan(1, 8, 4, 128, 4096, 4)[0] == 1          # decode: register split-K
+    # decode: 64 splits of two 32-key tiles per group (512 workgroups, two per CU); over a
+    # 32768-slot window, 64 splits of 16 tiles
+    assert B.chunk_plan(1, 8, 4, 128, 4096, 4) == (1, 4, 64, 64)
+    assert B.chunk_plan(1, 8, 4, 128, 32768, 4) == (1, 4, 64, 512)
     assert B.chunk_plan(4, 8, 4, 128, 4096, 4)[0] == 3          # 16 queries: LDS vector kernel
     assert B.chunk_plan(512, 8, 4, 128, 4096, 4)[0] == 2        # prefill: matrix cores
     k, qb, splits, kps = B.chunk_plan(2048, 8, 8, 128, 32768, 4)

@@ -278,6 +278,13 @@ int attn_mfma_layout_probe(float* out, void* stream);
  * out: device [64][4] floats; out[lane*4 + r] = accumulator r of lane `lane`. */
 int attn_mfma16_layout_probe(float* out, void* stream);
 
+/* Measurement aid: the achievable HBM read rate for a buffer of a given size. One launch reads
+ * every 16-byte element of src[0 .. bytes) once (coalesced 16-byte loads, eight in flight per
+ * thread, one workgroup of 256 threads per 32 KiB) and folds them into per-thread sums; sink
+ * (device, 256 floats) is written only if the data holds a NaN. bytes: a positive multiple of
+ * 16; src 16-byte aligned. Returns 0, WINATTN_EINVAL or WINATTN_ELAUNCH. */
+int attn_read_probe(const void* src, size_t bytes, float* sink, void* stream);
+
 /* Tuning knobs for tests and benchmarks (process-wide, not thread-safe; 0 = automatic).
  * They change the launch plan and therefore the workspace size: query the size after setting
  * them. */

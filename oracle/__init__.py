@@ -69,6 +69,8 @@ def load_library(path: str):
                                             i, i, i, i, i, i, f, i]
     lib.oracle_encoder_attention.argtypes = [_f32p, _f32p, _f32p, _f32p, _u32p, i, i, i, i, i,
                                              i, i, i, i, f]
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = ctypes.c_int
     for name in ("oracle_encoder_attention", "oracle_window_chunk", "oracle_window_chunk_select",
                  "oracle_window_chunk_weights", "oracle_window_gated", "oracle_meta_ok",
                  "oracle_window_commit", "oracle_window_chunk_far", "oracle_window_commit_far",
@@ -268,6 +270,11 @@ def encoder_attention(inp, out=None) -> np.ndarray:
     if rc != 0:
         raise ValueError(f"oracle_encoder_attention rejected its arguments (rc={rc})")
     return out
+
+
+def threads() -> int:
+    """Threads the oracle's parallel loops use (its OpenMP team size)."""
+    return int(_load().oracle_threads())
 
 
 def meta_ok(meta, ng: int, w: int) -> bool:

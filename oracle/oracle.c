@@ -34,6 +34,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* Per-group window: a non-zero override in meta field 3 replaces the default w (`wgf`). */
 static uint32_t group_window(const uint32_t *meta, int g, int w) {
@@ -749,6 +752,15 @@ int oracle_encoder_attention(const float *q, const float *k, const float *v, flo
         free(kp); free(vp); free(sc); free(acc); free(qd);
     }
     return bad ? -1 : 0;
+}
+
+/* Threads the parallel loops of this library use (1 when built without OpenMP). */
+int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
 
 /* Host-side meta validation with the same rules the oracle enforces (1 = valid). */

@@ -1,21 +1,32 @@
 """Summaries of rocprofv3 output for the profiles folder.
 
 Reads the CSV files rocprofv3 writes (`--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` counter
-collections, `--kernel-trace --stats` kernel statistics and traces) and prints markdown tables;
-`decode-json` writes the calibrated per-call HBM bytes of the decode workload that `bench.py`
-reports as `roofline.traffic`.
+collections, `--pmc` SQ counter collections, `--kernel-trace --stats` kernel statistics and
+traces) and prints markdown tables; `decode-json` writes the calibrated per-call HBM bytes of
+the decode workload that `bench.py` reports as `roofline.traffic`; `mfma` turns one SQ counter
+pass into matrix-core utilisation per kernel.
 
 Calibration: the counter run first copies 64 MiB device to device (`__amd_rocclr_copyBuffer`,
 reading and writing exactly 64 MiB); each counter is scaled by 64 MiB / its reading for that
 copy. Bytes are per dispatch: the median over the workload's dispatches of each kernel.
 
-    python -m sliding_window_gqa_group_amd.profile_summary counters <pmc dir> <title>
-    python -m sliding_window_gqa_group_amd.profile_summary stats <kernel_stats.csv>
-    python -m sliding_window_gqa_group_amd.profile_summary trace <kernel_trace.csv> <name substring>
-    python -m sliding_window_gqa_group_amd.profile_summary decode-json <pmc dir> <out.json>
+    python profile_summary.py counters <pmc dir> <title>
+    python profile_summary.py stats <kernel_stats.csv>
+    python profile_summary.py trace <kernel_trace.csv> <name substring>
+    python profile_summary.py decode-json <pmc dir> <out.json>
+    python profile_summary.py mfma <counter_collection.csv> <title>
+
+Matrix-core utilisation (`mfma`): the pass collects SQ_INSTS_VALU_MFMA_F32 (f32 matrix
+instructions issued, one per wave instruction), SQ_VALU_MFMA_BUSY_CYCLES (matrix-unit busy
+cycles summed over every SIMD), GRBM_GUI_ACTIVE (GPU-busy cycles summed over the 8 XCDs) and
+SQ_BUSY_CYCLES. Per dispatch: busy fraction = MFMA busy cycles / (GRBM_GUI_ACTIVE / 8 x 1024
+SIMDs), the share of all matrix-unit cycles of the dispatch's lifetime that did work; and the
+issued instructions times the flops of one instruction (`--flops-per-inst`) against the
+algorithmic flops, which shows padding and masked work.
 """
 from __future__ import annotations
 
+import argparse
 import csv
 import glob
 import json
@@ -119,6 +130,46 @@ def decode_json(pmc_dir: str, out_path: str, digest: str) -> dict:
     return doc
 
 
+XCDS = 8
+SIMDS = 1024
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_F32", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE",
+                 "SQ_BUSY_CYCLES")
+
+
+def mfma_values(path: str):
+    """{kernel: {counter: [value per dispatch]}} of the winattn kernels in one SQ pass."""
+    per = {}
+    for r in _rows(path):
+        name = r["Kernel_Name"]
+        if WINATTN not in name or r["Counter_Name"] not in MFMA_COUNTERS:
+            continue
+        per.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def mfma_md(path: str, title: str, expected=None) -> str:
+    """Markdown table of matrix-core use per kernel. `expected` maps a kernel-name substring to
+    (flops of one matrix instruction, algorithmic flops per dispatch)."""
+    lines = [f"### {title}", "",
+             "| kernel | dispatches | MFMA instructions | MFMA busy cycles | GPU-busy cycles per XCD "
+             "| busy fraction | issued flops / algorithmic |",
+             "|---|---|---|---|---|---|---|"]
+    for name, c in mfma_values(path).items():
+        med = {k: statistics.median(v) for k, v in c.items()}
+        n = len(c.get("SQ_INSTS_VALU_MFMA_F32", []))
+        inst = med.get("SQ_INSTS_VALU_MFMA_F32", 0.0)
+        busy = med.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        gui = med.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+        frac = busy / (gui * SIMDS) if gui > 0 else 0.0
+        ratio = "—"
+        for needle, (fpi, alg) in (expected or {}).items():
+            if needle in name and alg > 0:
+                ratio = f"{inst * fpi / alg:.3f}"
+        short = name if len(name) <= 90 else name[:87] + "..."
+        lines.append(f"| `{short}` | {n} | {inst:.0f} | {busy:.0f} | {gui:.0f} | {frac:.3f} | {ratio} |")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv):
     if len(argv) < 2:
         print(__doc__)
@@ -133,10 +184,18 @@ def main(argv):
         print(f"{len(d)} dispatches, mean {statistics.mean(d):.0f} ns, median "
               f"{statistics.median(d):.0f} ns")
     elif cmd == "decode-json":
-        root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-        sys.path.insert(0, root)
-        import bench
-        print(json.dumps(decode_json(argv[2], argv[3], bench.kernel_source_digest()), indent=1))
+        sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+        from sliding_window_gqa_group_amd.build import source_digest
+        print(json.dumps(decode_json(argv[2], argv[3], source_digest()), indent=1))
+    elif cmd == "mfma":
+        ap = argparse.ArgumentParser(prog="profile_summary.py mfma")
+        ap.add_argument("csv")
+        ap.add_argument("title")
+        ap.add_argument("--expect", nargs=3, action="append", default=[],
+                        metavar=("KERNEL_SUBSTRING", "FLOPS_PER_INST", "ALG_FLOPS"))
+        a = ap.parse_args(argv[2:])
+        exp = {k: (float(f), float(g)) for k, f, g in a.expect}
+        print(mfma_md(a.csv, a.title, exp))
     else:
         print(__doc__)
         return 2

@@ -74,6 +74,8 @@ def load(path: str = LIB_PATH):
     lib.attn_window_gated_far_workspace.restype = _sz
     lib.attn_encoder.argtypes = [_vp] * 5 + [_i] * 10 + [_f, _vp]
     lib.attn_encoder.restype = _i
+    lib.attn_read_probe.argtypes = [_vp, _sz, _vp, _vp]
+    lib.attn_read_probe.restype = _i
     lib.attn_tuning_set.argtypes = [_i, _i]
     lib.attn_tuning_set.restype = _i
     lib.attn_strerror.argtypes = [_i]
@@ -388,6 +390,17 @@ def mfma16_layout_probe(device="cuda", stream=None):
     if rc != OK:
         raise WinattnError("attn_mfma16_layout_probe", rc)
     return out
+
+
+def read_probe(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """One plain streaming read of every byte of the contiguous device tensor `src` (the
+    achievable HBM read rate; see attn_read_probe in include/winattn.h). sink: 256 floats."""
+    if sink.numel() < 256:
+        raise ValueError("sink must hold 256 floats")
+    rc = load().attn_read_probe(_ptr(src, "src", (src.dtype,)), src.numel() * src.element_size(),
+                                _ptr(sink, "sink"), _stream_ptr(stream, src.device))
+    if rc != OK:
+        raise WinattnError("attn_read_probe", rc)
 
 
 def workspace_init(buf: torch.Tensor, stream=None) -> None:

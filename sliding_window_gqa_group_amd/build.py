@@ -5,6 +5,7 @@ shared library (no relocatable device code: every kernel lives with its launcher
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -18,7 +19,7 @@ LIB = os.path.join(HERE, "libwinattn.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "attn_dec.hip", "attn_valu.hip", "attn_mfma.hip", "attn_mfma16.hip",
            "gated_prep.hip", "ring_commit.hip", "far_field.hip",
-           "enc_attn.hip", "attn_dec_far.hip"]
+           "enc_attn.hip", "attn_dec_far.hip", "read_probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -27,6 +28,16 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 _NOISE = "packed-fp32-ops' is not a recognized feature"
+
+
+def source_digest() -> str:
+    """Digest of the kernel sources (every file under csrc/): measurements taken on other
+    sources are not reported as current."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def _run(cmd):

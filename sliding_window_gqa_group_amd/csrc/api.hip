@@ -267,11 +267,19 @@ size_t attn_window_chunk_workspace(int rows, int ng, int hpg, int d, int w, int 
     return make_plan(rows, ng, hpg, d, w, ns, 0).bytes;
 }
 
-int attn_window_chunk(const float* ring_k, const float* ring_v, const uint32_t* meta,
-                      const float* sink_k, const float* sink_v, const float* q,
-                      const float* chunk_k, const float* chunk_v, float* out, int rows, int ng,
-                      int hpg, int d, int w, int ns, float scale, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace winattn {
+namespace {
+
+// attn_window_chunk with its workspace given: argument checks, the plan, the launches.
+// `ws_cap` = 0 and `ws` = NULL ask only for the checks (the return is the plan's workspace
+// bytes as a positive value, or a negative code), so a caller can size its scratch first.
+long long chunk_call(const float* ring_k, const float* ring_v, const uint32_t* meta,
+                     const float* sink_k, const float* sink_v, const float* q,
+                     const float* chunk_k, const float* chunk_v, float* out, int rows, int ng,
+                     int hpg, int d, int w, int ns, float scale, void* workspace,
+                     size_t workspace_bytes, void* stream, bool check_only) {
     if (!chunk_shape_ok(rows, ng, hpg, d, w, ns) || !std::isfinite(scale)) return WINATTN_EINVAL;
     if (!ring_k || !ring_v || !meta || !q || !chunk_k || !chunk_v || !out) return WINATTN_EINVAL;
     if (ns > 0 && (!sink_k || !sink_v)) return WINATTN_EINVAL;
@@ -280,6 +288,7 @@ int attn_window_chunk(const float* ring_k, const float* ring_v, const uint32_t* 
         return WINATTN_EINVAL;
     if (ns > 0 && (!aligned16(sink_k) || !aligned16(sink_v))) return WINATTN_EINVAL;
     const Plan pl = make_plan(rows, ng, hpg, d, w, ns, 0);
+    if (check_only) return (long long)pl.bytes;
     if (pl.bytes > 0 && (!workspace || workspace_bytes < pl.bytes)) return WINATTN_EWORKSPACE;
     if (pl.bytes > 0 && !aligned16(workspace)) return WINATTN_EINVAL;
 
@@ -308,6 +317,21 @@ int attn_window_chunk(const float* ring_k, const float* ring_v, const uint32_t* 
     return launch_attention(pl, p, false, static_cast<char*>(workspace),
                             static_cast<hipStream_t>(stream));
 }
+
+}  // namespace
+}  // namespace winattn
+
+extern "C" {
+
+int attn_window_chunk(const float* ring_k, const float* ring_v, const uint32_t* meta,
+                      const float* sink_k, const float* sink_v, const float* q,
+                      const float* chunk_k, const float* chunk_v, float* out, int rows, int ng,
+                      int hpg, int d, int w, int ns, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    return (int)chunk_call(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v, out, rows,
+                           ng, hpg, d, w, ns, scale, workspace, workspace_bytes, stream, false);
+}
+
 
 namespace {
 
@@ -689,6 +713,13 @@ int attn_mfma_layout_probe(float* out, void* stream) {
 int attn_mfma16_layout_probe(float* out, void* stream) {
     if (!out) return WINATTN_EINVAL;
     return launch_mfma16_probe(out, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? WINATTN_OK
+               : WINATTN_ELAUNCH;
+}
+
+int attn_read_probe(const void* src, size_t bytes, float* sink, void* stream) {
+    if (!src || !sink || !aligned16(src) || bytes < 16 || bytes % 16 != 0) return WINATTN_EINVAL;
+    return launch_read_probe(src, bytes, sink, static_cast<hipStream_t>(stream)) == hipSuccess
                ? WINATTN_OK
                : WINATTN_ELAUNCH;
 }

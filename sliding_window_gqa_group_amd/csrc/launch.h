@@ -120,6 +120,10 @@ struct EncParams {
 hipError_t launch_enc_attn(const EncParams& p, int dpad, hipStream_t stream);
 int enc_query_block();
 
+// Plain streaming read of `bytes` (a multiple of 16) at `src`; `sink` ([256] floats) is written
+// only if the data holds a NaN.
+hipError_t launch_read_probe(const void* src, size_t bytes, float* sink, hipStream_t stream);
+
 constexpr int kFarMaxRows = 64;
 constexpr int kFarMaxLandmarks = 64;
 

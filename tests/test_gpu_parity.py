@@ -1,8 +1,7 @@
 """Parity of the HIP path (through the C-ABI) with the CPU oracle, on seeded synthetic inputs.
 
 Bar (per element): |gpu - oracle| <= max(1e-4 * |oracle|, 1e-5). The named workloads run at
-their full sizes in the launch plan the benchmark uses; where the oracle would be slow (the
-512- and 2048-row chunks) it computes sampled (row, head) outputs one by one.
+their full sizes in the launch plan the benchmark uses, and every output is compared.
 """
 import zlib
 
@@ -116,33 +115,21 @@ def test_decode_long_window():
     assert_close(gpu_chunk(inp).cpu().numpy(), oracle.window_chunk(inp), "decode, overrides")
 
 
-def _sampled_rows(rows, k, seed):
-    rng = np.random.default_rng(seed)
-    fixed = {0, 1, 2, 15, 16, 31, 32, 33, 127, 128, rows // 2, rows - 2, rows - 1}
-    pick = set(int(x) for x in rng.choice(rows, size=min(k, rows), replace=False))
-    return sorted(r for r in fixed | pick if 0 <= r < rows)
-
-
-def test_prefill_sampled_rows():
+def test_prefill():
+    """Every output of the 512-row chunk (the 32x32 matrix-core kernel at its benchmark plan)."""
     _case("prefill")
     inp = gen.prefill()
-    got = gpu_chunk(inp).cpu().numpy()
-    rows = _sampled_rows(inp.rows, 24, 2)
-    rr = np.repeat(rows, inp.nh)
-    hh = np.tile(np.arange(inp.nh), len(rows))
-    ref = oracle.window_chunk_select(inp, rr, hh)
-    assert_close(got[rr, hh], ref, "prefill")
+    assert_close(gpu_chunk(inp).cpu().numpy(), oracle.window_chunk(inp), "prefill")
 
 
-def test_large_sampled():
+def test_large():
+    """Every output of the 2048-row chunk over 32768-slot rings with per-group overrides and
+    partial rings (the paths that only run at full size: long windows, the split caps, the
+    round-robin work order). The oracle needs about 30 s of one host's cores here."""
     _case("large")
     inp = gen.large()
     got = gpu_chunk(inp).cpu().numpy()
-    rng = np.random.default_rng(44)
-    rows = np.concatenate([[0, 0, 1, 2047, 2047, 1024], rng.integers(0, inp.rows, 250)])
-    heads = np.concatenate([[0, 63, 8, 0, 63, 31], rng.integers(0, inp.nh, 250)])
-    ref = oracle.window_chunk_select(inp, rows, heads)
-    assert_close(got[rows, heads], ref, "large")
+    assert_close(got, oracle.window_chunk(inp), "large")
 
 
 def test_gated():

@@ -1,8 +1,10 @@
 """The rocprofv3 summariser: calibration against the 64 MiB copy, per-dispatch medians."""
 import csv
 import os
+import sys
 
-from sliding_window_gqa_group_amd import profile_summary as P
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+import profile_summary as P  # noqa: E402
 
 FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
 
@@ -33,3 +35,23 @@ def test_counters_are_scaled_by_the_copy(tmp_path):
     doc = P.decode_json(str(tmp_path), str(tmp_path / "out.json"), "digest")
     assert doc["hbm_bytes_per_launch"] == int(rb + wb)
     assert doc["kernel_source_digest"] == "digest"
+
+
+def test_mfma_utilisation(tmp_path):
+    k = "void winattn::attn_mfma_kernel<128, false>(winattn::AttnParams)"
+    path = str(tmp_path / "sq_counter_collection.csv")
+    rows = []
+    for inst, busy, gui in ((1000.0, 64000.0, 8000.0), (1000.0, 64000.0, 8000.0)):
+        rows += [(k, "SQ_INSTS_VALU_MFMA_F32", inst), (k, "SQ_VALU_MFMA_BUSY_CYCLES", busy),
+                 (k, "GRBM_GUI_ACTIVE", gui)]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, c, v) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i // 3, "Kernel_Name": name, "Counter_Name": c,
+                        "Counter_Value": v})
+    md = P.mfma_md(path, "t", {"attn_mfma_kernel": (4096.0, 2048000.0)})
+    line = [ln for ln in md.splitlines() if "attn_mfma_kernel" in ln][0]
+    cells = [c.strip() for c in line.split("|")]
+    # busy 64000 over (8000 / 8 XCDs) x 1024 SIMDs; 1000 x 4096 flops over 2048000
+    assert cells[2] == "2" and cells[6] == f"{64000 / (1000 * 1024):.3f}" and cells[7] == "2.000"

@@ -92,6 +92,29 @@ int attn_window_chunk(const float* ring_k, const float* ring_v, const uint32_t* 
 size_t attn_window_chunk_workspace(int rows, int ng, int hpg, int d, int w, int ns);
 
 /*
+ * attn_window_chunk_noalloc — attn_window_chunk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same operation, arguments, layouts and result, with no workspace argument. The split
+ * partials and split counters live instead in a static device array of
+ * WINATTN_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds for the life of the
+ * process (its address is looked up on the first call on a device, which also clears the
+ * counters with a fill kernel on `stream`). Nothing is allocated or freed, by this call or the
+ * library routines it uses.
+ *   - Calls whose plan needs more scratch than WINATTN_NOALLOC_SCRATCH_BYTES (the need is what
+ *     attn_window_chunk_workspace reports for the same sizes) return WINATTN_EWORKSPACE and
+ *     launch nothing.
+ *   - All calls on one GPU share that GPU's array, which keeps the last call's contents: two
+ *     calls that may overlap on one GPU (other streams, other threads) race and must not be
+ *     made. Calls in sequence on one stream are safe (the counters are left at zero).
+ * Returns as attn_window_chunk, plus WINATTN_ELAUNCH if the device array cannot be located.
+ */
+#define WINATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+int attn_window_chunk_noalloc(const float* ring_k, const float* ring_v, const uint32_t* meta,
+                              const float* sink_k, const float* sink_v, const float* q,
+                              const float* chunk_k, const float* chunk_v, float* out, int rows,
+                              int ng, int hpg, int d, int w, int ns, float scale, void* stream);
+
+/*
  * attn_window_gated — the gated unit-head call for rows at positions pos0 .. pos0+rows-1
  * (dory page). Steps, in this order:
  *  1. For each row and KV head kh: x, y = the halves of yk[row][kh]; c, s = the halves of

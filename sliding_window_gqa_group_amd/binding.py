@@ -44,6 +44,8 @@ def load(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     lib.attn_window_chunk.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _vp, _sz, _vp]
     lib.attn_window_chunk.restype = _i
+    lib.attn_window_chunk_noalloc.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _vp]
+    lib.attn_window_chunk_noalloc.restype = _i
     lib.attn_window_chunk_workspace.argtypes = [_i] * 6
     lib.attn_window_chunk_workspace.restype = _sz
     lib.attn_window_gated.argtypes = [_vp] * 10 + [_i] * 7 + [_f, _f, _vp, _sz, _vp]
@@ -210,6 +212,29 @@ def attn_window_chunk(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v,
         _ptr(out, "out"), rows, ng, nh // ng, d, w, ns, float(scale), wp, wb, st)
     if rc != OK:
         raise WinattnError("attn_window_chunk", rc)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # WINATTN_NOALLOC_SCRATCH_BYTES
+
+
+def attn_window_chunk_noalloc(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v, scale,
+                              out, stream=None):
+    """attn_window_chunk with the library's static per-device scratch instead of a workspace
+    (see attn_window_chunk_noalloc in include/winattn.h). `out` is required: nothing is
+    allocated on this path."""
+    ng, w, d = ring_k.shape
+    rows, nh, dq = q.shape
+    if dq != d or nh % ng or tuple(out.shape) != (rows, nh, d):
+        raise ValueError("q and out must be [rows][ng*hpg][d] matching ring_k [ng][w][d]")
+    ns = 0 if sink_k is None else sink_k.shape[1]
+    rc = load().attn_window_chunk_noalloc(
+        _ptr(ring_k, "ring_k"), _ptr(ring_v, "ring_v"),
+        _ptr(meta, "meta", (torch.int32, torch.uint32)), _ptr(sink_k, "sink_k"),
+        _ptr(sink_v, "sink_v"), _ptr(q, "q"), _ptr(chunk_k, "chunk_k"), _ptr(chunk_v, "chunk_v"),
+        _ptr(out, "out"), rows, ng, nh // ng, d, w, ns, float(scale), _stream_ptr(stream, q.device))
+    if rc != OK:
+        raise WinattnError("attn_window_chunk_noalloc", rc)
     return out
 
 

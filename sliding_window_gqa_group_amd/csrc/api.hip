@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "launch.h"
 #include "winattn.h"
@@ -332,6 +333,60 @@ int attn_window_chunk(const float* ring_k, const float* ring_v, const uint32_t* 
                            ng, hpg, d, w, ns, scale, workspace, workspace_bytes, stream, false);
 }
 
+}  // extern "C"
+
+// Scratch of attn_window_chunk_noalloc: split partials and split counters of the calls whose
+// caller cannot allocate. Every GPU the library runs on holds its own copy, zero when the code
+// object is loaded, for the life of the process. In host code `scratch` is only a handle for
+// hipGetSymbolAddress: its device address is looked up once per device and used from then on.
+static __device__ __align__(256) unsigned char scratch[WINATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace winattn {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, once looked up
+
+// The current device's copy of `scratch`. On the first call on a device (that device current):
+// hipGetSymbolAddress, then the split counters at its start are cleared by a fill kernel on
+// `stream` (they must start at zero; every call leaves them at zero).
+int scratch_on_current_device(void** ptr, hipStream_t stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return WINATTN_ELAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return WINATTN_ELAUNCH;
+        if (launch_fill_zero(p, kTicketBytes, stream) != hipSuccess) return WINATTN_ELAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return WINATTN_OK;
+}
+
+}  // namespace
+}  // namespace winattn
+
+extern "C" {
+
+int attn_window_chunk_noalloc(const float* ring_k, const float* ring_v, const uint32_t* meta,
+                              const float* sink_k, const float* sink_v, const float* q,
+                              const float* chunk_k, const float* chunk_v, float* out, int rows,
+                              int ng, int hpg, int d, int w, int ns, float scale, void* stream) {
+    const long long need = chunk_call(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v,
+                                      out, rows, ng, hpg, d, w, ns, scale, nullptr, 0, stream, true);
+    if (need < 0) return (int)need;
+    if (need > (long long)WINATTN_NOALLOC_SCRATCH_BYTES) return WINATTN_EWORKSPACE;
+    void* ws = nullptr;
+    if (need > 0) {
+        const int rc = scratch_on_current_device(&ws, static_cast<hipStream_t>(stream));
+        if (rc != WINATTN_OK) return rc;
+    }
+    return (int)chunk_call(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v, out, rows,
+                           ng, hpg, d, w, ns, scale, ws, WINATTN_NOALLOC_SCRATCH_BYTES, stream,
+                           false);
+}
 
 namespace {
 

@@ -273,3 +273,34 @@ def test_workspace_init_validation(lib):
     assert lib.attn_workspace_init(None, 0, None) == 0
     assert lib.attn_workspace_init(None, 64, None) == B.EINVAL
     assert lib.attn_workspace_init(FAKE + 4, 64, None) == B.EINVAL
+
+
+def _noalloc(lib, **kw):
+    a = dict(ring_k=FAKE, ring_v=FAKE, meta=FAKE, sink_k=FAKE, sink_v=FAKE, q=FAKE, chunk_k=FAKE,
+             chunk_v=FAKE, out=FAKE, rows=1, ng=1, hpg=1, d=64, w=16, ns=0, scale=0.125,
+             stream=None)
+    a.update(kw)
+    return lib.attn_window_chunk_noalloc(a["ring_k"], a["ring_v"], a["meta"], a["sink_k"],
+                                         a["sink_v"], a["q"], a["chunk_k"], a["chunk_v"], a["out"],
+                                         a["rows"], a["ng"], a["hpg"], a["d"], a["w"], a["ns"],
+                                         a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(rows=0), dict(d=6), dict(scale=float("nan")), dict(q=None), dict(ns=2, sink_v=None),
+    dict(out=FAKE + 8),
+])
+def test_noalloc_rejects_invalid_arguments(lib, kw):
+    assert _noalloc(lib, **kw) == B.EINVAL
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch(lib):
+    """A call whose plan needs more than the static scratch is refused before any device work."""
+    shape = dict(rows=2048, ng=8, hpg=8, d=128, w=32768, ns=4)
+    need = B.chunk_workspace_bytes(*shape.values())
+    assert need > B.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(lib, **shape) == B.EWORKSPACE
+    import re
+    hdr = open(B.HEADER).read()
+    m = re.search(r"#define WINATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES

@@ -35,7 +35,7 @@ HBM_PEAK_GBS = 8000.0
 F32_PEAK_TFLOPS = 157.3
 METRIC = "KV GB/s and rows/s for windowed GQA attention; % of HBM peak"
 KERNEL_NAMES = {1: "attn_dec_kernel", 2: "attn_mfma_kernel", 3: "attn_valu_kernel",
-                4: "attn_mfma16_kernel"}
+                4: "attn_mfma16_kernel", 5: "attn_decode_kernel"}
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_dec_kernel_decode_counters.json")
 CALIBRATION_COPY_BYTES = 64 << 20
 # Rotating input copies of a workload together hold at least this many bytes (more than the

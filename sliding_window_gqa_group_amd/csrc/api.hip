@@ -15,7 +15,8 @@ namespace winattn {
 namespace {
 
 // Tuning knobs (attn_tuning_set); 0 = automatic.
-int g_force_kernel = 0;     // 1 register, 2 MFMA 32x32, 3 LDS vector, 4 MFMA 16x16 kernel
+int g_force_kernel = 0;     // 1 register, 2 MFMA 32x32, 3 LDS vector, 4 MFMA 16x16,
+                            // 5 single-launch register kernel in slot order
 int g_tiles_per_split = 0;
 int g_target_blocks = 0;
 int g_merge_kernel = -1;    // -1 automatic, 0 merge in the last split, 1 separate merge launch
@@ -28,7 +29,14 @@ constexpr int kValuMaxQ = 16;
 constexpr size_t kTicketBytes = 64 * 1024;
 constexpr long long kMaxTickets = kTicketBytes / sizeof(unsigned int);
 
-enum Kind { kKindDec = 1, kKindMfma = 2, kKindValu = 3, kKindMfma16 = 4 };
+enum Kind { kKindDec = 1, kKindMfma = 2, kKindValu = 3, kKindMfma16 = 4, kKindDecode = 5 };
+
+// The single-launch slot-order kernel's last split gathers at most this many partials (two
+// 64-bit masks of splits; its ring tiles per split, held in registers, are bounded by
+// decode_max_tiles).
+constexpr int kDecodeMaxSplits = 128;
+constexpr int kDecodeTargetBlocks = 512;
+constexpr int kDecodeMaxGatherers = 128;
 
 struct Plan {
     int kind;
@@ -37,7 +45,8 @@ struct Plan {
     int qb;             // query vectors per block
     int nqblocks;
     int tk;             // keys per tile
-    int tps;            // tiles per split
+    int tps;            // tiles per split (ring tiles per split for kKindDecode)
+    int gather_k;       // gatherers per group (kKindDecode)
     int nsplit;         // splits reserved per block
     int slots;          // partial slots per block: nsplit plus extra (the far field's)
     bool merge_kernel;  // merge splits in a separate launch
@@ -50,11 +59,65 @@ int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 int pad_d(int d) { return d <= 64 ? 64 : (d <= 128 ? 128 : 256); }
 
+// Plan of a plain chunk call on the single-launch slot-order kernel: every query of a group in
+// one block, the group's w ring slots cut into splits of `tps` tiles, partials merged by the
+// last split. False if the shape is not one it takes.
+bool decode_plan(int rows, int ng, int hpg, int d, int w, Plan& pl) {
+    const long long nq_tot = (long long)rows * hpg;
+    if (nq_tot > 8 || (g_force_kernel != 0 && g_force_kernel != kKindDecode)) return false;
+    pl.kind = kKindDecode;
+    pl.mfma = false;
+    pl.dpad = pad_d(d);
+    pl.qb = nq_tot <= 4 ? 4 : 8;
+    pl.nqblocks = 1;
+    pl.tk = decode_tile_keys(pl.dpad);
+    const int rt = cdiv(w, pl.tk);   // ring tiles of a group
+    // tiles per split: the workgroups aim for two per CU (measured best for the decode shapes)
+    int tiles = g_tiles_per_split > 0 ? g_tiles_per_split : cdiv((long long)rt * ng, kDecodeTargetBlocks);
+    tiles = std::max(1, std::min(std::min(tiles, rt), decode_max_tiles(pl.dpad, pl.qb)));
+    if (cdiv(rt, tiles) > kDecodeMaxSplits) return false;
+    // Gatherers per group: up to 8 column chunks (a power of two dividing the d/4 columns and
+    // at most the splits), while the waiting gatherers of all groups stay far below the
+    // workgroups the GPU holds at once (they wait only for workgroups dispatched before them).
+    const int nsp = cdiv(rt, tiles);
+    int gk = 8;
+    while (gk > 1 && (gk > nsp || (long long)ng * gk > kDecodeMaxGatherers)) gk /= 2;
+    if ((long long)ng * gk > kDecodeMaxGatherers) return false;
+    pl.gather_k = gk;
+    // one ready flag per (gatherer, split) of every group, in the counter region
+    if ((long long)ng * gk * nsp > kMaxTickets) return false;
+    pl.tps = tiles;
+    pl.nsplit = cdiv(rt, tiles);
+    pl.slots = pl.nsplit;
+    pl.merge_kernel = false;
+    pl.xcd_map = 0;
+    if (pl.nsplit == 1) {
+        pl.bytes = 0;
+        return true;
+    }
+    size_t off = kTicketBytes;
+    const size_t slots = (size_t)ng * pl.nsplit * pl.qb;
+    pl.off_tickets = 0;
+    pl.off_q = off;
+    pl.off_pacc = off;
+    off = align_up(off + slots * pl.dpad * sizeof(float), 256);
+    pl.off_pm = off;
+    off = align_up(off + slots * sizeof(float), 256);
+    pl.off_pl = off;
+    off = align_up(off + slots * sizeof(float), 256);
+    pl.bytes = off;
+    return true;
+}
+
 // rows/hpg/d: the call's shape; wcap: the largest window any row can have; qbuf_floats: extra
-// workspace for the gated call's prepared queries.
+// workspace for the gated call's prepared queries. `plain`: a plain chunk call (no far field,
+// not gated), which the single-launch slot-order kernel may take.
 Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_floats,
-               int extra_slots = 0) {
+               int extra_slots = 0, bool plain = false) {
     Plan pl{};
+    if (plain && extra_slots == 0 && qbuf_floats == 0 && decode_plan(rows, ng, hpg, d, wcap, pl))
+        return pl;
+    pl = Plan{};
     const long long nq_tot = (long long)rows * hpg;
     pl.dpad = pad_d(d);
     // Matrix cores for more than 16 query vectors per group: 32x32 tiles with 32 queries per
@@ -190,6 +253,7 @@ int launch_attention(const Plan& pl, AttnParams& p, bool gated, char* ws, hipStr
         p.tickets = reinterpret_cast<unsigned int*>(ws + pl.off_tickets);
     }
     p.merge_kernel = pl.merge_kernel && pl.slots > 1 ? 1 : 0;
+    p.gather_k = pl.gather_k;
     hipError_t err = hipSuccess;
     const dim3 grid(pl.nsplit, pl.nqblocks, p.ng);
     bool fused = false;
@@ -206,6 +270,8 @@ int launch_attention(const Plan& pl, AttnParams& p, bool gated, char* ws, hipStr
     }
     if (fused)
         ;   // the near splits ran in the far part's launch
+    else if (pl.kind == kKindDecode)
+        err = launch_decode(p, pl.dpad, pl.qb, pl.tps, stream);   // merges in its last splits
     else if (pl.kind == kKindMfma)
         err = launch_mfma(p, gated, pl.dpad, stream);
     else if (pl.kind == kKindMfma16)
@@ -265,7 +331,7 @@ int attn_window_commit(float* ring_k, float* ring_v, uint32_t* meta, const float
 
 size_t attn_window_chunk_workspace(int rows, int ng, int hpg, int d, int w, int ns) {
     if (!chunk_shape_ok(rows, ng, hpg, d, w, ns)) return 0;
-    return make_plan(rows, ng, hpg, d, w, ns, 0).bytes;
+    return make_plan(rows, ng, hpg, d, w, ns, 0, 0, true).bytes;
 }
 
 }  // extern "C"
@@ -288,7 +354,7 @@ long long chunk_call(const float* ring_k, const float* ring_v, const uint32_t* m
         !aligned16(chunk_v) || !aligned16(out) || ((uintptr_t)meta & 3u) != 0)
         return WINATTN_EINVAL;
     if (ns > 0 && (!aligned16(sink_k) || !aligned16(sink_v))) return WINATTN_EINVAL;
-    const Plan pl = make_plan(rows, ng, hpg, d, w, ns, 0);
+    const Plan pl = make_plan(rows, ng, hpg, d, w, ns, 0, 0, true);
     if (check_only) return (long long)pl.bytes;
     if (pl.bytes > 0 && (!workspace || workspace_bytes < pl.bytes)) return WINATTN_EWORKSPACE;
     if (pl.bytes > 0 && !aligned16(workspace)) return WINATTN_EINVAL;
@@ -751,7 +817,7 @@ int attn_workspace_init(void* workspace, size_t bytes, void* stream) {
 int attn_window_chunk_plan(int rows, int ng, int hpg, int d, int w, int ns, int* kernel,
                            int* query_block, int* splits, int* keys_per_split) {
     if (!chunk_shape_ok(rows, ng, hpg, d, w, ns)) return WINATTN_EINVAL;
-    const Plan pl = make_plan(rows, ng, hpg, d, w, ns, 0);
+    const Plan pl = make_plan(rows, ng, hpg, d, w, ns, 0, 0, true);
     if (kernel) *kernel = pl.kind;
     if (query_block) *query_block = pl.qb;
     if (splits) *splits = pl.nsplit;
@@ -783,7 +849,7 @@ int attn_tuning_set(int knob, int value) {
     if (value < 0) return WINATTN_EINVAL;
     switch (knob) {
         case WINATTN_TUNE_FORCE_KERNEL:
-            if (value > 4) return WINATTN_EINVAL;
+            if (value > 5) return WINATTN_EINVAL;
             g_force_kernel = value;
             return WINATTN_OK;
         case WINATTN_TUNE_TILES_PER_SPLIT:

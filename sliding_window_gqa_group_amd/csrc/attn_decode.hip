@@ -1,0 +1,652 @@
+// Split-K attention for decode-sized chunks (at most 8 query vectors per KV group) in one
+// launch, streaming each group's ring in storage order.
+//
+// Prior art on the o1c page ("A sealed layer's attention for a chunk of rows, on Metal"): the
+// token path `o1c_tok_near` gives each simdgroup a stripe of the window, keeps the row's queries
+// in registers and updates a running (max, sum, accumulator) per head; `o1c_tok_merge` combines
+// the stripes' partials in the last threadgroup to finish. What changes on gfx950:
+//
+//  - Key order. Softmax attention does not depend on the order of its keys, so a split takes a
+//    fixed range of ring SLOTS (storage order) rather than a range of the window's entries.
+//    Every K/V address of the call (ring slots, sinks, the chunk's rows) is then known before
+//    the group's metadata arrives: all of a workgroup's loads are requested at once, at the
+//    start, and the metadata (one more memory round trip) is read while they are in flight. It
+//    only decides, per key and query, whether the key is visible: slot s holds entry
+//    x = (s - head) mod wg, which row i sees when it is held (s < wg, x < len) and inside the
+//    row's window (x >= lo_i). A slot outside every window may hold anything (never written,
+//    NaN): its score is masked to -inf and its value zeroed by select, so it adds exactly 0.
+//    The price: the whole w-slot ring of every group is read, however few of its slots are
+//    live, so a call costs what a full ring costs.
+//  - Split 0 also takes the group's extra keys: the sinks, then the chunk's rows (at most 8).
+//  - Registers, no LDS in the key loop: a lane group of TPK = D*NQ/32 lanes owns one key per
+//    pass (its lanes hold float4 columns of the key's K and V rows and of every query); scores
+//    are partial dot products summed over the lane group with DPP; each lane group keeps a
+//    running max, sum and accumulator per query, merged once through LDS at the end.
+//  - One launch. Each split writes its partial (max, sum, accumulator per query) with
+//    device-scope stores, waits for them to complete and raises ready flags; the group's last
+//    few splits each gather one column chunk of every partial as the flags rise and fold them
+//    (the token path's merge rule), so most of the merge overlaps the streaming and no CU reads
+//    more than its share. No second kernel, no kernel boundary, no read-modify-write.
+//  - Work order: workgroup b takes group b mod ng, split b / ng. Workgroups are dealt to the 8
+//    XCDs round-robin, so with 8 groups every split of a group runs on one XCD, next to the
+//    partials its merge reads.
+#include <type_traits>
+
+#include "attn_dec_block.h"
+#include "launch.h"
+
+namespace winattn {
+
+// Buffer resource word 3 for raw (untyped) buffer accesses on gfx9-family GPUs (32-bit data
+// format), and the sc1 cache-policy bit of a buffer store: device (agent) scope.
+constexpr int kBufferWord3 = 0x00020000;
+typedef unsigned int vu4 __attribute__((ext_vector_type(4)));
+constexpr int kCachePolicyDevice = 16;
+
+// A group's ring geometry from its metadata (len, head, far count, window override), clamped
+// so that no access leaves the ring (as resolve_group clamps it): window wg, entries held len0,
+// slot of the oldest entry head0.
+struct RingGeom {
+    int wg, len0, head0;
+};
+
+__device__ inline RingGeom ring_geom(vu4 m, int w) {
+    const uint32_t wg = (m.w != 0u && m.w < (uint32_t)w) ? m.w : (uint32_t)w;
+    const uint32_t len0 = m.x < wg ? m.x : wg;
+    const uint32_t head0 = m.y >= wg ? m.y % wg : m.y;
+    return RingGeom{(int)wg, (int)len0, (int)head0};
+}
+
+
+// Max / sum over the lane groups of a wave: lanes l, l ^ TPK, l ^ 2 TPK, ... (TPK = 8, 16, 32 or
+// 64 lanes per group), result in every lane. Lanes l ^ 8 meet by a DPP rotation within a row of
+// 16, lanes l ^ 16 and l ^ 32 by gfx950's row and half-wave swaps.
+constexpr int kDppRowRor8 = 0x128;
+
+template <int TPK>
+__device__ inline float lane_groups_max(float v) {
+    if constexpr (TPK <= 8) v = fmaxf(v, dpp<kDppRowRor8>(v, -INFINITY));
+    if constexpr (TPK <= 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    if constexpr (TPK <= 32) v = half_swap_max(v);
+    return v;
+}
+
+template <int TPK>
+__device__ inline float lane_groups_sum(float v) {
+    if constexpr (TPK <= 8) v += dpp<kDppRowRor8>(v, 0.0f);
+    if constexpr (TPK <= 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    if constexpr (TPK <= 32) v = half_swap_sum(v);
+    return v;
+}
+
+// The group's last `nk` splits are its gatherers (the last of the group's workgroups in dispatch
+// order, so every split a gatherer waits for was dispatched before it, and the non-gatherers
+// never wait). Gatherer k owns output columns [k, k + 1) * D / (4 nk) float4 of every query of
+// the group: it reads only those columns of the group's nsplit partials, as their ready flags
+// rise, and folds them: c = max_s m_s, out = sum_s acc_s 2^(m_s - c) / sum_s l_s 2^(m_s - c)
+// (the token path's merge, `o1c_tok_merge`). One CU reads freshly written partials at only tens
+// of GB/s, so the merge is spread over nk CUs and most of it overlaps the other splits'
+// streaming; after the last flag only that split's columns remain to be read.
+//  - Every split raises one flag per gatherer (flags[k][s]), so each gatherer polls and clears
+//    flags nobody else reads.
+//  - Each thread owns IPT (query j, float4 column c) items of the chunk and the splits
+//    s = sub (mod NSUB). A wave polls every flag of its gatherer (one device-scope load per
+//    lane, two rounds beyond 64 splits); each lane then reads up to MB of its own newly
+//    ready splits per round, all loads of a round issued together with the next poll behind
+//    them.
+//  - The poll is bounded: after kGatherPolls rounds without every flag, the chunk is written as
+//    NaN rather than waiting longer (it cannot happen while every split runs).
+//  - Once every wave has left its poll loop, the gatherer's flags are cleared, so the next call
+//    starts from zero; the NSUB subsets meet in LDS (`scratch`: 6 * NT floats and a word).
+constexpr int kGatherPolls = 1 << 18;
+
+template <int NQ, int D, int NT>
+__device__ inline void gather_chunk(const AttnParams& p, int g, int nsplit, int nq, int nk, int k,
+                                    unsigned int* flags, float* scratch) {
+    constexpr int D4 = D / 4;
+    constexpr int MB = 8;   // splits per lane per load round
+    const int cpk = D4 / nk;                  // float4 columns per gatherer
+    const int ipg = NQ * cpk;                 // items per gatherer
+    const int nsub = ipg >= NT ? 1 : NT / ipg;
+    const int ipt = ipg >= NT ? ipg / NT : 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int sub = nsub > 1 ? tid / ipg : 0;
+    const size_t grp = (size_t)g * nsplit * NQ;   // first partial slot of the group
+    const __amdgpu_buffer_rsrc_t racc =
+        __builtin_amdgcn_make_buffer_rsrc(p.pacc + grp * D, 0, nsplit * NQ * D * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rm =
+        __builtin_amdgcn_make_buffer_rsrc(p.pm + grp, 0, nsplit * NQ * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rl =
+        __builtin_amdgcn_make_buffer_rsrc(p.pl + grp, 0, nsplit * NQ * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rf =
+        __builtin_amdgcn_make_buffer_rsrc(flags, 0, nsplit * 4, kBufferWord3);
+    float* s_m = scratch;
+    float* s_l = scratch + NT;
+    vf4* s_a = reinterpret_cast<vf4*>(scratch + 2 * NT);
+    int* s_bad = reinterpret_cast<int*>(scratch + 6 * NT);
+
+    // IPT is 1 unless one gatherer owns more items than threads (a single gatherer of 8 queries
+    // of width 256): then 2
+    constexpr int IPTM = NQ * D4 > NT ? NQ * D4 / NT : 1;
+    float cm[IPTM], cl[IPTM];
+    vf4 ca[IPTM];
+    int jj[IPTM], cc[IPTM];
+#pragma unroll
+    for (int it = 0; it < IPTM; ++it) {
+        const int item = (nsub > 1 ? tid % ipg : tid + it * NT) % ipg;
+        jj[it] = item / cpk;
+        cc[it] = k * cpk + item % cpk;
+        cm[it] = -INFINITY;
+        cl[it] = 0.0f;
+        ca[it] = vf4{0.f, 0.f, 0.f, 0.f};
+    }
+    // this lane's splits still awaited: s < nsplit and s = sub (mod nsub)
+    unsigned long long pend[2] = {0ull, 0ull};
+    for (int s = sub; s < nsplit; s += nsub) pend[s >> 6] |= 1ull << (s & 63);
+    unsigned fl[2];
+    auto poll = [&]() {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int s = min(h * 64 + lane, nsplit - 1);
+            fl[h] = __builtin_amdgcn_raw_buffer_load_b32(rf, s * 4, 0, kCachePolicyDevice);
+        }
+    };
+    poll();
+    unsigned long long todo[2] = {0ull, 0ull};   // ready, not yet read (this lane's splits)
+    int polls = 0;
+    // wave-uniform loop: every lane of the wave leaves together
+    while (__builtin_amdgcn_ballot_w64((pend[0] | pend[1] | todo[0] | todo[1]) != 0ull) &&
+           polls < kGatherPolls) {
+        ++polls;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const unsigned long long r = __builtin_amdgcn_ballot_w64(fl[h] != 0u) & pend[h];
+            pend[h] &= ~r;
+            todo[h] |= r;
+        }
+        if (!__builtin_amdgcn_ballot_w64((todo[0] | todo[1]) != 0ull)) {
+            __builtin_amdgcn_s_sleep(2);
+            poll();
+            continue;
+        }
+        // up to MB of this lane's ready splits
+        int idx[MB];
+        int n = 0;
+#pragma unroll
+        for (int u = 0; u < MB; ++u) {
+            const bool any = (todo[0] | todo[1]) != 0ull;
+            const int h = todo[0] ? 0 : 1;
+            const unsigned long long word = h ? todo[1] : todo[0];
+            const int b = __builtin_ctzll(word | (any ? 0ull : 1ull));
+            idx[u] = any ? h * 64 + b : -1;
+            if (any) {
+                if (h) todo[1] &= todo[1] - 1ull; else todo[0] &= todo[0] - 1ull;
+            }
+            n += any ? 1 : 0;
+        }
+        float m[IPTM][MB], l[IPTM][MB];
+        vf4 a[IPTM][MB];
+#pragma unroll
+        for (int it = 0; it < IPTM; ++it) {
+#pragma unroll
+            for (int u = 0; u < MB; ++u) {
+                const int su = idx[u] >= 0 ? idx[u] : 0;   // past n: dropped below
+                const int at = su * NQ + jj[it];
+                m[it][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, at * 4, 0, kCachePolicyDevice));
+                l[it][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, at * 4, 0, kCachePolicyDevice));
+                a[it][u] = __builtin_bit_cast(
+                    vf4, __builtin_amdgcn_raw_buffer_load_b128(racc, (at * D + 4 * cc[it]) * 4, 0, kCachePolicyDevice));
+            }
+        }
+        if (__builtin_amdgcn_ballot_w64((pend[0] | pend[1]) != 0ull)) poll();   // behind the batch
+#pragma unroll
+        for (int it = 0; it < IPTM; ++it) {
+            if (it >= ipt) break;
+            float bm = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < MB; ++u) {
+                m[it][u] = u < n ? m[it][u] : -INFINITY;   // a split with no keys is -inf too
+                bm = fmaxf(bm, m[it][u]);
+            }
+            const float nm = fmaxf(cm[it], bm), mu = safe_max(nm);
+            const float f0 = __builtin_amdgcn_exp2f(cm[it] - mu);
+            cl[it] *= f0;
+            ca[it] *= f0;
+#pragma unroll
+            for (int u = 0; u < MB; ++u) {
+                const bool real = m[it][u] > -INFINITY;
+                const float f = __builtin_amdgcn_exp2f(m[it][u] - mu);
+                cl[it] += (real ? l[it][u] : 0.0f) * f;
+                ca[it] += (real ? a[it][u] : vf4{0.f, 0.f, 0.f, 0.f}) * f;
+            }
+            cm[it] = nm;
+        }
+    }
+    const bool complete = !(pend[0] | pend[1] | todo[0] | todo[1]);
+    if (tid == 0) *s_bad = 0;
+    __syncthreads();
+    if (!complete) *s_bad = 1;
+    __syncthreads();
+    // every wave has left its poll loop: this gatherer's flags back to zero for the next call
+    if (!*s_bad && tid < 64) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int s = h * 64 + lane;
+            if (s < nsplit) __hip_atomic_store(flags + s, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < IPTM; ++it) {
+        if (it >= ipt) break;
+        if (nsub > 1) {
+            s_m[tid] = cm[it];
+            s_l[tid] = cl[it];
+            s_a[tid] = ca[it];
+        }
+        __syncthreads();
+        const int item = nsub > 1 ? tid % ipg : tid + it * NT;
+        if (nsub > 1 && sub == 0) {
+            float mm = cm[it];
+            for (int u = 1; u < nsub; ++u) mm = fmaxf(mm, s_m[u * ipg + item]);
+            const float mu = safe_max(mm);
+            const float f0 = __builtin_amdgcn_exp2f(cm[it] - mu);
+            cl[it] *= f0;
+            ca[it] *= f0;
+            for (int u = 1; u < nsub; ++u) {
+                const float f = __builtin_amdgcn_exp2f(s_m[u * ipg + item] - mu);
+                cl[it] += s_l[u * ipg + item] * f;
+                ca[it] += s_a[u * ipg + item] * f;
+            }
+        }
+        if (sub == 0 && item < ipg && jj[it] < nq && cc[it] < p.d / 4) {
+            vf4 o = ca[it] * (1.0f / fmaxf(cl[it], 1e-30f));
+            if (*s_bad) o = vf4{NAN, NAN, NAN, NAN};
+            store_out<false>(p, jj[it], g, 4 * cc[it], make_float4(o.x, o.y, o.z, o.w));
+        }
+        __syncthreads();
+    }
+}
+
+// Lanes per key, float4 columns per lane, keys per pass and passes per tile of a workgroup of
+// NT threads: TPK = D*NQ/32 lanes own a key (4 float4 of K and of V per lane per tile of
+// TK = 4096 / D keys with 256 threads).
+template <int D, int NQ, int NT>
+struct DecodeShape {
+    static constexpr int TPK = D * NQ / 32;
+    static constexpr int F4 = D / (4 * TPK);
+    static constexpr int KPP = NT / TPK;
+    static constexpr int TK = 4096 / D;
+    static constexpr int PASSES = TK / KPP;
+    static_assert(TPK >= 4 && TPK <= 64 && F4 >= 1 && PASSES >= 1, "unsupported shape");
+    // passes a split holds in registers without spilling (all requested up front)
+    static constexpr int MAX_PASSES = 8;
+    static constexpr int MAX_TILES = MAX_PASSES / PASSES;
+};
+
+// T: ring tiles per split (TK = 4096 / D slots each), all requested up front; NT threads.
+template <int D, int NQ, int T, int NT>
+__global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) {
+    using S = DecodeShape<D, NQ, NT>;
+    constexpr int TPK = S::TPK, F4 = S::F4, KPP = S::KPP, TK = S::TK, PASSES = S::PASSES;
+    constexpr int NP = T * PASSES;   // ring passes of a split (one key per lane group each)
+    static_assert(T <= S::MAX_TILES, "too many tiles for the registers");
+
+    constexpr int NW = NT / 64;                           // waves
+    // each wave's state at the end, then the merge's scratch
+    constexpr int kAccFloats = NW * NQ * D > 6 * NT + 4 ? NW * NQ * D : 6 * NT + 4;
+    __shared__ __align__(16) float s_acc[kAccFloats];
+    __shared__ float s_wm[NW * NQ], s_wl[NW * NQ];
+    __shared__ int s_flag;
+
+    const int tid = threadIdx.x;
+    const int gi = tid / TPK, sl = tid % TPK;   // lane group (key slot), lane within the group
+    const int g = blockIdx.x % p.ng;
+    const int split = blockIdx.x / p.ng;
+    const int nsplit = p.nsplit_grid;
+    const int nq = p.rows * p.hpg;              // every query of the group: one block
+    const int d4 = p.d / 4;
+
+    // ---- the group's metadata is requested first, ahead of the call's K/V traffic, as a
+    // vector load: vector loads return in order, so waiting for it waits for nothing issued
+    // after it, and it never holds up the scalar loads of the kernel's arguments (scalar loads
+    // return out of order and are waited for all together). Nothing reads it until every load
+    // of the split has been requested.
+    vu4 meta_v = __builtin_amdgcn_raw_buffer_load_b128(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(p.meta + 4 * g), 0, 16, kBufferWord3),
+        0, 0, 0);
+
+    // ---- queries: this lane's columns of every query, times scale*log2(e); addresses clamped
+    // to a live element, padding scaled by 0 (a factor keeps the load unconditional)
+    vf4 qr[NQ][F4];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        const int qi = min(j, nq - 1);
+        const int row = qi / p.hpg, gh = g * p.hpg + qi % p.hpg;
+        const float* qp = p.q + ((size_t)row * p.nh + gh) * p.d;
+#pragma unroll
+        for (int f = 0; f < F4; ++f) {
+            const int c = sl + TPK * f;
+            const bool live = (j < nq) & (c < d4);
+            const vf4 v = *reinterpret_cast<const vf4*>(qp + 4 * (c < d4 ? c : 0));
+            qr[j][f] = v * (live ? p.scale_log2 : 0.0f);
+        }
+    }
+
+    const KVBases b = kv_bases(p);
+    const unsigned long long rk = b.rk + 4ull * (unsigned long long)((long long)g * p.ring_gs);
+    const unsigned long long rv = b.rv + 4ull * (unsigned long long)((long long)g * p.ring_gs);
+    const unsigned long long ck = b.ck + 4ull * (unsigned long long)((long long)g * p.chunk_gs);
+    const unsigned long long cv = b.cv + 4ull * (unsigned long long)((long long)g * p.chunk_gs);
+    const unsigned long long sk = b.sk + 4ull * (unsigned long long)((long long)g * p.ns * p.d);
+    const unsigned long long sv = b.sv + 4ull * (unsigned long long)((long long)g * p.ns * p.d);
+    const int ss = (int)p.ring_ss, crs = (int)p.chunk_rs;
+    const int nextra = p.ns + p.rows;
+
+    // Extra key e of the group: sink e (e < ns), else chunk row e - ns; padding (e >= nextra)
+    // loads the chunk's last row, a live address.
+    auto load_extra = [&](vf4 (&k)[F4], vf4 (&v)[F4], int e) {
+        const bool sink = e < p.ns;
+        const int crow = min(e - p.ns, p.rows - 1);
+        const int row = sink ? e * p.d : crow * crs;
+        const unsigned long long bk = sink ? sk : ck, bv = sink ? sv : cv;
+#pragma unroll
+        for (int f = 0; f < F4; ++f) {
+            const int c = sl + TPK * f;
+            const int off = c < d4 ? row + 4 * c : row;
+            k[f] = *reinterpret_cast<gvf4p>(bk + 4ull * (unsigned)off);
+            v[f] = *reinterpret_cast<gvf4p>(bv + 4ull * (unsigned)off);
+        }
+    };
+
+    // ---- every load of the split, before the metadata: split 0's first pass of extra keys,
+    // then the ring slots split*T*TK + i*KPP + gi of pass i (slots past w load slot w-1)
+    vf4 kx[F4], vx[F4];
+    if (split == 0) load_extra(kx, vx, gi);
+    const int slot0 = split * (T * TK) + gi;
+    vf4 kr[NP][F4], vr[NP][F4];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        const int slot = min(slot0 + i * KPP, p.w - 1);
+#pragma unroll
+        for (int f = 0; f < F4; ++f) {
+            const int c = sl + TPK * f;
+            const int off = slot * ss + (c < d4 ? 4 * c : 0);
+            kr[i][f] = *reinterpret_cast<gvf4p>(rk + 4ull * (unsigned)off);
+            vr[i][f] = *reinterpret_cast<gvf4p>(rv + 4ull * (unsigned)off);
+        }
+    }
+
+    // ---- each query's window, from the metadata. The empty asm pins the first use of the
+    // metadata here, after every load above (its memory clobber keeps them above it), so the
+    // wait for the metadata cannot be scheduled ahead of them (all four words stay live until
+    // then, so no register of the load in flight is reused before it lands).
+    asm volatile("" : "+v"(meta_v.x), "+v"(meta_v.y), "+v"(meta_v.z), "+v"(meta_v.w) : : "memory");
+    const RingGeom rg = ring_geom(meta_v, p.w);
+    int qlo[NQ], qrow[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        const int row = min(j, nq - 1) / p.hpg;
+        const int hi = rg.len0 + row + 1;
+        qlo[j] = j < nq ? window_lo(hi, rg.wg) : 0x7fffffff;   // padding sees nothing
+        qrow[j] = j < nq ? row : -1;
+    }
+
+    float mrun[NQ], lrun[NQ];
+    vf4 acc[NQ][F4];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        mrun[j] = -INFINITY;
+        lrun[j] = 0.0f;
+#pragma unroll
+        for (int f = 0; f < F4; ++f) acc[j][f] = vf4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // ---- NPS passes: scores, visibility (bit j of vis[ps]: query j sees the pass's key of this
+    // lane group), online softmax of this lane group, value update
+    auto step = [&](auto& kk, auto& vv, const auto& vis) {
+        constexpr int NPS = std::extent<std::remove_reference_t<decltype(kk)>>::value;
+        float sc[NPS * NQ];
+#pragma unroll
+        for (int ps = 0; ps < NPS; ++ps)
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                float s = 0.0f;
+#pragma unroll
+                for (int f = 0; f < F4; ++f) {
+                    float h = kk[ps][f].x * qr[j][f].x;
+                    h = __builtin_fmaf(kk[ps][f].y, qr[j][f].y, h);
+                    h = __builtin_fmaf(kk[ps][f].z, qr[j][f].z, h);
+                    h = __builtin_fmaf(kk[ps][f].w, qr[j][f].w, h);
+                    s = f == 0 ? h : s + h;
+                }
+                sc[ps * NQ + j] = s;
+            }
+        constexpr int kSumMax = NQ >= 8 ? 1 : 8;
+        constexpr int kSumBlock = NPS * NQ < kSumMax ? NPS * NQ : kSumMax;
+#pragma unroll
+        for (int bb = 0; bb < NPS * NQ; bb += kSumBlock) lane_group_sum_n<TPK, kSumBlock>(sc + bb);
+#pragma unroll
+        for (int ps = 0; ps < NPS; ++ps) {
+#pragma unroll
+            for (int j = 0; j < NQ; ++j)
+                sc[ps * NQ + j] = (vis[ps] >> j) & 1u ? sc[ps * NQ + j] : -INFINITY;
+            // a key no query sees may hold anything (a slot never written): 0 * NaN must not
+            // reach the accumulators
+            const bool any = vis[ps] != 0u;
+#pragma unroll
+            for (int f = 0; f < F4; ++f) {
+                vv[ps][f].x = any ? vv[ps][f].x : 0.0f;
+                vv[ps][f].y = any ? vv[ps][f].y : 0.0f;
+                vv[ps][f].z = any ? vv[ps][f].z : 0.0f;
+                vv[ps][f].w = any ? vv[ps][f].w : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            float tmax = sc[j];
+#pragma unroll
+            for (int ps = 1; ps < NPS; ++ps) tmax = fmaxf(tmax, sc[ps * NQ + j]);
+            const float m_new = fmaxf(mrun[j], tmax);
+            const float mu = safe_max(m_new);
+            const float corr = __builtin_amdgcn_exp2f(mrun[j] - mu);
+            mrun[j] = m_new;
+            float lsum = 0.0f;
+#pragma unroll
+            for (int f = 0; f < F4; ++f) acc[j][f] *= corr;
+#pragma unroll
+            for (int ps = 0; ps < NPS; ++ps) {
+                const float pv = __builtin_amdgcn_exp2f(sc[ps * NQ + j] - mu);
+                lsum += pv;
+#pragma unroll
+                for (int f = 0; f < F4; ++f) {
+                    acc[j][f].x = __builtin_fmaf(pv, vv[ps][f].x, acc[j][f].x);
+                    acc[j][f].y = __builtin_fmaf(pv, vv[ps][f].y, acc[j][f].y);
+                    acc[j][f].z = __builtin_fmaf(pv, vv[ps][f].z, acc[j][f].z);
+                    acc[j][f].w = __builtin_fmaf(pv, vv[ps][f].w, acc[j][f].w);
+                }
+            }
+            lrun[j] = lrun[j] * corr + lsum;
+        }
+    };
+
+    // Visibility of extra key e: a sink to every real query; chunk row c to the queries of
+    // rows >= c whose window reaches back to it.
+    auto extra_vis = [&](int e) {
+        unsigned m = 0u;
+        const int c = e - p.ns;
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const bool v = e < p.ns ? j < nq
+                                    : (e < nextra) & (c <= qrow[j]) & (rg.len0 + c >= qlo[j]);
+            m |= v ? 1u << j : 0u;
+        }
+        return m;
+    };
+
+    // ---- split 0: its extra keys first (they arrived first), more passes of them if needed
+    if (split == 0) {
+        vf4 k1[1][F4], v1[1][F4];
+#pragma unroll
+        for (int f = 0; f < F4; ++f) {
+            k1[0][f] = kx[f];
+            v1[0][f] = vx[f];
+        }
+        unsigned vis1[1] = {extra_vis(gi)};
+        step(k1, v1, vis1);
+        for (int e0 = KPP; e0 < nextra; e0 += KPP) {   // more than one pass of sinks and rows
+            load_extra(k1[0], v1[0], e0 + gi);
+            vis1[0] = extra_vis(e0 + gi);
+            step(k1, v1, vis1);
+        }
+    }
+
+    // ---- the ring passes, one tile (PASSES passes) per online-softmax step
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        vf4 kt[PASSES][F4], vt[PASSES][F4];
+        unsigned vis[PASSES];
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps) {
+            const int i = t * PASSES + ps;
+#pragma unroll
+            for (int f = 0; f < F4; ++f) {
+                kt[ps][f] = kr[i][f];
+                vt[ps][f] = vr[i][f];
+            }
+            const int slot = slot0 + i * KPP;
+            int x = slot - rg.head0;
+            x = x < 0 ? x + rg.wg : x;
+            const bool held = (slot < rg.wg) & (x < rg.len0);
+            unsigned m = 0u;
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) m |= (held & (x >= qlo[j])) ? 1u << j : 0u;
+            vis[ps] = m;
+        }
+        step(kt, vt, vis);
+    }
+
+    // ---- merge the lane groups of each wave with cross-lane swaps (every lane of a group
+    // holds the group's state; groups of a wave differ in the lane bits above TPK), then the
+    // waves through LDS
+    const int wave = tid / 64;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        const float wm = lane_groups_max<TPK>(mrun[j]);
+        const float f = __builtin_amdgcn_exp2f(mrun[j] - safe_max(wm));
+        mrun[j] = wm;
+        lrun[j] = lane_groups_sum<TPK>(lrun[j] * f);
+#pragma unroll
+        for (int fc = 0; fc < F4; ++fc) {
+            acc[j][fc].x = lane_groups_sum<TPK>(acc[j][fc].x * f);
+            acc[j][fc].y = lane_groups_sum<TPK>(acc[j][fc].y * f);
+            acc[j][fc].z = lane_groups_sum<TPK>(acc[j][fc].z * f);
+            acc[j][fc].w = lane_groups_sum<TPK>(acc[j][fc].w * f);
+        }
+    }
+    if ((tid & 63) < TPK) {   // the wave's first lane group writes the wave's state
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+#pragma unroll
+            for (int fc = 0; fc < F4; ++fc)
+                *reinterpret_cast<vf4*>(s_acc + (wave * NQ + j) * D + 4 * (sl + TPK * fc)) = acc[j][fc];
+            if (sl == 0) {
+                s_wm[wave * NQ + j] = mrun[j];
+                s_wl[wave * NQ + j] = lrun[j];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- this split's partial (or the output when the group has a single split), folded over
+    // the waves per (query, float4 column) item. Partials are read within this launch by
+    // workgroups that may run on other XCDs, whose L2 caches are not coherent with this one:
+    // they are stored with the device-scope (sc1) cache policy, which writes them through to the
+    // device-coherent level (16-byte buffer stores).
+    constexpr int D4 = D / 4;
+    const size_t at0 = ((size_t)g * nsplit + split) * NQ;
+    const __amdgpu_buffer_rsrc_t part =
+        __builtin_amdgcn_make_buffer_rsrc(p.pacc + at0 * D, 0, NQ * D * 4, kBufferWord3);
+    for (int item = tid; item < NQ * D4; item += NT) {
+        const int j = item / D4, c = item % D4;
+        float m = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) m = fmaxf(m, s_wm[w * NQ + j]);
+        const float mu = safe_max(m);
+        float l = 0.0f;
+        vf4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = __builtin_amdgcn_exp2f(s_wm[w * NQ + j] - mu);
+            l += s_wl[w * NQ + j] * f;
+            o += *reinterpret_cast<const vf4*>(s_acc + (w * NQ + j) * D + 4 * c) * f;
+        }
+        if (j >= nq || c >= d4) continue;
+        if (nsplit == 1) {
+            o *= 1.0f / fmaxf(l, 1e-30f);
+            store_out<false>(p, j, g, 4 * c, make_float4(o.x, o.y, o.z, o.w));
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(vu4, o), part, (j * D + 4 * c) * 4,
+                                                   0, kCachePolicyDevice);
+            if (c == 0) {
+                store_dev(p.pm + at0 + j, m);
+                store_dev(p.pl + at0 + j, l);
+            }
+        }
+    }
+    if (nsplit == 1) return;
+
+    // ---- every thread waits until its partial stores are acknowledged (complete at the
+    // device-coherent level) before the barrier; then the split raises its ready flag for each
+    // of the group's gatherers with device-scope stores
+    const int nk = p.gather_k;
+    unsigned int* flags = p.tickets + (size_t)g * nk * nsplit;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid < nk) __hip_atomic_store(flags + tid * nsplit + split, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int k = split - (nsplit - nk);
+    if (k < 0) return;
+    __syncthreads();   // the wave states in LDS are read: the gather reuses it as scratch
+    gather_chunk<NQ, D, NT>(p, g, nsplit, nq, nk, k, flags + k * nsplit, s_acc);
+}
+
+template <int D, int NQ, int T, int NT>
+static hipError_t launch_decode_tt(const AttnParams& p, hipStream_t stream) {
+    const dim3 grid((unsigned)(p.nsplit_grid * p.ng)), block(NT);
+    hipLaunchKernelGGL((attn_decode_kernel<D, NQ, T, NT>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+// The instances: 1-4 ring tiles per split with 4 queries per block, 1-2 with 8.
+template <int D, int NQ>
+static hipError_t launch_decode_t(const AttnParams& p, int tiles, hipStream_t stream) {
+    constexpr int MT = DecodeShape<D, NQ, kThreads>::MAX_TILES;
+    if (tiles == 1) return launch_decode_tt<D, NQ, 1, kThreads>(p, stream);
+    if (tiles == 2 && MT >= 2) return launch_decode_tt<D, NQ, (MT >= 2 ? 2 : 1), kThreads>(p, stream);
+    if (tiles == 3 && MT >= 3) return launch_decode_tt<D, NQ, (MT >= 3 ? 3 : 1), kThreads>(p, stream);
+    if (tiles == 4 && MT >= 4) return launch_decode_tt<D, NQ, (MT >= 4 ? 4 : 1), kThreads>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+int decode_max_tiles(int dpad, int nq) {
+    if (dpad == 64) return nq == 4 ? DecodeShape<64, 4, kThreads>::MAX_TILES : DecodeShape<64, 8, kThreads>::MAX_TILES;
+    if (dpad == 128) return nq == 4 ? DecodeShape<128, 4, kThreads>::MAX_TILES : DecodeShape<128, 8, kThreads>::MAX_TILES;
+    return nq == 4 ? DecodeShape<256, 4, kThreads>::MAX_TILES : DecodeShape<256, 8, kThreads>::MAX_TILES;
+}
+
+hipError_t launch_decode(const AttnParams& p, int dpad, int nq, int tiles, hipStream_t stream) {
+    if (dpad == 64 && nq == 4) return launch_decode_t<64, 4>(p, tiles, stream);
+    if (dpad == 64 && nq == 8) return launch_decode_t<64, 8>(p, tiles, stream);
+    if (dpad == 128 && nq == 4) return launch_decode_t<128, 4>(p, tiles, stream);
+    if (dpad == 128 && nq == 8) return launch_decode_t<128, 8>(p, tiles, stream);
+    if (dpad == 256 && nq == 4) return launch_decode_t<256, 4>(p, tiles, stream);
+    if (dpad == 256 && nq == 8) return launch_decode_t<256, 8>(p, tiles, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace winattn

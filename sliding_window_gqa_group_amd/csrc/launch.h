@@ -19,6 +19,15 @@ hipError_t launch_dec(const AttnParams& p, bool gated, int dpad, int nq, dim3 gr
                       hipStream_t stream);
 int dec_tile_keys(int dpad);
 
+// Single-launch register kernel for <= 8 query vectors per group (one block per group) that
+// streams the ring in slot order; grid = nsplit_grid * ng workgroups; `tiles` ring tiles per
+// split; the group's last gather_k splits merge its partials, a column chunk each.
+hipError_t launch_decode(const AttnParams& p, int dpad, int nq, int tiles, hipStream_t stream);
+// Ring tiles per split the kernel holds in registers with nq queries per block.
+int decode_max_tiles(int dpad, int nq);
+// Keys per tile of that kernel.
+inline int decode_tile_keys(int dpad) { return 4096 / dpad; }
+
 // Separate launch that merges the split partials of every query block (qb query vectors per
 // block); it reads only the partials, never the ring metadata.
 hipError_t launch_split_merge(const AttnParams& p, bool gated, int qb, int dpad,

@@ -52,6 +52,7 @@ struct AttnParams {
     int g_base, g_mod, g_hi0, g_wcap;   // gated call's ring descriptor
     int merge_kernel;            // 1: splits are merged by a separate kernel launch
     int xcd_map;                 // matrix-core kernel's work order (see attn_mfma.hip)
+    int gather_k;                // slot-order kernel: gatherers (column chunks) per group
 };
 
 struct GroupWin {

@@ -216,18 +216,21 @@ def test_workspace_queries(lib):
     assert B.gated_workspace_bytes(1, 5, 2, 64, 8) == 0
     # a single-split plan needs no workspace at all
     kern, qb, splits, kps = B.chunk_plan(1, 1, 4, 64, 16, 2)
-    assert (kern, splits) == (1, 1)
+    assert (kern, splits) == (5, 1)
     assert B.chunk_workspace_bytes(1, 1, 4, 64, 16, 2) == 0
     # gated always holds its prepared queries
     assert B.gated_workspace_bytes(64, 16, 4, 256, 1024) >= 64 * 16 * 256 * 4
 
 
 def test_plans_of_the_named_workloads(lib):
-    assert B.chunk_plan(1, 8, 4, 128, 4096, 4)[0] == 1          # decode: register split-K
-    # decode: 64 splits of two 32-key tiles per group (512 workgroups, two per CU); over a
-    # 32768-slot window, 64 splits of 16 tiles
-    assert B.chunk_plan(1, 8, 4, 128, 4096, 4) == (1, 4, 64, 64)
+    # decode: the single-launch slot-order kernel, 64 splits of two 32-slot tiles per group
+    # (512 workgroups, two per CU); over a 32768-slot window the two-launch register kernel,
+    # 64 splits of 16 tiles
+    assert B.chunk_plan(1, 8, 4, 128, 4096, 4) == (5, 4, 64, 64)
     assert B.chunk_plan(1, 8, 4, 128, 32768, 4) == (1, 4, 64, 512)
+    assert B.chunk_plan(2, 8, 4, 128, 4096, 4) == (5, 8, 64, 64)  # two rows: 8 queries per block
+    # 8 queries per block hold at most two ring tiles per split
+    assert B.chunk_plan(1, 8, 8, 128, 8192, 4) == (5, 8, 128, 64)
     assert B.chunk_plan(4, 8, 4, 128, 4096, 4)[0] == 3          # 16 queries: LDS vector kernel
     assert B.chunk_plan(512, 8, 4, 128, 4096, 4)[0] == 2        # prefill: matrix cores
     k, qb, splits, kps = B.chunk_plan(2048, 8, 8, 128, 32768, 4)
@@ -256,8 +259,17 @@ def test_tuning_knobs_change_the_plan(lib):
         B.tuning_set(B.TUNE_TILES_PER_SPLIT, 0)
     with pytest.raises(B.WinattnError):
         B.tuning_set(99, 1)
-    with pytest.raises(B.WinattnError):
+    try:
         B.tuning_set(B.TUNE_FORCE_KERNEL, 5)
+        B.tuning_set(B.TUNE_TILES_PER_SPLIT, 4)
+        assert B.chunk_plan(1, 8, 4, 128, 4096, 4) == (5, 4, 32, 128)
+        assert B.chunk_plan(2, 8, 4, 128, 4096, 4) == (5, 8, 64, 64)   # capped at two tiles
+        assert B.chunk_plan(512, 8, 4, 128, 4096, 4)[0] == 2   # too many queries: automatic
+    finally:
+        B.tuning_set(B.TUNE_FORCE_KERNEL, 0)
+        B.tuning_set(B.TUNE_TILES_PER_SPLIT, 0)
+    with pytest.raises(B.WinattnError):
+        B.tuning_set(B.TUNE_FORCE_KERNEL, 6)
 
 
 def test_check_meta(lib):

@@ -189,6 +189,9 @@ VARIANTS = {
     "mfma_in_kernel_merge_other_order": {B.TUNE_FORCE_KERNEL: 2, B.TUNE_TILES_PER_SPLIT: 2,
                                          B.TUNE_MERGE_KERNEL: 1, B.TUNE_XCD_MAP: 2},
     "mfma16_many_splits": {B.TUNE_FORCE_KERNEL: 4, B.TUNE_TILES_PER_SPLIT: 1},
+    # the single-launch slot-order kernel (shapes of at most 8 query vectors per group)
+    "slot_order_one_tile": {B.TUNE_FORCE_KERNEL: 5, B.TUNE_TILES_PER_SPLIT: 1},
+    "slot_order_four_tiles": {B.TUNE_FORCE_KERNEL: 5, B.TUNE_TILES_PER_SPLIT: 4},
     "mfma16_one_split_in_kernel_merge": {B.TUNE_FORCE_KERNEL: 4, B.TUNE_TILES_PER_SPLIT: 3,
                                          B.TUNE_MERGE_KERNEL: 1, B.TUNE_XCD_MAP: 2},
 }
@@ -256,6 +259,60 @@ def test_register_kernel_instances(shape):
     assert_close(got, ref, f"{shape}")
 
 
+# The single-launch kernel that streams rings in slot order (kernel 5): every query of a group
+# in one block, ring tiles of 4096 / d slots, split 0 also takes the sinks and the chunk's rows
+# (more than one pass of them when they exceed a pass), the last split merges.
+SLOT_ORDER_CASES = [
+    # rows, ng, hpg, d, w, ns, meta kind, ring tiles per split
+    (1, 8, 4, 128, 4096, 4, "full", 2),      # the decode workload's plan
+    (1, 8, 4, 128, 4096, 4, "mix", 4),
+    (1, 2, 4, 128, 300, 40, "mix", 1),       # 44 sinks and rows: three passes of extra keys
+    (2, 3, 4, 256, 100, 17, "partial", 2),   # 8 queries, d = 256 (4 keys per pass)
+    (8, 2, 1, 64, 50, 3, "mix", 1),          # 8 rows of one head
+    (1, 1, 4, 36, 90, 0, "override", 3),     # d = 36, no sinks
+    (3, 2, 2, 100, 77, 5, "mix", 2),         # 6 queries, ragged ring
+    (1, 4, 1, 64, 1, 1, "full", 1),          # a one-slot ring
+    (4, 1, 2, 128, 20, 0, "empty", 1),       # an empty ring: the chunk's rows only
+    (6, 2, 1, 64, 8, 2, "override", 1),      # chunk longer than its group's window
+    (1, 3, 4, 256, 5000, 2, "mix", 4),       # a long ring: 79 splits
+    (1, 1, 4, 64, 16, 2, "full", 1),         # one split: no partials, output stored directly
+]
+
+
+@pytest.mark.parametrize("shape", SLOT_ORDER_CASES,
+                         ids=[f"r{s[0]}g{s[1]}h{s[2]}d{s[3]}w{s[4]}s{s[5]}{s[6]}t{s[7]}"
+                              for s in SLOT_ORDER_CASES])
+def test_slot_order_kernel(shape):
+    rows, ng, hpg, d, w, ns, kind, tiles = shape
+    _case(f"slot-order kernel {shape}")
+    rng = np.random.default_rng(zlib.crc32(repr(shape).encode()))
+    inp = gen.make_chunk(rows, ng, hpg, d, w, ns, _rand_meta(rng, ng, w, kind),
+                         seed=int(rng.integers(1 << 30)))
+    # slots no row sees hold NaN: they are read (slot order) and must add exactly nothing
+    for g in range(ng):
+        live = _visible_slots(inp, g)
+        for sl in range(w):
+            if sl not in live:
+                inp.ring_k[g, sl] = np.nan
+                inp.ring_v[g, sl] = np.nan
+    ref = oracle.window_chunk(inp)
+    knobs = {B.TUNE_FORCE_KERNEL: 5, B.TUNE_TILES_PER_SPLIT: tiles}
+    try:
+        for knob, val in knobs.items():
+            B.tuning_set(knob, val)
+        plan = B.chunk_plan(rows, ng, hpg, d, w, ns)
+        assert plan[0] == 5, plan
+        got = gpu_chunk(inp).cpu().numpy()
+        again = gpu_chunk(inp).cpu().numpy()   # the ready flags were left at zero
+    finally:
+        for knob in knobs:
+            B.tuning_set(knob, 0)
+    assert_close(got, ref, f"{shape}")
+    # the last split folds the others' partials in the order they become ready, so a repeat
+    # may differ in the last bits (never beyond the bar)
+    assert_close(again, ref, f"{shape}, repeated")
+
+
 GATED_SWEEP = [
     # rows, pos0, cap, window, nh, nk, hd
     (1, 5000, 4096, 1024, 8, 2, 128),
@@ -293,7 +350,7 @@ def _visible_slots(inp, g):
     return seen
 
 
-@pytest.mark.parametrize("rows,hpg", [(1, 4), (3, 4), (70, 4)])
+@pytest.mark.parametrize("rows,hpg", [(1, 4), (2, 4), (3, 4), (70, 4)])
 def test_poisoned_slots_and_canaries(rows, hpg):
     _case(f"poison rows={rows}")
     ng, d, w, ns = 4, 128, 96, 2

@@ -36,7 +36,7 @@ F32_PEAK_TFLOPS = 157.3
 METRIC = "KV GB/s and rows/s for windowed GQA attention; % of HBM peak"
 KERNEL_NAMES = {1: "attn_dec_kernel", 2: "attn_mfma_kernel", 3: "attn_valu_kernel",
                 4: "attn_mfma16_kernel", 5: "attn_decode_kernel"}
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_dec_kernel_decode_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_decode_kernel_decode_counters.json")
 CALIBRATION_COPY_BYTES = 64 << 20
 # Rotating input copies of a workload together hold at least this many bytes (more than the
 # 256 MB Infinity Cache), so that every call reads its inputs from HBM.
@@ -53,8 +53,8 @@ def measured_traffic():
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    from sliding_window_gqa_group_amd.build import source_digest
-    if c.get("kernel_source_digest") != source_digest():
+    from sliding_window_gqa_group_amd.build import DECODE_SOURCES, source_digest
+    if c.get("kernel_source_digest") != source_digest(DECODE_SOURCES):
         return None
     return c.get("hbm_bytes_per_launch")
 

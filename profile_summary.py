@@ -13,7 +13,7 @@ copy. Bytes are per dispatch: the median over the workload's dispatches of each 
     python profile_summary.py counters <pmc dir> <title>
     python profile_summary.py stats <kernel_stats.csv>
     python profile_summary.py trace <kernel_trace.csv> <name substring>
-    python profile_summary.py decode-json <pmc dir> <out.json>
+    python profile_summary.py decode-json <pmc dir> <out.json>   (kernel attn_decode_kernel)
     python profile_summary.py mfma <counter_collection.csv> <title>
 
 Matrix-core utilisation (`mfma`): the pass collects SQ_INSTS_VALU_MFMA_F32 (f32 matrix
@@ -110,15 +110,18 @@ def trace_durations(path: str, needle: str):
     return out
 
 
-def decode_json(pmc_dir: str, out_path: str, digest: str) -> dict:
+def decode_json(pmc_dir: str, out_path: str, digest: str,
+                kernels=("attn_decode_kernel",)) -> dict:
+    """The calibrated bytes of one decode call: the dispatches of every kernel whose name holds
+    one of `kernels` (all the call's launches)."""
     data, (_, ff), (_, wf) = calibrated(pmc_dir)
     per = {name: {"read_bytes": int(round(rb)), "write_bytes": int(round(wb))}
            for name, (_, _, rb, _, wb) in data.items()
-           if "attn_dec_kernel" in name or "split_merge_kernel" in name}
+           if any(k in name for k in kernels)}
     doc = {
         "kernel_source_digest": digest,
         "hbm_bytes_per_launch": sum(v["read_bytes"] + v["write_bytes"] for v in per.values()),
-        "launch": "one attn_window_chunk call on the decode workload: attn_dec_kernel + split_merge_kernel",
+        "launch": "one attn_window_chunk call on the decode workload: " + " + ".join(kernels),
         "per_kernel": per,
         "fetch_factor": ff,
         "write_factor": wf,
@@ -185,8 +188,8 @@ def main(argv):
               f"{statistics.median(d):.0f} ns")
     elif cmd == "decode-json":
         sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-        from sliding_window_gqa_group_amd.build import source_digest
-        print(json.dumps(decode_json(argv[2], argv[3], source_digest()), indent=1))
+        from sliding_window_gqa_group_amd.build import DECODE_SOURCES, source_digest
+        print(json.dumps(decode_json(argv[2], argv[3], source_digest(DECODE_SOURCES)), indent=1))
     elif cmd == "mfma":
         ap = argparse.ArgumentParser(prog="profile_summary.py mfma")
         ap.add_argument("csv")

@@ -30,11 +30,17 @@ HIPCC_FLAGS = [
 _NOISE = "packed-fp32-ops' is not a recognized feature"
 
 
-def source_digest() -> str:
-    """Digest of the kernel sources (every file under csrc/): measurements taken on other
-    sources are not reported as current."""
+# The sources the decode call's kernel is built from (its kernel, the shared device header, the
+# launch declarations and the plan): counters taken on the decode call stay current while
+# these are unchanged.
+DECODE_SOURCES = ("api.hip", "attn_decode.hip", "attn_dec_block.h", "launch.h", "winattn_dev.h")
+
+
+def source_digest(names=None) -> str:
+    """Digest of kernel sources (`names` under csrc/, default every file there): measurements
+    taken on other sources are not reported as current."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(names if names is not None else os.listdir(CSRC)):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]

@@ -336,7 +336,7 @@ __device__ __forceinline__ void attn_dec_block(const AttnParams& p, const int sp
             store_out<GATED>(p, q0 + j, g, 4 * c, make_float4(o.x, o.y, o.z, o.w));
         } else {
             const size_t at = ((size_t)blk * p.slot_stride + split) * NQ + j;
-            store_part4(p, p.pacc + at * D + 4 * c, make_float4(o.x, o.y, o.z, o.w));
+            store_part4<NQ, D>(p, blk, split, j, 4 * c, make_float4(o.x, o.y, o.z, o.w));
             if (c == 0) {
                 store_part(p, p.pm + at, s_m[j]);
                 store_part(p, p.pl + at, s_l[j]);

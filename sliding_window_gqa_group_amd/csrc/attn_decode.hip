@@ -37,12 +37,6 @@
 
 namespace winattn {
 
-// Buffer resource word 3 for raw (untyped) buffer accesses on gfx9-family GPUs (32-bit data
-// format), and the sc1 cache-policy bit of a buffer store: device (agent) scope.
-constexpr int kBufferWord3 = 0x00020000;
-typedef unsigned int vu4 __attribute__((ext_vector_type(4)));
-constexpr int kCachePolicyDevice = 16;
-
 // A group's ring geometry from its metadata (len, head, far count, window override), clamped
 // so that no access leaves the ring (as resolve_group clamps it): window wg, entries held len0,
 // slot of the oldest entry head0.
@@ -302,7 +296,6 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
     constexpr int kAccFloats = NW * NQ * D > 6 * NT + 4 ? NW * NQ * D : 6 * NT + 4;
     __shared__ __align__(16) float s_acc[kAccFloats];
     __shared__ float s_wm[NW * NQ], s_wl[NW * NQ];
-    __shared__ int s_flag;
 
     const int tid = threadIdx.x;
     const int gi = tid / TPK, sl = tid % TPK;   // lane group (key slot), lane within the group

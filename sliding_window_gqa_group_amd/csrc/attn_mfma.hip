@@ -235,8 +235,9 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int e = 32 * b + 8 * m + 4 * hb;
-                store_part4(p, p.pacc + at * D + e, make_float4(oacc[b][4 * m], oacc[b][4 * m + 1],
-                                                            oacc[b][4 * m + 2], oacc[b][4 * m + 3]));
+                store_part4<QB, D>(p, blk, split, jq, e,
+                                   make_float4(oacc[b][4 * m], oacc[b][4 * m + 1], oacc[b][4 * m + 2],
+                                               oacc[b][4 * m + 3]));
             }
         if (hb == 0) {
             store_part(p, p.pm + at, mrun);

@@ -396,8 +396,8 @@ __global__ __launch_bounds__(kThreads * m16_key_split<D>(), 1) void attn_mfma16_
         const size_t at = ((size_t)blk * p.slot_stride + split) * QB + jq;
 #pragma unroll
         for (int b = 0; b < NDB; ++b)
-            store_part4(p, p.pacc + at * D + 16 * b + 4 * kr4,
-                        make_float4(oacc[b][0], oacc[b][1], oacc[b][2], oacc[b][3]));
+            store_part4<QB, D>(p, blk, split, jq, 16 * b + 4 * kr4,
+                               make_float4(oacc[b][0], oacc[b][1], oacc[b][2], oacc[b][3]));
         if (kr4 == 0) {
             store_part(p, p.pm + at, mrun);
             store_part(p, p.pl + at, lrun);

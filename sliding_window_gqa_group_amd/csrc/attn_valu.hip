@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(const AttnParams p)
             store_out<GATED>(p, q0 + j, g, 4 * c, o);
         } else {
             const size_t at = ((size_t)blk * p.slot_stride + split) * NQ + j;
-            store_part4(p, p.pacc + at * D + 4 * c, o);
+            store_part4<NQ, D>(p, blk, split, j, 4 * c, o);
             if (c == 0) {
                 store_part(p, p.pm + at, s_m[j]);
                 store_part(p, p.pl + at, s_l[j]);

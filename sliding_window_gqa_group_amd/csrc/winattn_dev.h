@@ -300,25 +300,24 @@ __device__ inline void store_out(const AttnParams& p, int qi, int g, int e, floa
     *reinterpret_cast<float4*>(p.out + ((size_t)row * p.nh + gh) * p.d + e) = o;
 }
 
-// Split partials cross XCDs, whose L2 caches are not coherent with each other. Rather than a
-// release fence in every workgroup (which writes back a whole L2), the partials are stored
-// with device-scope stores (relaxed agent-scope atomics, emitted with the device-scope cache
-// bit, acknowledged once visible device-wide); only the one merging workgroup per block then
-// performs an agent-scope acquire before reading them.
+// Split partials merged inside the launch cross XCDs, whose L2 caches are not coherent with
+// each other. The protocol (specific to gfx950's memory hierarchy):
+//  - partials are stored with the device-scope (sc1) cache policy: agent-scope atomic stores for
+//    scalars, 16-byte buffer stores with that policy for float4s; such stores are written
+//    through to the device-coherent level and acknowledged from there;
+//  - every thread waits for its stores' acknowledgements (vmcnt 0) before a barrier, so all of a
+//    workgroup's partial stores are complete device-wide before its ticket or flag is set, which
+//    is itself an agent-scope atomic;
+//  - the reader acquires at agent scope (or reads with device-scope loads) after it saw the
+//    ticket or flag.
+// An agent-scope release fence per workgroup would do the same formally but writes back the
+// whole L2 each time; hundreds of them serialise into tens of microseconds.
+typedef unsigned int vu4 __attribute__((ext_vector_type(4)));
+constexpr int kBufferWord3 = 0x00020000;    // raw (untyped) buffer resource word 3 on gfx9
+constexpr int kCachePolicyDevice = 16;      // sc1: device (agent) scope
+
 __device__ inline void store_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void store_dev4(float* p, float4 v) {
-    store_dev(p, v.x);
-    store_dev(p + 1, v.y);
-    store_dev(p + 2, v.z);
-    store_dev(p + 3, v.w);
-}
-__device__ inline float load_dev(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline float4 load_dev4(const float* p) {
-    return make_float4(load_dev(p), load_dev(p + 1), load_dev(p + 2), load_dev(p + 3));
 }
 
 // After every split of a query block has written its partial (m, l, acc), the last one to
@@ -465,8 +464,20 @@ __device__ inline void merge_if_last(const AttnParams& p, int blk, int nsplit, i
 __device__ inline void store_part(const AttnParams& p, float* dst, float v) {
     if (p.merge_kernel) *dst = v; else store_dev(dst, v);
 }
-__device__ inline void store_part4(const AttnParams& p, float* dst, float4 v) {
-    if (p.merge_kernel) *reinterpret_cast<float4*>(dst) = v; else store_dev4(dst, v);
+// float4 column `col` of query j's accumulator in partial slot `split` of query block `blk`
+// (QB queries of D floats per slot). The device-scope store is one 16-byte buffer store
+// addressed from the slot's base, which is uniform over the workgroup.
+template <int QB, int D>
+__device__ inline void store_part4(const AttnParams& p, int blk, int split, int j, int col, float4 v) {
+    float* slot = p.pacc + ((size_t)blk * p.slot_stride + split) * QB * D;
+    if (p.merge_kernel) {
+        *reinterpret_cast<float4*>(slot + (size_t)j * D + col) = v;
+    } else {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(slot, 0, QB * D * 4, kBufferWord3);
+        __builtin_amdgcn_raw_buffer_store_b128(vu4{__float_as_uint(v.x), __float_as_uint(v.y),
+                                                   __float_as_uint(v.z), __float_as_uint(v.w)},
+                                               r, (j * D + col) * 4, 0, kCachePolicyDevice);
+    }
 }
 
 }  // namespace winattn

@@ -20,7 +20,7 @@ def _write(path, counter, rows):
 
 
 def test_counters_are_scaled_by_the_copy(tmp_path):
-    k = "void winattn::attn_dec_kernel<128, 4, false, true>(winattn::AttnParams)"
+    k = "void winattn::attn_decode_kernel<128, 4, 2, 256>(winattn::AttnParams)"
     copy_kib = 64 * 1024
     # FETCH_SIZE reads half of the copy; WRITE_SIZE all of it
     _write(str(tmp_path / "FETCH_SIZE" / "x_counter_collection.csv"), "FETCH_SIZE",

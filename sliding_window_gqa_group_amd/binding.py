@@ -126,7 +126,8 @@ def gated_far_workspace_bytes(nh, nk, hd, w, ns, m) -> int:
 
 
 def chunk_plan(rows, ng, hpg, d, w, ns):
-    """(kernel 1=VALU 2=MFMA, query block, splits, keys per split) for these sizes."""
+    """(kernel, query block, splits, keys per split) for these sizes, as
+    attn_window_chunk_plan reports them (kernel numbers in include/winattn.h)."""
     vals = [ctypes.c_int(0) for _ in range(4)]
     rc = load().attn_window_chunk_plan(rows, ng, hpg, d, w, ns, *[ctypes.byref(v) for v in vals])
     if rc != OK:

@@ -52,13 +52,16 @@ def _run(cmd):
     return res.returncode, msgs
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, defines=(), lib: str = LIB, objdir: str = OBJDIR) -> str:
+    """Compile every source and link `lib`. `defines`: extra preprocessor macros (a timing
+    build: see phase_stamps.py), with their own object folder and library name."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    os.makedirs(OBJDIR, exist_ok=True)
+    os.makedirs(objdir, exist_ok=True)
+    extra = [f"-D{m}" for m in defines]
     jobs = []
     for s in SOURCES:
-        obj = os.path.join(OBJDIR, os.path.splitext(s)[0] + ".o")
-        jobs.append((obj, [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
+        obj = os.path.join(objdir, os.path.splitext(s)[0] + ".o")
+        jobs.append((obj, [hipcc, *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c",
                            os.path.join(CSRC, s), "-o", obj]))
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with ThreadPoolExecutor(workers) as ex:
@@ -70,15 +73,15 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
         if verbose and msgs:
             print("\n".join(msgs))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     link = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in jobs], "-o", tmp]
     rc, msgs = _run(link)
     if verbose:
         print(" ".join(link), flush=True)
     if rc != 0:
         raise RuntimeError("link failed:\n" + "\n".join(msgs))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

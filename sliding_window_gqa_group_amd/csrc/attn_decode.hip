@@ -37,6 +37,47 @@
 
 namespace winattn {
 
+// Phase stamps, in timing builds only (compiled with WINATTN_PHASE_STAMPS; the library's normal
+// build contains none of this code). Every wave reads the 100 MHz real-time counter at the
+// kernel's phase boundaries, keeps the readings in registers and writes them once, at its end,
+// with the number of the XCD it ran on, to g_phase_stamps[block * waves + wave][kStampWords]
+// when the host has set that pointer (attn_phase_stamps_set). The kernel's work is unchanged.
+#ifdef WINATTN_PHASE_STAMPS
+constexpr int kStampWords = 10;
+__device__ unsigned long long* g_phase_stamps;
+struct PhaseStamps {
+    unsigned long long t[kStampWords - 1] = {};
+    __device__ void mark(int k) { t[k] = __builtin_amdgcn_s_memrealtime(); }
+    // the reading waits until `v` is available (the empty asm uses it)
+    template <class V>
+    __device__ void mark_after(int k, const V& v) {
+        asm volatile("" : : "v"(v));
+        mark(k);
+    }
+    // the reading waits until every memory access of the wave has completed
+    __device__ void mark_drained(int k) {
+        __builtin_amdgcn_s_waitcnt(0);
+        mark(k);
+    }
+    __device__ void flush(int tid, int waves) {
+        unsigned long long* o = g_phase_stamps;
+        if (!o || (tid & 63) != 0) return;
+        o += ((size_t)blockIdx.x * waves + tid / 64) * kStampWords;
+        for (int k = 0; k < kStampWords - 1; ++k) o[k] = t[k];
+        // hardware register 20 (XCC_ID), bits 0-3: the XCD of this wave
+        o[kStampWords - 1] = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11));
+    }
+};
+#else
+struct PhaseStamps {
+    __device__ void mark(int) {}
+    template <class V>
+    __device__ void mark_after(int, const V&) {}
+    __device__ void mark_drained(int) {}
+    __device__ void flush(int, int) {}
+};
+#endif
+
 // A group's ring geometry from its metadata (len, head, far count, window override), clamped
 // so that no access leaves the ring (as resolve_group clamps it): window wg, entries held len0,
 // slot of the oldest entry head0.
@@ -79,6 +120,35 @@ __device__ inline float lane_groups_sum(float v) {
     return v;
 }
 
+// Max / sum over lanes l, l + span, l + 2 span, ... of the wave (span a power of two, 1 to 64,
+// uniform over the wave), result in every lane: rotations within each row of 16 lanes by span,
+// 2 span, ... 8, then the row and half-wave swaps.
+__device__ inline float lanes_max_spaced(float v, int span) {
+    if (span <= 1) v = fmaxf(v, dpp<0x121>(v, -INFINITY));
+    if (span <= 2) v = fmaxf(v, dpp<0x122>(v, -INFINITY));
+    if (span <= 4) v = fmaxf(v, dpp<0x124>(v, -INFINITY));
+    if (span <= 8) v = fmaxf(v, dpp<kDppRowRor8>(v, -INFINITY));
+    if (span <= 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    if (span <= 32) v = half_swap_max(v);
+    return v;
+}
+
+__device__ inline float lanes_sum_spaced(float v, int span) {
+    if (span <= 1) v += dpp<0x121>(v, 0.0f);
+    if (span <= 2) v += dpp<0x122>(v, 0.0f);
+    if (span <= 4) v += dpp<0x124>(v, 0.0f);
+    if (span <= 8) v += dpp<kDppRowRor8>(v, 0.0f);
+    if (span <= 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    if (span <= 32) v = half_swap_sum(v);
+    return v;
+}
+
 // The group's last `nk` splits are its gatherers (the last of the group's workgroups in dispatch
 // order, so every split a gatherer waits for was dispatched before it, and the non-gatherers
 // never wait). Gatherer k owns output columns [k, k + 1) * D / (4 nk) float4 of every query of
@@ -89,28 +159,34 @@ __device__ inline float lane_groups_sum(float v) {
 // streaming; after the last flag only that split's columns remain to be read.
 //  - Every split raises one flag per gatherer (flags[k][s]), so each gatherer polls and clears
 //    flags nobody else reads.
-//  - Each thread owns IPT (query j, float4 column c) items of the chunk and the splits
-//    s = sub (mod NSUB). A wave polls every flag of its gatherer (one device-scope load per
-//    lane, two rounds beyond 64 splits); each lane then reads up to MB of its own newly
-//    ready splits per round, all loads of a round issued together with the next poll behind
-//    them.
+//  - Each wave owns ipw = NQ * D / (4 nk) / waves (query j, float4 column c) items. Lane
+//    l = sub * ipw + item (ipw < 64) takes the splits s = sub (mod 64 / ipw) of its item, so the
+//    lanes of one item differ only in the bits above ipw and meet by cross-lane reductions, with
+//    no LDS and no barrier (ipw >= 64: a lane owns ipw / 64 items and every split of them).
+//  - A wave polls every flag of its gatherer (one device-scope load per lane, two rounds beyond
+//    64 splits); each lane then reads up to MB of its own newly ready splits per round, all
+//    loads of a round issued together with the next poll behind them.
 //  - The poll is bounded: after kGatherPolls rounds without every flag, the chunk is written as
 //    NaN rather than waiting longer (it cannot happen while every split runs).
-//  - Once every wave has left its poll loop, the gatherer's flags are cleared, so the next call
-//    starts from zero; the NSUB subsets meet in LDS (`scratch`: 6 * NT floats and a word).
+//  - After one barrier (every wave has left its poll loop and said whether it saw every flag in
+//    `scratch`, NT / 64 words), the gatherer's flags are cleared for the next call.
 constexpr int kGatherPolls = 1 << 18;
 
 template <int NQ, int D, int NT>
 __device__ inline void gather_chunk(const AttnParams& p, int g, int nsplit, int nq, int nk, int k,
-                                    unsigned int* flags, float* scratch) {
-    constexpr int D4 = D / 4;
-    constexpr int MB = 8;   // splits per lane per load round
+                                    unsigned int* flags, int* scratch) {
+    constexpr int D4 = D / 4, NW = NT / 64;
+    constexpr int MB = 8;                     // splits per lane per load round
+    // items per lane at most: more than 64 per wave only for a single gatherer of 8 queries of
+    // width 256
+    constexpr int IPTM = NQ * D4 > NW * 64 ? NQ * D4 / (NW * 64) : 1;
     const int cpk = D4 / nk;                  // float4 columns per gatherer
-    const int ipg = NQ * cpk;                 // items per gatherer
-    const int nsub = ipg >= NT ? 1 : NT / ipg;
-    const int ipt = ipg >= NT ? ipg / NT : 1;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int sub = nsub > 1 ? tid / ipg : 0;
+    const int ipw = NQ * cpk / NW;            // items per wave (>= 2)
+    const int span = ipw < 64 ? ipw : 64;     // lanes of one item are `span` apart
+    const int nsub = 64 / span;               // lanes per item
+    const int ipt = ipw / span;               // items per lane
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid / 64;
+    const int sub = lane / span;
     const size_t grp = (size_t)g * nsplit * NQ;   // first partial slot of the group
     const __amdgpu_buffer_rsrc_t racc =
         __builtin_amdgcn_make_buffer_rsrc(p.pacc + grp * D, 0, nsplit * NQ * D * 4, kBufferWord3);
@@ -120,20 +196,13 @@ __device__ inline void gather_chunk(const AttnParams& p, int g, int nsplit, int 
         __builtin_amdgcn_make_buffer_rsrc(p.pl + grp, 0, nsplit * NQ * 4, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rf =
         __builtin_amdgcn_make_buffer_rsrc(flags, 0, nsplit * 4, kBufferWord3);
-    float* s_m = scratch;
-    float* s_l = scratch + NT;
-    vf4* s_a = reinterpret_cast<vf4*>(scratch + 2 * NT);
-    int* s_bad = reinterpret_cast<int*>(scratch + 6 * NT);
 
-    // IPT is 1 unless one gatherer owns more items than threads (a single gatherer of 8 queries
-    // of width 256): then 2
-    constexpr int IPTM = NQ * D4 > NT ? NQ * D4 / NT : 1;
     float cm[IPTM], cl[IPTM];
     vf4 ca[IPTM];
     int jj[IPTM], cc[IPTM];
 #pragma unroll
     for (int it = 0; it < IPTM; ++it) {
-        const int item = (nsub > 1 ? tid % ipg : tid + it * NT) % ipg;
+        const int item = wave * ipw + lane % span + span * (it < ipt ? it : 0);
         jj[it] = item / cpk;
         cc[it] = k * cpk + item % cpk;
         cm[it] = -INFINITY;
@@ -222,48 +291,41 @@ __device__ inline void gather_chunk(const AttnParams& p, int g, int nsplit, int 
             cm[it] = nm;
         }
     }
-    const bool complete = !(pend[0] | pend[1] | todo[0] | todo[1]);
-    if (tid == 0) *s_bad = 0;
-    __syncthreads();
-    if (!complete) *s_bad = 1;
-    __syncthreads();
-    // every wave has left its poll loop: this gatherer's flags back to zero for the next call
-    if (!*s_bad && tid < 64) {
+    const bool complete = !__builtin_amdgcn_ballot_w64((pend[0] | pend[1] | todo[0] | todo[1]) != 0ull);
+
+    // the lanes of each item meet: c = max over them, then the rescaled sums
+#pragma unroll
+    for (int it = 0; it < IPTM; ++it) {
+        if (it >= ipt) break;
+        const float c = lanes_max_spaced(cm[it], span);
+        const float f = __builtin_amdgcn_exp2f(cm[it] - safe_max(c));
+        cl[it] = lanes_sum_spaced(cl[it] * f, span);
+        ca[it].x = lanes_sum_spaced(ca[it].x * f, span);
+        ca[it].y = lanes_sum_spaced(ca[it].y * f, span);
+        ca[it].z = lanes_sum_spaced(ca[it].z * f, span);
+        ca[it].w = lanes_sum_spaced(ca[it].w * f, span);
+    }
+    if (lane == 0) scratch[wave] = complete ? 1 : 0;
+    __syncthreads();   // every wave has left its poll loop
+    bool bad = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) bad |= scratch[w] == 0;
+    if (sub == 0) {
+#pragma unroll
+        for (int it = 0; it < IPTM; ++it) {
+            if (it >= ipt || jj[it] >= nq || cc[it] >= p.d / 4) continue;
+            vf4 o = ca[it] * (1.0f / fmaxf(cl[it], 1e-30f));
+            if (bad) o = vf4{NAN, NAN, NAN, NAN};
+            store_out<false>(p, jj[it], g, 4 * cc[it], make_float4(o.x, o.y, o.z, o.w));
+        }
+    }
+    // this gatherer's flags back to zero for the next call
+    if (!bad && tid < 64) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int s = h * 64 + lane;
             if (s < nsplit) __hip_atomic_store(flags + s, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-    }
-#pragma unroll
-    for (int it = 0; it < IPTM; ++it) {
-        if (it >= ipt) break;
-        if (nsub > 1) {
-            s_m[tid] = cm[it];
-            s_l[tid] = cl[it];
-            s_a[tid] = ca[it];
-        }
-        __syncthreads();
-        const int item = nsub > 1 ? tid % ipg : tid + it * NT;
-        if (nsub > 1 && sub == 0) {
-            float mm = cm[it];
-            for (int u = 1; u < nsub; ++u) mm = fmaxf(mm, s_m[u * ipg + item]);
-            const float mu = safe_max(mm);
-            const float f0 = __builtin_amdgcn_exp2f(cm[it] - mu);
-            cl[it] *= f0;
-            ca[it] *= f0;
-            for (int u = 1; u < nsub; ++u) {
-                const float f = __builtin_amdgcn_exp2f(s_m[u * ipg + item] - mu);
-                cl[it] += s_l[u * ipg + item] * f;
-                ca[it] += s_a[u * ipg + item] * f;
-            }
-        }
-        if (sub == 0 && item < ipg && jj[it] < nq && cc[it] < p.d / 4) {
-            vf4 o = ca[it] * (1.0f / fmaxf(cl[it], 1e-30f));
-            if (*s_bad) o = vf4{NAN, NAN, NAN, NAN};
-            store_out<false>(p, jj[it], g, 4 * cc[it], make_float4(o.x, o.y, o.z, o.w));
-        }
-        __syncthreads();
     }
 }
 
@@ -292,8 +354,8 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
     static_assert(T <= S::MAX_TILES, "too many tiles for the registers");
 
     constexpr int NW = NT / 64;                           // waves
-    // each wave's state at the end, then the merge's scratch
-    constexpr int kAccFloats = NW * NQ * D > 6 * NT + 4 ? NW * NQ * D : 6 * NT + 4;
+    // each wave's state at the end (then the gather's NW words)
+    constexpr int kAccFloats = NW * NQ * D;
     __shared__ __align__(16) float s_acc[kAccFloats];
     __shared__ float s_wm[NW * NQ], s_wl[NW * NQ];
 
@@ -304,6 +366,8 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
     const int nsplit = p.nsplit_grid;
     const int nq = p.rows * p.hpg;              // every query of the group: one block
     const int d4 = p.d / 4;
+    PhaseStamps ps_;
+    ps_.mark(0);   // phase 0: start
 
     // ---- the group's metadata is requested first, ahead of the call's K/V traffic, as a
     // vector load: vector loads return in order, so waiting for it waits for nothing issued
@@ -358,7 +422,9 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
     };
 
     // ---- every load of the split, before the metadata: split 0's first pass of extra keys,
-    // then the ring slots split*T*TK + i*KPP + gi of pass i (slots past w load slot w-1)
+    // then the ring slots split*T*TK + i*KPP + gi of pass i (slots past w load slot w-1). The
+    // ring is read once per call: its loads are non-temporal, so the stream does not push the
+    // kernel's code, metadata and queries out of the caches (measured 3 % faster).
     vf4 kx[F4], vx[F4];
     if (split == 0) load_extra(kx, vx, gi);
     const int slot0 = split * (T * TK) + gi;
@@ -370,8 +436,8 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
         for (int f = 0; f < F4; ++f) {
             const int c = sl + TPK * f;
             const int off = slot * ss + (c < d4 ? 4 * c : 0);
-            kr[i][f] = *reinterpret_cast<gvf4p>(rk + 4ull * (unsigned)off);
-            vr[i][f] = *reinterpret_cast<gvf4p>(rv + 4ull * (unsigned)off);
+            kr[i][f] = __builtin_nontemporal_load(reinterpret_cast<gvf4p>(rk + 4ull * (unsigned)off));
+            vr[i][f] = __builtin_nontemporal_load(reinterpret_cast<gvf4p>(rv + 4ull * (unsigned)off));
         }
     }
 
@@ -389,6 +455,7 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
         qlo[j] = j < nq ? window_lo(hi, rg.wg) : 0x7fffffff;   // padding sees nothing
         qrow[j] = j < nq ? row : -1;
     }
+    ps_.mark_after(1, qlo[0]);   // phase 1: metadata arrived
 
     float mrun[NQ], lrun[NQ];
     vf4 acc[NQ][F4];
@@ -522,7 +589,9 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
             vis[ps] = m;
         }
         step(kt, vt, vis);
+        if (t == 0) ps_.mark_after(2, mrun[0]);   // phase 2: first ring tile done
     }
+    ps_.mark_after(3, lrun[0]);   // phase 3: last ring tile done
 
     // ---- merge the lane groups of each wave with cross-lane swaps (every lane of a group
     // holds the group's state; groups of a wave differ in the lane bits above TPK), then the
@@ -555,6 +624,7 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
         }
     }
     __syncthreads();
+    ps_.mark(4);   // phase 4: lane groups and waves merged into LDS
 
     // ---- this split's partial (or the output when the group has a single split), folded over
     // the waves per (query, float4 column) item. Partials are read within this launch by
@@ -592,7 +662,11 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
             }
         }
     }
-    if (nsplit == 1) return;
+    ps_.mark(5);   // phase 5: partial (or output) stores issued
+    if (nsplit == 1) {
+        ps_.flush(tid, NW);
+        return;
+    }
 
     // ---- every thread waits until its partial stores are acknowledged (complete at the
     // device-coherent level) before the barrier; then the split raises its ready flag for each
@@ -600,12 +674,19 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
     const int nk = p.gather_k;
     unsigned int* flags = p.tickets + (size_t)g * nk * nsplit;
     __builtin_amdgcn_s_waitcnt(0);
+    ps_.mark(6);   // phase 6: partial stores acknowledged
     __syncthreads();
     if (tid < nk) __hip_atomic_store(flags + tid * nsplit + split, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int k = split - (nsplit - nk);
-    if (k < 0) return;
-    __syncthreads();   // the wave states in LDS are read: the gather reuses it as scratch
-    gather_chunk<NQ, D, NT>(p, g, nsplit, nq, nk, k, flags + k * nsplit, s_acc);
+    ps_.mark(7);   // phase 7: ready flags raised
+    if (k < 0) {
+        ps_.flush(tid, NW);
+        return;
+    }
+    // the barrier above ended every read of the wave states: the gather reuses that LDS
+    gather_chunk<NQ, D, NT>(p, g, nsplit, nq, nk, k, flags + k * nsplit, reinterpret_cast<int*>(s_acc));
+    ps_.mark_drained(8);   // phase 8: column chunk gathered and its output stored
+    ps_.flush(tid, NW);
 }
 
 template <int D, int NQ, int T, int NT>
@@ -643,3 +724,13 @@ hipError_t launch_decode(const AttnParams& p, int dpad, int nq, int tiles, hipSt
 }
 
 }  // namespace winattn
+
+#ifdef WINATTN_PHASE_STAMPS
+// Timing builds: where the decode kernel writes its phase stamps (NULL: nowhere). The buffer
+// holds kStampWords u64 per wave of the launch; each launch overwrites it.
+extern "C" int attn_phase_stamps_set(void* device_ptr) {
+    return hipMemcpyToSymbol(HIP_SYMBOL(winattn::g_phase_stamps), &device_ptr, sizeof(device_ptr)) == hipSuccess
+               ? 0
+               : -3;
+}
+#endif

@@ -1,0 +1,127 @@
+"""Phase timing of the single-launch decode kernel from in-kernel clock stamps.
+
+    python -m sliding_window_gqa_group_amd.phase_stamps build      # on any host: compiles
+    python -m sliding_window_gqa_group_amd.phase_stamps run        # on the GPU: prints markdown
+
+`build` compiles the library a second time with WINATTN_PHASE_STAMPS defined, into
+libwinattn_stamps.so beside the normal one (the normal library has no stamp code). `run` loads
+that library instead of the normal one and makes decode calls (1 row, 8 KV groups x 4 query
+heads, d 128, full 4096-slot rings, 4 sinks) on 20 rotating input sets. Each recorded call is
+the last of 8 back-to-back calls, as in the bench's timed loop; every wave of it wrote the
+100 MHz real-time counter at its phase boundaries. The report gives, per phase, the spread over
+all waves of the recorded calls of the time since the call's first wave started.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+STAMPS_LIB = os.path.join(HERE, "libwinattn_stamps.so")
+STAMPS_OBJDIR = os.path.join(HERE, "_build_stamps")
+WORDS = 10   # u64 per wave: 9 phase stamps, then the XCD number
+PHASES = [
+    ("start", "the wave starts"),
+    ("meta", "the group's metadata has arrived (every K/V load of the split is in flight)"),
+    ("tile0", "the first ring tile's scores, softmax and value update are done"),
+    ("tiles", "every ring tile is done"),
+    ("merged", "lane groups and waves merged into LDS"),
+    ("issued", "partial stores issued"),
+    ("acked", "partial stores acknowledged device-wide"),
+    ("flagged", "ready flags raised (waves of non-gathering splits end here)"),
+    ("gathered", "a gatherer's column chunk folded and stored (gatherers only)"),
+]
+
+
+def build() -> str:
+    sys.path.insert(0, os.path.dirname(HERE))
+    from sliding_window_gqa_group_amd import build as b
+    return b.build(defines=("WINATTN_PHASE_STAMPS",), lib=STAMPS_LIB, objdir=STAMPS_OBJDIR)
+
+
+def run(calls: int = 10) -> str:
+    sys.path.insert(0, os.path.dirname(HERE))
+    import numpy as np
+    import torch
+    from sliding_window_gqa_group_amd import binding as B, inputs as gen
+
+    lib = B.load(STAMPS_LIB)   # every binding call below goes to the timing build
+    lib.attn_phase_stamps_set.argtypes = [ctypes.c_void_p]
+    lib.attn_phase_stamps_set.restype = ctypes.c_int
+    dev = "cuda:0"
+    inp = gen.decode()
+    base = gen.to_device(inp, dev)
+    nsets = 20
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+    outs = [torch.empty((inp.rows, inp.nh, inp.d), dtype=torch.float32, device=dev)
+            for _ in range(nsets)]
+    plan = B.chunk_plan(inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns)
+    nsplit = plan[2]
+    waves = inp.ng * nsplit * 4
+    ws = B.Workspace(dev)
+    ws.get(B.chunk_workspace_bytes(inp.rows, inp.ng, inp.hpg, inp.d, inp.w, inp.ns))
+    stamps = torch.zeros(waves * WORDS, dtype=torch.int64, device=dev)
+
+    def call(i):
+        t = sets[i % nsets]
+        B.attn_window_chunk(t["ring_k"], t["ring_v"], t["meta"], t["sink_k"], t["sink_v"], t["q"],
+                            t["chunk_k"], t["chunk_v"], inp.scale, out=outs[i % nsets], workspace=ws)
+
+    def set_ptr(ptr):
+        torch.cuda.synchronize()
+        if lib.attn_phase_stamps_set(ctypes.c_void_p(ptr)) != 0:
+            raise RuntimeError("attn_phase_stamps_set failed")
+        torch.cuda.synchronize()
+
+    set_ptr(0)
+    print(f"plan {tuple(plan)}: warming up", file=sys.stderr, flush=True)
+    for i in range(200):   # untimed: clocks up, code and buffers touched
+        call(i)
+    rel = [[] for _ in PHASES]
+    ends = []
+    xcd = np.zeros(8, dtype=np.int64)
+    for r in range(calls):
+        stamps.zero_()
+        set_ptr(stamps.data_ptr())
+        for i in range(8):
+            call(r * 8 + i)
+        set_ptr(0)
+        t = stamps.cpu().numpy().reshape(waves, WORDS)
+        if (t[:, 0] == 0).any():
+            raise RuntimeError("a wave wrote no stamps")
+        t0 = t[:, 0].min()
+        for k in range(len(PHASES)):
+            col = t[:, k]
+            rel[k].append((col[col != 0] - t0) * 0.01)
+        last = np.where(t[:, 8] != 0, t[:, 8], t[:, 7])
+        last = np.where(last != 0, last, t[:, 5])
+        ends.append((last.max() - t0) * 0.01)
+        xcd += np.bincount((t[:, 9] & 0xF).astype(np.int64), minlength=8)[:8]
+        print(f"recorded call {r + 1} of {calls}", file=sys.stderr, flush=True)
+
+    lines = [f"Decode call: plan (kernel, queries per block, splits, keys per split) = {tuple(plan)}, "
+             f"{inp.ng * nsplit} workgroups of 4 waves; {calls} recorded calls, each the last of 8 "
+             "back-to-back calls on 20 rotating input sets. Times in us since the call's first "
+             "wave started (100 MHz counter), over every wave that reached the phase.",
+             "",
+             "| phase | waves | min | p10 | p50 | p90 | max | meaning |",
+             "|---|---|---|---|---|---|---|---|"]
+    for k, (name, meaning) in enumerate(PHASES):
+        v = np.concatenate(rel[k])
+        lines.append(f"| {name} | {len(v)} | {v.min():.2f} | {np.percentile(v, 10):.2f} | "
+                     f"{np.median(v):.2f} | {np.percentile(v, 90):.2f} | {v.max():.2f} | {meaning} |")
+    e = np.array(ends)
+    lines += ["", f"First wave start to last wave end: median {np.median(e):.2f} us "
+              f"(min {e.min():.2f}, max {e.max():.2f}).",
+              "Waves per XCD (hardware register XCC_ID): " + ", ".join(str(int(x)) for x in xcd) + "."]
+    return "\n".join(lines)
+
+
+if __name__ == "__main__":
+    if len(sys.argv) < 2 or sys.argv[1] not in ("build", "run"):
+        raise SystemExit(__doc__)
+    if sys.argv[1] == "build":
+        print(build())
+    else:
+        print(run(int(sys.argv[2]) if len(sys.argv) > 2 else 10))

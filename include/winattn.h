@@ -22,10 +22,14 @@
  *    for WINATTN_ELAUNCH, which reports a failed launch.
  *  - `workspace` is caller-owned device memory of at least the size the matching *_workspace
  *    query returns (0 means the call needs none and NULL may be passed). Its first 64 KiB hold
- *    split counters at a fixed place for every call shape: they must be zero before the first
- *    call that uses the workspace (a fresh zeroed allocation, or attn_workspace_init), and
- *    every call leaves them at zero again, so one workspace serves calls of any shapes in
- *    sequence. Two calls that may run at the same time must not share a workspace.
+ *    split counters at a fixed place for every call shape. The plans that combine split
+ *    partials inside one launch use them: the single-launch decode kernel's ready flags
+ *    (kernel 5), the gated single launch's ready flags (kernel 6) and the last-split merge of
+ *    kernels 1 to 4 when WINATTN_TUNE_MERGE_KERNEL selects it; plans that merge in a separate
+ *    launch never touch them. They must be zero before the first call that uses the workspace
+ *    (a fresh zeroed allocation, or attn_workspace_init), and every call leaves them at zero
+ *    again, so one workspace serves calls of any shapes in sequence. Two calls that may run at
+ *    the same time must not share a workspace.
  */
 #ifndef WINATTN_H
 #define WINATTN_H
@@ -136,6 +140,13 @@ int attn_window_chunk_noalloc(const float* ring_k, const float* ring_v, const ui
  *   8 <= hd <= 256; cap >= window + rows - 1 (so no row's write clobbers a key an earlier
  *   row still needs); eps >= 0.
  * Ring slots that no row reads and no row writes are left untouched.
+ * Plans: widths 160, 192, 224 and 256 with at least 16 query vectors (rows * nh / nk) per KV
+ * head run in one launch (kernel 6: the rotations where the heads are loaded, the ring write by
+ * the workgroup that reads the row, split partials folded by each query set's last split); its
+ * workspace holds the split counters and the partials (none with a single split per set).
+ * Other shapes prepare the unit heads and the ring in a first launch, then run the chunk
+ * kernels on the prepared queries (the workspace also holds them) and, with several splits, a
+ * merge launch. Every plan writes the same results within the tolerance of f32 rounding.
  */
 int attn_window_gated(const float* yq, const float* yk, const float* yv, const float* rope,
                       const float* q_scale, const float* gate, const float* gate_scale,
@@ -313,9 +324,12 @@ int attn_read_probe(const void* src, size_t bytes, float* sink, void* stream);
 /* Tuning knobs for tests and benchmarks (process-wide, not thread-safe; 0 = automatic).
  * They change the launch plan and therefore the workspace size: query the size after setting
  * them. */
-#define WINATTN_TUNE_FORCE_KERNEL 1    /* kernel number as reported by attn_window_chunk_plan */
+#define WINATTN_TUNE_FORCE_KERNEL 1    /* kernel number as reported by attn_window_chunk_plan;
+                                         6: the gated call's single launch where its width
+                                         allows (chunk calls then plan as with 0) */
 #define WINATTN_TUNE_TILES_PER_SPLIT 2 /* key tiles per split */
-#define WINATTN_TUNE_TARGET_BLOCKS 3   /* workgroups the split count aims for */
+#define WINATTN_TUNE_TARGET_BLOCKS 3   /* workgroups the split count aims for (also the gated
+                                         single launch's) */
 #define WINATTN_TUNE_MERGE_KERNEL 4    /* 1 = splits merge in the last split, 2 = separate launch */
 #define WINATTN_TUNE_XCD_MAP 5         /* matrix-core and encoder work order: 1 = round-robin, 2 = groups per XCD */
 int attn_tuning_set(int knob, int value);

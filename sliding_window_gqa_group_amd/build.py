@@ -19,7 +19,8 @@ LIB = os.path.join(HERE, "libwinattn.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "attn_dec.hip", "attn_valu.hip", "attn_mfma.hip", "attn_mfma16.hip",
            "gated_prep.hip", "ring_commit.hip", "far_field.hip",
-           "enc_attn.hip", "attn_dec_far.hip", "read_probe.hip", "attn_decode.hip"]
+           "enc_attn.hip", "attn_dec_far.hip", "read_probe.hip", "attn_decode.hip",
+           "attn_gated.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

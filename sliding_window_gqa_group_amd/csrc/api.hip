@@ -16,7 +16,8 @@ namespace {
 
 // Tuning knobs (attn_tuning_set); 0 = automatic.
 int g_force_kernel = 0;     // 1 register, 2 MFMA 32x32, 3 LDS vector, 4 MFMA 16x16,
-                            // 5 single-launch register kernel in slot order
+                            // 5 single-launch register kernel in slot order,
+                            // 6 single-launch gated kernel (gated calls)
 int g_tiles_per_split = 0;
 int g_target_blocks = 0;
 int g_merge_kernel = -1;    // -1 automatic, 0 merge in the last split, 1 separate merge launch
@@ -29,7 +30,7 @@ constexpr int kValuMaxQ = 16;
 constexpr size_t kTicketBytes = 64 * 1024;
 constexpr long long kMaxTickets = kTicketBytes / sizeof(unsigned int);
 
-enum Kind { kKindDec = 1, kKindMfma = 2, kKindValu = 3, kKindMfma16 = 4, kKindDecode = 5 };
+enum Kind { kKindDec = 1, kKindMfma = 2, kKindValu = 3, kKindMfma16 = 4, kKindDecode = 5, kKindGated = 6 };
 
 // The single-launch slot-order kernel's last split gathers at most this many partials (two
 // 64-bit masks of splits; its ring tiles per split, held in registers, are bounded by
@@ -64,7 +65,8 @@ int pad_d(int d) { return d <= 64 ? 64 : (d <= 128 ? 128 : 256); }
 // last split. False if the shape is not one it takes.
 bool decode_plan(int rows, int ng, int hpg, int d, int w, Plan& pl) {
     const long long nq_tot = (long long)rows * hpg;
-    if (nq_tot > 8 || (g_force_kernel != 0 && g_force_kernel != kKindDecode)) return false;
+    if (nq_tot > 8 || (g_force_kernel != 0 && g_force_kernel != kKindDecode && g_force_kernel != kKindGated))
+        return false;
     pl.kind = kKindDecode;
     pl.mfma = false;
     pl.dpad = pad_d(d);
@@ -207,6 +209,53 @@ Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_f
     }
     pl.bytes = off;
     return pl;
+}
+
+// Plan of the gated call in one launch (kernel 6): unit heads of width 160, 192, 224 or 256 and
+// at least one full query set (16 query vectors) per KV head. nsplit workgroups per query set
+// aim at one per CU; each of their 4 waves should keep at least one 16-key block.
+struct GatedPlan {
+    int nqs, nsplit;
+    size_t off_pacc, off_pm, off_pl, bytes;
+};
+
+constexpr int kGatedTargetBlocks = 256;
+constexpr int kGatedMaxSplits = 64;
+
+bool gated_fused_plan(int rows, int nh, int nk, int hd, int window, GatedPlan& gp) {
+    if (g_force_kernel != 0 && g_force_kernel != kKindGated) return false;
+    if (hd <= 128 || hd > 256 || hd % 32 != 0) return false;
+    const int hpg = nh / nk;
+    const long long nqv = (long long)rows * hpg;
+    if (nqv < 16 && g_force_kernel != kKindGated) return false;
+    const long long nqs = (nqv + 15) / 16;
+    const long long sets = nqs * nk;
+    if (sets > (1LL << 24)) return false;
+    // positions a set can span: its rows' windows, at most window + rows spanned - 1
+    const long long span = std::min<long long>(rows, 15 / hpg + 2);
+    const long long nb = ((long long)window + span - 1 + 15) / 16;
+    const int target = g_target_blocks > 0 ? g_target_blocks : kGatedTargetBlocks;
+    long long ns = (target + sets - 1) / sets;
+    ns = std::min<long long>(ns, std::max<long long>(1, nb / 4));
+    ns = std::max<long long>(1, std::min<long long>(ns, kGatedMaxSplits));
+    while (ns > 1 && sets * ns > kMaxTickets) --ns;
+    gp.nqs = (int)nqs;
+    gp.nsplit = (int)ns;
+    if (ns == 1) {
+        gp.off_pacc = gp.off_pm = gp.off_pl = 0;
+        gp.bytes = 0;
+        return true;
+    }
+    const size_t items = (size_t)sets * ns;
+    size_t off = kTicketBytes;
+    gp.off_pacc = off;
+    off = align_up(off + items * 16 * 256 * sizeof(float), 256);
+    gp.off_pm = off;
+    off = align_up(off + items * 16 * sizeof(float), 256);
+    gp.off_pl = off;
+    off = align_up(off + items * 16 * sizeof(float), 256);
+    gp.bytes = off;
+    return true;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -741,6 +790,8 @@ size_t attn_window_gated_workspace(int rows, int nh, int nk, int hd, int window)
     if (rows < 1 || nh < 1 || nk < 1 || window < 1 || nh % nk != 0 || hd < 8 || hd > 256 ||
         hd % 8 != 0)
         return 0;
+    GatedPlan gp;
+    if (gated_fused_plan(rows, nh, nk, hd, window, gp)) return gp.bytes;
     return make_plan(rows, nk, nh / nk, hd, window, 0, (size_t)rows * nh * hd).bytes;
 }
 
@@ -755,11 +806,47 @@ int attn_window_gated(const float* yq, const float* yk, const float* yv, const f
     for (const void* ptr : ptrs)
         if (!ptr || !aligned16(ptr)) return WINATTN_EINVAL;
     const int hpg = nh / nk;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    GatedPlan gp;
+    if (gated_fused_plan(rows, nh, nk, hd, window, gp)) {
+        if (gp.bytes > 0 && (!workspace || workspace_bytes < gp.bytes)) return WINATTN_EWORKSPACE;
+        if (gp.bytes > 0 && !aligned16(workspace)) return WINATTN_EINVAL;
+        char* ws = static_cast<char*>(workspace);
+        GatedFusedParams f{};
+        f.yq = yq;
+        f.yk = yk;
+        f.yv = yv;
+        f.rope = rope;
+        f.q_scale = q_scale;
+        f.gate = gate;
+        f.gate_scale = gate_scale;
+        f.ring_k = ring_k;
+        f.ring_v = ring_v;
+        f.out = out;
+        if (gp.nsplit > 1) {
+            f.flags = reinterpret_cast<unsigned int*>(ws);
+            f.pacc = reinterpret_cast<float*>(ws + gp.off_pacc);
+            f.pm = reinterpret_cast<float*>(ws + gp.off_pm);
+            f.pl = reinterpret_cast<float*>(ws + gp.off_pl);
+        }
+        f.rows = rows;
+        f.pos0 = pos0;
+        f.cap = cap;
+        f.window = window;
+        f.nh = nh;
+        f.nk = nk;
+        f.hd = hd;
+        f.hpg = hpg;
+        f.nqs = gp.nqs;
+        f.nsplit = gp.nsplit;
+        f.scale_log2 = scale * kLog2e;
+        f.eps = eps;
+        return launch_gated_fused(f, st) == hipSuccess ? WINATTN_OK : WINATTN_ELAUNCH;
+    }
     const Plan pl = make_plan(rows, nk, hpg, hd, window, 0, (size_t)rows * nh * hd);
     if (!workspace || workspace_bytes < pl.bytes) return WINATTN_EWORKSPACE;
     if (!aligned16(workspace)) return WINATTN_EINVAL;
     char* ws = static_cast<char*>(workspace);
-    hipStream_t st = static_cast<hipStream_t>(stream);
 
     PrepParams pp{};
     pp.yq = yq;
@@ -849,7 +936,7 @@ int attn_tuning_set(int knob, int value) {
     if (value < 0) return WINATTN_EINVAL;
     switch (knob) {
         case WINATTN_TUNE_FORCE_KERNEL:
-            if (value > 5) return WINATTN_EINVAL;
+            if (value > 6) return WINATTN_EINVAL;
             g_force_kernel = value;
             return WINATTN_OK;
         case WINATTN_TUNE_TILES_PER_SPLIT:

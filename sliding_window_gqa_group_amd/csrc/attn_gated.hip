@@ -1,0 +1,479 @@
+// The gated call in one launch for wide unit heads (head width in (128, 256], a multiple of 32):
+// rotation and unit norms of the queries and of the chunk's keys, the ring write, attention over
+// each row's window and the sigmoid gate (dory page, "Dory's token path": `dory_prep`,
+// `low_key`, `dory_score`, `dory_soft`, `dory_sum`, `dory_gate`).
+//
+// Prior art on that page: a preparation dispatch writes the unit heads and the ring, then score,
+// softmax, sum and gate dispatches run over the materialised scores. Here nothing is
+// materialised and nothing waits for a preparation pass:
+//  - A query set is 16 query vectors of one KV head (consecutive (row, head) pairs). The
+//    workgroup rotates and normalises them once, from the raw heads, the table row and the
+//    learned scale, into LDS, where every wave reads them as the B operand of
+//    v_mfma_f32_16x16x4f32.
+//  - The set's key positions are cut into 16-key blocks. A workgroup (4 waves, one per SIMD)
+//    takes one split of them and its waves take every fourth block; each wave loads its blocks'
+//    K and V straight from memory into registers in MFMA operand order (no LDS staging, no
+//    barrier in the loop), two blocks ahead in two register buffers: a block's loads have the
+//    products of the block before it to arrive.
+//  - Keys at positions before the chunk come from the ring, which already holds unit keys; keys
+//    of the chunk's own rows are rotated and normalised from the raw heads where they are used,
+//    so no wave waits for another's ring write. The wave that owns a chunk row's block in the
+//    row's own query set also writes that row's unit key and raw value into the ring. No reader
+//    reads those slots in this call (the ring holds more than window + rows - 1 positions).
+//  - The 4 waves of a workgroup meet in LDS; the splits of a set meet as in the decode kernel:
+//    partials stored with the device-scope cache policy and acknowledged, then a ready flag;
+//    the set's last split (dispatched after all the others) folds them, each wave a quarter of
+//    the columns, and applies 1 / sum and the gate.
+//
+// Layout on v_mfma_f32_16x16x4f32 (lane l supplies A[l%16][l/16] and B[l/16][l%16];
+// accumulator r of lane l is element (4*(l/16) + r, l%16)):
+//   scores  S^T = K . Q^T: A = K (key l%16, d = 16m + 4*(l/16) + e at step (m, e)),
+//           B = Q^T (query l%16, same d); lane l holds query l%16 against keys 4*(l/16) + r
+//   values  O^T = V^T . P^T: at step c (keys 4j + c, j = l/16) B = P^T is the lane's score r = c
+//           and A = V^T with d-row l%16 of block db = 4q + e meaning d = 64q + 4*(l%16) + e,
+//           so each lane reads V as float4s; accumulator r of block db holds
+//           d = 64q + 16*(l/16) + 4r + e.
+// Rotation pairs d and d + hd/2 sit in the same lane (hd/2 is a multiple of 16), and the sums
+// of squares of a query or key run over the lane's values and its three partner lanes
+// l ^ 16, l ^ 32, l ^ 48.
+#include "winattn_dev.h"
+#include "launch.h"
+
+namespace winattn {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGatedPolls = 1 << 18;
+constexpr float kLazyRescale = 8.0f;   // log2 units
+
+// Max / sum over the four lanes of a column: l, l ^ 16, l ^ 32, l ^ 48.
+__device__ inline float col_max(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return half_swap_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ inline float col_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return half_swap_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+__device__ inline f32x4 ldg4(const float* base, long long off) {
+    return *reinterpret_cast<const f32x4*>(base + off);
+}
+
+}  // namespace
+
+// HM = hd / 32: the head width, 32 HM (5 to 8). NW waves per workgroup, one per SIMD; each keeps
+// two blocks of K and V in flight (register buffers A and B), so that a block's loads have the
+// products of the block before it to arrive.
+template <int HM, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void attn_gated_kernel(const GatedFusedParams p) {
+    constexpr int NT = 64 * NW;
+    constexpr int QST = 256 + 4;          // LDS row of a query (padded: no bank conflicts)
+    constexpr int CPW = 256 / NW;         // output columns each wave folds at the end
+    constexpr int R = CPW / 16;           // float4s per lane of those columns
+    static_assert(NT >= 256 && CPW % 16 == 0, "workgroup shape");
+    __shared__ __align__(16) float s_q[16 * QST];         // the set's rotated unit queries
+    __shared__ __align__(16) float s_o[NW * 16 * 256];    // each wave's (query, d) accumulators
+    __shared__ float s_m[NW * 16], s_l[NW * 16];
+    __shared__ int s_done[NW];
+
+    // Block -> (split, query set), splits major: a set's last split (its gatherer) is dispatched
+    // after every other split. Blocks go to the 8 XCDs round-robin; sets are dealt in contiguous
+    // eighths of (KV head, set) order, so an XCD's sets share few KV heads (their K/V stay in its
+    // L2) and every split of a set runs on one XCD.
+    const int nqs_tot = p.nk * p.nqs;
+    const int bid = (int)blockIdx.x;
+    const int split = bid / nqs_tot;
+    const int rr = bid % nqs_tot;
+    const int qsg = nqs_tot % 8 == 0 ? (rr % 8) * (nqs_tot / 8) + rr / 8 : rr;
+    const int kh = qsg / p.nqs, qs = qsg % p.nqs;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lr = lane >> 4;
+    constexpr int hd = 32 * HM, half = 16 * HM;
+    const int nqv = p.rows * p.hpg;              // query vectors of a KV head
+    const int v0 = qs * 16;
+
+    // This lane's query vector (column li of the set; padding repeats the last one) and window.
+    const bool qvalid = v0 + li < nqv;
+    const int vq = qvalid ? v0 + li : nqv - 1;
+    const int qrow = vq / p.hpg, qhead = kh * p.hpg + vq % p.hpg;
+    const int qpos = p.pos0 + qrow;
+    const int qlo = max(0, qpos + 1 - p.window);
+    // The set's key positions [plo, phi] in 16-key blocks; this split's blocks [b0, b1), of which
+    // the wave takes b0 + wave, b0 + wave + NW, ...
+    const int r_first = v0 / p.hpg, r_last = min(v0 + 15, nqv - 1) / p.hpg;
+    const int plo = max(0, p.pos0 + r_first + 1 - p.window), phi = p.pos0 + r_last;
+    const int nb = (phi - plo + 16) / 16;
+    const int b0 = (int)((long long)nb * split / p.nsplit);
+    const int b1 = (int)((long long)nb * (split + 1) / p.nsplit);
+
+    // column offset of this lane's float4 for step m (d = 16m + 4 lr)
+    auto dcol = [&](int m) { return 16 * m + 4 * lr; };
+
+    // ---- key block loads (block kb: positions plo + 16 kb + 0..15; past phi: position phi).
+    // Ring position pos: slot pos mod cap; chunk row c = pos - pos0: the raw heads (rotated and
+    // normalised after the load).
+    const long long ring_row = (long long)p.nk * hd;
+    auto k_src = [&](int pos) -> const float* {
+        return pos < p.pos0 ? p.ring_k + (long long)(pos % p.cap) * ring_row + (long long)kh * hd
+                            : p.yk + ((long long)(pos - p.pos0) * p.nk + kh) * hd;
+    };
+    auto v_src = [&](int pos) -> const float* {
+        return pos < p.pos0 ? p.ring_v + (long long)(pos % p.cap) * ring_row + (long long)kh * hd
+                            : p.yv + ((long long)(pos - p.pos0) * p.nk + kh) * hd;
+    };
+    auto load_k = [&](f32x4 (&kf)[16], int kb) {
+        const float* src = k_src(min(plo + 16 * kb + li, phi));
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const bool in = dcol(m) < hd;
+            kf[m] = in ? ldg4(src, dcol(m)) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    auto load_v = [&](f32x4 (&vf)[16], int kb) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float* src = v_src(min(plo + 16 * kb + 4 * lr + c, phi));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int d = 64 * q + 4 * li;
+                vf[4 * c + q] = d < hd ? ldg4(src, d) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    };
+    // Owner of chunk row c: the set holding the row's first query vector; there the row's block
+    // belongs to exactly one (split, wave).
+    auto owns_row = [&](int pos) {
+        const int c = pos - p.pos0;
+        return pos >= p.pos0 && pos <= phi && (c * p.hpg) / 16 == qs;
+    };
+
+    // The wave's first block is requested before the queries, so both round trips overlap.
+    // Loads are never skipped: past the wave's last block they repeat that block (or the set's
+    // first block when the wave has none), so every iteration has the same loads in flight and
+    // the waits before the products name exactly the block they need.
+    const int kb0 = b0 + wave;
+    const int klast = max(0, b1 - 1);
+    // DB: two register buffers per wave (one wave per SIMD); else one (two waves per SIMD, the
+    // other wave's products cover a wave's waits)
+    constexpr bool DB = NW == 4;
+    f32x4 ka[16], va[16], kb_[DB ? 16 : 1], vb_[DB ? 16 : 1];
+    load_k(ka, min(kb0, klast));
+    load_v(va, min(kb0, klast));
+    if constexpr (DB) {
+        load_k(kb_, min(kb0 + NW, klast));
+        load_v(vb_, min(kb0 + NW, klast));
+    }
+
+    // ---- the set's queries, once per workgroup: thread t < 512 takes query t / 32 and the
+    // float4 pair (4j, 4j + hd/2), j = t % 32 < hd/8: rotation, unit norm over the query's 32
+    // threads (half a wave), learned scale, scale * log2 e; columns past hd are zero
+    for (int i = tid; i < 16 * QST / 4; i += NT)
+        reinterpret_cast<f32x4*>(s_q)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 512 / NT; ++k) {   // all loads of the queries in flight together
+        const int t = tid + k * NT;
+        const int q = t >> 5, j = t & 31;
+        const bool on = 4 * j < half;
+        const int vt = min(v0 + q, nqv - 1);
+        const int row = vt / p.hpg, head = kh * p.hpg + vt % p.hpg;
+        const int d = on ? 4 * j : 0;
+        const float* yq = p.yq + ((long long)row * p.nh + head) * hd;
+        const float* rope = p.rope + (long long)row * hd;
+        const float* qsc = p.q_scale + (long long)head * hd;
+        const f32x4 a = ldg4(yq, d), b = ldg4(yq, d + half), cs = ldg4(rope, d), sn = ldg4(rope, d + half);
+        const f32x4 sa = ldg4(qsc, d), sb = ldg4(qsc, d + half);
+        const f32x4 u = a * cs - b * sn, v = b * cs + a * sn;
+        float ss = on ? (u.x * u.x + u.y * u.y) + (u.z * u.z + u.w * u.w) +
+                            (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w)
+                      : 0.0f;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o);
+        const float f = p.scale_log2 / sqrtf(ss + p.eps);
+        if (on) {
+            *reinterpret_cast<f32x4*>(s_q + q * QST + d) = u * sa * f;
+            *reinterpret_cast<f32x4*>(s_q + q * QST + d + half) = v * sb * f;
+        }
+    }
+    __syncthreads();
+
+    f32x4 oacc[16];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) oacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float mrun = -INFINITY, lrun = 0.0f;
+    const float* qrowp = s_q + li * QST;   // B operand: query li, d = 16m + 4 lr + e
+
+    // One block from the register buffers (kf, vf), which then take block kn. An inactive step
+    // (past the wave's last block) skips the arithmetic but issues the same loads.
+    auto step = [&](f32x4 (&kf)[16], f32x4 (&vf)[16], int kb, int kn, bool active)
+                    __attribute__((always_inline)) {
+      if (active) {
+        const int base = plo + 16 * kb;
+        // a block holding chunk rows: this lane's key (column li), where it is a chunk row, is
+        // rotated and normalised in place with its table row (read here: such blocks are few)
+        if (base + 15 >= p.pos0) {
+            const int pos = min(base + li, phi);
+            const bool chunk = pos >= p.pos0;
+            const float* rope = p.rope + (long long)max(0, pos - p.pos0) * hd;
+            float ss = 0.0f;
+#pragma unroll
+            for (int m = 0; m < HM; ++m) {
+                const f32x4 cs = ldg4(rope, dcol(m)), sn = ldg4(rope, dcol(m + HM));
+                const f32x4 a = kf[m], b = kf[m + HM];
+                const f32x4 u = a * cs - b * sn, v = b * cs + a * sn;
+                kf[m] = chunk ? u : a;
+                kf[m + HM] = chunk ? v : b;
+                ss += (u.x * u.x + u.y * u.y) + (u.z * u.z + u.w * u.w);
+                ss += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+            }
+            const float inv = chunk ? 1.0f / sqrtf(col_sum(ss) + p.eps) : 1.0f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) kf[m] *= inv;
+            if (owns_row(base + li)) {
+                float* dst = p.ring_k + (long long)((base + li) % p.cap) * ring_row + (long long)kh * hd;
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                    if (dcol(m) < hd) *reinterpret_cast<f32x4*>(dst + dcol(m)) = kf[m];
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int vpos = base + 4 * lr + c;
+                if (owns_row(vpos)) {
+                    float* dst = p.ring_v + (long long)(vpos % p.cap) * ring_row + (long long)kh * hd;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (64 * q + 4 * li < hd) *reinterpret_cast<f32x4*>(dst + 64 * q + 4 * li) = vf[4 * c + q];
+                }
+            }
+        }
+
+        // scores: four independent accumulation chains (one per float4 component). The queries
+        // are read from LDS for every block: the empty asm keeps the compiler from hoisting
+        // those reads out of the loop into 64 more live registers.
+        asm volatile("" : : : "memory");
+        f32x4 s4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s4[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const f32x4 q4 = *reinterpret_cast<const f32x4*>(qrowp + dcol(m));
+            s4[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[m].x, q4.x, s4[0], 0, 0, 0);
+            s4[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[m].y, q4.y, s4[1], 0, 0, 0);
+            s4[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[m].z, q4.z, s4[2], 0, 0, 0);
+            s4[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[m].w, q4.w, s4[3], 0, 0, 0);
+        }
+        f32x4 s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        load_k(kf, kn);   // K registers are free: a later block's keys
+
+        // visibility (the query's window, inside the set's range) and the online softmax
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int pos = base + 4 * lr + r;
+            const bool vis = pos >= qlo && pos <= qpos && pos <= phi;
+            s[r] = vis ? s[r] : -INFINITY;
+            tmax = fmaxf(tmax, s[r]);
+        }
+        // The exponentials are taken against a reference max mrun that moves only when a score
+        // exceeds it by more than kLazyRescale (a factor 2^8 at most on any weight): the
+        // accumulators are then rescaled rarely after the first block. (m, l, O) stay
+        // consistent with mrun, which is what the merges take.
+        tmax = col_max(tmax);
+        const bool grow = tmax > mrun + kLazyRescale;
+        if (__any(grow)) {
+            const float m_new = grow ? tmax : mrun;
+            const float corr = __builtin_amdgcn_exp2f(mrun - safe_max(m_new));
+            lrun *= corr;
+#pragma unroll
+            for (int b = 0; b < 16; ++b) oacc[b] *= corr;
+            mrun = m_new;
+        }
+        const float mu = safe_max(mrun);
+        float psum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s[r] = __builtin_amdgcn_exp2f(s[r] - mu);
+            psum += s[r];
+        }
+        lrun += col_sum(psum);
+
+        // values
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 v = vf[4 * c + q];
+                oacc[4 * q + 0] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.x, s[c], oacc[4 * q + 0], 0, 0, 0);
+                oacc[4 * q + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.y, s[c], oacc[4 * q + 1], 0, 0, 0);
+                oacc[4 * q + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.z, s[c], oacc[4 * q + 2], 0, 0, 0);
+                oacc[4 * q + 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.w, s[c], oacc[4 * q + 3], 0, 0, 0);
+            }
+        load_v(vf, kn);   // V registers are free
+      } else {
+        load_k(kf, kn);
+        load_v(vf, kn);
+      }
+    };
+    if constexpr (DB) {
+        for (int kb = kb0; kb < b1; kb += 2 * NW) {
+            step(ka, va, kb, min(kb + 2 * NW, klast), true);
+            step(kb_, vb_, kb + NW, min(kb + 3 * NW, klast), kb + NW < b1);
+        }
+    } else {
+        for (int kb = kb0; kb < b1; kb += NW) step(ka, va, kb, min(kb + NW, klast), true);
+    }
+
+    // ---- the waves of the workgroup meet: each publishes (m, l, O) in LDS, then wave w folds
+    // output columns [CPW w, CPW (w + 1)) of the 16 queries over the NW waves
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int d = 64 * q + 16 * lr + 4 * r;
+            *reinterpret_cast<f32x4*>(s_o + (wave * 16 + li) * 256 + d) =
+                f32x4{oacc[4 * q + 0][r], oacc[4 * q + 1][r], oacc[4 * q + 2][r], oacc[4 * q + 3][r]};
+        }
+    if (lr == 0) {
+        s_m[wave * 16 + li] = mrun;
+        s_l[wave * 16 + li] = lrun;
+    }
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * 16 + li]);
+    float L = 0.0f;
+    f32x4 O[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) O[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // this lane: query li, columns d = CPW wave + 4 R lr + 4 r
+    const int dl = CPW * wave + 4 * R * lr;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const float f = __builtin_amdgcn_exp2f(s_m[w * 16 + li] - safe_max(M));
+        L += s_l[w * 16 + li] * f;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            O[r] += *reinterpret_cast<const f32x4*>(s_o + (w * 16 + li) * 256 + dl + 4 * r) * f;
+    }
+
+    // the gate of this lane's output columns, requested before any wait for partials
+    f32x4 gv[R], gsv[R];
+    {
+        const float* g = p.gate + (long long)qrow * p.nh * hd + (long long)qhead * hd;
+        const float* gs = p.gate_scale + (long long)qhead * hd;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int d = dl + 4 * r;
+            gv[r] = ldg4(g, d < hd ? d : 0);
+            gsv[r] = ldg4(gs, d < hd ? d : 0);
+        }
+    }
+    auto finish = [&](bool bad) {
+        const float inv = 1.0f / fmaxf(L, 1e-30f);
+        float* dst = p.out + ((long long)qrow * p.nh + qhead) * hd;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int d = dl + 4 * r;
+            f32x4 o = O[r] * inv;
+            o.x = o.x / (1.0f + expf(-(gv[r].x * gsv[r].x)));
+            o.y = o.y / (1.0f + expf(-(gv[r].y * gsv[r].y)));
+            o.z = o.z / (1.0f + expf(-(gv[r].z * gsv[r].z)));
+            o.w = o.w / (1.0f + expf(-(gv[r].w * gsv[r].w)));
+            if (bad) o = f32x4{NAN, NAN, NAN, NAN};
+            if (qvalid && d < hd) *reinterpret_cast<f32x4*>(dst + d) = o;
+        }
+    };
+    if (p.nsplit == 1) {
+        finish(false);
+        return;
+    }
+
+    // ---- splits of a set: partial (M, L, O) of item (set, split), written through to the
+    // device-coherent level, acknowledged, then the split's ready flag
+    const int last = p.nsplit - 1;
+    unsigned int* flags = p.flags + (long long)qsg * p.nsplit;
+    const long long item0 = (long long)qsg * p.nsplit;
+    if (split < last) {
+        const long long it = item0 + split;
+        const __amdgpu_buffer_rsrc_t part =
+            __builtin_amdgcn_make_buffer_rsrc(p.pacc + it * 16 * 256, 0, 16 * 256 * 4, kBufferWord3);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(vu4, O[r]), part,
+                                                   (li * 256 + dl + 4 * r) * 4, 0, kCachePolicyDevice);
+        if (wave == 0 && lr == 0) {
+            store_dev(p.pm + it * 16 + li, M);
+            store_dev(p.pl + it * 16 + li, L);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(flags + split, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+
+    // ---- the gatherer: each wave polls the set's flags and folds its columns
+    const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc(flags, 0, last * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t racc =
+        __builtin_amdgcn_make_buffer_rsrc(p.pacc + item0 * 16 * 256, 0, last * 16 * 256 * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(p.pm + item0 * 16, 0, last * 16 * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(p.pl + item0 * 16, 0, last * 16 * 4, kBufferWord3);
+    unsigned long long pend = last >= 64 ? ~0ull : ((1ull << last) - 1ull);
+    int polls = 0;
+    while (pend != 0ull && polls < kGatedPolls) {
+        ++polls;
+        const unsigned f = __builtin_amdgcn_raw_buffer_load_b32(rf, min(lane, last - 1) * 4, 0, kCachePolicyDevice);
+        unsigned long long ready = __builtin_amdgcn_ballot_w64(f != 0u && lane < last) & pend;
+        if (ready == 0ull) {
+            __builtin_amdgcn_s_sleep(2);
+            continue;
+        }
+        pend &= ~ready;
+        while (ready != 0ull) {   // wave-uniform
+            const int sp = __builtin_ctzll(ready);
+            ready &= ready - 1ull;
+            const int at = sp * 16 + li;
+            const float m1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, at * 4, 0, kCachePolicyDevice));
+            const float l1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, at * 4, 0, kCachePolicyDevice));
+            f32x4 a[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                a[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     racc, (at * 256 + dl + 4 * r) * 4, 0, kCachePolicyDevice));
+            const float mn = fmaxf(M, m1), mu = safe_max(mn);
+            const float f0 = __builtin_amdgcn_exp2f(M - mu), f1 = __builtin_amdgcn_exp2f(m1 - mu);
+            L = L * f0 + l1 * f1;
+#pragma unroll
+            for (int r = 0; r < R; ++r) O[r] = O[r] * f0 + a[r] * f1;
+            M = mn;
+        }
+    }
+    if (lane == 0) s_done[wave] = pend == 0ull ? 1 : 0;
+    __syncthreads();   // every wave has left its poll loop
+    bool bad = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) bad |= s_done[w] == 0;
+    finish(bad);
+    if (!bad && tid < last) __hip_atomic_store(flags + tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kGatedWaves = 4;
+
+hipError_t launch_gated_fused(const GatedFusedParams& p, hipStream_t stream) {
+    const long long blocks = (long long)p.nk * p.nqs * p.nsplit;
+    if (blocks < 1 || blocks > 0x7fffffffLL || p.nsplit < 1 || p.nsplit > 64) return hipErrorInvalidValue;
+    constexpr int NW = kGatedWaves;
+    const dim3 grid((unsigned)blocks), block(64 * NW);
+    switch (p.hd) {
+        case 160: hipLaunchKernelGGL((attn_gated_kernel<5, NW>), grid, block, 0, stream, p); break;
+        case 192: hipLaunchKernelGGL((attn_gated_kernel<6, NW>), grid, block, 0, stream, p); break;
+        case 224: hipLaunchKernelGGL((attn_gated_kernel<7, NW>), grid, block, 0, stream, p); break;
+        case 256: hipLaunchKernelGGL((attn_gated_kernel<8, NW>), grid, block, 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace winattn

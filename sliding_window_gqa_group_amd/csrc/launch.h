@@ -60,6 +60,29 @@ struct PrepParams {
 };
 hipError_t launch_gated_prep(const PrepParams& p, hipStream_t stream);
 
+// The gated call in one launch (attn_gated.hip): head width in (128, 256], a multiple of 32.
+struct GatedFusedParams {
+    const float* yq;          // [rows][nh][hd] raw query heads
+    const float* yk;          // [rows][nk][hd] raw key heads
+    const float* yv;          // [rows][nk][hd]
+    const float* rope;        // [rows][hd] cos | sin
+    const float* q_scale;     // [nh][hd]
+    const float* gate;        // [rows][nh * hd]
+    const float* gate_scale;  // [nh * hd]
+    float* ring_k;            // [cap][nk][hd]
+    float* ring_v;
+    float* out;               // [rows][nh][hd]
+    float* pacc;              // split partials [set][split][16][256] (nsplit > 1)
+    float* pm;                // [set][split][16]
+    float* pl;
+    unsigned int* flags;      // [set][split], zero between calls
+    int rows, pos0, cap, window, nh, nk, hd, hpg;
+    int nqs;                  // query sets (16 query vectors) per KV head
+    int nsplit;               // workgroups per query set, at most 64
+    float scale_log2, eps;
+};
+hipError_t launch_gated_fused(const GatedFusedParams& p, hipStream_t stream);
+
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
 
 struct CommitParams {

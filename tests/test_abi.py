@@ -269,7 +269,29 @@ def test_tuning_knobs_change_the_plan(lib):
         B.tuning_set(B.TUNE_FORCE_KERNEL, 0)
         B.tuning_set(B.TUNE_TILES_PER_SPLIT, 0)
     with pytest.raises(B.WinattnError):
-        B.tuning_set(B.TUNE_FORCE_KERNEL, 6)
+        B.tuning_set(B.TUNE_FORCE_KERNEL, 7)
+
+
+def test_gated_single_launch_workspace(lib):
+    # the gated call in one launch (kernel 6): 16 query vectors per set, 4 splits per set for
+    # the 64-row, 16/4-head, width-256 workload (256 workgroups): counters + partials
+    items = 4 * 16 * 4
+    need = B.gated_workspace_bytes(64, 16, 4, 256, 1024)
+    assert need == 65536 + items * 16 * 256 * 4 + 2 * items * 16 * 4
+    try:
+        B.tuning_set(B.TUNE_TARGET_BLOCKS, 64)   # one workgroup per set: no partials at all
+        assert B.gated_workspace_bytes(64, 16, 4, 256, 1024) == 0
+        B.tuning_set(B.TUNE_TARGET_BLOCKS, 0)
+        B.tuning_set(B.TUNE_FORCE_KERNEL, 6)     # fewer than 16 query vectors per KV head, forced
+        assert B.gated_workspace_bytes(2, 8, 2, 256, 64) == 0
+        B.tuning_set(B.TUNE_FORCE_KERNEL, 4)     # the three-launch path keeps its prepared queries
+        assert B.gated_workspace_bytes(64, 16, 4, 256, 1024) >= 64 * 16 * 256 * 4
+    finally:
+        B.tuning_set(B.TUNE_FORCE_KERNEL, 0)
+        B.tuning_set(B.TUNE_TARGET_BLOCKS, 0)
+    # widths the single launch does not take keep the three-launch plan
+    assert B.gated_workspace_bytes(64, 16, 4, 128, 1024) >= 64 * 16 * 128 * 4
+    assert B.gated_workspace_bytes(64, 16, 4, 200, 1024) >= 64 * 16 * 200 * 4
 
 
 def test_check_meta(lib):

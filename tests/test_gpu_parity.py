@@ -320,20 +320,48 @@ GATED_SWEEP = [
     (20, 100, 300, 256, 8, 2, 64),
     (64, 20000, 8192, 1024, 16, 4, 256),
     (40, 10, 64, 25, 6, 3, 128),
+    # widths the single launch takes (160 to 256, multiples of 32)
+    (17, 3, 64, 40, 6, 2, 192),          # windows clipped at position 0, sets across rows
+    (40, 100, 200, 16, 8, 8, 256),       # more rows than the window, one head per KV head
+    (33, 5000, 2048, 512, 12, 3, 160),   # a partial last set
+    (16, 0, 64, 8, 4, 4, 224),           # one set per KV head
+    (4, 50, 128, 64, 8, 2, 256),
+    (2, 50, 128, 64, 8, 2, 256),         # fewer than 16 query vectors per KV head
 ]
 
+# plans of the gated call: automatic; the single launch with one, the automatic and many
+# workgroups per set; the three-launch path (prepared queries, 16x16 matrix-core kernel)
+GATED_VARIANTS = {
+    "auto": {},
+    "single_launch_one_split": {B.TUNE_FORCE_KERNEL: 6, B.TUNE_TARGET_BLOCKS: 1},
+    "single_launch": {B.TUNE_FORCE_KERNEL: 6},
+    "single_launch_many_splits": {B.TUNE_FORCE_KERNEL: 6, B.TUNE_TARGET_BLOCKS: 4096},
+    "three_launches": {B.TUNE_FORCE_KERNEL: 4},
+}
 
+
+@pytest.mark.parametrize("variant", list(GATED_VARIANTS))
 @pytest.mark.parametrize("shape", GATED_SWEEP, ids=[f"r{s[0]}p{s[1]}c{s[2]}w{s[3]}h{s[4]}k{s[5]}d{s[6]}" for s in GATED_SWEEP])
-def test_gated_sweep(shape):
+def test_gated_sweep(shape, variant):
     rows, pos0, cap, window, nh, nk, hd = shape
-    _case(f"gated sweep {shape}")
-    for scale in (None, float(np.sqrt(hd))):   # 1/sqrt(hd) and a sharp nGPT-like softmax
-        inp = gen.make_gated(rows, pos0, cap, window, nh, nk, hd, seed=rows + pos0, scale=scale)
-        z, rk, rv = gpu_gated(inp)
-        oz, ork, orv = oracle.window_gated(inp)
-        assert_close(z, oz, f"gated {shape} scale={scale}")
-        assert_close(rk, ork, "ring k")
-        np.testing.assert_array_equal(rv, orv)
+    _case(f"gated sweep {shape} {variant}")
+    knobs = GATED_VARIANTS[variant]
+    try:
+        for knob, val in knobs.items():
+            B.tuning_set(knob, val)
+        for scale in (None, float(np.sqrt(hd))):   # 1/sqrt(hd) and a sharp nGPT-like softmax
+            inp = gen.make_gated(rows, pos0, cap, window, nh, nk, hd, seed=rows + pos0, scale=scale)
+            z, rk, rv = gpu_gated(inp)
+            oz, ork, orv = oracle.window_gated(inp)
+            assert_close(z, oz, f"gated {shape} {variant} scale={scale}")
+            assert_close(rk, ork, "ring k")
+            np.testing.assert_array_equal(rv, orv)
+            # a second call on the same inputs: the ready flags were left at zero
+            z2, _, _ = gpu_gated(inp)
+            assert_close(z2, oz, f"gated {shape} {variant} scale={scale}, repeated")
+    finally:
+        for knob in knobs:
+            B.tuning_set(knob, 0)
 
 
 # ── strict: nothing outside the window is read, nothing outside out is written ───────────────
@@ -381,9 +409,10 @@ def test_poisoned_slots_and_canaries(rows, hpg):
     assert np.all(ws.buf[need:].cpu().numpy() == 0xAB), "wrote outside the workspace"
 
 
-def test_gated_untouched_slots():
-    _case("gated untouched slots")
-    inp = gen.make_gated(6, 40, 64, 16, 4, 2, 64, seed=5)
+@pytest.mark.parametrize("nh,hd", [(4, 64), (8, 256)])   # three launches; one launch
+def test_gated_untouched_slots(nh, hd):
+    _case(f"gated untouched slots nh={nh} hd={hd}")
+    inp = gen.make_gated(6, 40, 64, 16, nh, 2, hd, seed=5)
     read_or_written = set()
     for r in range(inp.rows):
         pos = inp.pos0 + r

@@ -150,27 +150,41 @@ Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_f
     const long long keys_max = (long long)wcap + span - 1;
     const int max_tiles = cdiv(keys_max, pl.tk);
     const long long blocks = (long long)pl.nqblocks * ng;
-    // Workgroups the split count aims for: the register kernel runs two per CU, the LDS
-    // vector kernel one, the 32x32 matrix-core kernel two per CU in three rounds (its blocks'
-    // key ranges differ along a causal chunk; finer splits balance them: the 512-row prefill
-    // chunk measured 284 us at 12 splits against 316 us at 8), the 16x16 one a single round.
-    const int target = g_target_blocks > 0
-                           ? g_target_blocks
-                           : (pl.kind == kKindMfma ? 1536
-                                                   : (pl.kind == kKindDec ? 512 : 256));
-    int s_target = cdiv(target, blocks);
-    if (s_target < 1) s_target = 1;
-    if (s_target > max_tiles) s_target = max_tiles;
-    int tps = cdiv(max_tiles, s_target);
     // A matrix-core split should amortise its partial (qb x d floats) over a few tiles.
     const int tps_min = pl.kind == kKindMfma ? 4 : (pl.kind == kKindMfma16 ? 2 : 1);
-    if (tps < tps_min) tps = tps_min;
     // Long windows: bound a split's work so the blocks of unequal groups balance.
     const int tps_cap = pl.mfma ? 128 : 64;
-    if (tps > tps_cap) tps = tps_cap;
     // The merge is one CU reading every split's partial of a block: keep that under 2 MiB.
     const long long nsplit_cap = std::max<long long>(1, (2LL << 20) / ((long long)pl.qb * pl.dpad * 4));
-    if (cdiv(max_tiles, tps) > nsplit_cap) tps = cdiv(max_tiles, nsplit_cap);
+    int tps;
+    if (pl.mfma) {
+        // Matrix-core kernels divide each block's real tiles evenly among its splits, so the
+        // split count sets the work per workgroup, and the launch is as long as the busiest CU.
+        // The splits fill the GPU's 256 CUs once: with one workgroup per CU when there are at
+        // most 16 blocks (their workgroups stay short, and a second one per CU would mostly add
+        // fixed costs and partials: a 64-row chunk of the decode heads measured 69 us at 13
+        // splits against 76 us at 26), else two per CU for the 32x32 kernel (its waves then
+        // share each SIMD, which keeps the matrix units busier: the 512-row prefill chunk
+        // measured 269 us at 4 splits against 277 us at 8 and 284 us at 12); the 16x16 kernel
+        // holds one per CU. Never more than 256 splits, nor fewer than long windows need.
+        const long long per_cu = (pl.kind == kKindMfma && blocks > 16) ? 2 : 1;
+        const long long slots = g_target_blocks > 0 ? g_target_blocks : 256 * per_cu;
+        const long long s_hi = std::max<long long>(1, std::min<long long>(
+                                   std::min<long long>(max_tiles / tps_min, nsplit_cap), 256));
+        const long long s_lo = std::min<long long>(s_hi, cdiv(max_tiles, tps_cap));
+        const long long s_pick = std::max(s_lo, std::min(s_hi, std::max<long long>(1, slots / blocks)));
+        tps = cdiv(max_tiles, s_pick);
+    } else {
+        // Vector kernels: the register kernel runs two workgroups per CU, the LDS one one.
+        const int target = g_target_blocks > 0 ? g_target_blocks : (pl.kind == kKindDec ? 512 : 256);
+        int s_target = cdiv(target, blocks);
+        if (s_target < 1) s_target = 1;
+        if (s_target > max_tiles) s_target = max_tiles;
+        tps = cdiv(max_tiles, s_target);
+        if (tps < tps_min) tps = tps_min;
+        if (tps > tps_cap) tps = tps_cap;
+        if (cdiv(max_tiles, tps) > nsplit_cap) tps = cdiv(max_tiles, nsplit_cap);
+    }
     if (g_tiles_per_split > 0) tps = g_tiles_per_split;
     if (blocks > kMaxTickets) tps = max_tiles;
     pl.tps = tps;

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
     const int hi_first = gw.hi0 + r_first;
     const int xlo = window_lo(hi_first, gw.wcap);
     const int xhi = gw.hi0 + r_last;
-    const Tiles tr = tile_range<TK>(p.ns, xlo, xhi, p.tps, split);
+    const Tiles tr = tile_range<TK>(p.ns, xlo, xhi, p.nsplit_grid, split);
     const int nsplit = tr.nsplit, nst = tr.nst;
     if (split >= nsplit) {
         mark_split_empty<QB>(p, g * p.nqblocks + qb, split);

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kThreads * m16_key_split<D>(), 1) void attn_mfma16_
     const int r_first = q0 / p.hpg, r_last = (q0 + nq - 1) / p.hpg;
     const int xlo = window_lo(gw.hi0 + r_first, gw.wcap);
     const int xhi = gw.hi0 + r_last;
-    const Tiles tr = tile_range<TK>(p.ns, xlo, xhi, p.tps, split);
+    const Tiles tr = tile_range<TK>(p.ns, xlo, xhi, p.nsplit_grid, split);
     const int nsplit = tr.nsplit, nst = tr.nst;
     if (split >= nsplit) {
         mark_split_empty<QB>(p, g * p.nqblocks + qb, split);

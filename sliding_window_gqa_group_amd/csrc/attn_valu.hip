@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void attn_valu_kernel(const AttnParams p)
     const int hi_first = gw.hi0 + r_first;
     const int xlo = window_lo(hi_first, gw.wcap);
     const int xhi = gw.hi0 + r_last;
-    const Tiles tr = tile_range<TK>(p.ns, xlo, xhi, p.tps, split);
+    const Tiles tr = tile_range<TK>(p.ns, xlo, xhi, p.nsplit_grid, split);
     const int nsplit = tr.nsplit, nst = tr.nst;
     if (split >= nsplit) {
         mark_split_empty<NQ>(p, g * p.nqblocks + qb, split);

@@ -102,22 +102,29 @@ __device__ inline int window_lo(int hi, int wcap) { return hi - (wcap < hi ? wca
 
 // Key tiles of a query block: first ceil(ns / TK) sink tiles (sink index t*TK + k), then stream
 // tiles covering the block's stream range [xlo, xhi) (entry xlo + (t - nst)*TK + k). Sink tiles
-// belong to split 0; the stream tiles are cut into splits of `tps` tiles.
+// belong to split 0. The block's stream tiles (known only here: they depend on the ring's
+// metadata) are divided evenly among the nsplit_grid splits the launch reserves per block, so
+// every split gets the same work whatever the window's fill; with fewer tiles than splits the
+// leading splits take one tile each and the rest are empty. The plan sizes nsplit_grid so that
+// no split exceeds its tiles-per-split bound.
 struct Tiles {
     int nst;       // sink tiles
     int nstream;   // stream tiles
-    int nsplit;    // splits that have work
+    int nsplit;    // splits that have work (the leading ones)
     int t_begin, t_end;
 };
 
 template <int TK>
-__device__ inline Tiles tile_range(int ns, int xlo, int xhi, int tps, int split) {
+__device__ inline Tiles tile_range(int ns, int xlo, int xhi, int nsplit_grid, int split) {
     Tiles r;
     r.nst = (ns + TK - 1) / TK;
     r.nstream = (xhi - xlo + TK - 1) / TK;
-    r.nsplit = (r.nstream + tps - 1) / tps;
-    r.t_begin = split == 0 ? 0 : r.nst + split * tps;
-    r.t_end = r.nst + min(r.nstream, (split + 1) * tps);
+    r.nsplit = min(nsplit_grid, r.nstream);
+    const int div = max(r.nsplit, 1);   // no stream tiles: no split has work
+    const int lo = (int)((long long)split * r.nstream / div);
+    const int hi = (int)((long long)(split + 1) * r.nstream / div);
+    r.t_begin = split == 0 ? 0 : r.nst + lo;
+    r.t_end = r.nst + hi;
     return r;
 }
 

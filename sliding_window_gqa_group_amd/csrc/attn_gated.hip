@@ -45,7 +45,6 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGatedPolls = 1 << 18;
-constexpr float kLazyRescale = 8.0f;   // log2 units
 
 // Max / sum over the four lanes of a column: l, l ^ 16, l ^ 32, l ^ 48.
 __device__ inline float col_max(float v) {

@@ -173,26 +173,29 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
             tmax = fmaxf(tmax, sacc[r]);
         }
         tmax = half_swap_max(tmax);
-        const float m_new = fmaxf(mrun, tmax);
-        const float mu = safe_max(m_new);
-        const float corr = __builtin_amdgcn_exp2f(mrun - mu);
+        // The exponentials are taken against a reference max that moves only when a score
+        // exceeds it by more than kLazyRescale (so no weight exceeds 2^8): the accumulators are
+        // rescaled rarely after the first tile. (m, l, O) stay consistent with it, which is
+        // all the merges need.
+        const bool grow = tmax > mrun + kLazyRescale;
+        if (__any(grow)) {
+            const float m_new = grow ? tmax : mrun;
+            const float corr = __builtin_amdgcn_exp2f(mrun - safe_max(m_new));
+            lrun *= corr;
+#pragma unroll
+            for (int b = 0; b < NDB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[b][r] *= corr;
+            mrun = m_new;
+        }
+        const float mu = safe_max(mrun);
         float psum = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             sacc[r] = __builtin_amdgcn_exp2f(sacc[r] - mu);
             psum += sacc[r];
         }
-        psum = half_swap_sum(psum);
-        lrun = lrun * corr + psum;
-        // Rescale the accumulators only when some lane's running max moved (after the first
-        // few tiles of a long window it rarely does).
-        if (__any(m_new != mrun)) {
-#pragma unroll
-            for (int b = 0; b < NDB; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[b][r] *= corr;
-        }
-        mrun = m_new;
+        lrun += half_swap_sum(psum);
 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {

@@ -276,9 +276,17 @@ __global__ __launch_bounds__(kThreads * m16_key_split<D>(), 1) void attn_mfma16_
                 tmax = fmaxf(tmax, sacc[kw][r]);
             }
         tmax = half_swap_max(quarter_swap_max(tmax));
-        const float m_new = fmaxf(mrun, tmax);
-        const float mu = safe_max(m_new);
-        const float corr = __builtin_amdgcn_exp2f(mrun - mu);
+        // lazy rescaling against a reference max (kLazyRescale)
+        const bool grow = tmax > mrun + kLazyRescale;
+        if (__any(grow)) {
+            const float m_new = grow ? tmax : mrun;
+            const float corr = __builtin_amdgcn_exp2f(mrun - safe_max(m_new));
+            lrun *= corr;
+#pragma unroll
+            for (int b = 0; b < NDB; ++b) oacc[b] *= corr;
+            mrun = m_new;
+        }
+        const float mu = safe_max(mrun);
         float psum = 0.0f;
 #pragma unroll
         for (int kw = 0; kw < NKBW; ++kw)
@@ -287,14 +295,7 @@ __global__ __launch_bounds__(kThreads * m16_key_split<D>(), 1) void attn_mfma16_
                 sacc[kw][r] = __builtin_amdgcn_exp2f(sacc[kw][r] - mu);
                 psum += sacc[kw][r];
             }
-        psum = half_swap_sum(quarter_swap_sum(psum));
-        lrun = lrun * corr + psum;
-        // Rescale the accumulators only when some lane's running max moved.
-        if (__any(m_new != mrun)) {
-#pragma unroll
-            for (int b = 0; b < NDB; ++b) oacc[b] *= corr;
-        }
-        mrun = m_new;
+        lrun += half_swap_sum(quarter_swap_sum(psum));
 
 #pragma unroll
         for (int st = 0; st < NST; ++st) {

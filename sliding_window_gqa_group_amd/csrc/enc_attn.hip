@@ -174,24 +174,26 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void enc_attn_kernel(co
             tmax = fmaxf(tmax, sacc[r]);
         }
         tmax = half_swap_max(tmax);
-        const float m_new = fmaxf(mrun, tmax);
-        const float mu = safe_max(m_new);
-        const float corr = __builtin_amdgcn_exp2f(mrun - mu);
+        // lazy rescaling against a reference max (kLazyRescale)
+        const bool grow = tmax > mrun + kLazyRescale;
+        if (__any(grow)) {
+            const float m_new = grow ? tmax : mrun;
+            const float corr = __builtin_amdgcn_exp2f(mrun - safe_max(m_new));
+            lrun *= corr;
+#pragma unroll
+            for (int b = 0; b < NDB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[b][r] *= corr;
+            mrun = m_new;
+        }
+        const float mu = safe_max(mrun);
         float psum = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             sacc[r] = __builtin_amdgcn_exp2f(sacc[r] - mu);
             psum += sacc[r];
         }
-        psum = half_swap_sum(psum);
-        lrun = lrun * corr + psum;
-        if (__any(m_new != mrun)) {
-#pragma unroll
-            for (int b = 0; b < NDB; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[b][r] *= corr;
-        }
-        mrun = m_new;
+        lrun += half_swap_sum(psum);
 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {

@@ -288,6 +288,11 @@ __device__ inline float wave_sum(float v) {
 // exp2(-inf - m) = 0 instead of NaN).
 __device__ inline float safe_max(float m_new) { return m_new == -INFINITY ? 0.0f : m_new; }
 
+// Lazy rescaling of an online softmax: the running reference max moves only when a score
+// exceeds it by more than this (log2 units), so every weight exp2(s - m) stays below 2^8 and
+// the accumulators are rescaled rarely.
+constexpr float kLazyRescale = 8.0f;
+
 // Gate epilogue of the gated call (`dory_gate`): o / (1 + exp(-g * s)).
 __device__ inline float4 gate4(const AttnParams& p, int row, int gh, int e, float4 o) {
     const size_t at = (size_t)gh * p.d + e;

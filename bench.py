@@ -400,7 +400,7 @@ def bench_others(args, torch, B, gen, acct):
                     "tflops": round(flops / ms / 1e9, 3),
                     "tflops_frac_f32_peak": round(flops / ms / 1e9 / F32_PEAK_TFLOPS, 4),
                     # width 256 and 256 query vectors per KV head: the single-launch plan
-                    "kernel": "attn_gated_kernel",
+                    "kernel": "attn_gated_tiles_kernel",
                     "workspace_bytes": B.gated_workspace_bytes(g.rows, g.nh, g.nk, g.hd, g.window),
                     "cache": cache_label(n, nbytes)}
     del sets, base

@@ -142,8 +142,11 @@ int attn_window_chunk_noalloc(const float* ring_k, const float* ring_v, const ui
  * Ring slots that no row reads and no row writes are left untouched.
  * Plans: widths 160, 192, 224 and 256 with at least 16 query vectors (rows * nh / nk) per KV
  * head run in one launch (kernel 6: the rotations where the heads are loaded, the ring write by
- * the workgroup that reads the row, split partials folded by each query set's last split); its
- * workspace holds the split counters and the partials (none with a single split per set).
+ * the workgroups that read the row, split partials folded by each query block's last splits;
+ * blocks of 16 query vectors below 64 per KV head, of 64 from there on); its workspace holds the
+ * split counters and the partials (none with a single split per block). In the 64-vector form
+ * a chunk row's ring key slot may be written by several workgroups of the call, always with the
+ * same bytes.
  * Other shapes prepare the unit heads and the ring in a first launch, then run the chunk
  * kernels on the prepared queries (the workspace also holds them) and, with several splits, a
  * merge launch. Every plan writes the same results within the tolerance of f32 rounding.

@@ -226,15 +226,17 @@ Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_f
 }
 
 // Plan of the gated call in one launch (kernel 6): unit heads of width 160, 192, 224 or 256 and
-// at least one full query set (16 query vectors) per KV head. nsplit workgroups per query set
-// aim at one per CU; each of their 4 waves should keep at least one 16-key block.
+// at least one full query set (16 query vectors) per KV head. From 64 query vectors per KV head
+// on, the tile form (blocks of 64 queries, LDS-staged 32-key tiles, two waves per SIMD);
+// below, the register form (sets of 16). Splits per block aim at one workgroup per CU.
 struct GatedPlan {
-    int nqs, nsplit;
+    int qb, nqs, nsplit, gather_k;
     size_t off_pacc, off_pm, off_pl, bytes;
 };
 
 constexpr int kGatedTargetBlocks = 256;
 constexpr int kGatedMaxSplits = 64;
+constexpr int kGatedMaxGatherers = 128;   // waiting gatherers stay far below the CUs
 
 bool gated_fused_plan(int rows, int nh, int nk, int hd, int window, GatedPlan& gp) {
     if (g_force_kernel != 0 && g_force_kernel != kKindGated) return false;
@@ -242,32 +244,44 @@ bool gated_fused_plan(int rows, int nh, int nk, int hd, int window, GatedPlan& g
     const int hpg = nh / nk;
     const long long nqv = (long long)rows * hpg;
     if (nqv < 16 && g_force_kernel != kKindGated) return false;
-    const long long nqs = (nqv + 15) / 16;
-    const long long sets = nqs * nk;
-    if (sets > (1LL << 24)) return false;
-    // positions a set can span: its rows' windows, at most window + rows spanned - 1
-    const long long span = std::min<long long>(rows, 15 / hpg + 2);
+    const int qb = nqv >= 64 ? 64 : 16;
+    const long long nqs = (nqv + qb - 1) / qb;
+    const long long blocks = nqs * nk;
+    if (blocks > (1LL << 24)) return false;
+    // positions a block can span: its rows' windows, at most window + rows spanned - 1
+    const long long span = std::min<long long>(rows, (qb - 1) / hpg + 2);
     const long long nb = ((long long)window + span - 1 + 15) / 16;
     const int target = g_target_blocks > 0 ? g_target_blocks : kGatedTargetBlocks;
-    long long ns = (target + sets - 1) / sets;
-    ns = std::min<long long>(ns, std::max<long long>(1, nb / 4));
+    long long ns = (target + blocks - 1) / blocks;
+    // every wave of a split should keep at least one 16-key block (the tile form: one tile)
+    ns = std::min<long long>(ns, std::max<long long>(1, nb / (qb == 64 ? 2 : 4)));
     ns = std::max<long long>(1, std::min<long long>(ns, kGatedMaxSplits));
-    while (ns > 1 && sets * ns > kMaxTickets) --ns;
+    int gk = 1;
+    if (qb == 64) {
+        gk = 8;
+        while (gk > 1 && (gk > ns || blocks * gk > kGatedMaxGatherers)) gk /= 2;
+        while (ns > 1 && blocks * gk * ns > kMaxTickets) --ns;
+        if (gk > ns) gk = 1;
+    } else {
+        while (ns > 1 && blocks * ns > kMaxTickets) --ns;
+    }
+    gp.qb = qb;
     gp.nqs = (int)nqs;
     gp.nsplit = (int)ns;
+    gp.gather_k = gk;
     if (ns == 1) {
         gp.off_pacc = gp.off_pm = gp.off_pl = 0;
         gp.bytes = 0;
         return true;
     }
-    const size_t items = (size_t)sets * ns;
+    const size_t items = (size_t)blocks * ns;
     size_t off = kTicketBytes;
     gp.off_pacc = off;
-    off = align_up(off + items * 16 * 256 * sizeof(float), 256);
+    off = align_up(off + items * qb * 256 * sizeof(float), 256);
     gp.off_pm = off;
-    off = align_up(off + items * 16 * sizeof(float), 256);
+    off = align_up(off + items * qb * sizeof(float), 256);
     gp.off_pl = off;
-    off = align_up(off + items * 16 * sizeof(float), 256);
+    off = align_up(off + items * qb * sizeof(float), 256);
     gp.bytes = off;
     return true;
 }
@@ -851,8 +865,10 @@ int attn_window_gated(const float* yq, const float* yk, const float* yv, const f
         f.nk = nk;
         f.hd = hd;
         f.hpg = hpg;
+        f.qb = gp.qb;
         f.nqs = gp.nqs;
         f.nsplit = gp.nsplit;
+        f.gather_k = gp.gather_k;
         f.scale_log2 = scale * kLog2e;
         f.eps = eps;
         return launch_gated_fused(f, st) == hipSuccess ? WINATTN_OK : WINATTN_ELAUNCH;

@@ -5,7 +5,9 @@
 //
 // Prior art on that page: a preparation dispatch writes the unit heads and the ring, then score,
 // softmax, sum and gate dispatches run over the materialised scores. Here nothing is
-// materialised and nothing waits for a preparation pass:
+// materialised and nothing waits for a separate preparation pass. Two forms share the plan:
+//
+// Register form (16 to 63 query vectors per KV head), attn_gated_kernel:
 //  - A query set is 16 query vectors of one KV head (consecutive (row, head) pairs). The
 //    workgroup rotates and normalises them once, from the raw heads, the table row and the
 //    learned scale, into LDS, where every wave reads them as the B operand of
@@ -19,11 +21,15 @@
 //    of the chunk's own rows are rotated and normalised from the raw heads where they are used,
 //    so no wave waits for another's ring write. The wave that owns a chunk row's block in the
 //    row's own query set also writes that row's unit key and raw value into the ring. No reader
-//    reads those slots in this call (the ring holds more than window + rows - 1 positions).
+//    outside this call's own writers reads those slots (the ring holds more than
+//    window + rows - 1 positions).
 //  - The 4 waves of a workgroup meet in LDS; the splits of a set meet as in the decode kernel:
 //    partials stored with the device-scope cache policy and acknowledged, then a ready flag;
 //    the set's last split (dispatched after all the others) folds them, each wave a quarter of
 //    the columns, and applies 1 / sum and the gate.
+//
+// Tile form (64 or more query vectors per KV head), attn_gated_tiles_kernel: blocks of 64
+// queries, 32-key tiles staged in LDS, two waves per SIMD; described at the kernel.
 //
 // Layout on v_mfma_f32_16x16x4f32 (lane l supplies A[l%16][l/16] and B[l/16][l%16];
 // accumulator r of lane l is element (4*(l/16) + r, l%16)):
@@ -36,6 +42,8 @@
 // Rotation pairs d and d + hd/2 sit in the same lane (hd/2 is a multiple of 16), and the sums
 // of squares of a query or key run over the lane's values and its three partner lanes
 // l ^ 16, l ^ 32, l ^ 48.
+#include <type_traits>
+
 #include "winattn_dev.h"
 #include "launch.h"
 
@@ -58,6 +66,10 @@ __device__ inline float col_sum(float v) {
 
 __device__ inline f32x4 ldg4(const float* base, long long off) {
     return *reinterpret_cast<const f32x4*>(base + off);
+}
+
+__device__ inline f32x4 shfl4(f32x4 v, int src) {
+    return f32x4{__shfl(v.x, src), __shfl(v.y, src), __shfl(v.z, src), __shfl(v.w, src)};
 }
 
 }  // namespace
@@ -460,9 +472,516 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_gated_kernel(const GatedFused
 
 constexpr int kGatedWaves = 4;
 
+// ---- Tile form, for 64 or more query vectors per KV head. The same work in the layout of the
+// 16x16 matrix-core kernel of the three-launch path: a block is 64 query vectors (four sets of
+// 16) of one KV head; its positions are cut into 16-key blocks, shared among the block's
+// splits; each split streams 32-key tiles into double-buffered LDS with direct global-to-LDS
+// loads only, and runs 8 waves, two per SIMD: waves w and w + 4 own the same 16 queries and
+// take the two 16-key halves of each tile, so that one wave's softmax overlaps the other's
+// products.
+//  - Prologue: the workgroup makes the block's 64 unit queries once (each wave 8 of them) and
+//    passes them through LDS; tile 0 is in flight meanwhile.
+//  - Chunk rows: a split whose range holds positions of the chunk first rotates and normalises
+//    those rows' raw keys into the ring (several blocks may write one slot, always with the same
+//    bytes; the raw value goes to the ring once, from the split that owns the row in the block
+//    of its first query vector); its tiles then load them from there like any ring row, and
+//    take chunk values straight from the raw heads. That split is counted one 16-key block
+//    more than it streams, so that its extra work does not make it the last to finish.
+//  - The two key halves of a query set fold in LDS (each wave keeps half of the columns); the
+//    splits meet as in the decode kernel: partials with device-scope stores, acknowledged, one
+//    ready flag per gatherer; the block's last gather_k splits wait for every flag, then each
+//    reads its column chunk of all partials at once, folds them in split order, applies
+//    1 / sum and the gate (read before the wait) and stores it.
+constexpr int kGTK = 32;          // keys per tile
+constexpr int kGKST = 256 + 4;    // LDS row stride (floats)
+
+template <int HM>
+__global__ __launch_bounds__(512, 1) void attn_gated_tiles_kernel(const GatedFusedParams p) {
+    constexpr int NT = 512, NW = 8, TK = kGTK, KST = kGKST, QB = 64;
+    constexpr int hd = 32 * HM, half = 16 * HM, d4 = hd / 4;
+    // Each LDS tile buffer is its own array, so that the compiler sees that reading one buffer
+    // never conflicts with the direct loads still filling the other, and leaves them in flight.
+    __shared__ __align__(16) float s_k0[TK * KST];
+    __shared__ __align__(16) float s_v0[TK * KST];
+    __shared__ __align__(16) float s_k1[TK * KST];
+    __shared__ __align__(16) float s_v1[TK * KST];
+    __shared__ int s_done[NW];
+
+    // Block -> (split, query block), splits major: every split that a gatherer waits for is
+    // dispatched before the gatherers' splits, or is itself a gatherer (and raises its flags
+    // before it gathers). Query blocks are dealt to the XCDs in contiguous eighths of
+    // (KV head, block) order, so an XCD's blocks share few KV heads.
+    const int nqb_tot = p.nk * p.nqs;
+    const int bid = (int)blockIdx.x;
+    const int split = bid / nqb_tot;
+    const int rr = bid % nqb_tot;
+    const int qbg = nqb_tot % 8 == 0 ? (rr % 8) * (nqb_tot / 8) + rr / 8 : rr;
+    const int kvh = qbg / p.nqs, qb = qbg % p.nqs;
+    const int S = p.nsplit;
+
+    // the wave index as a scalar: row indices, pointer choices and branches derived from it
+    // stay on the scalar unit
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qw = wave & 3, kh = wave >> 2;          // query set, key half of each tile
+    const int qcol = lane & 15, kr4 = lane >> 4;
+    const int nqv = p.rows * p.hpg;
+    const int v0 = qb * QB;
+
+    // This lane's query vector (column qcol of set qw; padding repeats the last) and window.
+    const int jq = 16 * qw + qcol;
+    const bool qvalid = v0 + jq < nqv;
+    const int vq = qvalid ? v0 + jq : nqv - 1;
+    const int qrow = vq / p.hpg;
+    const int qpos = p.pos0 + qrow, qlo = max(0, qpos + 1 - p.window);
+    // The block's positions [plo, phi], its 16-key blocks, this split's share [ks0, ks1)
+    const int r_first = v0 / p.hpg, r_last = min(v0 + QB - 1, nqv - 1) / p.hpg;
+    const int plo = max(0, p.pos0 + r_first + 1 - p.window), phi = p.pos0 + r_last;
+    const int nb = (phi - plo + 16) / 16;
+    // The last split also makes the chunk rows' unit keys: it is counted one 16-key block more
+    // than it streams (nb + 1 shares, larger ones first).
+    const int bs0 = min(nb, (int)(((long long)(nb + 1) * split + S - 1) / S));
+    const int bs1 = min(nb, (int)(((long long)(nb + 1) * (split + 1) + S - 1) / S));
+    const int ks0 = plo + 16 * bs0, ks1 = min(plo + 16 * bs1, phi + 1);
+    const int ntile = (bs1 - bs0 + 1) / 2;
+
+    // ---- tile t of the split (positions ks0 + 32 t + key) into LDS buffers (tkb, tvb), straight
+    // from memory: wave w loads rows w, w + 8, w + 16, w + 24; positions past phi load position phi
+    // (masked later). Keys always come from the ring: a chunk row's unit key is written there by
+    // this workgroup before its first tile (see below); values of chunk rows come from the raw
+    // heads. Nothing is waited for here, so the loads stay in flight under the current tile's
+    // products.
+    const long long ring_row = (long long)p.nk * hd;
+    const unsigned col = 4u * (unsigned)(lane < d4 ? lane : 0);
+    auto issue_tile = [&](int t, float* tkb, float* tvb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < TK / NW; ++i) {
+            const int key = wave + NW * i;
+            const int pos = min(ks0 + TK * t + key, phi);
+            const long long at = (long long)(pos % p.cap) * ring_row + (long long)kvh * hd + col;
+            const long long cat = ((long long)max(0, pos - p.pos0) * p.nk + kvh) * hd + col;
+            __builtin_amdgcn_global_load_lds(p.ring_k + at, tkb + key * KST, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(pos < p.pos0 ? p.ring_v + at : p.yv + cat, tvb + key * KST, 16, 0, 0);
+        }
+    };
+    // the split's chunk rows: positions [cs0, ks1) (empty for most splits)
+    const int cs0 = max(ks0, p.pos0);
+    auto tile_has_chunk = [&](int t) { return ks0 + TK * t + TK - 1 >= p.pos0; };
+
+    // ---- chunk rows in the split's range: rotation and unit norm of the raw keys into the ring
+    // (read back by the tile loads; every workgroup whose range holds the row writes the same
+    // bytes), and the raw value into the ring by the one split that owns the row in the block
+    // holding its first query vector. Wave w takes rows cs0 + w, cs0 + w + 8, ..., eight at a
+    // time with all their loads in flight; lane l the float4 at d = 4l, its rotation partner
+    // in lane l +- hd/8.
+    auto make_chunk_keys = [&]() __attribute__((always_inline)) {
+        const int pl_lane = lane < 4 * HM ? lane + 4 * HM : lane - 4 * HM;
+        const int dm = 4 * (lane < 4 * HM ? lane : lane - 4 * HM);   // d mod hd/2
+        const bool on = lane < d4;
+        constexpr int PR = 8;
+        for (int r0 = cs0 + wave; r0 < ks1; r0 += PR * NW) {
+            f32x4 ka[PR], kc[PR], ksn[PR], va[PR];
+#pragma unroll
+            for (int i = 0; i < PR; ++i) {
+                const int c = min(r0 + NW * i, ks1 - 1) - p.pos0;
+                const long long cat = ((long long)c * p.nk + kvh) * hd;
+                const float* rope = p.rope + (long long)c * hd;
+                ka[i] = ldg4(p.yk + cat, col);
+                va[i] = ldg4(p.yv + cat, col);
+                kc[i] = ldg4(rope, on ? dm : 0);
+                ksn[i] = ldg4(rope, on ? half + dm : 0);
+            }
+#pragma unroll
+            for (int i = 0; i < PR; ++i) {
+                const int pos = r0 + NW * i;
+                const f32x4 a = ka[i], b = shfl4(a, pl_lane);
+                f32x4 r = lane < 4 * HM ? a * kc[i] - b * ksn[i] : a * kc[i] + b * ksn[i];
+                r = on ? r : f32x4{0.f, 0.f, 0.f, 0.f};
+                const float ss = wave_sum((r.x * r.x + r.y * r.y) + (r.z * r.z + r.w * r.w));
+                r *= 1.0f / sqrtf(ss + p.eps);
+                if (pos < ks1 && on) {
+                    const int c = pos - p.pos0;
+                    const long long rat = (long long)(pos % p.cap) * ring_row + (long long)kvh * hd + col;
+                    *reinterpret_cast<f32x4*>(p.ring_k + rat) = r;
+                    if ((c * p.hpg) / QB == qb) *reinterpret_cast<f32x4*>(p.ring_v + rat) = va[i];
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // the unit keys are written before any wave loads them
+    };
+
+    // ---- the block's 64 unit queries (times q_scale, scale and log2 e), made once per workgroup
+    // into the second tile buffers (queries 0..31 in s_k1, 32..63 in s_v1), which tile 1 takes
+    // only after the loop's first barrier: wave w makes queries 8w .. 8w + 7, lane 8 j + c the
+    // float4 pairs (4 c', 4 c' + hd/2) for c' = c, c + 8, c + 16, c + 24 below hd/8. The query
+    // loads are requested before tile 0's, so that waiting for them leaves the tile in flight
+    // (tile 0 is requested on every path, so that the wait can name the query loads alone).
+    {
+        const int qj = 8 * wave + (lane >> 3), c8 = lane & 7;
+        const int vt = min(v0 + qj, nqv - 1);
+        const int row = vt / p.hpg, head = kvh * p.hpg + vt % p.hpg;
+        const float* yq = p.yq + ((long long)row * p.nh + head) * hd;
+        const float* rope = p.rope + (long long)row * hd;
+        const float* qsc = p.q_scale + (long long)head * hd;
+        f32x4 a[4], b[4], cs[4], sn[4], sa[4], sb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = c8 + 8 * i;
+            const int d = 4 * c < half ? 4 * c : 0;
+            a[i] = ldg4(yq, d);
+            b[i] = ldg4(yq, d + half);
+            cs[i] = ldg4(rope, d);
+            sn[i] = ldg4(rope, d + half);
+            sa[i] = ldg4(qsc, d);
+            sb[i] = ldg4(qsc, d + half);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue_tile(0, s_k0, s_v0);
+        __builtin_amdgcn_sched_barrier(0);
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 u = a[i] * cs[i] - b[i] * sn[i], v = b[i] * cs[i] + a[i] * sn[i];
+            a[i] = u;
+            b[i] = v;
+            if (4 * (c8 + 8 * i) < half)
+                ss += ((u.x * u.x + u.y * u.y) + (u.z * u.z + u.w * u.w)) +
+                      ((v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w));
+        }
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        ss += __shfl_xor(ss, 4);
+        const float f = p.scale_log2 / sqrtf(ss + p.eps);
+        // (a branch on the wave, not a pointer choice, names the array each store writes, so that
+        // the compiler sees that they do not touch the buffers tile 0 is loading into)
+        auto put = [&](float* qd) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d = 4 * (c8 + 8 * i);
+                if (d < half) {
+                    *reinterpret_cast<f32x4*>(qd + d) = a[i] * sa[i] * f;
+                    *reinterpret_cast<f32x4*>(qd + d + half) = b[i] * sb[i] * f;
+                }
+            }
+        };
+        if (wave < 4) put(s_k1 + qj * KST);
+        else put(s_v1 + (qj - 32) * KST);
+    }
+    if (cs0 < ks1) make_chunk_keys();
+    __syncthreads();
+    // a first tile holding chunk rows of this split is loaded again now that their unit keys
+    // are in the ring (the first load has landed: the chunk-key pass waited for it)
+    if (cs0 < ks1 && tile_has_chunk(0)) issue_tile(0, s_k0, s_v0);
+    // this wave's queries as the B operand: qreg[m] holds query jq at d = 16m + 4 kr4 (+ 0..3),
+    // zero past hd
+    f32x4 qreg[16];
+    auto get_q = [&](const float* ql) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+            qreg[m] = 16 * m + 4 * kr4 < hd ? *reinterpret_cast<const f32x4*>(ql + 16 * m)
+                                            : f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    if (qw < 2) get_q(s_k1 + jq * KST + 4 * kr4);
+    else get_q(s_v1 + (jq - 32) * KST + 4 * kr4);
+
+    f32x4 oacc[16];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) oacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float mrun = -INFINITY, lrun = 0.0f;
+    // this lane's visible positions within the split
+    const int vlo = max(qlo, ks0), vhi = min(qpos, ks1 - 1);
+
+    // One tile: this wave's 16-key half (keys 16 kh .. 16 kh + 15 of the tile).
+    auto compute_tile = [&](int t, const float* tk, const float* tv) __attribute__((always_inline)) {
+        const int base = ks0 + TK * t + 16 * kh;
+        if (base >= ks1) return;   // the split's last tile may have one half only
+        const int klo = vlo - base, khi = vhi - base + 1;
+        if (!__any(klo < 16 && khi > 0 && khi > klo)) return;
+        constexpr int PF = 2;
+        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 kbuf[PF + 1];
+        const float* krow = tk + (16 * kh + qcol) * KST + 4 * kr4;
+#pragma unroll
+        for (int m = 0; m < PF; ++m) kbuf[m] = *reinterpret_cast<const f32x4*>(krow + 16 * m);
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            if (m + PF < 16) kbuf[(m + PF) % (PF + 1)] = *reinterpret_cast<const f32x4*>(krow + 16 * (m + PF));
+            __builtin_amdgcn_sched_barrier(0);
+            const f32x4 k4 = kbuf[m % (PF + 1)];
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.x, qreg[m].x, sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.y, qreg[m].y, sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.z, qreg[m].z, sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(k4.w, qreg[m].w, sacc, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the first V^T operands, read now so that their latency hides under the softmax
+        float vbuf[2][16];
+#pragma unroll
+        for (int b = 0; b < 16; ++b) vbuf[0][b] = tv[(16 * kh + 4 * kr4) * KST + qcol + 16 * b];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int k = 4 * kr4 + r;
+            sacc[r] = (k >= klo && k < khi) ? sacc[r] : -INFINITY;
+            tmax = fmaxf(tmax, sacc[r]);
+        }
+        tmax = col_max(tmax);
+        // lazy rescaling against a reference max (kLazyRescale)
+        const bool grow = tmax > mrun + kLazyRescale;
+        if (__any(grow)) {
+            const float m_new = grow ? tmax : mrun;
+            const float corr = __builtin_amdgcn_exp2f(mrun - safe_max(m_new));
+            lrun *= corr;
+#pragma unroll
+            for (int b = 0; b < 16; ++b) oacc[b] *= corr;
+            mrun = m_new;
+        }
+        const float mu = safe_max(mrun);
+        float psum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            sacc[r] = __builtin_amdgcn_exp2f(sacc[r] - mu);
+            psum += sacc[r];
+        }
+        lrun += col_sum(psum);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            if (st + 1 < 4) {
+                const float* vp = tv + (16 * kh + 4 * kr4 + st + 1) * KST + qcol;
+#pragma unroll
+                for (int b = 0; b < 16; ++b) vbuf[(st + 1) & 1][b] = vp[16 * b];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int b = 0; b < 16; ++b)
+                oacc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(vbuf[st & 1][b], sacc[st], oacc[b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Wait for this wave's rows of tile t; the barrier makes every wave's rows visible and tells
+    // that nobody still reads the other buffer (tile t - 1), which then takes t + 1.
+    for (int t = 0; t < ntile; t += 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (t + 1 < ntile) issue_tile(t + 1, s_k1, s_v1);
+        compute_tile(t, s_k0, s_v0);
+        if (t + 1 < ntile) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (t + 2 < ntile) issue_tile(t + 2, s_k0, s_v0);
+            compute_tile(t + 1, s_k1, s_v1);
+        }
+    }
+
+    // ---- the two key halves of each query set meet: wave w (key half kh) keeps the output
+    // columns of blocks b in [8 kh, 8 kh + 8), publishes the other half and its (m, l) in the
+    // tile buffers and folds in its partner's
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int li = qw * 64 + lane;
+    // [b][query set][lane] float4s: columns 0..127 in s_k0, 128..255 in s_k1
+    auto fo = [&](int b) { return (b < 8 ? s_k0 : s_k1) + ((b & 7) * 256 + li) * 4; };
+    float* fm = s_v0;                        // [key half][m | l][query set][lane]
+    // Each branch names its registers at compile time (H is the wave's key half).
+    auto publish = [&](auto h_c) __attribute__((always_inline)) {
+        constexpr int H = decltype(h_c)::value;
+#pragma unroll
+        for (int b = 8 * (1 - H); b < 8 * (1 - H) + 8; ++b) *reinterpret_cast<f32x4*>(fo(b)) = oacc[b];
+    };
+    if (kh == 0) publish(std::integral_constant<int, 0>{});
+    else publish(std::integral_constant<int, 1>{});
+    fm[kh * 512 + li] = mrun;
+    fm[kh * 512 + 256 + li] = lrun;
+    __syncthreads();
+    {
+        const float m1 = fm[(1 - kh) * 512 + li], l1 = fm[(1 - kh) * 512 + 256 + li];
+        const float mt = fmaxf(mrun, m1), mu = safe_max(mt);
+        const float f0 = __builtin_amdgcn_exp2f(mrun - mu), f1 = __builtin_amdgcn_exp2f(m1 - mu);
+        lrun = lrun * f0 + l1 * f1;
+        mrun = mt;
+        auto fold = [&](auto h_c) __attribute__((always_inline)) {
+            constexpr int H = decltype(h_c)::value;
+#pragma unroll
+            for (int b = 8 * H; b < 8 * H + 8; ++b)
+                oacc[b] = oacc[b] * f0 + *reinterpret_cast<const f32x4*>(fo(b)) * f1;
+        };
+        if (kh == 0) fold(std::integral_constant<int, 0>{});
+        else fold(std::integral_constant<int, 1>{});
+    }
+    // Wave w holds, for query jq, d = 16 b + 4 kr4 + (0..3) in oacc[b], b in [8 kh, 8 kh + 8).
+    auto out_gated = [&](int v, int d, f32x4 o) {   // gate and store query vector v, column d
+        const int row = v / p.hpg, head = kvh * p.hpg + v % p.hpg;
+        const f32x4 gv = ldg4(p.gate + (long long)row * p.nh * hd + (long long)head * hd, d);
+        const f32x4 sv = ldg4(p.gate_scale + (long long)head * hd, d);
+        o.x = o.x / (1.0f + expf(-(gv.x * sv.x)));
+        o.y = o.y / (1.0f + expf(-(gv.y * sv.y)));
+        o.z = o.z / (1.0f + expf(-(gv.z * sv.z)));
+        o.w = o.w / (1.0f + expf(-(gv.w * sv.w)));
+        *reinterpret_cast<f32x4*>(p.out + ((long long)row * p.nh + head) * hd + d) = o;
+    };
+    if (S == 1) {
+        if (qvalid) {
+            const float inv = 1.0f / fmaxf(lrun, 1e-30f);
+            auto out_half = [&](auto h_c) __attribute__((always_inline)) {
+                constexpr int H = decltype(h_c)::value;
+#pragma unroll
+                for (int b = 8 * H; b < 8 * H + 8; ++b) {
+                    const int d = 16 * b + 4 * kr4;
+                    if (d < hd) out_gated(vq, d, oacc[b] * inv);
+                }
+            };
+            if (kh == 0) out_half(std::integral_constant<int, 0>{});
+            else out_half(std::integral_constant<int, 1>{});
+        }
+        return;
+    }
+
+    // ---- partial of (block, split): written through to the device-coherent level, then one
+    // ready flag per gatherer once every store is acknowledged
+    const int G = p.gather_k;
+    const long long it = (long long)qbg * S + split;
+    {
+        const __amdgpu_buffer_rsrc_t part =
+            __builtin_amdgcn_make_buffer_rsrc(p.pacc + it * QB * 256, 0, QB * 256 * 4, kBufferWord3);
+        auto store_half = [&](auto h_c) __attribute__((always_inline)) {
+            constexpr int H = decltype(h_c)::value;
+#pragma unroll
+            for (int b = 8 * H; b < 8 * H + 8; ++b)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(vu4, oacc[b]), part,
+                                                       (jq * 256 + 16 * b + 4 * kr4) * 4, 0, kCachePolicyDevice);
+        };
+        if (kh == 0) store_half(std::integral_constant<int, 0>{});
+        else store_half(std::integral_constant<int, 1>{});
+        if (kh == 0 && kr4 == 0) {
+            store_dev(p.pm + it * QB + jq, mrun);
+            store_dev(p.pl + it * QB + jq, lrun);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    unsigned int* flags = p.flags + (long long)qbg * G * S;   // [gatherer][split]
+    if (tid < G) __hip_atomic_store(flags + tid * S + split, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int k = split - (S - G);
+    if (k < 0) return;
+
+    // ---- gatherer k: columns [k CW, (k + 1) CW) of the block's 64 queries, CW = 256 / G; item
+    // i = (query i / (CW / 4), float4 column i % (CW / 4)), IPT = 8 / G items per thread. The
+    // waves first wait for every split's flag, then read the partials 16 (item, split) pairs at a
+    // time, all requested before any is used, and fold them in split order.
+    const int cw4 = 64 / G;                    // float4 columns per gatherer
+    unsigned int* gflags = flags + k * S;
+    const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc(gflags, 0, S * 4, kBufferWord3);
+    const long long item0 = (long long)qbg * S;
+    const __amdgpu_buffer_rsrc_t racc =
+        __builtin_amdgcn_make_buffer_rsrc(p.pacc + item0 * QB * 256, 0, S * QB * 256 * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(p.pm + item0 * QB, 0, S * QB * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(p.pl + item0 * QB, 0, S * QB * 4, kBufferWord3);
+    bool bad = false;
+    auto gather = [&](auto ipt_c) __attribute__((always_inline)) {
+        // SB splits per batch; with many items per thread, smaller batches and the gate read at
+        // the end keep everything in registers
+        constexpr int IPT = decltype(ipt_c)::value, SB = IPT <= 2 ? 16 / IPT : 8 / IPT;
+        constexpr bool kGatePre = IPT <= 2;
+        float gm[IPT], gl[IPT];
+        f32x4 go[IPT], gg[IPT], gs[IPT];
+        int gq[IPT], gc[IPT];
+#pragma unroll
+        for (int j = 0; j < IPT; ++j) {
+            const int i = j * NT + tid;
+            gq[j] = i / cw4;
+            gc[j] = k * cw4 + i % cw4;
+            gm[j] = -INFINITY;
+            gl[j] = 0.0f;
+            go[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        auto load_gate = [&](int j) {
+            const int v = min(v0 + gq[j], nqv - 1), d = min(4 * gc[j], hd - 4);
+            const int head = kvh * p.hpg + v % p.hpg;
+            gg[j] = ldg4(p.gate + ((long long)(v / p.hpg) * p.nh + head) * hd, d);
+            gs[j] = ldg4(p.gate_scale + (long long)head * hd, d);
+        };
+        if constexpr (kGatePre) {   // requested before the wait
+#pragma unroll
+            for (int j = 0; j < IPT; ++j) load_gate(j);
+        }
+        unsigned long long pend = S >= 64 ? ~0ull : ((1ull << S) - 1ull);
+        int polls = 0;
+        while (pend != 0ull && polls < kGatedPolls) {
+            ++polls;
+            const unsigned f = __builtin_amdgcn_raw_buffer_load_b32(rf, min(lane, S - 1) * 4, 0, kCachePolicyDevice);
+            pend &= ~__builtin_amdgcn_ballot_w64(f != 0u && lane < S);
+            if (pend != 0ull) __builtin_amdgcn_s_sleep(2);
+        }
+        if (lane == 0) s_done[wave] = pend == 0ull ? 1 : 0;
+        __syncthreads();   // every wave has left its poll loop
+#pragma unroll
+        for (int w = 0; w < NW; ++w) bad |= s_done[w] == 0;
+        for (int s0 = 0; s0 < S && !bad; s0 += SB) {
+            float m1[IPT][SB], l1[IPT][SB];
+            f32x4 a1[IPT][SB];
+#pragma unroll
+            for (int j = 0; j < IPT; ++j)
+#pragma unroll
+                for (int u = 0; u < SB; ++u) {
+                    const int at = min(s0 + u, S - 1) * QB + gq[j];
+                    m1[j][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, at * 4, 0, kCachePolicyDevice));
+                    l1[j][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, at * 4, 0, kCachePolicyDevice));
+                    a1[j][u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                             racc, (at * 256 + 4 * gc[j]) * 4, 0, kCachePolicyDevice));
+                }
+#pragma unroll
+            for (int j = 0; j < IPT; ++j)
+#pragma unroll
+                for (int u = 0; u < SB; ++u) {
+                    if (s0 + u < S) {
+                        const float mn = fmaxf(gm[j], m1[j][u]), mu = safe_max(mn);
+                        const float f0 = __builtin_amdgcn_exp2f(gm[j] - mu), f1 = __builtin_amdgcn_exp2f(m1[j][u] - mu);
+                        gl[j] = gl[j] * f0 + l1[j][u] * f1;
+                        go[j] = go[j] * f0 + a1[j][u] * f1;
+                        gm[j] = mn;
+                    }
+                }
+        }
+#pragma unroll
+        for (int j = 0; j < IPT; ++j) {
+            const int v = v0 + gq[j], d = 4 * gc[j];
+            if constexpr (!kGatePre) load_gate(j);
+            if (v < nqv && d < hd) {
+                f32x4 o = go[j] * (1.0f / fmaxf(gl[j], 1e-30f));
+                o.x = o.x / (1.0f + expf(-(gg[j].x * gs[j].x)));
+                o.y = o.y / (1.0f + expf(-(gg[j].y * gs[j].y)));
+                o.z = o.z / (1.0f + expf(-(gg[j].z * gs[j].z)));
+                o.w = o.w / (1.0f + expf(-(gg[j].w * gs[j].w)));
+                if (bad) o = f32x4{NAN, NAN, NAN, NAN};
+                const int head = kvh * p.hpg + v % p.hpg;
+                *reinterpret_cast<f32x4*>(p.out + ((long long)(v / p.hpg) * p.nh + head) * hd + d) = o;
+            }
+        }
+    };
+    switch (G) {
+        case 8: gather(std::integral_constant<int, 1>{}); break;
+        case 4: gather(std::integral_constant<int, 2>{}); break;
+        case 2: gather(std::integral_constant<int, 4>{}); break;
+        default: gather(std::integral_constant<int, 8>{}); break;
+    }
+    if (!bad && tid < S) __hip_atomic_store(gflags + tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 hipError_t launch_gated_fused(const GatedFusedParams& p, hipStream_t stream) {
     const long long blocks = (long long)p.nk * p.nqs * p.nsplit;
     if (blocks < 1 || blocks > 0x7fffffffLL || p.nsplit < 1 || p.nsplit > 64) return hipErrorInvalidValue;
+    if (p.qb == 64) {
+        if (p.gather_k < 1 || p.gather_k > 8 || p.gather_k > p.nsplit) return hipErrorInvalidValue;
+        const dim3 grid((unsigned)blocks), block(512);
+        switch (p.hd) {
+            case 160: hipLaunchKernelGGL(attn_gated_tiles_kernel<5>, grid, block, 0, stream, p); break;
+            case 192: hipLaunchKernelGGL(attn_gated_tiles_kernel<6>, grid, block, 0, stream, p); break;
+            case 224: hipLaunchKernelGGL(attn_gated_tiles_kernel<7>, grid, block, 0, stream, p); break;
+            case 256: hipLaunchKernelGGL(attn_gated_tiles_kernel<8>, grid, block, 0, stream, p); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     constexpr int NW = kGatedWaves;
     const dim3 grid((unsigned)blocks), block(64 * NW);
     switch (p.hd) {

@@ -72,13 +72,15 @@ struct GatedFusedParams {
     float* ring_k;            // [cap][nk][hd]
     float* ring_v;
     float* out;               // [rows][nh][hd]
-    float* pacc;              // split partials [set][split][16][256] (nsplit > 1)
-    float* pm;                // [set][split][16]
+    float* pacc;              // split partials [block][split][QB][256] (nsplit > 1)
+    float* pm;                // [block][split][QB]
     float* pl;
-    unsigned int* flags;      // [set][split], zero between calls
+    unsigned int* flags;      // ready flags, zero between calls
     int rows, pos0, cap, window, nh, nk, hd, hpg;
-    int nqs;                  // query sets (16 query vectors) per KV head
-    int nsplit;               // workgroups per query set, at most 64
+    int qb;                   // query vectors per block: 16 (register form) or 64 (tile form)
+    int nqs;                  // query blocks per KV head
+    int nsplit;               // workgroups per query block, at most 64
+    int gather_k;             // tile form: gatherers per block (the block's last splits)
     float scale_log2, eps;
 };
 hipError_t launch_gated_fused(const GatedFusedParams& p, hipStream_t stream);

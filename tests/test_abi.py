@@ -273,13 +273,17 @@ def test_tuning_knobs_change_the_plan(lib):
 
 
 def test_gated_single_launch_workspace(lib):
-    # the gated call in one launch (kernel 6): 16 query vectors per set, 4 splits per set for
-    # the 64-row, 16/4-head, width-256 workload (256 workgroups): counters + partials
-    items = 4 * 16 * 4
+    # the gated call in one launch (kernel 6), tile form for the 64-row, 16/4-head, width-256
+    # workload: 4 blocks of 64 query vectors per KV head, 16 splits each (256 workgroups):
+    # counters + partials
+    items = 4 * 4 * 16
     need = B.gated_workspace_bytes(64, 16, 4, 256, 1024)
-    assert need == 65536 + items * 16 * 256 * 4 + 2 * items * 16 * 4
+    assert need == 65536 + items * 64 * 256 * 4 + 2 * items * 64 * 4
+    # register form (16 to 63 query vectors per KV head): sets of 16, 4 splits each
+    items = 2 * 2 * 16
+    assert B.gated_workspace_bytes(8, 8, 2, 256, 1024) == 65536 + items * 16 * 256 * 4 + 2 * items * 16 * 4
     try:
-        B.tuning_set(B.TUNE_TARGET_BLOCKS, 64)   # one workgroup per set: no partials at all
+        B.tuning_set(B.TUNE_TARGET_BLOCKS, 1)    # one workgroup per block: no partials at all
         assert B.gated_workspace_bytes(64, 16, 4, 256, 1024) == 0
         B.tuning_set(B.TUNE_TARGET_BLOCKS, 0)
         B.tuning_set(B.TUNE_FORCE_KERNEL, 6)     # fewer than 16 query vectors per KV head, forced

@@ -327,6 +327,10 @@ GATED_SWEEP = [
     (16, 0, 64, 8, 4, 4, 224),           # one set per KV head
     (4, 50, 128, 64, 8, 2, 256),
     (2, 50, 128, 64, 8, 2, 256),         # fewer than 16 query vectors per KV head
+    # 64 query vectors or more per KV head: the tile form
+    (80, 3, 200, 100, 8, 2, 256),        # windows clipped at position 0
+    (70, 100, 300, 30, 8, 8, 192),       # more rows than the window, one head per KV head
+    (64, 5, 128, 48, 16, 4, 224),
 ]
 
 # plans of the gated call: automatic; the single launch with one, the automatic and many
@@ -409,22 +413,30 @@ def test_poisoned_slots_and_canaries(rows, hpg):
     assert np.all(ws.buf[need:].cpu().numpy() == 0xAB), "wrote outside the workspace"
 
 
-@pytest.mark.parametrize("nh,hd", [(4, 64), (8, 256)])   # three launches; one launch
-def test_gated_untouched_slots(nh, hd):
-    _case(f"gated untouched slots nh={nh} hd={hd}")
-    inp = gen.make_gated(6, 40, 64, 16, nh, 2, hd, seed=5)
+# three launches; the register form; the tile form
+@pytest.mark.parametrize("rows,nh,hd", [(6, 4, 64), (6, 8, 256), (24, 8, 256)])
+def test_gated_untouched_slots(rows, nh, hd):
+    _case(f"gated untouched slots rows={rows} nh={nh} hd={hd}")
+    inp = gen.make_gated(rows, 40, 64, 16, nh, 2, hd, seed=5)
     read_or_written = set()
     for r in range(inp.rows):
         pos = inp.pos0 + r
         for p in range(max(0, pos + 1 - inp.window), pos + 1):
             read_or_written.add(p % inp.cap)
     untouched = [s for s in range(inp.cap) if s not in read_or_written]
+    # the slots the rows write hold NaN before the call too: nothing may read them before the
+    # call has written them
+    written = sorted({(inp.pos0 + r) % inp.cap for r in range(inp.rows)})
     inp.ring_k[untouched] = np.nan
     inp.ring_v[untouched] = np.nan
+    inp.ring_k[written] = np.nan
+    inp.ring_v[written] = np.nan
     z, rk, rv = gpu_gated(inp)
-    oz, _, _ = oracle.window_gated(inp)
+    oz, ork, orv = oracle.window_gated(inp)
     assert_close(z, oz, "gated poisoned")
     assert np.isnan(rk[untouched]).all() and np.isnan(rv[untouched]).all()
+    assert_close(rk[written], ork[written], "written ring keys")
+    np.testing.assert_array_equal(rv[written], orv[written])
 
 
 # ── invariants on the GPU ────────────────────────────────────────────────────────────────────

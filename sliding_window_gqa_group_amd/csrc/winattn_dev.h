@@ -399,17 +399,56 @@ __device__ inline void merge_block(const AttnParams& p, int blk, int nsplit, int
     const size_t base = (size_t)blk * p.slot_stride * QB;
     constexpr int ITEMS = QB * D4;
     if constexpr (ITEMS >= NT) {
+        // Several items per thread, KG at a time: the loads of a group's items for a batch of U
+        // splits issue together (storing one item's output before the next item's loads would
+        // make each item a round trip of its own: the compiler cannot tell the output from the
+        // partials).
         constexpr int IPT = ITEMS / NT;
+        constexpr int KG = IPT < 4 ? IPT : 4;
+        constexpr int U = 16 / KG;
+        static_assert(IPT % KG == 0, "item groups");
+#pragma unroll 1
+        for (int k0 = 0; k0 < IPT; k0 += KG) {
+            Part x[KG];
+            int jj[KG], cc[KG];
 #pragma unroll
-        for (int k = 0; k < IPT; ++k) {
-            const int item = threadIdx.x + NT * k;
-            const int j = item / D4, c = c0 + item % D4;
-            Part x{-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
-            fold_splits<QB, D>(p, base, j, c, 0, 1, nsplit, x);
-            if (j < nq && c < d4) {
-                const float inv = 1.0f / fmaxf(x.l, 1e-30f);
-                store_out<GATED>(p, q0 + j, g, 4 * c,
-                                 make_float4(x.a.x * inv, x.a.y * inv, x.a.z * inv, x.a.w * inv));
+            for (int k = 0; k < KG; ++k) {
+                const int item = threadIdx.x + NT * (k0 + k);
+                jj[k] = item / D4;
+                cc[k] = c0 + item % D4;
+                x[k] = Part{-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
+            }
+            for (int s = 0; s < nsplit; s += U) {
+                float m[KG][U], l[KG][U];
+                float4 a[KG][U];
+#pragma unroll
+                for (int k = 0; k < KG; ++k)
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        // unconditional (past the end: the last split again, dropped below)
+                        const size_t at = base + (size_t)min(s + u, nsplit - 1) * QB + jj[k];
+                        m[k][u] = p.pm[at];
+                        l[k][u] = p.pl[at];
+                        a[k][u] = *reinterpret_cast<const float4*>(p.pacc + at * D + 4 * cc[k]);
+                    }
+#pragma unroll
+                for (int k = 0; k < KG; ++k)
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        // past the end, or a split that marked its slot empty (m = -inf)
+                        const bool real = s + u < nsplit && m[k][u] > -INFINITY;
+                        part_fold(x[k], real ? m[k][u] : -INFINITY, real ? l[k][u] : 0.0f,
+                                  real ? a[k][u] : make_float4(0.f, 0.f, 0.f, 0.f));
+                    }
+            }
+#pragma unroll
+            for (int k = 0; k < KG; ++k) {
+                if (jj[k] < nq && cc[k] < d4) {
+                    const float inv = 1.0f / fmaxf(x[k].l, 1e-30f);
+                    store_out<GATED>(p, q0 + jj[k], g, 4 * cc[k],
+                                     make_float4(x[k].a.x * inv, x[k].a.y * inv, x[k].a.z * inv,
+                                                 x[k].a.w * inv));
+                }
             }
         }
     } else {

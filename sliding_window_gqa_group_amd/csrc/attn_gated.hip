@@ -538,9 +538,11 @@ __global__ __launch_bounds__(512, 1) void attn_gated_tiles_kernel(const GatedFus
     const int plo = max(0, p.pos0 + r_first + 1 - p.window), phi = p.pos0 + r_last;
     const int nb = (phi - plo + 16) / 16;
     // The last split also makes the chunk rows' unit keys: it is counted one 16-key block more
-    // than it streams (nb + 1 shares, larger ones first).
-    const int bs0 = min(nb, (int)(((long long)(nb + 1) * split + S - 1) / S));
-    const int bs1 = min(nb, (int)(((long long)(nb + 1) * (split + 1) + S - 1) / S));
+    // than it streams (nb + 1 shares). The larger shares go to the first splits, which gather
+    // nothing, so that every gatherer is done with its own tiles early.
+    const int shq = (nb + 1) / S, shr = (nb + 1) % S;
+    const int bs0 = min(nb, split * shq + min(split, shr));
+    const int bs1 = min(nb, (split + 1) * shq + min(split + 1, shr));
     const int ks0 = plo + 16 * bs0, ks1 = min(plo + 16 * bs1, phi + 1);
     const int ntile = (bs1 - bs0 + 1) / 2;
 
@@ -906,17 +908,53 @@ __global__ __launch_bounds__(512, 1) void attn_gated_tiles_kernel(const GatedFus
         }
         unsigned long long pend = S >= 64 ? ~0ull : ((1ull << S) - 1ull);
         int polls = 0;
+        // One item per thread and at most 16 splits: each split's partial is requested as soon
+        // as its flag is seen (so that only the last splits' loads remain after the last
+        // flag), into registers of its own; the fold below still runs in split order.
+        constexpr bool kEarly = IPT == 1;
+        float em[kEarly ? 16 : 1], el[kEarly ? 16 : 1];
+        f32x4 ea[kEarly ? 16 : 1];
+        const bool early = kEarly && S <= 16;
         while (pend != 0ull && polls < kGatedPolls) {
             ++polls;
             const unsigned f = __builtin_amdgcn_raw_buffer_load_b32(rf, min(lane, S - 1) * 4, 0, kCachePolicyDevice);
-            pend &= ~__builtin_amdgcn_ballot_w64(f != 0u && lane < S);
+            const unsigned long long ready = __builtin_amdgcn_ballot_w64(f != 0u && lane < S) & pend;
+            pend &= ~ready;
+            if constexpr (kEarly) {
+                if (early) {
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) {
+                        if ((ready >> u) & 1ull) {
+                            const int at = u * QB + gq[0];
+                            em[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, at * 4, 0, kCachePolicyDevice));
+                            el[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, at * 4, 0, kCachePolicyDevice));
+                            ea[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                  racc, (at * 256 + 4 * gc[0]) * 4, 0, kCachePolicyDevice));
+                        }
+                    }
+                }
+            }
             if (pend != 0ull) __builtin_amdgcn_s_sleep(2);
         }
         if (lane == 0) s_done[wave] = pend == 0ull ? 1 : 0;
         __syncthreads();   // every wave has left its poll loop
 #pragma unroll
         for (int w = 0; w < NW; ++w) bad |= s_done[w] == 0;
-        for (int s0 = 0; s0 < S && !bad; s0 += SB) {
+        if constexpr (kEarly) {
+            if (early && !bad) {
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    if (u < S) {
+                        const float mn = fmaxf(gm[0], em[u]), mu = safe_max(mn);
+                        const float f0 = __builtin_amdgcn_exp2f(gm[0] - mu), f1 = __builtin_amdgcn_exp2f(em[u] - mu);
+                        gl[0] = gl[0] * f0 + el[u] * f1;
+                        go[0] = go[0] * f0 + ea[u] * f1;
+                        gm[0] = mn;
+                    }
+                }
+            }
+        }
+        for (int s0 = 0; s0 < S && !bad && !early; s0 += SB) {
             float m1[IPT][SB], l1[IPT][SB];
             f32x4 a1[IPT][SB];
 #pragma unroll

@@ -495,6 +495,47 @@ constexpr int kGatedWaves = 4;
 constexpr int kGTK = 32;          // keys per tile
 constexpr int kGKST = 256 + 4;    // LDS row stride (floats)
 
+// Phase stamps of the tile form, in timing builds only (compiled with WINATTN_PHASE_STAMPS; the
+// normal build contains none of this code): every wave reads the 100 MHz real-time counter at
+// the phase boundaries below, keeps the readings in registers and writes them once, at its end,
+// with its XCD number, to g_gated_stamps[block * 8 + wave][kGatedStampWords] when the host has
+// set that pointer (attn_gated_stamps_set). The kernel's work is unchanged.
+//   0 start, 1 queries in registers, 2 tile 0 in LDS, 3 tile 0 done, 4 tile 1 in LDS,
+//   5 tile 1 done, 6 every tile done, 7 key halves folded, 8 flags raised (non-gatherers end),
+//   9 every flag seen (gatherers), 10 outputs stored and drained (gatherers, single splits)
+#ifdef WINATTN_PHASE_STAMPS
+constexpr int kGatedStampWords = 12;
+__device__ unsigned long long* g_gated_stamps;
+struct GatedStamps {
+    unsigned long long t[kGatedStampWords - 1] = {};
+    __device__ void mark(int k) { t[k] = __builtin_amdgcn_s_memrealtime(); }
+    template <class V>
+    __device__ void mark_after(int k, const V& v) {
+        asm volatile("" : : "v"(v));
+        mark(k);
+    }
+    __device__ void mark_drained(int k) {
+        __builtin_amdgcn_s_waitcnt(0);
+        mark(k);
+    }
+    __device__ void flush(int tid) {
+        unsigned long long* o = g_gated_stamps;
+        if (!o || (tid & 63) != 0) return;
+        o += ((size_t)blockIdx.x * 8 + tid / 64) * kGatedStampWords;
+        for (int k = 0; k < kGatedStampWords - 1; ++k) o[k] = t[k];
+        o[kGatedStampWords - 1] = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11));   // XCC_ID
+    }
+};
+#else
+struct GatedStamps {
+    __device__ void mark(int) {}
+    template <class V>
+    __device__ void mark_after(int, const V&) {}
+    __device__ void mark_drained(int) {}
+    __device__ void flush(int) {}
+};
+#endif
+
 template <int HM>
 __global__ __launch_bounds__(512, 1) void attn_gated_tiles_kernel(const GatedFusedParams p) {
     constexpr int NT = 512, NW = 8, TK = kGTK, KST = kGKST, QB = 64;
@@ -523,6 +564,8 @@ __global__ __launch_bounds__(512, 1) void attn_gated_tiles_kernel(const GatedFus
     // stay on the scalar unit
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qw = wave & 3, kh = wave >> 2;          // query set, key half of each tile
+    GatedStamps stamps;
+    stamps.mark(0);
     const int qcol = lane & 15, kr4 = lane >> 4;
     const int nqv = p.rows * p.hpg;
     const int v0 = qb * QB;
@@ -684,6 +727,7 @@ __global__ __launch_bounds__(512, 1) void attn_gated_tiles_kernel(const GatedFus
     };
     if (qw < 2) get_q(s_k1 + jq * KST + 4 * kr4);
     else get_q(s_v1 + (jq - 32) * KST + 4 * kr4);
+    stamps.mark_after(1, qreg[15].w);
 
     f32x4 oacc[16];
 #pragma unroll
@@ -765,15 +809,20 @@ __global__ __launch_bounds__(512, 1) void attn_gated_tiles_kernel(const GatedFus
     for (int t = 0; t < ntile; t += 2) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if (t == 0) stamps.mark(2);
         if (t + 1 < ntile) issue_tile(t + 1, s_k1, s_v1);
         compute_tile(t, s_k0, s_v0);
+        if (t == 0) stamps.mark_after(3, oacc[15].w);
         if (t + 1 < ntile) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
+            if (t == 0) stamps.mark(4);
             if (t + 2 < ntile) issue_tile(t + 2, s_k0, s_v0);
             compute_tile(t + 1, s_k1, s_v1);
+            if (t == 0) stamps.mark_after(5, oacc[15].w);
         }
     }
+    stamps.mark_after(6, oacc[15].w);
 
     // ---- the two key halves of each query set meet: wave w (key half kh) keeps the output
     // columns of blocks b in [8 kh, 8 kh + 8), publishes the other half and its (m, l) in the
@@ -821,6 +870,7 @@ __global__ __launch_bounds__(512, 1) void attn_gated_tiles_kernel(const GatedFus
         o.w = o.w / (1.0f + expf(-(gv.w * sv.w)));
         *reinterpret_cast<f32x4*>(p.out + ((long long)row * p.nh + head) * hd + d) = o;
     };
+    stamps.mark_after(7, oacc[15].w);
     if (S == 1) {
         if (qvalid) {
             const float inv = 1.0f / fmaxf(lrun, 1e-30f);
@@ -835,6 +885,8 @@ __global__ __launch_bounds__(512, 1) void attn_gated_tiles_kernel(const GatedFus
             if (kh == 0) out_half(std::integral_constant<int, 0>{});
             else out_half(std::integral_constant<int, 1>{});
         }
+        stamps.mark_drained(10);
+        stamps.flush(tid);
         return;
     }
 
@@ -863,8 +915,12 @@ __global__ __launch_bounds__(512, 1) void attn_gated_tiles_kernel(const GatedFus
     __syncthreads();
     unsigned int* flags = p.flags + (long long)qbg * G * S;   // [gatherer][split]
     if (tid < G) __hip_atomic_store(flags + tid * S + split, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    stamps.mark(8);
     const int k = split - (S - G);
-    if (k < 0) return;
+    if (k < 0) {
+        stamps.flush(tid);
+        return;
+    }
 
     // ---- gatherer k: columns [k CW, (k + 1) CW) of the block's 64 queries, CW = 256 / G; item
     // i = (query i / (CW / 4), float4 column i % (CW / 4)), IPT = 8 / G items per thread. The
@@ -936,6 +992,7 @@ __global__ __launch_bounds__(512, 1) void attn_gated_tiles_kernel(const GatedFus
             }
             if (pend != 0ull) __builtin_amdgcn_s_sleep(2);
         }
+        stamps.mark(9);
         if (lane == 0) s_done[wave] = pend == 0ull ? 1 : 0;
         __syncthreads();   // every wave has left its poll loop
 #pragma unroll
@@ -1003,6 +1060,8 @@ __global__ __launch_bounds__(512, 1) void attn_gated_tiles_kernel(const GatedFus
         default: gather(std::integral_constant<int, 8>{}); break;
     }
     if (!bad && tid < S) __hip_atomic_store(gflags + tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    stamps.mark_drained(10);
+    stamps.flush(tid);
 }
 
 hipError_t launch_gated_fused(const GatedFusedParams& p, hipStream_t stream) {
@@ -1033,3 +1092,14 @@ hipError_t launch_gated_fused(const GatedFusedParams& p, hipStream_t stream) {
 }
 
 }  // namespace winattn
+
+#ifdef WINATTN_PHASE_STAMPS
+// Timing builds: where the gated tile kernel writes its phase stamps (NULL: nowhere). The buffer
+// holds kGatedStampWords u64 per wave of the launch (8 waves per workgroup); each launch
+// overwrites it.
+extern "C" int attn_gated_stamps_set(void* device_ptr) {
+    return hipMemcpyToSymbol(HIP_SYMBOL(winattn::g_gated_stamps), &device_ptr, sizeof(device_ptr)) == hipSuccess
+               ? 0
+               : -3;
+}
+#endif

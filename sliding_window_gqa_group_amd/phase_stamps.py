@@ -1,7 +1,8 @@
-"""Phase timing of the single-launch decode kernel from in-kernel clock stamps.
+"""Phase timing of the single-launch decode and gated kernels from in-kernel clock stamps.
 
-    python -m sliding_window_gqa_group_amd.phase_stamps build      # on any host: compiles
-    python -m sliding_window_gqa_group_amd.phase_stamps run        # on the GPU: prints markdown
+    python -m sliding_window_gqa_group_amd.phase_stamps build             # any host: compiles
+    python -m sliding_window_gqa_group_amd.phase_stamps run [calls]       # GPU: decode table
+    python -m sliding_window_gqa_group_amd.phase_stamps gated [calls]     # GPU: gated table
 
 `build` compiles the library a second time with WINATTN_PHASE_STAMPS defined, into
 libwinattn_stamps.so beside the normal one (the normal library has no stamp code). `run` loads
@@ -9,7 +10,9 @@ that library instead of the normal one and makes decode calls (1 row, 8 KV group
 heads, d 128, full 4096-slot rings, 4 sinks) on 20 rotating input sets. Each recorded call is
 the last of 8 back-to-back calls, as in the bench's timed loop; every wave of it wrote the
 100 MHz real-time counter at its phase boundaries. The report gives, per phase, the spread over
-all waves of the recorded calls of the time since the call's first wave started.
+all waves of the recorded calls of the time since the call's first wave started. `gated` does
+the same for the gated workload's single launch (64 rows at pos0 20000, 16 query heads over 4
+KV heads, hd 256, window 1024) on its rotating input sets.
 """
 from __future__ import annotations
 
@@ -118,10 +121,114 @@ def run(calls: int = 10) -> str:
     return "\n".join(lines)
 
 
+GATED_WORDS = 12   # u64 per wave: 11 phase stamps, then the XCD number
+GATED_PHASES = [
+    ("start", "the wave starts"),
+    ("queries", "the block's unit queries are in the wave's registers (tile 0 requested)"),
+    ("tile0 in", "tile 0 is in LDS (first barrier of the loop)"),
+    ("tile0 done", "the wave's half of tile 0: scores, softmax, value products"),
+    ("tile1 in", "tile 1 is in LDS"),
+    ("tile1 done", "the wave's half of tile 1"),
+    ("tiles", "every tile of the split is done"),
+    ("folded", "the two key halves of each query set folded in LDS"),
+    ("flagged", "partials stored, acknowledged, flags raised (non-gatherers end here)"),
+    ("flags seen", "a gatherer has seen every split's flag (partials requested as seen)"),
+    ("end", "a gatherer's outputs stored and drained"),
+]
+
+
+def run_gated(calls: int = 10) -> str:
+    sys.path.insert(0, os.path.dirname(HERE))
+    import numpy as np
+    import torch
+    from sliding_window_gqa_group_amd import binding as B, inputs as gen
+
+    lib = B.load(STAMPS_LIB)   # every binding call below goes to the timing build
+    lib.attn_gated_stamps_set.argtypes = [ctypes.c_void_p]
+    lib.attn_gated_stamps_set.restype = ctypes.c_int
+    dev = "cuda:0"
+    g = gen.gated()
+    base = gen.to_device(g, dev)
+    nsets = 5   # 5 copies of the inputs (about 350 MB): each call reads its window from HBM
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+    out = torch.empty((g.rows, g.nh, g.hd), dtype=torch.float32, device=dev)
+    ws = B.Workspace(dev)
+    max_blocks = 4096
+    stamps = torch.zeros(max_blocks * 8 * GATED_WORDS, dtype=torch.int64, device=dev)
+    nqs = -(-g.rows * (g.nh // g.nk) // 64)
+    per_split = g.nk * nqs                   # workgroups per split index
+
+    def call(i):
+        t = sets[i % nsets]
+        B.attn_window_gated(t["yq"], t["yk"], t["yv"], t["rope"], t["q_scale"], t["gate"],
+                            t["gate_scale"], t["ring_k"], t["ring_v"], g.pos0, g.window, g.scale,
+                            g.eps, out=out, workspace=ws)
+
+    def set_ptr(ptr):
+        torch.cuda.synchronize()
+        if lib.attn_gated_stamps_set(ctypes.c_void_p(ptr)) != 0:
+            raise RuntimeError("attn_gated_stamps_set failed")
+        torch.cuda.synchronize()
+
+    set_ptr(0)
+    print("gated: warming up", file=sys.stderr, flush=True)
+    for i in range(200):
+        call(i)
+    groups = {"all waves": [], "split 0": [], "last split": []}
+    rel = {k: [[] for _ in GATED_PHASES] for k in groups}
+    ends, nsplit = [], 0
+    for r in range(calls):
+        stamps.zero_()
+        set_ptr(stamps.data_ptr())
+        for i in range(8):
+            call(r * 8 + i)
+        set_ptr(0)
+        t = stamps.cpu().numpy().reshape(max_blocks * 8, GATED_WORDS)
+        live = t[:, 0] != 0
+        waves = np.nonzero(live)[0]
+        split = (waves // 8) // per_split
+        nsplit = int(split.max()) + 1
+        t = t[live]
+        t0 = t[:, 0].min()
+        sel = {"all waves": np.ones(len(t), bool), "split 0": split == 0,
+               "last split": split == nsplit - 1}
+        for name, m in sel.items():
+            for k in range(len(GATED_PHASES)):
+                col = t[m, k]
+                rel[name][k].append((col[col != 0] - t0) * 0.01)
+        ends.append((t[:, :GATED_WORDS - 1].max() - t0) * 0.01)
+        print(f"recorded call {r + 1} of {calls}", file=sys.stderr, flush=True)
+
+    lines = [f"Gated call: {per_split * nsplit} workgroups of 8 waves ({nsplit} splits of each of "
+             f"{per_split} query blocks); {calls} recorded calls, each the last of 8 back-to-back "
+             f"calls on {nsets} rotating input sets. Times in us since the call's first wave "
+             "started (100 MHz counter), medians over the waves of each group that reached the "
+             "phase (split 0 holds the largest share of key blocks; the last split also makes "
+             "the chunk rows' unit keys and gathers).",
+             "",
+             "| phase | waves | min | p50 all | p90 all | max | p50 split 0 | p50 last split | meaning |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for k, (name, meaning) in enumerate(GATED_PHASES):
+        v = np.concatenate(rel["all waves"][k])
+        if len(v) == 0:
+            continue
+        s0 = np.concatenate(rel["split 0"][k])
+        sl = np.concatenate(rel["last split"][k])
+        f = lambda a: f"{np.median(a):.2f}" if len(a) else "—"
+        lines.append(f"| {name} | {len(v)} | {v.min():.2f} | {np.median(v):.2f} | "
+                     f"{np.percentile(v, 90):.2f} | {v.max():.2f} | {f(s0)} | {f(sl)} | {meaning} |")
+    e = np.array(ends)
+    lines += ["", f"First wave start to last stamp: median {np.median(e):.2f} us "
+              f"(min {e.min():.2f}, max {e.max():.2f})."]
+    return "\n".join(lines)
+
+
 if __name__ == "__main__":
-    if len(sys.argv) < 2 or sys.argv[1] not in ("build", "run"):
+    if len(sys.argv) < 2 or sys.argv[1] not in ("build", "run", "gated"):
         raise SystemExit(__doc__)
     if sys.argv[1] == "build":
         print(build())
-    else:
+    elif sys.argv[1] == "run":
         print(run(int(sys.argv[2]) if len(sys.argv) > 2 else 10))
+    else:
+        print(run_gated(int(sys.argv[2]) if len(sys.argv) > 2 else 10))

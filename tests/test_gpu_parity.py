@@ -331,6 +331,8 @@ GATED_SWEEP = [
     (80, 3, 200, 100, 8, 2, 256),        # windows clipped at position 0
     (70, 100, 300, 30, 8, 8, 192),       # more rows than the window, one head per KV head
     (64, 5, 128, 48, 16, 4, 224),
+    (64, 300, 512, 64, 64, 16, 256),     # 64 blocks: 2 gatherers per block, 4 items per thread
+    (64, 300, 192, 64, 128, 32, 256),    # 128 blocks: 1 gatherer per block, 8 items per thread
 ]
 
 # plans of the gated call: automatic; the single launch with one, the automatic and many

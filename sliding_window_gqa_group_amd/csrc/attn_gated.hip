@@ -502,12 +502,14 @@ constexpr int kGKST = 256 + 4;    // LDS row stride (floats)
 // set that pointer (attn_gated_stamps_set). The kernel's work is unchanged.
 //   0 start, 1 queries in registers, 2 tile 0 in LDS, 3 tile 0 done, 4 tile 1 in LDS,
 //   5 tile 1 done, 6 every tile done, 7 key halves folded, 8 flags raised (non-gatherers end),
-//   9 every flag seen (gatherers), 10 outputs stored and drained (gatherers, single splits)
+//   9 every flag seen (gatherers), 10 outputs stored and drained (gatherers, single splits);
+//   then the XCD, and the shader-clock counter at the start and when the stamps are written
 #ifdef WINATTN_PHASE_STAMPS
-constexpr int kGatedStampWords = 12;
+constexpr int kGatedStampWords = 14;
 __device__ unsigned long long* g_gated_stamps;
 struct GatedStamps {
-    unsigned long long t[kGatedStampWords - 1] = {};
+    unsigned long long t[11] = {};
+    unsigned long long clk0 = __builtin_amdgcn_s_memtime();
     __device__ void mark(int k) { t[k] = __builtin_amdgcn_s_memrealtime(); }
     template <class V>
     __device__ void mark_after(int k, const V& v) {
@@ -521,9 +523,12 @@ struct GatedStamps {
     __device__ void flush(int tid) {
         unsigned long long* o = g_gated_stamps;
         if (!o || (tid & 63) != 0) return;
+        const unsigned long long clk1 = __builtin_amdgcn_s_memtime();
         o += ((size_t)blockIdx.x * 8 + tid / 64) * kGatedStampWords;
-        for (int k = 0; k < kGatedStampWords - 1; ++k) o[k] = t[k];
-        o[kGatedStampWords - 1] = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11));   // XCC_ID
+        for (int k = 0; k < 11; ++k) o[k] = t[k];
+        o[11] = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11));   // XCC_ID
+        o[12] = clk0;
+        o[13] = clk1;
     }
 };
 #else

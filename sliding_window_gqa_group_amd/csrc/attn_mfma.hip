@@ -27,6 +27,14 @@ namespace winattn {
 constexpr int kMfmaQB = 128;
 constexpr int kMfmaTK = 32;
 
+#ifdef WINATTN_PHASE_STAMPS
+// Timing builds only: thread 0 of every workgroup records the 100 MHz real-time counter and the
+// shader-clock counter when the workgroup starts and when its last tile is done, as
+// g_mfma_clock[block][4] = {real0, clock0, real1, clock1} (attn_mfma_clock_set), from which
+// the clock the matrix cores ran at follows.
+__device__ unsigned long long* g_mfma_clock;
+#endif
+
 template <int D, bool GATED>
 __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(const AttnParams p) {
     constexpr int TK = kMfmaTK, QB = kMfmaQB;
@@ -58,6 +66,9 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int qcol = lane & 31, hb = lane >> 5;
+#ifdef WINATTN_PHASE_STAMPS
+    const unsigned long long ck_real0 = __builtin_amdgcn_s_memrealtime(), ck_clk0 = __builtin_amdgcn_s_memtime();
+#endif
     const int nq_tot = p.rows * p.hpg;
     const int q0 = qb * QB;
     const int nq = min(QB, nq_tot - q0);
@@ -212,6 +223,17 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_mfma_kernel(c
         }
     }
 
+#ifdef WINATTN_PHASE_STAMPS
+    if (g_mfma_clock && tid == 0) {
+        asm volatile("" : : "v"(oacc[0][0]), "v"(lrun));
+        const unsigned long long real1 = __builtin_amdgcn_s_memrealtime(), clk1 = __builtin_amdgcn_s_memtime();
+        unsigned long long* o = g_mfma_clock + (size_t)blockIdx.x * 4;
+        o[0] = ck_real0;
+        o[1] = ck_clk0;
+        o[2] = real1;
+        o[3] = clk1;
+    }
+#endif
     // Lane holds, for its query, d = 32b + 8m + 4*hb + (0..3) in oacc[b][4m .. 4m+3].
     const int blk = g * p.nqblocks + qb;
     if (nsplit == 1 && !p.merge_kernel) {
@@ -295,3 +317,13 @@ int mfma_query_block() { return kMfmaQB; }
 int mfma_tile_keys() { return kMfmaTK; }
 
 }  // namespace winattn
+
+#ifdef WINATTN_PHASE_STAMPS
+// Timing builds: where the 32x32 matrix-core kernel records its clock readings (NULL: nowhere);
+// 4 u64 per workgroup of the launch, each launch overwrites them.
+extern "C" int attn_mfma_clock_set(void* device_ptr) {
+    return hipMemcpyToSymbol(HIP_SYMBOL(winattn::g_mfma_clock), &device_ptr, sizeof(device_ptr)) == hipSuccess
+               ? 0
+               : -3;
+}
+#endif

@@ -3,6 +3,7 @@
     python -m sliding_window_gqa_group_amd.phase_stamps build             # any host: compiles
     python -m sliding_window_gqa_group_amd.phase_stamps run [calls]       # GPU: decode table
     python -m sliding_window_gqa_group_amd.phase_stamps gated [calls]     # GPU: gated table
+    python -m sliding_window_gqa_group_amd.phase_stamps clock [calls]     # GPU: prefill/large clock
 
 `build` compiles the library a second time with WINATTN_PHASE_STAMPS defined, into
 libwinattn_stamps.so beside the normal one (the normal library has no stamp code). `run` loads
@@ -12,7 +13,9 @@ the last of 8 back-to-back calls, as in the bench's timed loop; every wave of it
 100 MHz real-time counter at its phase boundaries. The report gives, per phase, the spread over
 all waves of the recorded calls of the time since the call's first wave started. `gated` does
 the same for the gated workload's single launch (64 rows at pos0 20000, 16 query heads over 4
-KV heads, hd 256, window 1024) on its rotating input sets.
+KV heads, hd 256, window 1024) on its rotating input sets, and reports the shader clock the waves
+ran at (the shader-clock counter over the real-time counter). `clock` reports that clock for the
+32x32 matrix-core kernel on the prefill and large workloads (one reading per workgroup).
 """
 from __future__ import annotations
 
@@ -121,7 +124,7 @@ def run(calls: int = 10) -> str:
     return "\n".join(lines)
 
 
-GATED_WORDS = 12   # u64 per wave: 11 phase stamps, then the XCD number
+GATED_WORDS = 14   # u64 per wave: 11 phase stamps, the XCD number, the shader clock at start and end
 GATED_PHASES = [
     ("start", "the wave starts"),
     ("queries", "the block's unit queries are in the wave's registers (tile 0 requested)"),
@@ -176,7 +179,7 @@ def run_gated(calls: int = 10) -> str:
         call(i)
     groups = {"all waves": [], "split 0": [], "last split": []}
     rel = {k: [[] for _ in GATED_PHASES] for k in groups}
-    ends, nsplit = [], 0
+    ends, nsplit, clocks = [], 0, []
     for r in range(calls):
         stamps.zero_()
         set_ptr(stamps.data_ptr())
@@ -190,13 +193,17 @@ def run_gated(calls: int = 10) -> str:
         nsplit = int(split.max()) + 1
         t = t[live]
         t0 = t[:, 0].min()
+        # shader clock of each wave: clock cycles over real time from its start to its last stamp
+        last = t[:, :11].max(axis=1)
+        dt = (last - t[:, 0]) * 1e-8
+        clocks.append(((t[:, 13] - t[:, 12]) / np.where(dt > 0, dt, np.nan)) * 1e-9)
         sel = {"all waves": np.ones(len(t), bool), "split 0": split == 0,
                "last split": split == nsplit - 1}
         for name, m in sel.items():
             for k in range(len(GATED_PHASES)):
                 col = t[m, k]
                 rel[name][k].append((col[col != 0] - t0) * 0.01)
-        ends.append((t[:, :GATED_WORDS - 1].max() - t0) * 0.01)
+        ends.append((t[:, :11].max() - t0) * 0.01)
         print(f"recorded call {r + 1} of {calls}", file=sys.stderr, flush=True)
 
     lines = [f"Gated call: {per_split * nsplit} workgroups of 8 waves ({nsplit} splits of each of "
@@ -218,17 +225,80 @@ def run_gated(calls: int = 10) -> str:
         lines.append(f"| {name} | {len(v)} | {v.min():.2f} | {np.median(v):.2f} | "
                      f"{np.percentile(v, 90):.2f} | {v.max():.2f} | {f(s0)} | {f(sl)} | {meaning} |")
     e = np.array(ends)
+    c = np.concatenate(clocks)
+    c = c[np.isfinite(c)]
     lines += ["", f"First wave start to last stamp: median {np.median(e):.2f} us "
-              f"(min {e.min():.2f}, max {e.max():.2f})."]
+              f"(min {e.min():.2f}, max {e.max():.2f}).",
+              f"Shader clock over each wave's life (shader-clock counter over the 100 MHz counter): "
+              f"median {np.median(c):.3f} GHz (p10 {np.percentile(c, 10):.3f}, p90 {np.percentile(c, 90):.3f})."]
+    return "\n".join(lines)
+
+
+def run_clock(calls: int = 5) -> str:
+    """The shader clock while the 32x32 matrix-core kernel runs the prefill and large workloads."""
+    sys.path.insert(0, os.path.dirname(HERE))
+    import numpy as np
+    import torch
+    from sliding_window_gqa_group_amd import binding as B, inputs as gen
+
+    lib = B.load(STAMPS_LIB)
+    lib.attn_mfma_clock_set.argtypes = [ctypes.c_void_p]
+    lib.attn_mfma_clock_set.restype = ctypes.c_int
+    dev = "cuda:0"
+    ws = B.Workspace(dev)
+    buf = torch.zeros(65536 * 4, dtype=torch.int64, device=dev)
+
+    def set_ptr(ptr):
+        torch.cuda.synchronize()
+        if lib.attn_mfma_clock_set(ctypes.c_void_p(ptr)) != 0:
+            raise RuntimeError("attn_mfma_clock_set failed")
+        torch.cuda.synchronize()
+
+    lines = ["| workload | workgroups | median clock | p10 | p90 | median workgroup life |",
+             "|---|---|---|---|---|---|"]
+    for name, inp, warm in (("prefill", gen.prefill(), 50), ("large", gen.large(), 3)):
+        base = gen.to_device(inp, dev)
+        sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(1 if name == "large" else 4)]
+        out = torch.empty((inp.rows, inp.nh, inp.d), dtype=torch.float32, device=dev)
+
+        def call(i):
+            t = sets[i % len(sets)]
+            B.attn_window_chunk(t["ring_k"], t["ring_v"], t["meta"], t["sink_k"], t["sink_v"],
+                                t["q"], t["chunk_k"], t["chunk_v"], inp.scale, out=out, workspace=ws)
+
+        set_ptr(0)
+        for i in range(warm):
+            call(i)
+        cs, lives = [], []
+        for r in range(calls):
+            buf.zero_()
+            set_ptr(buf.data_ptr())
+            call(r)
+            set_ptr(0)
+            t = buf.cpu().numpy().reshape(-1, 4)
+            t = t[t[:, 0] != 0]
+            dt = (t[:, 2] - t[:, 0]) * 1e-8
+            ok = dt > 0
+            cs.append((t[ok, 3] - t[ok, 1]) / dt[ok] * 1e-9)
+            lives.append(dt[ok] * 1e6)
+        c, lv = np.concatenate(cs), np.concatenate(lives)
+        lines.append(f"| {name} | {len(c) // calls} | {np.median(c):.3f} GHz | {np.percentile(c, 10):.3f} | "
+                     f"{np.percentile(c, 90):.3f} | {np.median(lv):.1f} us |")
+        print(f"clock: {name} done", file=sys.stderr, flush=True)
+        del sets, base
+        torch.cuda.empty_cache()
     return "\n".join(lines)
 
 
 if __name__ == "__main__":
-    if len(sys.argv) < 2 or sys.argv[1] not in ("build", "run", "gated"):
+    if len(sys.argv) < 2 or sys.argv[1] not in ("build", "run", "gated", "clock"):
         raise SystemExit(__doc__)
+    n = int(sys.argv[2]) if len(sys.argv) > 2 else None
     if sys.argv[1] == "build":
         print(build())
     elif sys.argv[1] == "run":
-        print(run(int(sys.argv[2]) if len(sys.argv) > 2 else 10))
+        print(run(n or 10))
+    elif sys.argv[1] == "gated":
+        print(run_gated(n or 10))
     else:
-        print(run_gated(int(sys.argv[2]) if len(sys.argv) > 2 else 10))
+        print(run_clock(n or 5))

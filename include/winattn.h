@@ -74,7 +74,7 @@ typedef struct {
  *
  * Arguments (all device pointers):
  *   ring_k, ring_v   [ng][w][d]   ring storage; the slot stride is w even when wg < w
- *   meta             [ng][4] u32  attn_ring_meta per group; read only. Requirements (not
+ *   meta             [ng] attn_ring_meta (four u32 per group); read only. Requirements (not
  *                                 checked on the device: see attn_window_check_meta):
  *                                 window <= w, len <= wg, head < wg when len > 0. The kernels
  *                                 clamp out-of-range fields so they never read out of bounds;
@@ -86,7 +86,7 @@ typedef struct {
  *   rows, ng, hpg, w >= 1; ns >= 0; d a multiple of 4, 4 <= d <= 256; scale finite
  * Only `out` and the workspace are written.
  */
-int attn_window_chunk(const float* ring_k, const float* ring_v, const uint32_t* meta,
+int attn_window_chunk(const float* ring_k, const float* ring_v, const attn_ring_meta* meta,
                       const float* sink_k, const float* sink_v, const float* q,
                       const float* chunk_k, const float* chunk_v, float* out, int rows, int ng,
                       int hpg, int d, int w, int ns, float scale, void* workspace,
@@ -113,7 +113,7 @@ size_t attn_window_chunk_workspace(int rows, int ng, int hpg, int d, int w, int 
  * Returns as attn_window_chunk, plus WINATTN_ELAUNCH if the device array cannot be located.
  */
 #define WINATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
-int attn_window_chunk_noalloc(const float* ring_k, const float* ring_v, const uint32_t* meta,
+int attn_window_chunk_noalloc(const float* ring_k, const float* ring_v, const attn_ring_meta* meta,
                               const float* sink_k, const float* sink_v, const float* q,
                               const float* chunk_k, const float* chunk_v, float* out, int rows,
                               int ng, int hpg, int d, int w, int ns, float scale, void* stream);
@@ -173,7 +173,7 @@ int attn_window_gated(const float* yq, const float* yk, const float* yv, const f
  * the chunk's attention call on the same stream (that call reads the slots this one
  * overwrites). Invalid device meta is clamped as in attn_window_chunk. Returns 0,
  * WINATTN_EINVAL (nothing launched) or WINATTN_ELAUNCH. */
-int attn_window_commit(float* ring_k, float* ring_v, uint32_t* meta, const float* chunk_k,
+int attn_window_commit(float* ring_k, float* ring_v, attn_ring_meta* meta, const float* chunk_k,
                        const float* chunk_v, int rows, int ng, int d, int w, void* stream);
 
 /*
@@ -204,7 +204,7 @@ int attn_window_commit(float* ring_k, float* ring_v, uint32_t* meta, const float
  * rows; larger chunks or m return WINATTN_EUNSUPPORTED). The workspace is required (see
  * attn_window_chunk_far_workspace) and follows the convention above.
  */
-int attn_window_chunk_far(const float* ring_k, const float* ring_v, const uint32_t* meta,
+int attn_window_chunk_far(const float* ring_k, const float* ring_v, const attn_ring_meta* meta,
                           const float* sink_k, const float* sink_v, const float* q,
                           const float* chunk_k, const float* chunk_v, const float* k_tilde,
                           const float* q_tilde, const float* mu, const float* mz,
@@ -226,7 +226,7 @@ size_t attn_window_chunk_far_workspace(int rows, int ng, int hpg, int d, int w, 
  * chunk's attention call on the same stream. Returns 0, WINATTN_EINVAL, WINATTN_EUNSUPPORTED
  * (nothing launched) or WINATTN_ELAUNCH.
  */
-int attn_window_commit_far(float* ring_k, float* ring_v, uint32_t* meta, const float* chunk_k,
+int attn_window_commit_far(float* ring_k, float* ring_v, attn_ring_meta* meta, const float* chunk_k,
                            const float* chunk_v, const float* q_tilde, float* mz, float* t_hat,
                            int rows, int ng, int hpg, int d, int w, int m, float scale,
                            void* stream);
@@ -252,7 +252,7 @@ int attn_window_commit_far(float* ring_k, float* ring_v, uint32_t* meta, const f
  * rect 0 or 1. Workspace as attn_window_gated_far_workspace returns (always non-zero).
  */
 int attn_window_gated_far(const float* q, const float* ring_k, const float* ring_v,
-                          const uint32_t* meta, const float* sink_k, const float* sink_v,
+                          const attn_ring_meta* meta, const float* sink_k, const float* sink_v,
                           const float* k_tilde, const float* mu, const float* mz,
                           const float* t_hat, const float* gate, const float* gate_scale,
                           float* out, int nh, int nk, int hd, int w, int ns, int m, float scale,
@@ -293,7 +293,7 @@ int attn_workspace_init(void* workspace, size_t bytes, void* stream);
 
 /* Host-side check of ring metadata in HOST memory against the rules above: 0 if every group is
  * valid, WINATTN_EINVAL otherwise (also for a NULL pointer or ng, w < 1). */
-int attn_window_check_meta(const uint32_t* host_meta, int ng, int w);
+int attn_window_check_meta(const attn_ring_meta* host_meta, int ng, int w);
 
 /* Diagnostics: how attn_window_chunk would run these sizes. kernel = 1 (register-resident
  * split-K kernel, up to 8 query vectors per block, split merge in a second launch), 2 (f32

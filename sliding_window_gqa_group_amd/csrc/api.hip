@@ -11,6 +11,10 @@
 #include "launch.h"
 #include "winattn.h"
 
+// The kernels read ring metadata as four consecutive u32 per group.
+static_assert(sizeof(attn_ring_meta) == 4 * sizeof(uint32_t) && alignof(attn_ring_meta) == alignof(uint32_t),
+              "attn_ring_meta must be four packed u32");
+
 namespace winattn {
 namespace {
 
@@ -382,10 +386,10 @@ const char* attn_strerror(int code) {
     }
 }
 
-int attn_window_check_meta(const uint32_t* host_meta, int ng, int w) {
+int attn_window_check_meta(const attn_ring_meta* host_meta, int ng, int w) {
     if (!host_meta || ng < 1 || w < 1) return WINATTN_EINVAL;
     for (int g = 0; g < ng; ++g) {
-        const uint32_t len = host_meta[4 * g], head = host_meta[4 * g + 1], ov = host_meta[4 * g + 3];
+        const uint32_t len = host_meta[g].len, head = host_meta[g].head, ov = host_meta[g].window;
         if (ov > (uint32_t)w) return WINATTN_EINVAL;
         const uint32_t wg = ov != 0u ? ov : (uint32_t)w;
         if (len > wg) return WINATTN_EINVAL;
@@ -394,8 +398,9 @@ int attn_window_check_meta(const uint32_t* host_meta, int ng, int w) {
     return WINATTN_OK;
 }
 
-int attn_window_commit(float* ring_k, float* ring_v, uint32_t* meta, const float* chunk_k,
+int attn_window_commit(float* ring_k, float* ring_v, attn_ring_meta* meta_, const float* chunk_k,
                        const float* chunk_v, int rows, int ng, int d, int w, void* stream) {
+    uint32_t* meta = reinterpret_cast<uint32_t*>(meta_);
     if (!chunk_shape_ok(rows, ng, 1, d, w, 0)) return WINATTN_EINVAL;
     if (!ring_k || !ring_v || !meta || !chunk_k || !chunk_v) return WINATTN_EINVAL;
     if (!aligned16(ring_k) || !aligned16(ring_v) || !aligned16(chunk_k) || !aligned16(chunk_v) ||
@@ -467,11 +472,12 @@ long long chunk_call(const float* ring_k, const float* ring_v, const uint32_t* m
 
 extern "C" {
 
-int attn_window_chunk(const float* ring_k, const float* ring_v, const uint32_t* meta,
+int attn_window_chunk(const float* ring_k, const float* ring_v, const attn_ring_meta* meta_,
                       const float* sink_k, const float* sink_v, const float* q,
                       const float* chunk_k, const float* chunk_v, float* out, int rows, int ng,
                       int hpg, int d, int w, int ns, float scale, void* workspace,
                       size_t workspace_bytes, void* stream) {
+    const uint32_t* meta = reinterpret_cast<const uint32_t*>(meta_);
     return (int)chunk_call(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v, out, rows,
                            ng, hpg, d, w, ns, scale, workspace, workspace_bytes, stream, false);
 }
@@ -513,10 +519,11 @@ int scratch_on_current_device(void** ptr, hipStream_t stream) {
 
 extern "C" {
 
-int attn_window_chunk_noalloc(const float* ring_k, const float* ring_v, const uint32_t* meta,
+int attn_window_chunk_noalloc(const float* ring_k, const float* ring_v, const attn_ring_meta* meta_,
                               const float* sink_k, const float* sink_v, const float* q,
                               const float* chunk_k, const float* chunk_v, float* out, int rows,
                               int ng, int hpg, int d, int w, int ns, float scale, void* stream) {
+    const uint32_t* meta = reinterpret_cast<const uint32_t*>(meta_);
     const long long need = chunk_call(ring_k, ring_v, meta, sink_k, sink_v, q, chunk_k, chunk_v,
                                       out, rows, ng, hpg, d, w, ns, scale, nullptr, 0, stream, true);
     if (need < 0) return (int)need;
@@ -566,13 +573,14 @@ size_t attn_window_chunk_far_workspace(int rows, int ng, int hpg, int d, int w, 
     return make_far_plan(rows, ng, hpg, d, w, ns, m).bytes;
 }
 
-int attn_window_chunk_far(const float* ring_k, const float* ring_v, const uint32_t* meta,
+int attn_window_chunk_far(const float* ring_k, const float* ring_v, const attn_ring_meta* meta_,
                           const float* sink_k, const float* sink_v, const float* q,
                           const float* chunk_k, const float* chunk_v, const float* k_tilde,
                           const float* q_tilde, const float* mu, const float* mz,
                           const float* t_hat, float* out, int rows, int ng, int hpg, int d, int w,
                           int ns, int m, float scale, void* workspace, size_t workspace_bytes,
                           void* stream) {
+    const uint32_t* meta = reinterpret_cast<const uint32_t*>(meta_);
     if (!chunk_shape_ok(rows, ng, hpg, d, w, ns) || !std::isfinite(scale)) return WINATTN_EINVAL;
     if (m < 1) return WINATTN_EINVAL;
     if (!far_shape_ok(rows, m)) return WINATTN_EUNSUPPORTED;
@@ -654,10 +662,11 @@ int attn_window_chunk_far(const float* ring_k, const float* ring_v, const uint32
     return launch_attention(pl, p, false, ws, st, rows == 1 ? &f : nullptr);
 }
 
-int attn_window_commit_far(float* ring_k, float* ring_v, uint32_t* meta, const float* chunk_k,
+int attn_window_commit_far(float* ring_k, float* ring_v, attn_ring_meta* meta_, const float* chunk_k,
                            const float* chunk_v, const float* q_tilde, float* mz, float* t_hat,
                            int rows, int ng, int hpg, int d, int w, int m, float scale,
                            void* stream) {
+    uint32_t* meta = reinterpret_cast<uint32_t*>(meta_);
     if (!chunk_shape_ok(rows, ng, hpg, d, w, 0) || !std::isfinite(scale)) return WINATTN_EINVAL;
     if (m < 1) return WINATTN_EINVAL;
     if (!far_shape_ok(rows, m)) return WINATTN_EUNSUPPORTED;
@@ -697,11 +706,12 @@ size_t attn_window_gated_far_workspace(int nh, int nk, int hd, int w, int ns, in
 }
 
 int attn_window_gated_far(const float* q, const float* ring_k, const float* ring_v,
-                          const uint32_t* meta, const float* sink_k, const float* sink_v,
+                          const attn_ring_meta* meta_, const float* sink_k, const float* sink_v,
                           const float* k_tilde, const float* mu, const float* mz,
                           const float* t_hat, const float* gate, const float* gate_scale,
                           float* out, int nh, int nk, int hd, int w, int ns, int m, float scale,
                           int rect, void* workspace, size_t workspace_bytes, void* stream) {
+    const uint32_t* meta = reinterpret_cast<const uint32_t*>(meta_);
     if (nh < 1 || nk < 1 || nh % nk != 0 || !chunk_shape_ok(1, nk, nh / nk, hd, w, ns))
         return WINATTN_EINVAL;
     if (!std::isfinite(scale) || m < 1 || (rect != 0 && rect != 1)) return WINATTN_EINVAL;

@@ -37,14 +37,18 @@ def _rotating(torch, base: dict):
 
 
 def _time(torch, fn, n_sets: int, steps: int) -> float:
-    """us per call: untimed calls for at least WARM_S of wall time (clocks up, code and buffers
-    touched), then `steps` back-to-back calls between two events."""
+    """us per call: rounds of n_sets untimed calls, each waited for, until WARM_S of wall time
+    has passed (clocks up, code and buffers touched; waiting per round keeps the queue from
+    holding seconds of calls), then `steps` back-to-back calls between two events."""
     import time
     t0, i = time.perf_counter(), 0
-    while time.perf_counter() - t0 < WARM_S or i < n_sets:
-        fn(i)
-        i += 1
-    torch.cuda.synchronize()
+    while True:
+        for _ in range(n_sets):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= WARM_S:
+            break
     stream = torch.cuda.current_stream()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

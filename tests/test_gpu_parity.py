@@ -216,6 +216,48 @@ def test_sweep(shape, variant):
     assert_close(got, ref, f"{shape} {variant}")
 
 
+# Shapes on which the matrix-core launch takes its paired order under the whole-groups-per-XCD
+# work order (the second half of each XCD's workgroups mirror their query blocks): items per
+# XCD a multiple of twice the query blocks, with invalid items at the end of the last XCD's
+# range. Checked against the oracle and bitwise against the round-robin order (the same splits
+# merged in the same order), with the merge in the last split and in its own launch.
+PAIRED = [
+    # rows, ng, hpg, d, w, ns, meta kind, tiles per split
+    (64, 5, 4, 128, 200, 4, "mix", 3),      # 2 query blocks, 3 splits: 4 items per XCD, 2 invalid
+    (96, 3, 4, 64, 400, 2, "partial", 3),   # 3 blocks, 5 splits: 6 per XCD, 3 invalid
+    (64, 7, 4, 128, 150, 3, "full", 3),     # 2 blocks, 2 splits: 4 per XCD, 4 invalid
+    (128, 3, 4, 128, 260, 2, "mix", 2),     # 4 blocks, 5 splits: 8 per XCD, 4 invalid
+]
+
+
+@pytest.mark.parametrize("merge", [1, 2], ids=["merge_in_kernel", "merge_launch"])
+@pytest.mark.parametrize("shape", PAIRED, ids=[f"r{s[0]}g{s[1]}d{s[3]}w{s[4]}t{s[7]}" for s in PAIRED])
+def test_paired_order(shape, merge):
+    rows, ng, hpg, d, w, ns, kind, tps = shape
+    _case(f"paired order {shape} merge {merge}")
+    rng = np.random.default_rng(zlib.crc32(repr((shape, "paired")).encode()))
+    inp = gen.make_chunk(rows, ng, hpg, d, w, ns, _rand_meta(rng, ng, w, kind),
+                         seed=int(rng.integers(1 << 30)))
+    ref = oracle.window_chunk(inp)
+    knobs = {B.TUNE_FORCE_KERNEL: 2, B.TUNE_TILES_PER_SPLIT: tps, B.TUNE_MERGE_KERNEL: merge}
+    got = {}
+    try:
+        for knob, val in knobs.items():
+            B.tuning_set(knob, val)
+        for order in (2, 1):   # knob value - 1 = xcd_map
+            B.tuning_set(B.TUNE_XCD_MAP, order)
+            plan = B.chunk_plan(rows, ng, hpg, d, w, ns)
+            nqb = -(-rows * hpg // 128)
+            per_xcd = -(-plan[2] * nqb * ng // 8)
+            assert plan[0] == 2 and per_xcd % (2 * nqb) == 0 and 8 * per_xcd > plan[2] * nqb * ng, plan
+            got[order] = gpu_chunk(inp).cpu().numpy()
+    finally:
+        for knob in list(knobs) + [B.TUNE_XCD_MAP]:
+            B.tuning_set(knob, 0)
+    assert_close(got[2], ref, f"{shape} paired order")
+    assert np.array_equal(got[2], got[1]), "paired and round-robin orders differ"
+
+
 # The register kernel runs splits of at most three tiles (split 0 also carries the sink tiles) as
 # a straight-line instance and longer ones as a two-buffer loop (its tile is 4096 / d keys):
 # both instances, one or two sink tiles, and both merge paths.

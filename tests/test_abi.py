@@ -265,6 +265,12 @@ def test_tuning_knobs_change_the_plan(lib):
         assert B.chunk_plan(1, 8, 4, 128, 4096, 4) == (5, 4, 32, 128)
         assert B.chunk_plan(2, 8, 4, 128, 4096, 4) == (5, 8, 64, 64)   # capped at two tiles
         assert B.chunk_plan(512, 8, 4, 128, 4096, 4)[0] == 2   # too many queries: automatic
+        # the slot-order kernel's limits: 128 splits per group (two 64-bit masks of splits per
+        # gatherer lane), 128 waiting gatherers over all groups
+        B.tuning_set(B.TUNE_TILES_PER_SPLIT, 1)
+        assert B.chunk_plan(1, 1, 4, 64, 8192, 2) == (5, 4, 128, 64)
+        assert B.chunk_plan(1, 2, 4, 64, 8256, 2)[:3] == (1, 4, 129)   # 129 splits: another kernel
+        assert B.chunk_plan(1, 16, 4, 128, 1024, 4) == (5, 4, 32, 32)   # 16 groups x 8 gatherers
     finally:
         B.tuning_set(B.TUNE_FORCE_KERNEL, 0)
         B.tuning_set(B.TUNE_TILES_PER_SPLIT, 0)

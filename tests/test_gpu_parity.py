@@ -318,6 +318,9 @@ SLOT_ORDER_CASES = [
     (6, 2, 1, 64, 8, 2, "override", 1),      # chunk longer than its group's window
     (1, 3, 4, 256, 5000, 2, "mix", 4),       # a long ring: 79 splits
     (1, 1, 4, 64, 16, 2, "full", 1),         # one split: no partials, output stored directly
+    (1, 1, 4, 64, 8192, 2, "full", 1),       # 128 splits, the most the kernel takes
+    (1, 16, 4, 128, 1024, 4, "mix", 1),      # 16 groups x 8 gatherers: 128 waiting, the cap
+    (2, 16, 4, 128, 2048, 4, "partial", 2),  # 8 queries per block over 16 groups
 ]
 
 

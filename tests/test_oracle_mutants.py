@@ -34,6 +34,11 @@ MUTANTS = [
      "const float *qv = q + ((size_t)0 * nh + gh) * d;"),
     ("rotation sign", "double u = x * c - y * s, v = y * c + x * s;",
      "double u = x * c + y * s, v = y * c - x * s;"),
+    ("sine of the neighbouring pair", "double c = rope_row[e], s = rope_row[half + e];",
+     "double c = rope_row[e], s = rope_row[half + (e + 1) % half];"),
+    ("key rotated with the previous row's table",
+     "rotate_unit(yk + ((size_t)r * nk + kh) * hd, rope + (size_t)r * hd, hd, (double)eps, tmp);",
+     "rotate_unit(yk + ((size_t)r * nk + kh) * hd, rope + (size_t)(r > 0 ? r - 1 : 0) * hd, hd, (double)eps, tmp);"),
     ("eps outside the square root", "double inv = 1.0 / sqrt(ss + eps);",
      "double inv = 1.0 / (sqrt(ss) + eps);"),
     ("gate sign", "z[e] = (float)(acc[e] / (1.0 + exp(-gs)));",

@@ -481,6 +481,42 @@ def test_gated_rotation_preserves_norm():
             assert float(np.dot(k, k)) == pytest.approx(1.0, abs=1e-6)
 
 
+def test_rope_table_angle_steps_follow_the_frequency_law():
+    """The rotation table's pair i (cos in column i, sin in column i + hd/2) turns by
+    base^(-2i/hd) radians from one position to the next, read back from consecutive rows with
+    atan2 (the f32 entries hold each angle to about 1e-7), and every pair lies on the unit
+    circle. Every frequency is at most 1 radian, so the wrapped steps are the frequencies."""
+    hd, base = 64, 10000.0
+    t = gen.rope_table(9, 123, hd, base).astype(np.float64)
+    half = hd // 2
+    ang = np.arctan2(t[:, half:], t[:, :half])
+    step = np.angle(np.exp(1j * (ang[1:] - ang[:-1])))
+    freq = base ** (-2.0 * np.arange(half) / hd)
+    np.testing.assert_allclose(step, np.broadcast_to(freq, step.shape), rtol=0, atol=1e-6)
+    np.testing.assert_allclose(t[:, :half] ** 2 + t[:, half:] ** 2, 1.0, rtol=0, atol=1e-6)
+
+
+def test_gated_output_depends_on_relative_positions_only():
+    """With pos0 = 0 every key a row sees is a chunk row, rotated by the same table as the
+    queries. With a query scale that is constant per head (the learned per-element scale does
+    not commute with the rotation), scores <s R(p) q, R(p') k> depend on p - p' only: the
+    table of positions c .. c + rows - 1 in place of 0 .. rows - 1 leaves the output unchanged
+    up to the f32 rounding of the table. Rotating queries and keys by different pairings or
+    angles, or only one of them, breaks this."""
+    inp = gen.make_gated(6, 0, 16, 8, 4, 2, 16, seed=75, scale=0.8)
+    inp.q_scale[:] = inp.q_scale[:, :1]
+    z0, _, _ = oracle.window_gated(inp)
+    for c in (1, 37, 1000):
+        inp.rope = gen.rope_table(inp.rows, c, inp.hd)
+        z1, _, _ = oracle.window_gated(inp)
+        np.testing.assert_allclose(z1, z0, rtol=1e-5, atol=1e-7)
+    # not vacuous: without rotation (the identity table) the relative angles are gone and the
+    # output changes
+    inp.rope[:, :inp.hd // 2] = 1.0
+    inp.rope[:, inp.hd // 2:] = 0.0
+    assert not np.allclose(oracle.window_gated(inp)[0], z0, rtol=1e-3)
+
+
 def test_gated_zero_gate_is_half_of_chunk_attention():
     """gate = 0 gives z = attn / 2; the attention equals the chunk path on the prepped ring with
     ns = 0, window override = window, the ring tail as the ring and the new rows as the chunk."""

@@ -152,20 +152,21 @@ __device__ inline float lanes_sum_spaced(float v, int span) {
 // The group's last `nk` splits are its gatherers (the last of the group's workgroups in dispatch
 // order, so every split a gatherer waits for was dispatched before it, and the non-gatherers
 // never wait). Gatherer k owns output columns [k, k + 1) * D / (4 nk) float4 of every query of
-// the group: it reads only those columns of the group's nsplit partials, as their ready flags
-// rise, and folds them: c = max_s m_s, out = sum_s acc_s 2^(m_s - c) / sum_s l_s 2^(m_s - c)
-// (the token path's merge, `o1c_tok_merge`). One CU reads freshly written partials at only tens
-// of GB/s, so the merge is spread over nk CUs and most of it overlaps the other splits'
-// streaming; after the last flag only that split's columns remain to be read.
+// the group: it reads only those columns of the group's nsplit partials and folds them:
+// c = max_s m_s, out = sum_s acc_s 2^(m_s - c) / sum_s l_s 2^(m_s - c) (the token path's merge,
+// `o1c_tok_merge`). One CU reads freshly written partials at only tens of GB/s, so the merge is
+// spread over nk CUs, each reading a few KB.
 //  - Every split raises one flag per gatherer (flags[k][s]), so each gatherer polls and clears
 //    flags nobody else reads.
 //  - Each wave owns ipw = NQ * D / (4 nk) / waves (query j, float4 column c) items. Lane
 //    l = sub * ipw + item (ipw < 64) takes the splits s = sub (mod 64 / ipw) of its item, so the
 //    lanes of one item differ only in the bits above ipw and meet by cross-lane reductions, with
 //    no LDS and no barrier (ipw >= 64: a lane owns ipw / 64 items and every split of them).
-//  - A wave polls every flag of its gatherer (one device-scope load per lane, two rounds beyond
-//    64 splits); each lane then reads up to MB of its own newly ready splits per round, all
-//    loads of a round issued together with the next poll behind them.
+//  - A wave first polls every flag of its gatherer (one flag read per lane and 64 splits) until
+//    all are raised, then reads its splits' columns MB splits at a time, every load of a batch
+//    issued before any is used. Reading each partial as its flag rises instead measured 1 us
+//    slower per call: the bookkeeping of which splits are ready sits between seeing the last
+//    flag and requesting its columns, and the columns are too few for the overlap to pay.
 //  - The poll is bounded: after kGatherPolls rounds without every flag, the chunk is written as
 //    NaN rather than waiting longer (it cannot happen while every split runs).
 //  - After one barrier (every wave has left its poll loop and said whether it saw every flag in
@@ -194,8 +195,6 @@ __device__ inline void gather_chunk(const AttnParams& p, int g, int nsplit, int 
         __builtin_amdgcn_make_buffer_rsrc(p.pm + grp, 0, nsplit * NQ * 4, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rl =
         __builtin_amdgcn_make_buffer_rsrc(p.pl + grp, 0, nsplit * NQ * 4, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rf =
-        __builtin_amdgcn_make_buffer_rsrc(flags, 0, nsplit * 4, kBufferWord3);
 
     float cm[IPTM], cl[IPTM];
     vf4 ca[IPTM];
@@ -209,81 +208,58 @@ __device__ inline void gather_chunk(const AttnParams& p, int g, int nsplit, int 
         cl[it] = 0.0f;
         ca[it] = vf4{0.f, 0.f, 0.f, 0.f};
     }
-    // this lane's splits still awaited: s < nsplit and s = sub (mod nsub)
-    unsigned long long pend[2] = {0ull, 0ull};
-    for (int s = sub; s < nsplit; s += nsub) pend[s >> 6] |= 1ull << (s & 63);
-    unsigned fl[2];
-    auto poll = [&]() {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int s = min(h * 64 + lane, nsplit - 1);
-            fl[h] = __builtin_amdgcn_raw_buffer_load_b32(rf, s * 4, 0, kCachePolicyDevice);
-        }
-    };
-    poll();
-    unsigned long long todo[2] = {0ull, 0ull};   // ready, not yet read (this lane's splits)
+    // phase 1: every flag of this gatherer, polled until all are raised (pend: the splits not
+    // yet seen, bit s of word s / 64 in lane s % 64 of every lane)
+    unsigned long long pend[2] = {nsplit >= 64 ? ~0ull : (1ull << nsplit) - 1ull,
+                                  nsplit >= 128 ? ~0ull : (nsplit > 64 ? (1ull << (nsplit - 64)) - 1ull : 0ull)};
+    const int nw = nsplit > 64 ? 2 : 1;
     int polls = 0;
-    // wave-uniform loop: every lane of the wave leaves together
-    while (__builtin_amdgcn_ballot_w64((pend[0] | pend[1] | todo[0] | todo[1]) != 0ull) &&
-           polls < kGatherPolls) {
+    bool complete = false;
+    while (polls < kGatherPolls) {
         ++polls;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const unsigned long long r = __builtin_amdgcn_ballot_w64(fl[h] != 0u) & pend[h];
-            pend[h] &= ~r;
-            todo[h] |= r;
+        for (int h = 0; h < 2; ++h)
+            if (h < nw) pend[h] &= ~__builtin_amdgcn_ballot_w64(poll_flag(flags + min(h * 64 + lane, nsplit - 1)) != 0u);
+        if ((pend[0] | pend[1]) == 0ull) {   // wave-uniform (ballot results)
+            complete = true;
+            break;
         }
-        if (!__builtin_amdgcn_ballot_w64((todo[0] | todo[1]) != 0ull)) {
-            __builtin_amdgcn_s_sleep(2);
-            poll();
-            continue;
-        }
-        // up to MB of this lane's ready splits
-        int idx[MB];
-        int n = 0;
-#pragma unroll
-        for (int u = 0; u < MB; ++u) {
-            const bool any = (todo[0] | todo[1]) != 0ull;
-            const int h = todo[0] ? 0 : 1;
-            const unsigned long long word = h ? todo[1] : todo[0];
-            const int b = __builtin_ctzll(word | (any ? 0ull : 1ull));
-            idx[u] = any ? h * 64 + b : -1;
-            if (any) {
-                if (h) todo[1] &= todo[1] - 1ull; else todo[0] &= todo[0] - 1ull;
-            }
-            n += any ? 1 : 0;
-        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    // phase 2: this lane's splits s = sub + nsub i, MB at a time
+    for (int s0 = sub; complete && s0 < nsplit; s0 += MB * nsub) {
         float m[IPTM][MB], l[IPTM][MB];
         vf4 a[IPTM][MB];
 #pragma unroll
         for (int it = 0; it < IPTM; ++it) {
 #pragma unroll
             for (int u = 0; u < MB; ++u) {
-                const int su = idx[u] >= 0 ? idx[u] : 0;   // past n: dropped below
+                const int su = s0 + u * nsub;
                 const int at = su * NQ + jj[it];
-                m[it][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, at * 4, 0, kCachePolicyDevice));
-                l[it][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, at * 4, 0, kCachePolicyDevice));
-                a[it][u] = __builtin_bit_cast(
-                    vf4, __builtin_amdgcn_raw_buffer_load_b128(racc, (at * D + 4 * cc[it]) * 4, 0, kCachePolicyDevice));
+                m[it][u] = -INFINITY;   // past the lane's splits: no keys
+                l[it][u] = 0.0f;
+                a[it][u] = vf4{0.f, 0.f, 0.f, 0.f};
+                if (su < nsplit) {
+                    m[it][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, at * 4, 0, kCachePolicyDevice));
+                    l[it][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, at * 4, 0, kCachePolicyDevice));
+                    a[it][u] = __builtin_bit_cast(
+                        vf4, __builtin_amdgcn_raw_buffer_load_b128(racc, (at * D + 4 * cc[it]) * 4, 0, kCachePolicyDevice));
+                }
             }
         }
-        if (__builtin_amdgcn_ballot_w64((pend[0] | pend[1]) != 0ull)) poll();   // behind the batch
 #pragma unroll
         for (int it = 0; it < IPTM; ++it) {
             if (it >= ipt) break;
             float bm = -INFINITY;
 #pragma unroll
-            for (int u = 0; u < MB; ++u) {
-                m[it][u] = u < n ? m[it][u] : -INFINITY;   // a split with no keys is -inf too
-                bm = fmaxf(bm, m[it][u]);
-            }
+            for (int u = 0; u < MB; ++u) bm = fmaxf(bm, m[it][u]);
             const float nm = fmaxf(cm[it], bm), mu = safe_max(nm);
             const float f0 = __builtin_amdgcn_exp2f(cm[it] - mu);
             cl[it] *= f0;
             ca[it] *= f0;
 #pragma unroll
             for (int u = 0; u < MB; ++u) {
-                const bool real = m[it][u] > -INFINITY;
+                const bool real = m[it][u] > -INFINITY;   // a split with no keys is -inf too
                 const float f = __builtin_amdgcn_exp2f(m[it][u] - mu);
                 cl[it] += (real ? l[it][u] : 0.0f) * f;
                 ca[it] += (real ? a[it][u] : vf4{0.f, 0.f, 0.f, 0.f}) * f;
@@ -291,7 +267,6 @@ __device__ inline void gather_chunk(const AttnParams& p, int g, int nsplit, int 
             cm[it] = nm;
         }
     }
-    const bool complete = !__builtin_amdgcn_ballot_w64((pend[0] | pend[1] | todo[0] | todo[1]) != 0ull);
 
     // the lanes of each item meet: c = max over them, then the rescaled sums
 #pragma unroll

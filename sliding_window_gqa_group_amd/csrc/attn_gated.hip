@@ -426,7 +426,6 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_gated_kernel(const GatedFused
     }
 
     // ---- the gatherer: each wave polls the set's flags and folds its columns
-    const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc(flags, 0, last * 4, kBufferWord3);
     const __amdgpu_buffer_rsrc_t racc =
         __builtin_amdgcn_make_buffer_rsrc(p.pacc + item0 * 16 * 256, 0, last * 16 * 256 * 4, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(p.pm + item0 * 16, 0, last * 16 * 4, kBufferWord3);
@@ -435,7 +434,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_gated_kernel(const GatedFused
     int polls = 0;
     while (pend != 0ull && polls < kGatedPolls) {
         ++polls;
-        const unsigned f = __builtin_amdgcn_raw_buffer_load_b32(rf, min(lane, last - 1) * 4, 0, kCachePolicyDevice);
+        const unsigned f = poll_flag(flags + min(lane, last - 1));
         unsigned long long ready = __builtin_amdgcn_ballot_w64(f != 0u && lane < last) & pend;
         if (ready == 0ull) {
             __builtin_amdgcn_s_sleep(2);
@@ -933,7 +932,6 @@ __global__ __launch_bounds__(512, 1) void attn_gated_tiles_kernel(const GatedFus
     // time, all requested before any is used, and fold them in split order.
     const int cw4 = 64 / G;                    // float4 columns per gatherer
     unsigned int* gflags = flags + k * S;
-    const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc(gflags, 0, S * 4, kBufferWord3);
     const long long item0 = (long long)qbg * S;
     const __amdgpu_buffer_rsrc_t racc =
         __builtin_amdgcn_make_buffer_rsrc(p.pacc + item0 * QB * 256, 0, S * QB * 256 * 4, kBufferWord3);
@@ -978,7 +976,7 @@ __global__ __launch_bounds__(512, 1) void attn_gated_tiles_kernel(const GatedFus
         const bool early = kEarly && S <= 16;
         while (pend != 0ull && polls < kGatedPolls) {
             ++polls;
-            const unsigned f = __builtin_amdgcn_raw_buffer_load_b32(rf, min(lane, S - 1) * 4, 0, kCachePolicyDevice);
+            const unsigned f = poll_flag(gflags + min(lane, S - 1));
             const unsigned long long ready = __builtin_amdgcn_ballot_w64(f != 0u && lane < S) & pend;
             pend &= ~ready;
             if constexpr (kEarly) {

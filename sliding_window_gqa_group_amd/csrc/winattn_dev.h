@@ -332,6 +332,13 @@ __device__ inline void store_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A ready flag as a poll loop reads it: a relaxed agent-scope atomic load, coherent at device
+// scope and, unlike a plain or buffer load, never hoisted out of the loop or merged with an
+// earlier read of the same flag by the compiler.
+__device__ inline unsigned poll_flag(const unsigned int* f) {
+    return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // After every split of a query block has written its partial (m, l, acc), the last one to
 // arrive combines them: c = max_s m_s, out = sum_s acc_s 2^(m_s - c) / sum_s l_s 2^(m_s - c)
 // (the token path's partial merge, `o1c_tok_merge`). All threads of the block call it after

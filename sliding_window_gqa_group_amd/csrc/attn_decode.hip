@@ -167,10 +167,11 @@ __device__ inline float lanes_sum_spaced(float v, int span) {
 //    issued before any is used. Reading each partial as its flag rises instead measured 1 us
 //    slower per call: the bookkeeping of which splits are ready sits between seeing the last
 //    flag and requesting its columns, and the columns are too few for the overlap to pay.
-//  - The poll is bounded: after kGatherPolls rounds without every flag, the chunk is written as
-//    NaN rather than waiting longer (it cannot happen while every split runs).
-//  - After one barrier (every wave has left its poll loop and said whether it saw every flag in
-//    `scratch`, NT / 64 words), the gatherer's flags are cleared for the next call.
+//  - The poll is bounded: after kGatherPolls rounds without every flag, a wave writes its items
+//    as NaN rather than waiting longer (it cannot happen while every split runs).
+//  - Each wave stores its items as soon as they are folded. After one barrier (every wave has
+//    left its poll loop and said whether it saw every flag in `scratch`, NT / 64 words), the
+//    gatherer's flags are cleared for the next call if every wave saw them all.
 constexpr int kGatherPolls = 1 << 18;
 
 template <int NQ, int D, int NT>
@@ -280,20 +281,22 @@ __device__ inline void gather_chunk(const AttnParams& p, int g, int nsplit, int 
         ca[it].z = lanes_sum_spaced(ca[it].z * f, span);
         ca[it].w = lanes_sum_spaced(ca[it].w * f, span);
     }
-    if (lane == 0) scratch[wave] = complete ? 1 : 0;
-    __syncthreads();   // every wave has left its poll loop
-    bool bad = false;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) bad |= scratch[w] == 0;
+    // each wave stores its items at once (NaN if it gave up on a flag); the barrier only
+    // guards the flag clearing below
     if (sub == 0) {
 #pragma unroll
         for (int it = 0; it < IPTM; ++it) {
             if (it >= ipt || jj[it] >= nq || cc[it] >= p.d / 4) continue;
             vf4 o = ca[it] * (1.0f / fmaxf(cl[it], 1e-30f));
-            if (bad) o = vf4{NAN, NAN, NAN, NAN};
+            if (!complete) o = vf4{NAN, NAN, NAN, NAN};
             store_out<false>(p, jj[it], g, 4 * cc[it], make_float4(o.x, o.y, o.z, o.w));
         }
     }
+    if (lane == 0) scratch[wave] = complete ? 1 : 0;
+    __syncthreads();   // every wave has left its poll loop
+    bool bad = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) bad |= scratch[w] == 0;
     // this gatherer's flags back to zero for the next call
     if (!bad && tid < 64) {
 #pragma unroll

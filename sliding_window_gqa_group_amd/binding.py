@@ -85,6 +85,7 @@ def load(path: str = LIB_PATH):
     lib.attn_abi_version.argtypes = []
     lib.attn_abi_version.restype = _i
     _lib = lib
+    _ws_sizes.clear()
     return lib
 
 
@@ -103,18 +104,32 @@ def abi_version() -> int:
     return load().attn_abi_version()
 
 
+# Workspace sizes by call shape: they depend only on the shape and the tuning knobs, so they are
+# asked of the library once per shape (cleared when a knob changes or a library is loaded).
+_ws_sizes = {}
+
+
 def tuning_set(knob: int, value: int) -> None:
     rc = load().attn_tuning_set(knob, value)
+    _ws_sizes.clear()
     if rc != OK:
         raise WinattnError("attn_tuning_set", rc)
 
 
 def chunk_workspace_bytes(rows, ng, hpg, d, w, ns) -> int:
-    return int(load().attn_window_chunk_workspace(rows, ng, hpg, d, w, ns))
+    key = ("chunk", rows, ng, hpg, d, w, ns)
+    n = _ws_sizes.get(key)
+    if n is None:
+        n = _ws_sizes[key] = int(load().attn_window_chunk_workspace(rows, ng, hpg, d, w, ns))
+    return n
 
 
 def gated_workspace_bytes(rows, nh, nk, hd, window) -> int:
-    return int(load().attn_window_gated_workspace(rows, nh, nk, hd, window))
+    key = ("gated", rows, nh, nk, hd, window)
+    n = _ws_sizes.get(key)
+    if n is None:
+        n = _ws_sizes[key] = int(load().attn_window_gated_workspace(rows, nh, nk, hd, window))
+    return n
 
 
 def chunk_far_workspace_bytes(rows, ng, hpg, d, w, ns, m) -> int:
@@ -182,8 +197,17 @@ def _ptr(t, name, dtypes=(torch.float32,)):
     return t.data_ptr()
 
 
+# torch's current stream of a device as a raw handle, without building a Stream object (that
+# costs about 2 us per call, as much as the rest of the argument marshalling); the public route
+# where this torch build has no such accessor.
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_ptr(stream, device):
     if stream is None:
+        if _raw_current_stream is not None:
+            idx = device.index if device.index is not None else torch.cuda.current_device()
+            return _raw_current_stream(idx)
         stream = torch.cuda.current_stream(device)
     return stream.cuda_stream
 

@@ -24,9 +24,9 @@
 //    running max, sum and accumulator per query, merged once through LDS at the end.
 //  - One launch. Each split writes its partial (max, sum, accumulator per query) with
 //    device-scope stores, waits for them to complete and raises ready flags; the group's last
-//    few splits each gather one column chunk of every partial as the flags rise and fold them
-//    (the token path's merge rule), so most of the merge overlaps the streaming and no CU reads
-//    more than its share. No second kernel, no kernel boundary, no read-modify-write.
+//    few splits each wait for every flag, then read one column chunk of every partial in one
+//    batch and fold it (the token path's merge rule), so no CU reads more than its share. No
+//    second kernel, no kernel boundary, no read-modify-write.
 //  - Work order: workgroup b takes group b mod ng, split b / ng. Workgroups are dealt to the 8
 //    XCDs round-robin, so with 8 groups every split of a group runs on one XCD, next to the
 //    partials its merge reads.

@@ -39,19 +39,16 @@ struct DecShape {
 };
 
 // Given per-row sums (every lane of a 16-lane row holds its row's sum), the sum over the
-// TPK = 32 or 64 lanes of the group, in every lane of the group.
+// TPK = 32 or 64 lanes of the group, in every lane of the group: rows 0-1 and 2-3 meet by
+// gfx950's row swap, the two halves of the wave by its half-wave swap (no lane reads through
+// scalar registers).
 template <int TPK>
 __device__ inline float lane_group_sum_above16(float v) {
     static_assert(TPK == 32 || TPK == 64, "groups above 16 lanes are 32 or 64 wide");
-    v += dpp<kDppBcast15, 0xA>(v, 0.0f);   // rows 1 and 3 now hold row pairs
-    if constexpr (TPK == 32) {
-        const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
-        const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-        return (threadIdx.x & 32) ? hi : lo;
-    } else {
-        v += dpp<kDppBcast31, 0xC>(v, 0.0f);
-        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-    }
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    if constexpr (TPK == 64) v = half_swap_sum(v);
+    return v;
 }
 
 // Sum over the TPK lanes of a group of each of N values, result in every lane of the group.
@@ -236,7 +233,7 @@ __device__ __forceinline__ void attn_dec_block(const AttnParams& p, const int sp
                 }
                 sc[ps * NQ + j] = s;
             }
-        constexpr int kSumMax = NQ >= 8 ? 1 : 8;   // eight queries hold too many registers already
+        constexpr int kSumMax = 8;   // sums of 8 values interleaved level by level
         constexpr int kSumBlock = PASSES * NQ < kSumMax ? PASSES * NQ : kSumMax;
 #pragma unroll
         for (int b = 0; b < PASSES * NQ; b += kSumBlock) lane_group_sum_n<TPK, kSumBlock>(sc + b);

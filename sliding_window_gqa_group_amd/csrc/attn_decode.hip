@@ -465,7 +465,7 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
                 }
                 sc[ps * NQ + j] = s;
             }
-        constexpr int kSumMax = NQ >= 8 ? 1 : 8;
+        constexpr int kSumMax = 8;   // sums of 8 values interleaved level by level
         constexpr int kSumBlock = NPS * NQ < kSumMax ? NPS * NQ : kSumMax;
 #pragma unroll
         for (int bb = 0; bb < NPS * NQ; bb += kSumBlock) lane_group_sum_n<TPK, kSumBlock>(sc + bb);

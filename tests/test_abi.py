@@ -280,6 +280,21 @@ def test_tuning_knobs_change_the_plan(lib):
         B.tuning_set(B.TUNE_FORCE_KERNEL, 7)
 
 
+def test_workspace_sizes_follow_the_tuning_knobs(lib):
+    # the binding keeps workspace sizes per call shape; a knob that changes the plan must change
+    # the size it reports
+    shape = (1, 8, 4, 128, 4096, 4)
+    auto = B.chunk_workspace_bytes(*shape)
+    assert auto == lib.attn_window_chunk_workspace(*shape)
+    try:
+        B.tuning_set(B.TUNE_FORCE_KERNEL, 2)
+        forced = B.chunk_workspace_bytes(*shape)
+        assert forced == lib.attn_window_chunk_workspace(*shape) and forced != auto
+    finally:
+        B.tuning_set(B.TUNE_FORCE_KERNEL, 0)
+    assert B.chunk_workspace_bytes(*shape) == auto
+
+
 def test_gated_single_launch_workspace(lib):
     # the gated call in one launch (kernel 6), tile form for the 64-row, 16/4-head, width-256
     # workload: 4 blocks of 64 query vectors per KV head, 16 splits each (256 workgroups):

@@ -24,7 +24,8 @@
  *    query returns (0 means the call needs none and NULL may be passed). Its first 64 KiB hold
  *    split counters at a fixed place for every call shape. The plans that combine split
  *    partials inside one launch use them: the single-launch decode kernel's ready flags
- *    (kernel 5), the gated single launch's ready flags (kernel 6) and the last-split merge of
+ *    (kernel 5, also for one-row attn_window_chunk_far calls, whose far part runs in that
+ *    launch), the gated single launch's ready flags (kernel 6) and the last-split merge of
  *    kernels 1 to 4 when WINATTN_TUNE_MERGE_KERNEL selects it; plans that merge in a separate
  *    launch never touch them. They must be zero before the first call that uses the workspace
  *    (a fresh zeroed allocation, or attn_workspace_init), and every call leaves them at zero

@@ -66,11 +66,15 @@ int pad_d(int d) { return d <= 64 ? 64 : (d <= 128 ? 128 : 256); }
 
 // Plan of a plain chunk call on the single-launch slot-order kernel: every query of a group in
 // one block, the group's w ring slots cut into splits of `tps` tiles, partials merged by the
-// last split. False if the shape is not one it takes.
-bool decode_plan(int rows, int ng, int hpg, int d, int w, Plan& pl) {
+// last split. `far`: a one-row chunk call with a far field, whose far partials (one workgroup
+// per head, in the same launch) take one more partial slot per group and hpg more ready flags
+// per gatherer. False if the shape is not one it takes.
+bool decode_plan(int rows, int ng, int hpg, int d, int w, Plan& pl, bool far = false) {
     const long long nq_tot = (long long)rows * hpg;
     if (nq_tot > 8 || (g_force_kernel != 0 && g_force_kernel != kKindDecode && g_force_kernel != kKindGated))
         return false;
+    if (far && rows != 1) return false;
+    const int nfar = far ? hpg : 0;   // the far part's flags per gatherer
     pl.kind = kKindDecode;
     pl.mfma = false;
     pl.dpad = pad_d(d);
@@ -78,10 +82,15 @@ bool decode_plan(int rows, int ng, int hpg, int d, int w, Plan& pl) {
     pl.nqblocks = 1;
     pl.tk = decode_tile_keys(pl.dpad);
     const int rt = cdiv(w, pl.tk);   // ring tiles of a group
-    // tiles per split: the workgroups aim for two per CU (measured best for the decode shapes)
-    int tiles = g_tiles_per_split > 0 ? g_tiles_per_split : cdiv((long long)rt * ng, kDecodeTargetBlocks);
+    // tiles per split: the workgroups aim for two per CU (measured best for the decode shapes),
+    // the far part's workgroups (one per head) included, so that every split, the gatherers
+    // last among them, is resident from the start (the 4096-slot decode heads with a far field:
+    // 43 splits of 3 tiles per group, 14.8 us; 64 of 2, with 32 workgroups waiting for a CU,
+    // 15.5 us)
+    const long long room = std::max<long long>(kDecodeTargetBlocks / 2, kDecodeTargetBlocks - (long long)ng * nfar);
+    int tiles = g_tiles_per_split > 0 ? g_tiles_per_split : cdiv((long long)rt * ng, room);
     tiles = std::max(1, std::min(std::min(tiles, rt), decode_max_tiles(pl.dpad, pl.qb)));
-    if (cdiv(rt, tiles) > kDecodeMaxSplits) return false;
+    if (cdiv(rt, tiles) + nfar > kDecodeMaxSplits) return false;
     // Gatherers per group: up to 8 column chunks (a power of two dividing the d/4 columns and
     // at most the splits), while the waiting gatherers of all groups stay far below the
     // workgroups the GPU holds at once (they wait only for workgroups dispatched before them).
@@ -90,19 +99,19 @@ bool decode_plan(int rows, int ng, int hpg, int d, int w, Plan& pl) {
     while (gk > 1 && (gk > nsp || (long long)ng * gk > kDecodeMaxGatherers)) gk /= 2;
     if ((long long)ng * gk > kDecodeMaxGatherers) return false;
     pl.gather_k = gk;
-    // one ready flag per (gatherer, split) of every group, in the counter region
-    if ((long long)ng * gk * nsp > kMaxTickets) return false;
+    // one ready flag per (gatherer, split or far head) of every group, in the counter region
+    if ((long long)ng * gk * (nsp + nfar) > kMaxTickets) return false;
     pl.tps = tiles;
     pl.nsplit = cdiv(rt, tiles);
-    pl.slots = pl.nsplit;
+    pl.slots = pl.nsplit + (far ? 1 : 0);
     pl.merge_kernel = false;
     pl.xcd_map = 0;
-    if (pl.nsplit == 1) {
+    if (pl.slots == 1) {
         pl.bytes = 0;
         return true;
     }
     size_t off = kTicketBytes;
-    const size_t slots = (size_t)ng * pl.nsplit * pl.qb;
+    const size_t slots = (size_t)ng * pl.slots * pl.qb;
     pl.off_tickets = 0;
     pl.off_q = off;
     pl.off_pacc = off;
@@ -117,11 +126,15 @@ bool decode_plan(int rows, int ng, int hpg, int d, int w, Plan& pl) {
 
 // rows/hpg/d: the call's shape; wcap: the largest window any row can have; qbuf_floats: extra
 // workspace for the gated call's prepared queries. `plain`: a plain chunk call (no far field,
-// not gated), which the single-launch slot-order kernel may take.
+// not gated), which the single-launch slot-order kernel may take; `far1`: a one-row chunk call
+// with a far field (extra_slots 1), which it may take with the far part in its launch.
 Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_floats,
-               int extra_slots = 0, bool plain = false) {
+               int extra_slots = 0, bool plain = false, bool far1 = false) {
     Plan pl{};
     if (plain && extra_slots == 0 && qbuf_floats == 0 && decode_plan(rows, ng, hpg, d, wcap, pl))
+        return pl;
+    pl = Plan{};
+    if (far1 && extra_slots == 1 && qbuf_floats == 0 && decode_plan(rows, ng, hpg, d, wcap, pl, true))
         return pl;
     pl = Plan{};
     const long long nq_tot = (long long)rows * hpg;
@@ -339,6 +352,11 @@ int launch_attention(const Plan& pl, AttnParams& p, bool gated, char* ws, hipStr
     p.gather_k = pl.gather_k;
     hipError_t err = hipSuccess;
     const dim3 grid(pl.nsplit, pl.nqblocks, p.ng);
+    if (pl.kind == kKindDecode) {   // merges in its last splits; the far part joins its launch
+        if (far1 && far_mode != 1) return WINATTN_ELAUNCH;
+        err = launch_decode(p, far1, pl.dpad, pl.qb, pl.tps, stream);
+        return err == hipSuccess ? WINATTN_OK : WINATTN_ELAUNCH;
+    }
     bool fused = false;
     if (far1) {
         if (pl.kind == kKindDec && p.merge_kernel) {
@@ -353,8 +371,6 @@ int launch_attention(const Plan& pl, AttnParams& p, bool gated, char* ws, hipStr
     }
     if (fused)
         ;   // the near splits ran in the far part's launch
-    else if (pl.kind == kKindDecode)
-        err = launch_decode(p, pl.dpad, pl.qb, pl.tps, stream);   // merges in its last splits
     else if (pl.kind == kKindMfma)
         err = launch_mfma(p, gated, pl.dpad, stream);
     else if (pl.kind == kKindMfma16)
@@ -551,7 +567,7 @@ struct FarPlan {
 
 FarPlan make_far_plan(int rows, int ng, int hpg, int d, int w, int ns, int m) {
     FarPlan f{};
-    f.pl = make_plan(rows, ng, hpg, d, w, ns, 0, 1);
+    f.pl = make_plan(rows, ng, hpg, d, w, ns, 0, 1, false, rows == 1);
     const size_t nhm = (size_t)ng * hpg * m;
     size_t off = f.pl.bytes;
     f.off_e = off;

@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "attn_dec_block.h"
+#include "far_part.h"
 #include "launch.h"
 
 namespace winattn {
@@ -41,7 +42,8 @@ namespace winattn {
 // build contains none of this code). Every wave reads the 100 MHz real-time counter at the
 // kernel's phase boundaries, keeps the readings in registers and writes them once, at its end,
 // with the number of the XCD it ran on, to g_phase_stamps[block * waves + wave][kStampWords]
-// when the host has set that pointer (attn_phase_stamps_set). The kernel's work is unchanged.
+// when the host has set that pointer (attn_phase_stamps_set); launches with a far part write
+// none. The kernel's work is unchanged.
 #ifdef WINATTN_PHASE_STAMPS
 constexpr int kStampWords = 10;
 __device__ unsigned long long* g_phase_stamps;
@@ -59,10 +61,10 @@ struct PhaseStamps {
         __builtin_amdgcn_s_waitcnt(0);
         mark(k);
     }
-    __device__ void flush(int tid, int waves) {
+    __device__ void flush(int blk, int tid, int waves) {
         unsigned long long* o = g_phase_stamps;
-        if (!o || (tid & 63) != 0) return;
-        o += ((size_t)blockIdx.x * waves + tid / 64) * kStampWords;
+        if (!o || blk < 0 || (tid & 63) != 0) return;
+        o += ((size_t)blk * waves + tid / 64) * kStampWords;
         for (int k = 0; k < kStampWords - 1; ++k) o[k] = t[k];
         // hardware register 20 (XCC_ID), bits 0-3: the XCD of this wave
         o[kStampWords - 1] = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11));
@@ -74,7 +76,7 @@ struct PhaseStamps {
     template <class V>
     __device__ void mark_after(int, const V&) {}
     __device__ void mark_drained(int) {}
-    __device__ void flush(int, int) {}
+    __device__ void flush(int, int, int) {}
 };
 #endif
 
@@ -175,8 +177,8 @@ __device__ inline float lanes_sum_spaced(float v, int span) {
 constexpr int kGatherPolls = 1 << 18;
 
 template <int NQ, int D, int NT>
-__device__ inline void gather_chunk(const AttnParams& p, int g, int nsplit, int nq, int nk, int k,
-                                    unsigned int* flags, int* scratch) {
+__device__ inline void gather_chunk(const AttnParams& p, int g, int nslot, int nflag, int nq, int nk,
+                                    int k, unsigned int* flags, int* scratch) {
     constexpr int D4 = D / 4, NW = NT / 64;
     constexpr int MB = 8;                     // splits per lane per load round
     // items per lane at most: more than 64 per wave only for a single gatherer of 8 queries of
@@ -189,13 +191,13 @@ __device__ inline void gather_chunk(const AttnParams& p, int g, int nsplit, int 
     const int ipt = ipw / span;               // items per lane
     const int tid = threadIdx.x, lane = tid & 63, wave = tid / 64;
     const int sub = lane / span;
-    const size_t grp = (size_t)g * nsplit * NQ;   // first partial slot of the group
+    const size_t grp = (size_t)g * nslot * NQ;   // first partial slot of the group
     const __amdgpu_buffer_rsrc_t racc =
-        __builtin_amdgcn_make_buffer_rsrc(p.pacc + grp * D, 0, nsplit * NQ * D * 4, kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc(p.pacc + grp * D, 0, nslot * NQ * D * 4, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rm =
-        __builtin_amdgcn_make_buffer_rsrc(p.pm + grp, 0, nsplit * NQ * 4, kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc(p.pm + grp, 0, nslot * NQ * 4, kBufferWord3);
     const __amdgpu_buffer_rsrc_t rl =
-        __builtin_amdgcn_make_buffer_rsrc(p.pl + grp, 0, nsplit * NQ * 4, kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc(p.pl + grp, 0, nslot * NQ * 4, kBufferWord3);
 
     float cm[IPTM], cl[IPTM];
     vf4 ca[IPTM];
@@ -209,26 +211,26 @@ __device__ inline void gather_chunk(const AttnParams& p, int g, int nsplit, int 
         cl[it] = 0.0f;
         ca[it] = vf4{0.f, 0.f, 0.f, 0.f};
     }
-    // phase 1: every flag of this gatherer, polled until all are raised (pend: the splits not
+    // phase 1: every flag of this gatherer, polled until all are raised (pend: the flags not
     // yet seen, bit s of word s / 64 in lane s % 64 of every lane)
-    unsigned long long pend[2] = {nsplit >= 64 ? ~0ull : (1ull << nsplit) - 1ull,
-                                  nsplit >= 128 ? ~0ull : (nsplit > 64 ? (1ull << (nsplit - 64)) - 1ull : 0ull)};
-    const int nw = nsplit > 64 ? 2 : 1;
+    unsigned long long pend[2] = {nflag >= 64 ? ~0ull : (1ull << nflag) - 1ull,
+                                  nflag >= 128 ? ~0ull : (nflag > 64 ? (1ull << (nflag - 64)) - 1ull : 0ull)};
+    const int nw = nflag > 64 ? 2 : 1;
     int polls = 0;
     bool complete = false;
     while (polls < kGatherPolls) {
         ++polls;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            if (h < nw) pend[h] &= ~__builtin_amdgcn_ballot_w64(poll_flag(flags + min(h * 64 + lane, nsplit - 1)) != 0u);
+            if (h < nw) pend[h] &= ~__builtin_amdgcn_ballot_w64(poll_flag(flags + min(h * 64 + lane, nflag - 1)) != 0u);
         if ((pend[0] | pend[1]) == 0ull) {   // wave-uniform (ballot results)
             complete = true;
             break;
         }
         __builtin_amdgcn_s_sleep(1);
     }
-    // phase 2: this lane's splits s = sub + nsub i, MB at a time
-    for (int s0 = sub; complete && s0 < nsplit; s0 += MB * nsub) {
+    // phase 2: this lane's slots s = sub + nsub i, MB at a time
+    for (int s0 = sub; complete && s0 < nslot; s0 += MB * nsub) {
         float m[IPTM][MB], l[IPTM][MB];
         vf4 a[IPTM][MB];
 #pragma unroll
@@ -237,10 +239,10 @@ __device__ inline void gather_chunk(const AttnParams& p, int g, int nsplit, int 
             for (int u = 0; u < MB; ++u) {
                 const int su = s0 + u * nsub;
                 const int at = su * NQ + jj[it];
-                m[it][u] = -INFINITY;   // past the lane's splits: no keys
+                m[it][u] = -INFINITY;   // past the lane's slots: no keys
                 l[it][u] = 0.0f;
                 a[it][u] = vf4{0.f, 0.f, 0.f, 0.f};
-                if (su < nsplit) {
+                if (su < nslot) {
                     m[it][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, at * 4, 0, kCachePolicyDevice));
                     l[it][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, at * 4, 0, kCachePolicyDevice));
                     a[it][u] = __builtin_bit_cast(
@@ -302,7 +304,7 @@ __device__ inline void gather_chunk(const AttnParams& p, int g, int nsplit, int 
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int s = h * 64 + lane;
-            if (s < nsplit) __hip_atomic_store(flags + s, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (s < nflag) __hip_atomic_store(flags + s, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -323,9 +325,14 @@ struct DecodeShape {
     static constexpr int MAX_TILES = MAX_PASSES / PASSES;
 };
 
-// T: ring tiles per split (TK = 4096 / D slots each), all requested up front; NT threads.
-template <int D, int NQ, int T, int NT>
-__global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) {
+// One split of the call: workgroup wg_index (counted from the first split's) takes group
+// wg_index mod ng, split wg_index / ng. T: ring tiles per split (TK = 4096 / D slots each), all
+// requested up front; NT threads. FAR: a one-row call with a far field; the group has one
+// partial slot more, nsplit, which other workgroups of the launch fill (query j: head j's far
+// partial), and each gatherer hpg flags more (nsplit + j for head j); the gatherers fold that
+// slot with the splits' ones.
+template <int D, int NQ, int T, int NT, bool FAR>
+__device__ __forceinline__ void decode_split(const AttnParams& p, const int wg_index) {
     using S = DecodeShape<D, NQ, NT>;
     constexpr int TPK = S::TPK, F4 = S::F4, KPP = S::KPP, TK = S::TK, PASSES = S::PASSES;
     constexpr int NP = T * PASSES;   // ring passes of a split (one key per lane group each)
@@ -339,9 +346,11 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
 
     const int tid = threadIdx.x;
     const int gi = tid / TPK, sl = tid % TPK;   // lane group (key slot), lane within the group
-    const int g = blockIdx.x % p.ng;
-    const int split = blockIdx.x / p.ng;
+    const int g = wg_index % p.ng;
+    const int split = wg_index / p.ng;
     const int nsplit = p.nsplit_grid;
+    const int nslot = FAR ? nsplit + 1 : nsplit;          // partial slots of the group
+    const int nflag = FAR ? nsplit + p.hpg : nsplit;      // ready flags of each gatherer
     const int nq = p.rows * p.hpg;              // every query of the group: one block
     const int d4 = p.d / 4;
     PhaseStamps ps_;
@@ -610,7 +619,7 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
     // they are stored with the device-scope (sc1) cache policy, which writes them through to the
     // device-coherent level (16-byte buffer stores).
     constexpr int D4 = D / 4;
-    const size_t at0 = ((size_t)g * nsplit + split) * NQ;
+    const size_t at0 = ((size_t)g * nslot + split) * NQ;
     const __amdgpu_buffer_rsrc_t part =
         __builtin_amdgcn_make_buffer_rsrc(p.pacc + at0 * D, 0, NQ * D * 4, kBufferWord3);
     for (int item = tid; item < NQ * D4; item += NT) {
@@ -628,7 +637,7 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
             o += *reinterpret_cast<const vf4*>(s_acc + (w * NQ + j) * D + 4 * c) * f;
         }
         if (j >= nq || c >= d4) continue;
-        if (nsplit == 1) {
+        if (!FAR && nsplit == 1) {
             o *= 1.0f / fmaxf(l, 1e-30f);
             store_out<false>(p, j, g, 4 * c, make_float4(o.x, o.y, o.z, o.w));
         } else {
@@ -641,8 +650,8 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
         }
     }
     ps_.mark(5);   // phase 5: partial (or output) stores issued
-    if (nsplit == 1) {
-        ps_.flush(tid, NW);
+    if (!FAR && nsplit == 1) {
+        ps_.flush(FAR ? -1 : wg_index, tid, NW);
         return;
     }
 
@@ -650,38 +659,73 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
     // device-coherent level) before the barrier; then the split raises its ready flag for each
     // of the group's gatherers with device-scope stores
     const int nk = p.gather_k;
-    unsigned int* flags = p.tickets + (size_t)g * nk * nsplit;
+    unsigned int* flags = p.tickets + (size_t)g * nk * nflag;
     __builtin_amdgcn_s_waitcnt(0);
     ps_.mark(6);   // phase 6: partial stores acknowledged
     __syncthreads();
-    if (tid < nk) __hip_atomic_store(flags + tid * nsplit + split, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < nk) __hip_atomic_store(flags + tid * nflag + split, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int k = split - (nsplit - nk);
     ps_.mark(7);   // phase 7: ready flags raised
     if (k < 0) {
-        ps_.flush(tid, NW);
+        ps_.flush(FAR ? -1 : wg_index, tid, NW);
         return;
     }
     // the barrier above ended every read of the wave states: the gather reuses that LDS
-    gather_chunk<NQ, D, NT>(p, g, nsplit, nq, nk, k, flags + k * nsplit, reinterpret_cast<int*>(s_acc));
+    gather_chunk<NQ, D, NT>(p, g, nslot, nflag, nq, nk, k, flags + k * nflag, reinterpret_cast<int*>(s_acc));
     ps_.mark_drained(8);   // phase 8: column chunk gathered and its output stored
-    ps_.flush(tid, NW);
+    ps_.flush(FAR ? -1 : wg_index, tid, NW);
 }
 
 template <int D, int NQ, int T, int NT>
-static hipError_t launch_decode_tt(const AttnParams& p, hipStream_t stream) {
-    const dim3 grid((unsigned)(p.nsplit_grid * p.ng)), block(NT);
-    hipLaunchKernelGGL((attn_decode_kernel<D, NQ, T, NT>), grid, block, 0, stream, p);
+__global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) {
+    decode_split<D, NQ, T, NT, false>(p, (int)blockIdx.x);
+}
+
+// A one-row call with a far field: first the far partials of the nh heads (far_part.h, one
+// workgroup each), so that their chain of dependent loads (group state, landmark keys, mixing
+// matrix, far numerators, the evicted row) starts with the launch and runs while the splits
+// stream the ring, then the splits. A far workgroup stores its partial at device scope, waits
+// for those stores and raises its flag for each of its group's gatherers. (The same partials
+// made by the group's first splits after their own work measured 18.2 against 14.8 us on the
+// 4096-slot decode heads: the chain then starts only when the ring has been read.)
+template <int D, int NQ, int T, int NT>
+__global__ __launch_bounds__(NT, 2) void attn_decode_far_kernel(const AttnParams p, const FarParams f) {
+    static_assert(NT == 256, "the far part runs on 256 threads");
+    const int bid = (int)blockIdx.x;
+    if (bid < f.nh) {
+        far_part_block<D, kFarFusedOneRow, true>(f, bid);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const int g = bid / p.hpg, nk = p.gather_k, nflag = p.nsplit_grid + p.hpg;
+        if ((int)threadIdx.x < nk)
+            __hip_atomic_store(p.tickets + ((size_t)g * nk + threadIdx.x) * nflag + p.nsplit_grid + bid % p.hpg,
+                               1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    decode_split<D, NQ, T, NT, true>(p, bid - f.nh);
+}
+
+template <int D, int NQ, int T, int NT>
+static hipError_t launch_decode_tt(const AttnParams& p, const FarParams* f, hipStream_t stream) {
+    const dim3 block(NT);
+    if (f) {
+        const dim3 grid((unsigned)(f->nh + p.nsplit_grid * p.ng));
+        hipLaunchKernelGGL((attn_decode_far_kernel<D, NQ, T, NT>), grid, block, 0, stream, p, *f);
+    } else {
+        const dim3 grid((unsigned)(p.nsplit_grid * p.ng));
+        hipLaunchKernelGGL((attn_decode_kernel<D, NQ, T, NT>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 
 // The instances: 1-4 ring tiles per split with 4 queries per block, 1-2 with 8.
 template <int D, int NQ>
-static hipError_t launch_decode_t(const AttnParams& p, int tiles, hipStream_t stream) {
+static hipError_t launch_decode_t(const AttnParams& p, const FarParams* f, int tiles, hipStream_t stream) {
     constexpr int MT = DecodeShape<D, NQ, kThreads>::MAX_TILES;
-    if (tiles == 1) return launch_decode_tt<D, NQ, 1, kThreads>(p, stream);
-    if (tiles == 2 && MT >= 2) return launch_decode_tt<D, NQ, (MT >= 2 ? 2 : 1), kThreads>(p, stream);
-    if (tiles == 3 && MT >= 3) return launch_decode_tt<D, NQ, (MT >= 3 ? 3 : 1), kThreads>(p, stream);
-    if (tiles == 4 && MT >= 4) return launch_decode_tt<D, NQ, (MT >= 4 ? 4 : 1), kThreads>(p, stream);
+    if (tiles == 1) return launch_decode_tt<D, NQ, 1, kThreads>(p, f, stream);
+    if (tiles == 2 && MT >= 2) return launch_decode_tt<D, NQ, (MT >= 2 ? 2 : 1), kThreads>(p, f, stream);
+    if (tiles == 3 && MT >= 3) return launch_decode_tt<D, NQ, (MT >= 3 ? 3 : 1), kThreads>(p, f, stream);
+    if (tiles == 4 && MT >= 4) return launch_decode_tt<D, NQ, (MT >= 4 ? 4 : 1), kThreads>(p, f, stream);
     return hipErrorInvalidValue;
 }
 
@@ -691,13 +735,19 @@ int decode_max_tiles(int dpad, int nq) {
     return nq == 4 ? DecodeShape<256, 4, kThreads>::MAX_TILES : DecodeShape<256, 8, kThreads>::MAX_TILES;
 }
 
-hipError_t launch_decode(const AttnParams& p, int dpad, int nq, int tiles, hipStream_t stream) {
-    if (dpad == 64 && nq == 4) return launch_decode_t<64, 4>(p, tiles, stream);
-    if (dpad == 64 && nq == 8) return launch_decode_t<64, 8>(p, tiles, stream);
-    if (dpad == 128 && nq == 4) return launch_decode_t<128, 4>(p, tiles, stream);
-    if (dpad == 128 && nq == 8) return launch_decode_t<128, 8>(p, tiles, stream);
-    if (dpad == 256 && nq == 4) return launch_decode_t<256, 4>(p, tiles, stream);
-    if (dpad == 256 && nq == 8) return launch_decode_t<256, 8>(p, tiles, stream);
+// f: the far part of a one-row chunk call (its partial in slot nsplit of each group, p.hpg
+// flags more per gatherer), or null.
+hipError_t launch_decode(const AttnParams& p, const FarParams* f, int dpad, int nq, int tiles,
+                         hipStream_t stream) {
+    if (f && (f->rows != 1 || f->dpad != dpad || f->nh != p.nh || f->qb != nq || f->nqblocks != 1 ||
+              f->far_slot != p.nsplit_grid || f->slot_stride != p.nsplit_grid + 1 || p.slot_stride != f->slot_stride))
+        return hipErrorInvalidValue;
+    if (dpad == 64 && nq == 4) return launch_decode_t<64, 4>(p, f, tiles, stream);
+    if (dpad == 64 && nq == 8) return launch_decode_t<64, 8>(p, f, tiles, stream);
+    if (dpad == 128 && nq == 4) return launch_decode_t<128, 4>(p, f, tiles, stream);
+    if (dpad == 128 && nq == 8) return launch_decode_t<128, 8>(p, f, tiles, stream);
+    if (dpad == 256 && nq == 4) return launch_decode_t<256, 4>(p, f, tiles, stream);
+    if (dpad == 256 && nq == 8) return launch_decode_t<256, 8>(p, f, tiles, stream);
     return hipErrorInvalidValue;
 }
 

@@ -167,8 +167,11 @@ enum FarMode {
 // The far partial of one (row i, head gh): a workgroup of 256 threads. Every operand is loaded
 // in a few wide rounds (mu and t_hat are prefetched at the start), dot products and landmark
 // sums are split across lanes, and the per-landmark scalars live in wave 0, lane b.
-// DP = padded head width (64, 128, 256): the partial row has DP floats.
-template <int DP, int MODE>
+// DP = padded head width (64, 128, 256): the partial row has DP floats. DEV: the partial is
+// read within the same launch by workgroups that may run on other XCDs, so it is stored with
+// the device-scope cache policy (written through to the device-coherent level); the caller
+// waits for those stores before it signals them.
+template <int DP, int MODE, bool DEV = false>
 __device__ __forceinline__ void far_part_block(const FarParams& p, const int bid) {
     constexpr int NT = 256;
     constexpr int D4P = DP / 4;             // float4 columns of a partial row
@@ -193,14 +196,31 @@ __device__ __forceinline__ void far_part_block(const FarParams& p, const int bid
     const int blk = g * p.nqblocks + qi / p.qb;
     const size_t at = ((size_t)blk * p.slot_stride + p.far_slot) * p.qb + qi % p.qb;
     float4* acc_out = reinterpret_cast<float4*>(p.pacc + at * DP);
+    auto put_acc = [&](int c, float4 v) {
+        if constexpr (DEV) {
+            const __amdgpu_buffer_rsrc_t r =
+                __builtin_amdgcn_make_buffer_rsrc(acc_out, 0, DP * 4, kBufferWord3);
+            __builtin_amdgcn_raw_buffer_store_b128(vu4{__float_as_uint(v.x), __float_as_uint(v.y),
+                                                       __float_as_uint(v.z), __float_as_uint(v.w)},
+                                                   r, c * 16, 0, kCachePolicyDevice);
+        } else {
+            acc_out[c] = v;
+        }
+    };
+    auto put_ml = [&](float mv, float lv) {
+        if constexpr (DEV) {
+            store_dev(p.pm + at, mv);
+            store_dev(p.pl + at, lv);
+        } else {
+            p.pm[at] = mv;
+            p.pl[at] = lv;
+        }
+    };
 
     const long long farl = (long long)gs.far0 + (i >= j0 ? i - j0 + 1 : 0);
     if (farl <= 0) {   // empty far field: an empty partial
-        if (t < D4P) acc_out[t] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (t == 0) {
-            p.pm[at] = -INFINITY;
-            p.pl[at] = 0.0f;
-        }
+        if (t < D4P) put_acc(t, make_float4(0.f, 0.f, 0.f, 0.f));
+        if (t == 0) put_ml(-INFINITY, 0.0f);
         return;
     }
 
@@ -349,11 +369,8 @@ __device__ __forceinline__ void far_part_block(const FarParams& p, const int bid
     }
     __syncthreads();
     if (!s_have) {   // negative far mass: the far part is dropped
-        if (t < D4P) acc_out[t] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (t == 0) {
-            p.pm[at] = -INFINITY;
-            p.pl[at] = 0.0f;
-        }
+        if (t < D4P) put_acc(t, make_float4(0.f, 0.f, 0.f, 0.f));
+        if (t == 0) put_ml(-INFINITY, 0.0f);
         return;
     }
 
@@ -427,13 +444,10 @@ __device__ __forceinline__ void far_part_block(const FarParams& p, const int bid
             z += s_acc[u + 2];
             w += s_acc[u + 3];
         }
-        acc_out[t] = t < d4 ? make_float4((float)x, (float)y, (float)z, (float)w)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        put_acc(t, t < d4 ? make_float4((float)x, (float)y, (float)z, (float)w)
+                          : make_float4(0.f, 0.f, 0.f, 0.f));
     }
-    if (t == 0) {
-        p.pm[at] = s_pm;   // the merge works in the log2 domain
-        p.pl[at] = s_F;
-    }
+    if (t == 0) put_ml(s_pm, s_F);   // the merge works in the log2 domain
 }
 
 }  // namespace

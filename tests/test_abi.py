@@ -295,6 +295,30 @@ def test_workspace_sizes_follow_the_tuning_knobs(lib):
     assert B.chunk_workspace_bytes(*shape) == auto
 
 
+def test_one_row_far_plan_workspace(lib):
+    # A one-row chunk call with a far field runs its far part inside the single-launch decode
+    # kernel, one workgroup per head ahead of the splits: for the 4096-slot decode heads (8
+    # groups x 4, d 128, 32-slot ring tiles) the 32 far workgroups and the splits fit two per
+    # CU (512): 3 tiles per split, 43 splits, and one partial slot more per group for the far
+    # part; then the f64 eviction arrays [nh][m][rows] (two) and [nh][m] (two), here m = 16.
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    def expect(nsplit):
+        slots = 8 * (nsplit + 1) * 4
+        return 65536 + al(slots * 128 * 4) + 2 * al(slots * 4) + 4 * al(32 * 16 * 8)
+    need = B.chunk_far_workspace_bytes(1, 8, 4, 128, 4096, 4, 16)
+    assert need == expect(43)
+    try:
+        B.tuning_set(B.TUNE_TILES_PER_SPLIT, 2)   # 64 splits: 68 ready flags per gatherer
+        assert B.chunk_far_workspace_bytes(1, 8, 4, 128, 4096, 4, 16) == expect(64)
+        B.tuning_set(B.TUNE_TILES_PER_SPLIT, 4)   # 32 splits
+        assert B.chunk_far_workspace_bytes(1, 8, 4, 128, 4096, 4, 16) == expect(32)
+    finally:
+        B.tuning_set(B.TUNE_TILES_PER_SPLIT, 0)
+    assert B.chunk_far_workspace_bytes(1, 8, 4, 128, 4096, 4, 16) == need
+
+
 def test_gated_single_launch_workspace(lib):
     # the gated call in one launch (kernel 6), tile form for the 64-row, 16/4-head, width-256
     # workload: 4 blocks of 64 query vectors per KV head, 16 splits each (256 workgroups):

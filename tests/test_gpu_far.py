@@ -88,6 +88,13 @@ FAR_VARIANTS = {
     # asks for the in-kernel merge: the far slot still merges in the merge launch
     "mfma_in_kernel_merge_asked": {B.TUNE_FORCE_KERNEL: 2, B.TUNE_TILES_PER_SPLIT: 2,
                                    B.TUNE_MERGE_KERNEL: 1},
+    # one-row calls: the far part inside the single-launch slot-order kernel (kernel 5) with
+    # other split sizes than its plan picks (the 4096-slot decode: 64 splits, 68 ready flags
+    # per gatherer, more workgroups than the GPU holds at once; with one tile, 128 splits and 4
+    # far flags are more than a gatherer polls, and the two-launch register plan takes it;
+    # small rings: a single split); other shapes take their usual plan
+    "decode_one_launch_two_tiles": {B.TUNE_FORCE_KERNEL: 5, B.TUNE_TILES_PER_SPLIT: 2},
+    "decode_one_launch_one_tile": {B.TUNE_FORCE_KERNEL: 5, B.TUNE_TILES_PER_SPLIT: 1},
 }
 
 
@@ -191,3 +198,23 @@ def test_far_workspace_reuse_with_stale_bytes():
     ws.buf[64 * 1024:] = 0x55
     for _ in range(2):
         assert_close(gpu_chunk_far(inp, far, workspace=ws), ref, "far with stale workspace")
+
+
+def test_one_row_far_calls_leave_the_counters_at_zero():
+    """One-row far calls take the single launch, whose far part and splits raise ready flags in
+    the workspace's counter region: calls of different shapes on one workspace (stale bytes
+    past the counters) each match the oracle, and the counters are all zero afterwards."""
+    _case("one-row far calls, shared workspace")
+    shapes = [(1, 8, 4, 128, 4096, 4, 16, "full", "positive"),
+              (1, 2, 2, 256, 70, 3, 12, "mix", "signed"),
+              (1, 3, 4, 64, 300, 0, 64, "partial", "signed"),
+              (1, 8, 4, 128, 4096, 4, 16, "full", "positive")]
+    need = max(B.chunk_far_workspace_bytes(*s[:7]) for s in shapes)
+    ws = B.Workspace(DEV)
+    ws.get(need)
+    ws.buf[64 * 1024:] = 0x55
+    for shape in shapes:
+        inp, far = _far_inputs(shape)
+        assert_close(gpu_chunk_far(inp, far, workspace=ws), oracle.window_chunk_far(inp, far),
+                     f"one-row far {shape}")
+        assert int(torch.count_nonzero(ws.buf[:64 * 1024])) == 0, f"counters left set after {shape}"

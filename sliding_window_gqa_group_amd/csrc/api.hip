@@ -88,7 +88,13 @@ bool decode_plan(int rows, int ng, int hpg, int d, int w, Plan& pl, bool far = f
     // 43 splits of 3 tiles per group, 14.8 us; 64 of 2, with 32 workgroups waiting for a CU,
     // 15.5 us)
     const long long room = std::max<long long>(kDecodeTargetBlocks / 2, kDecodeTargetBlocks - (long long)ng * nfar);
-    int tiles = g_tiles_per_split > 0 ? g_tiles_per_split : cdiv((long long)rt * ng, room);
+    int tiles = cdiv((long long)rt * ng, room);
+    // With a far part, splits of at least 64 KiB of ring (K and V): on small rings the far
+    // workgroups and the gather of many small partials outweigh the extra parallelism (the gated
+    // heads, 4 x 1024 slots of width 256, 8 MB: 1, 2 and 4 tiles of 32 KiB per split 15.9, 13.3
+    // and 13.0 us against 14.4 us for the two-launch path)
+    if (far) tiles = std::max(tiles, cdiv(64 << 10, (long long)pl.tk * pl.dpad * 8));
+    if (g_tiles_per_split > 0) tiles = g_tiles_per_split;
     tiles = std::max(1, std::min(std::min(tiles, rt), decode_max_tiles(pl.dpad, pl.qb)));
     if (cdiv(rt, tiles) + nfar > kDecodeMaxSplits) return false;
     // Gatherers per group: up to 8 column chunks (a power of two dividing the d/4 columns and
@@ -126,8 +132,9 @@ bool decode_plan(int rows, int ng, int hpg, int d, int w, Plan& pl, bool far = f
 
 // rows/hpg/d: the call's shape; wcap: the largest window any row can have; qbuf_floats: extra
 // workspace for the gated call's prepared queries. `plain`: a plain chunk call (no far field,
-// not gated), which the single-launch slot-order kernel may take; `far1`: a one-row chunk call
-// with a far field (extra_slots 1), which it may take with the far part in its launch.
+// not gated), which the single-launch slot-order kernel may take; `far1`: a one-row call with a
+// far field (extra_slots 1; the chunk call or the gated one), which it may take with the far
+// part in its launch.
 Plan make_plan(int rows, int ng, int hpg, int d, int wcap, int ns, size_t qbuf_floats,
                int extra_slots = 0, bool plain = false, bool far1 = false) {
     Plan pl{};
@@ -353,8 +360,8 @@ int launch_attention(const Plan& pl, AttnParams& p, bool gated, char* ws, hipStr
     hipError_t err = hipSuccess;
     const dim3 grid(pl.nsplit, pl.nqblocks, p.ng);
     if (pl.kind == kKindDecode) {   // merges in its last splits; the far part joins its launch
-        if (far1 && far_mode != 1) return WINATTN_ELAUNCH;
-        err = launch_decode(p, far1, pl.dpad, pl.qb, pl.tps, stream);
+        if (gated ? (!far1 || far_mode != 2) : (far1 && far_mode != 1)) return WINATTN_ELAUNCH;
+        err = launch_decode(p, far1, gated, pl.dpad, pl.qb, pl.tps, stream);
         return err == hipSuccess ? WINATTN_OK : WINATTN_ELAUNCH;
     }
     bool fused = false;
@@ -720,7 +727,7 @@ size_t attn_window_gated_far_workspace(int nh, int nk, int hd, int w, int ns, in
     if (nh < 1 || nk < 1 || nh % nk != 0 || !chunk_shape_ok(1, nk, nh / nk, hd, w, ns) ||
         !far_shape_ok(1, m))
         return 0;
-    return make_plan(1, nk, nh / nk, hd, w, ns, 0, 1).bytes;
+    return make_plan(1, nk, nh / nk, hd, w, ns, 0, 1, false, true).bytes;
 }
 
 int attn_window_gated_far(const float* q, const float* ring_k, const float* ring_v,
@@ -742,7 +749,7 @@ int attn_window_gated_far(const float* q, const float* ring_k, const float* ring
         return WINATTN_EINVAL;
     if ((long long)nh * m * hd > kMaxFloats) return WINATTN_EINVAL;
     const int hpg = nh / nk;
-    const Plan pl = make_plan(1, nk, hpg, hd, w, ns, 0, 1);
+    const Plan pl = make_plan(1, nk, hpg, hd, w, ns, 0, 1, false, true);
     if (!workspace || workspace_bytes < pl.bytes) return WINATTN_EWORKSPACE;
     if (!aligned16(workspace)) return WINATTN_EINVAL;
     char* ws = static_cast<char*>(workspace);

@@ -176,7 +176,7 @@ __device__ inline float lanes_sum_spaced(float v, int span) {
 //    gatherer's flags are cleared for the next call if every wave saw them all.
 constexpr int kGatherPolls = 1 << 18;
 
-template <int NQ, int D, int NT>
+template <int NQ, int D, int NT, bool GATED>
 __device__ inline void gather_chunk(const AttnParams& p, int g, int nslot, int nflag, int nq, int nk,
                                     int k, unsigned int* flags, int* scratch) {
     constexpr int D4 = D / 4, NW = NT / 64;
@@ -291,7 +291,7 @@ __device__ inline void gather_chunk(const AttnParams& p, int g, int nslot, int n
             if (it >= ipt || jj[it] >= nq || cc[it] >= p.d / 4) continue;
             vf4 o = ca[it] * (1.0f / fmaxf(cl[it], 1e-30f));
             if (!complete) o = vf4{NAN, NAN, NAN, NAN};
-            store_out<false>(p, jj[it], g, 4 * cc[it], make_float4(o.x, o.y, o.z, o.w));
+            store_out<GATED>(p, jj[it], g, 4 * cc[it], make_float4(o.x, o.y, o.z, o.w));
         }
     }
     if (lane == 0) scratch[wave] = complete ? 1 : 0;
@@ -330,9 +330,13 @@ struct DecodeShape {
 // requested up front; NT threads. FAR: a one-row call with a far field; the group has one
 // partial slot more, nsplit, which other workgroups of the launch fill (query j: head j's far
 // partial), and each gatherer hpg flags more (nsplit + j for head j); the gatherers fold that
-// slot with the splits' ones.
-template <int D, int NQ, int T, int NT, bool FAR>
+// slot with the splits' ones. GATED (with FAR): the gated one-row call (dory page, "Dory's token
+// path": `dory_os` ... `dory_ogate`), whose ring already holds the row's own key: slots
+// 0 .. len - 1 are its keys, all visible to the row, the extra keys are the sinks alone, and
+// the outputs pass through the sigmoid gate.
+template <int D, int NQ, int T, int NT, bool FAR, bool GATED>
 __device__ __forceinline__ void decode_split(const AttnParams& p, const int wg_index) {
+    static_assert(FAR || !GATED, "the gated call takes this kernel with its far part only");
     using S = DecodeShape<D, NQ, NT>;
     constexpr int TPK = S::TPK, F4 = S::F4, KPP = S::KPP, TK = S::TK, PASSES = S::PASSES;
     constexpr int NP = T * PASSES;   // ring passes of a split (one key per lane group each)
@@ -390,15 +394,16 @@ __device__ __forceinline__ void decode_split(const AttnParams& p, const int wg_i
     const unsigned long long sk = b.sk + 4ull * (unsigned long long)((long long)g * p.ns * p.d);
     const unsigned long long sv = b.sv + 4ull * (unsigned long long)((long long)g * p.ns * p.d);
     const int ss = (int)p.ring_ss, crs = (int)p.chunk_rs;
-    const int nextra = p.ns + p.rows;
+    const int nextra = p.ns + (GATED ? 0 : p.rows);
 
     // Extra key e of the group: sink e (e < ns), else chunk row e - ns; padding (e >= nextra)
-    // loads the chunk's last row, a live address.
+    // loads the chunk's last row, a live address (the gated call, which has no chunk rows
+    // here: the ring's slot 0).
     auto load_extra = [&](vf4 (&k)[F4], vf4 (&v)[F4], int e) {
         const bool sink = e < p.ns;
         const int crow = min(e - p.ns, p.rows - 1);
-        const int row = sink ? e * p.d : crow * crs;
-        const unsigned long long bk = sink ? sk : ck, bv = sink ? sv : cv;
+        const int row = sink ? e * p.d : (GATED ? 0 : crow * crs);
+        const unsigned long long bk = sink ? sk : (GATED ? rk : ck), bv = sink ? sv : (GATED ? rv : cv);
 #pragma unroll
         for (int f = 0; f < F4; ++f) {
             const int c = sl + TPK * f;
@@ -433,13 +438,15 @@ __device__ __forceinline__ void decode_split(const AttnParams& p, const int wg_i
     // wait for the metadata cannot be scheduled ahead of them (all four words stay live until
     // then, so no register of the load in flight is reused before it lands).
     asm volatile("" : "+v"(meta_v.x), "+v"(meta_v.y), "+v"(meta_v.z), "+v"(meta_v.w) : : "memory");
-    const RingGeom rg = ring_geom(meta_v, p.w);
+    // (the gated call: slots 0 .. len - 1 hold the row's window, len clamped to w)
+    const RingGeom rg = GATED ? RingGeom{p.w, (int)(meta_v.x < (uint32_t)p.w ? meta_v.x : (uint32_t)p.w), 0}
+                              : ring_geom(meta_v, p.w);
     int qlo[NQ], qrow[NQ];
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
         const int row = min(j, nq - 1) / p.hpg;
         const int hi = rg.len0 + row + 1;
-        qlo[j] = j < nq ? window_lo(hi, rg.wg) : 0x7fffffff;   // padding sees nothing
+        qlo[j] = j < nq ? (GATED ? 0 : window_lo(hi, rg.wg)) : 0x7fffffff;   // padding sees nothing
         qrow[j] = j < nq ? row : -1;
     }
     ps_.mark_after(1, qlo[0]);   // phase 1: metadata arrived
@@ -639,7 +646,7 @@ __device__ __forceinline__ void decode_split(const AttnParams& p, const int wg_i
         if (j >= nq || c >= d4) continue;
         if (!FAR && nsplit == 1) {
             o *= 1.0f / fmaxf(l, 1e-30f);
-            store_out<false>(p, j, g, 4 * c, make_float4(o.x, o.y, o.z, o.w));
+            store_out<GATED>(p, j, g, 4 * c, make_float4(o.x, o.y, o.z, o.w));
         } else {
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(vu4, o), part, (j * D + 4 * c) * 4,
                                                    0, kCachePolicyDevice);
@@ -671,14 +678,14 @@ __device__ __forceinline__ void decode_split(const AttnParams& p, const int wg_i
         return;
     }
     // the barrier above ended every read of the wave states: the gather reuses that LDS
-    gather_chunk<NQ, D, NT>(p, g, nslot, nflag, nq, nk, k, flags + k * nflag, reinterpret_cast<int*>(s_acc));
+    gather_chunk<NQ, D, NT, GATED>(p, g, nslot, nflag, nq, nk, k, flags + k * nflag, reinterpret_cast<int*>(s_acc));
     ps_.mark_drained(8);   // phase 8: column chunk gathered and its output stored
     ps_.flush(FAR ? -1 : wg_index, tid, NW);
 }
 
 template <int D, int NQ, int T, int NT>
 __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) {
-    decode_split<D, NQ, T, NT, false>(p, (int)blockIdx.x);
+    decode_split<D, NQ, T, NT, false, false>(p, (int)blockIdx.x);
 }
 
 // A one-row call with a far field: first the far partials of the nh heads (far_part.h, one
@@ -687,13 +694,14 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const AttnParams p) 
 // stream the ring, then the splits. A far workgroup stores its partial at device scope, waits
 // for those stores and raises its flag for each of its group's gatherers. (The same partials
 // made by the group's first splits after their own work measured 18.2 against 14.8 us on the
-// 4096-slot decode heads: the chain then starts only when the ring has been read.)
-template <int D, int NQ, int T, int NT>
+// 4096-slot decode heads: the chain then starts only when the ring has been read.) GATED: the
+// gated one-row call, whose far state is current (no eviction in the call).
+template <int D, int NQ, int T, int NT, bool GATED>
 __global__ __launch_bounds__(NT, 2) void attn_decode_far_kernel(const AttnParams p, const FarParams f) {
     static_assert(NT == 256, "the far part runs on 256 threads");
     const int bid = (int)blockIdx.x;
     if (bid < f.nh) {
-        far_part_block<D, kFarFusedOneRow, true>(f, bid);
+        far_part_block<D, GATED ? kFarCurrent : kFarFusedOneRow, true>(f, bid);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         const int g = bid / p.hpg, nk = p.gather_k, nflag = p.nsplit_grid + p.hpg;
@@ -702,15 +710,18 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_far_kernel(const AttnParams
                                1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    decode_split<D, NQ, T, NT, true>(p, bid - f.nh);
+    decode_split<D, NQ, T, NT, true, GATED>(p, bid - f.nh);
 }
 
 template <int D, int NQ, int T, int NT>
-static hipError_t launch_decode_tt(const AttnParams& p, const FarParams* f, hipStream_t stream) {
+static hipError_t launch_decode_tt(const AttnParams& p, const FarParams* f, bool gated, hipStream_t stream) {
     const dim3 block(NT);
     if (f) {
         const dim3 grid((unsigned)(f->nh + p.nsplit_grid * p.ng));
-        hipLaunchKernelGGL((attn_decode_far_kernel<D, NQ, T, NT>), grid, block, 0, stream, p, *f);
+        if (gated)
+            hipLaunchKernelGGL((attn_decode_far_kernel<D, NQ, T, NT, true>), grid, block, 0, stream, p, *f);
+        else
+            hipLaunchKernelGGL((attn_decode_far_kernel<D, NQ, T, NT, false>), grid, block, 0, stream, p, *f);
     } else {
         const dim3 grid((unsigned)(p.nsplit_grid * p.ng));
         hipLaunchKernelGGL((attn_decode_kernel<D, NQ, T, NT>), grid, block, 0, stream, p);
@@ -720,12 +731,13 @@ static hipError_t launch_decode_tt(const AttnParams& p, const FarParams* f, hipS
 
 // The instances: 1-4 ring tiles per split with 4 queries per block, 1-2 with 8.
 template <int D, int NQ>
-static hipError_t launch_decode_t(const AttnParams& p, const FarParams* f, int tiles, hipStream_t stream) {
+static hipError_t launch_decode_t(const AttnParams& p, const FarParams* f, bool gated, int tiles,
+                                  hipStream_t stream) {
     constexpr int MT = DecodeShape<D, NQ, kThreads>::MAX_TILES;
-    if (tiles == 1) return launch_decode_tt<D, NQ, 1, kThreads>(p, f, stream);
-    if (tiles == 2 && MT >= 2) return launch_decode_tt<D, NQ, (MT >= 2 ? 2 : 1), kThreads>(p, f, stream);
-    if (tiles == 3 && MT >= 3) return launch_decode_tt<D, NQ, (MT >= 3 ? 3 : 1), kThreads>(p, f, stream);
-    if (tiles == 4 && MT >= 4) return launch_decode_tt<D, NQ, (MT >= 4 ? 4 : 1), kThreads>(p, f, stream);
+    if (tiles == 1) return launch_decode_tt<D, NQ, 1, kThreads>(p, f, gated, stream);
+    if (tiles == 2 && MT >= 2) return launch_decode_tt<D, NQ, (MT >= 2 ? 2 : 1), kThreads>(p, f, gated, stream);
+    if (tiles == 3 && MT >= 3) return launch_decode_tt<D, NQ, (MT >= 3 ? 3 : 1), kThreads>(p, f, gated, stream);
+    if (tiles == 4 && MT >= 4) return launch_decode_tt<D, NQ, (MT >= 4 ? 4 : 1), kThreads>(p, f, gated, stream);
     return hipErrorInvalidValue;
 }
 
@@ -735,19 +747,20 @@ int decode_max_tiles(int dpad, int nq) {
     return nq == 4 ? DecodeShape<256, 4, kThreads>::MAX_TILES : DecodeShape<256, 8, kThreads>::MAX_TILES;
 }
 
-// f: the far part of a one-row chunk call (its partial in slot nsplit of each group, p.hpg
-// flags more per gatherer), or null.
-hipError_t launch_decode(const AttnParams& p, const FarParams* f, int dpad, int nq, int tiles,
+// f: the far part of a one-row call (its partial in slot nsplit of each group, p.hpg flags
+// more per gatherer), or null; gated (with f): the gated one-row call.
+hipError_t launch_decode(const AttnParams& p, const FarParams* f, bool gated, int dpad, int nq, int tiles,
                          hipStream_t stream) {
+    if (gated && !f) return hipErrorInvalidValue;
     if (f && (f->rows != 1 || f->dpad != dpad || f->nh != p.nh || f->qb != nq || f->nqblocks != 1 ||
               f->far_slot != p.nsplit_grid || f->slot_stride != p.nsplit_grid + 1 || p.slot_stride != f->slot_stride))
         return hipErrorInvalidValue;
-    if (dpad == 64 && nq == 4) return launch_decode_t<64, 4>(p, f, tiles, stream);
-    if (dpad == 64 && nq == 8) return launch_decode_t<64, 8>(p, f, tiles, stream);
-    if (dpad == 128 && nq == 4) return launch_decode_t<128, 4>(p, f, tiles, stream);
-    if (dpad == 128 && nq == 8) return launch_decode_t<128, 8>(p, f, tiles, stream);
-    if (dpad == 256 && nq == 4) return launch_decode_t<256, 4>(p, f, tiles, stream);
-    if (dpad == 256 && nq == 8) return launch_decode_t<256, 8>(p, f, tiles, stream);
+    if (dpad == 64 && nq == 4) return launch_decode_t<64, 4>(p, f, gated, tiles, stream);
+    if (dpad == 64 && nq == 8) return launch_decode_t<64, 8>(p, f, gated, tiles, stream);
+    if (dpad == 128 && nq == 4) return launch_decode_t<128, 4>(p, f, gated, tiles, stream);
+    if (dpad == 128 && nq == 8) return launch_decode_t<128, 8>(p, f, gated, tiles, stream);
+    if (dpad == 256 && nq == 4) return launch_decode_t<256, 4>(p, f, gated, tiles, stream);
+    if (dpad == 256 && nq == 8) return launch_decode_t<256, 8>(p, f, gated, tiles, stream);
     return hipErrorInvalidValue;
 }
 

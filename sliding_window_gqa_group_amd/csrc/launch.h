@@ -24,10 +24,11 @@ struct FarParams;
 // Single-launch register kernel for <= 8 query vectors per group (one block per group) that
 // streams the ring in slot order; grid = nsplit_grid * ng workgroups; `tiles` ring tiles per
 // split; the group's last gather_k splits merge its partials, a column chunk each. With `far`
-// (a one-row chunk call's far field, or null) the far part of every head runs in the same
-// launch, ahead of the splits, and its partial (slot nsplit_grid) joins the gather.
-hipError_t launch_decode(const AttnParams& p, const FarParams* far, int dpad, int nq, int tiles,
-                         hipStream_t stream);
+// (a one-row call's far field, or null) the far part of every head runs in the same launch,
+// ahead of the splits, and its partial (slot nsplit_grid) joins the gather; `gated` (with
+// `far` only): the gated one-row call (ring slots 0 .. len-1, sinks, the sigmoid gate).
+hipError_t launch_decode(const AttnParams& p, const FarParams* far, bool gated, int dpad, int nq,
+                         int tiles, hipStream_t stream);
 // Ring tiles per split the kernel holds in registers with nq queries per block.
 int decode_max_tiles(int dpad, int nq);
 // Keys per tile of that kernel.

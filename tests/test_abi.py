@@ -319,6 +319,27 @@ def test_one_row_far_plan_workspace(lib):
     assert B.chunk_far_workspace_bytes(1, 8, 4, 128, 4096, 4, 16) == need
 
 
+def test_gated_one_row_far_plan_workspace(lib):
+    # The gated one-row far call at the gated heads (16 query / 4 KV heads, hd 256, 1024-slot
+    # rings) runs in the single-launch decode kernel: 16-slot ring tiles (32 KiB of K and V),
+    # two per split for at least 64 KiB, 32 splits per group plus the far slot; counters +
+    # partials, no eviction arrays.
+    def al(x):
+        return (x + 255) // 256 * 256
+
+    def expect(nsplit):
+        slots = 4 * (nsplit + 1) * 4
+        return 65536 + al(slots * 256 * 4) + 2 * al(slots * 4)
+    assert B.gated_far_workspace_bytes(16, 4, 256, 1024, 0, 32) == expect(32)
+    try:
+        B.tuning_set(B.TUNE_TILES_PER_SPLIT, 4)
+        assert B.gated_far_workspace_bytes(16, 4, 256, 1024, 0, 32) == expect(16)
+        B.tuning_set(B.TUNE_TILES_PER_SPLIT, 1)   # 64 splits: 68 ready flags per gatherer
+        assert B.gated_far_workspace_bytes(16, 4, 256, 1024, 0, 32) == expect(64)
+    finally:
+        B.tuning_set(B.TUNE_TILES_PER_SPLIT, 0)
+
+
 def test_gated_single_launch_workspace(lib):
     # the gated call in one launch (kernel 6), tile form for the 64-row, 16/4-head, width-256
     # workload: 4 blocks of 64 query vectors per KV head, 16 splits each (256 workgroups):

@@ -72,6 +72,12 @@ VARIANTS = {
     "mfma_many_splits": {B.TUNE_FORCE_KERNEL: 2, B.TUNE_TILES_PER_SPLIT: 1},
     "lds_vector_many_splits": {B.TUNE_FORCE_KERNEL: 3, B.TUNE_TILES_PER_SPLIT: 1},
     "mfma16_many_splits": {B.TUNE_FORCE_KERNEL: 4, B.TUNE_TILES_PER_SPLIT: 1},
+    # up to 8 query vectors per KV head: the far part inside the single-launch slot-order
+    # kernel (kernel 5) with other splits than its plan picks (the gated heads, d 256: 64
+    # splits and 68 ready flags per gatherer, or 16 splits, instead of 32); other shapes take
+    # their usual plan
+    "decode_one_launch_one_tile": {B.TUNE_FORCE_KERNEL: 5, B.TUNE_TILES_PER_SPLIT: 1},
+    "decode_one_launch_four_tiles": {B.TUNE_FORCE_KERNEL: 5, B.TUNE_TILES_PER_SPLIT: 4},
 }
 
 
@@ -100,3 +106,20 @@ def test_gated_far_stale_workspace():
     ws.buf[64 * 1024:] = 0x55
     for _ in range(2):
         assert_close(gpu_gated_far(inp, workspace=ws), ref, "gated far, stale workspace")
+
+
+def test_gated_far_calls_leave_the_counters_at_zero():
+    """The single launch's far part and splits raise ready flags in the workspace's counter
+    region: gated one-row far calls of several shapes on one workspace (stale bytes past the
+    counters) each match the oracle and leave the counters all zero."""
+    _case("gated far calls, shared workspace")
+    shapes = [CASES[0], CASES[2], CASES[3], CASES[4], CASES[0]]
+    need = max(B.gated_far_workspace_bytes(*c[:6]) for c in shapes)
+    ws = B.Workspace(DEV)
+    ws.get(need)
+    ws.buf[64 * 1024:] = 0x55
+    for shape in shapes:
+        inp = _inputs(shape)
+        assert_close(gpu_gated_far(inp, workspace=ws), oracle.window_gated_far(inp),
+                     f"gated far {shape}")
+        assert int(torch.count_nonzero(ws.buf[:64 * 1024])) == 0, f"counters left set after {shape}"

@@ -303,7 +303,8 @@ int attn_window_check_meta(const attn_ring_meta* host_meta, int ng, int w);
  * matrix-core kernel on 16x16 tiles, 64 per block: 9 to 256 query vectors per group, and every
  * width above 8 at d > 128) or 5 (single-launch register kernel streaming the rings in slot
  * order, up to 8 query vectors: every query of a group in one block; the group's last splits
- * merge); query_block = query vectors per workgroup; splits = key splits reserved per query
+ * merge; it also takes one-row attn_window_chunk_far and attn_window_gated_far calls, with the
+ * far part in its launch); query_block = query vectors per workgroup; splits = key splits reserved per query
  * block; keys_per_split = keys each split covers at most. Output pointers may be NULL.
  * Returns 0 or WINATTN_EINVAL. */
 int attn_window_chunk_plan(int rows, int ng, int hpg, int d, int w, int ns, int* kernel,
